@@ -1,0 +1,132 @@
+"""Float64 reference of DoSA's certified pruning for the indexer Top-K.
+
+TEST INFRASTRUCTURE ONLY.
+
+Sources:
+* DoSA reading notes (notes.kuangjux.top, "DoSA: Dots Sparse Attention"),
+  annotation LBKERZAW, the three-step prefill flow (paper sections 2.2-2.4):
+  1. seeds: at least K distinct visible keys, scored with all heads; tau is
+     their K-th highest score, which cannot exceed the true K-th score;
+  2. bound: exact retained-head terms, plus an upper bound on the omitted
+     positive-weight heads (projection onto the retained heads plus a
+     residual term prepared per query), minus a lower bound on the omitted
+     negative-weight heads' penalty (their queries folded by |w| into one
+     vector, then a single ReLU, which never exceeds the sum of ReLUs);
+     a key is excluded only if its bound is strictly below tau;
+  3. survivors are scored with all heads, those below tau are dropped, the
+     rest merge with the seed Top-K and the final K is chosen by exact score.
+* 机器之心 article on DoSA (163.com), section 03: the same two quantities
+  (threshold lower bound, per-candidate upper bound) and strict exclusion.
+
+The bound here is written term by term in that order; the GPU folds the same
+terms into per-retained-head coefficients, which is algebraically equal.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .indexer import index_score_row, topk_row
+
+
+def seed_threshold(seed_scores: np.ndarray, k: int) -> float:
+    """tau = K-th highest full score among the seeds (-inf if fewer than K seeds)."""
+    s = np.asarray(seed_scores, np.float64)
+    if s.size < k:
+        return -np.inf
+    return float(np.sort(s)[::-1][k - 1])
+
+
+def project_positive_heads(q_row: np.ndarray, retained: np.ndarray, positive: np.ndarray):
+    """Least-squares coefficients C [|P|, |R|] and residuals r_j = q_j - C_j Q_R.
+
+    Any C gives a valid bound; least squares makes the residuals small.
+    """
+    QR = np.asarray(q_row, np.float64)[retained]  # [|R|, d]
+    QP = np.asarray(q_row, np.float64)[positive]  # [|P|, d]
+    if len(positive) == 0 or len(retained) == 0:
+        C = np.zeros((len(positive), len(retained)))
+    else:
+        C = np.linalg.lstsq(QR.T, QP.T, rcond=None)[0].T  # [|P|, |R|]
+    resid = QP - C @ QR
+    return C, resid
+
+
+def upper_bound(
+    q_row: np.ndarray,
+    w_row: np.ndarray,
+    keys: np.ndarray,
+    retained,
+    neg_fold=None,
+) -> np.ndarray:
+    """Certified upper bound U(s) >= I(s) for every key row in ``keys``.
+
+    q_row [H, d], w_row [H], keys [n, d]; ``retained`` is the set R of heads
+    scored exactly; ``neg_fold`` is the subset N' of omitted negative-weight
+    heads folded into the penalty (default: all of them).
+    """
+    q = np.asarray(q_row, np.float64)
+    w = np.asarray(w_row, np.float64)
+    K = np.asarray(keys, np.float64)
+    H = q.shape[0]
+    R = np.asarray(sorted(set(int(i) for i in retained)), dtype=np.int64)
+    omitted = np.setdiff1d(np.arange(H), R)
+    P = omitted[w[omitted] > 0]
+    Nn = omitted[w[omitted] < 0]
+    Nf = Nn if neg_fold is None else np.asarray(sorted(set(int(j) for j in neg_fold)), dtype=np.int64)
+    if not set(Nf.tolist()) <= set(Nn.tolist()):
+        raise ValueError("the folded set must hold only omitted negative-weight heads")
+    knorm = np.linalg.norm(K, axis=1)
+
+    # retained heads, exact
+    d = q[R] @ K.T  # [|R|, n]
+    retained_term = w[R] @ np.maximum(d, 0.0)
+
+    # omitted positive heads: q_j = sum_i C_ji q_i + r_j, and
+    # ReLU(a + b) <= ReLU(a) + ReLU(b), ReLU(c x) = c ReLU(x) (c >= 0),
+    # r_j . k <= |r_j| |k|.
+    C, resid = project_positive_heads(q, R, P)
+    Cp, Cm = np.maximum(C, 0.0), np.maximum(-C, 0.0)
+    per_head = Cp @ np.maximum(d, 0.0) + Cm @ np.maximum(-d, 0.0)  # [|P|, n]
+    per_head = per_head + np.linalg.norm(resid, axis=1)[:, None] * knorm[None, :]
+    positive_term = w[P] @ per_head
+
+    # omitted negative heads: sum_j |w_j| ReLU(x_j) >= ReLU(sum_{j in N'} |w_j| x_j)
+    q_neg = np.abs(w[Nf]) @ q[Nf] if Nf.size else np.zeros(q.shape[1])
+    penalty = np.maximum(K @ q_neg, 0.0)
+
+    return retained_term + positive_term - penalty
+
+
+def pruned_topk_row(
+    q_row: np.ndarray,
+    w_row: np.ndarray,
+    keys_visible: np.ndarray,
+    k: int,
+    seeds: np.ndarray,
+    retained,
+    neg_fold=None,
+):
+    """The whole DoSA flow for one query row, in float64.
+
+    Returns (selected indices, tau, survivor mask over non-seed keys).
+    The selection equals ``topk_row`` of all visible scores; that identity is
+    what the pruning must preserve.
+    """
+    n = keys_visible.shape[0]
+    seeds = np.asarray(seeds, np.int64)
+    seeds = seeds[seeds < n]
+    seed_scores = index_score_row(q_row, keys_visible[seeds], w_row)
+    tau = seed_threshold(seed_scores, k)
+    seed_keep = seeds[topk_row(seed_scores, k)]
+
+    rest = np.setdiff1d(np.arange(n), seeds)
+    U = upper_bound(q_row, w_row, keys_visible[rest], retained, neg_fold)
+    survive = U >= tau  # exclude only when strictly below
+    cand = rest[survive]
+    exact = index_score_row(q_row, keys_visible[cand], w_row)
+    kept = cand[exact >= tau]
+
+    pool = np.concatenate([seed_keep, kept])
+    pool_scores = index_score_row(q_row, keys_visible[pool], w_row)
+    order = np.lexsort((pool, -pool_scores))
+    return pool[order[: min(int(k), n)]], tau, survive

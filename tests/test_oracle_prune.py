@@ -1,0 +1,120 @@
+"""Pins of the float64 pruning reference (seed threshold and upper bound).
+
+The facts pinned: the seed threshold never exceeds the true K-th score; the
+bound never falls below the true score, on random, clustered and adversarial
+rows; with every head retained the bound is the score itself; the whole
+seed -> bound -> refine -> merge flow returns the plain Top-K; and a planted
+mistake (the residual term dropped) is caught by the same checks.
+"""
+import numpy as np
+import pytest
+
+from dsa_lightning_indexer_04_amd import inputs
+from oracle import indexer, prune
+
+
+def _row(seed, dist="iid", n=600):
+    d = inputs.make_inputs(1, 1, n, "bf16", dist, pos_start=n - 1, seed=seed)
+    qf, kf = indexer.dequantize(inputs.to_bits(d["q"]), inputs.to_bits(d["k"]), "bf16")
+    return qf[0, 0], kf[0], d["w"].numpy()[0, 0].astype(np.float64)
+
+
+def test_relu_fold_inequality():
+    # ReLU(sum_j a_j x_j) <= sum_j a_j ReLU(x_j) for a_j >= 0 (the folded penalty)
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        a = rng.random(7) * 3
+        x = rng.standard_normal(7)
+        assert max(a @ x, 0) <= a @ np.maximum(x, 0) + 1e-15
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_seed_threshold_below_true_kth(seed):
+    q, K, w = _row(seed, "clustered")
+    s = indexer.index_score_row(q, K, w)
+    rng = np.random.default_rng(seed)
+    k = 50
+    for ns in (50, 120, 400):
+        seeds = np.sort(rng.choice(K.shape[0], ns, replace=False))
+        tau = prune.seed_threshold(s[seeds], k)
+        assert tau <= indexer.kth_score(s, k)
+
+
+def test_seeds_equal_all_keys_gives_exact_kth():
+    q, K, w = _row(11)
+    s = indexer.index_score_row(q, K, w)
+    tau = prune.seed_threshold(s, 64)
+    assert tau == indexer.kth_score(s, 64)
+    assert prune.seed_threshold(s[:10], 64) == -np.inf
+
+
+@pytest.mark.parametrize("dist", ["iid", "clustered"])
+@pytest.mark.parametrize("nret", [0, 1, 8, 16, 40])
+def test_upper_bound_dominates_score(dist, nret):
+    rng = np.random.default_rng(nret + (100 if dist == "clustered" else 0))
+    for seed in range(3):
+        q, K, w = _row(seed + 20, dist)
+        R = rng.choice(64, nret, replace=False)
+        I = indexer.index_score_row(q, K, w)
+        U = prune.upper_bound(q, w, K, R)
+        scale = np.abs(w) @ np.linalg.norm(q, axis=1) * np.linalg.norm(K, axis=1)
+        assert np.all(U >= I - 1e-12 * scale)
+        # a random subset of the negative heads folded is still a valid bound
+        omitted = np.setdiff1d(np.arange(64), R)
+        neg = omitted[w[omitted] < 0]
+        sub = neg[rng.random(neg.size) < 0.5]
+        U2 = prune.upper_bound(q, w, K, R, neg_fold=sub)
+        assert np.all(U2 >= I - 1e-12 * scale)
+
+
+def test_upper_bound_adversarial_rows():
+    rng = np.random.default_rng(9)
+    d = 128
+    K = np.concatenate([rng.standard_normal((200, d)), np.zeros((2, d)), 1e6 * rng.standard_normal((3, d))])
+    base = rng.standard_normal((4, d))
+    # collinear retained heads and heads that are exact combinations of them
+    q = np.concatenate([base, base[:1] * 2.0, base[:2].sum(0, keepdims=True), rng.standard_normal((58, d))])
+    for w in (rng.standard_normal(64), -np.abs(rng.standard_normal(64)), np.abs(rng.standard_normal(64))):
+        I = indexer.index_score_row(q, K, w)
+        for R in ([0, 4, 5], [0, 1, 2, 3], list(range(64))[::3], []):
+            U = prune.upper_bound(q, w, K, R)
+            scale = np.abs(w) @ np.linalg.norm(q, axis=1) * np.linalg.norm(K, axis=1)
+            assert np.all(U >= I - 1e-12 * (scale + 1))
+    # zero keys: score and bound are both 0
+    assert np.all(prune.upper_bound(q, w, np.zeros((3, d)), [0, 1]) == 0)
+
+
+def test_all_heads_retained_bound_is_score():
+    q, K, w = _row(3)
+    I = indexer.index_score_row(q, K, w)
+    U = prune.upper_bound(q, w, K, np.arange(64))
+    np.testing.assert_allclose(U, I, rtol=1e-12, atol=1e-12)
+
+
+def test_dropping_the_residual_breaks_the_bound(monkeypatch):
+    # plant a mistake in the oracle (residual norms forced to zero) and check
+    # that the dominance test above would catch it
+    q, K, w = _row(5, "iid")
+    I = indexer.index_score_row(q, K, w)
+    R = np.arange(4)
+    orig = prune.project_positive_heads
+
+    def no_residual(q_row, retained, positive):
+        C, r = orig(q_row, retained, positive)
+        return C, np.zeros_like(r)
+
+    monkeypatch.setattr(prune, "project_positive_heads", no_residual)
+    U = prune.upper_bound(q, w, K, R)
+    assert np.any(U < I - 1e-9)
+
+
+@pytest.mark.parametrize("dist,nret", [("iid", 16), ("clustered", 16), ("clustered", 4), ("iid", 0)])
+def test_pruned_flow_equals_plain_topk(dist, nret):
+    q, K, w = _row(30 + nret, dist, n=2000)
+    k = 64
+    seeds = inputs.evenly_spaced_seeds(384, K.shape[0] - 1)
+    R = np.argsort(-np.abs(w))[:nret]
+    sel, tau, survive = prune.pruned_topk_row(q, w, K, k, seeds, R)
+    ref = indexer.topk_row(indexer.index_score_row(q, K, w), k)
+    assert sorted(sel.tolist()) == sorted(ref.tolist())
+    assert tau <= indexer.kth_score(indexer.index_score_row(q, K, w), k)
