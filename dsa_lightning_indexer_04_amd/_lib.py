@@ -1,0 +1,260 @@
+"""ctypes binding of libdsa_indexer.so.
+
+Argument marshalling only: tensors supply device pointers, torch's current
+HIP stream supplies the stream, and torch allocates outputs and workspace.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  If the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
+
+DSA_BF16, DSA_FP8_E4M3 = 0, 1
+DSA_OP_SCORES, DSA_OP_TOPK, DSA_OP_TOPK_PRUNED = 0, 1, 2
+ERR = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
+
+
+class Inputs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q", ctypes.c_int32),
+        ("num_k", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("w", ctypes.c_void_p),
+        ("q_scale", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p),
+    ]
+
+
+class PruneOpts(ctypes.Structure):
+    _fields_ = [
+        ("num_seeds", ctypes.c_int32),
+        ("num_retained", ctypes.c_int32),
+        ("seed_idx", ctypes.c_void_p),
+        ("force_recover", ctypes.c_void_p),
+    ]
+
+
+class PruneStats(ctypes.Structure):
+    _fields_ = [
+        ("tau", ctypes.c_void_p),
+        ("screened", ctypes.c_void_p),
+        ("survivors", ctypes.c_void_p),
+        ("recovered", ctypes.c_void_p),
+        ("upper_bound", ctypes.c_void_p),
+    ]
+
+
+EXPORTED = [
+    "dsa_indexer_scores",
+    "dsa_indexer_topk",
+    "dsa_indexer_topk_pruned",
+    "dsa_indexer_workspace_bytes",
+    "dsa_indexer_error_string",
+    "dsa_indexer_last_error",
+]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m dsa_lightning_indexer_04_amd.build_lib` "
+            "(the indexer has no non-HIP fallback)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.dsa_indexer_scores.argtypes = [ctypes.POINTER(Inputs), P, P]
+    lib.dsa_indexer_scores.restype = ctypes.c_int
+    lib.dsa_indexer_topk.argtypes = [ctypes.POINTER(Inputs), I32, P, P, P, SZ, P]
+    lib.dsa_indexer_topk.restype = ctypes.c_int
+    lib.dsa_indexer_topk_pruned.argtypes = [
+        ctypes.POINTER(Inputs),
+        I32,
+        ctypes.POINTER(PruneOpts),
+        P,
+        P,
+        ctypes.POINTER(PruneStats),
+        P,
+        SZ,
+        P,
+    ]
+    lib.dsa_indexer_topk_pruned.restype = ctypes.c_int
+    lib.dsa_indexer_workspace_bytes.argtypes = [ctypes.c_int, ctypes.POINTER(Inputs), I32, ctypes.POINTER(PruneOpts)]
+    lib.dsa_indexer_workspace_bytes.restype = SZ
+    lib.dsa_indexer_error_string.argtypes = [ctypes.c_int]
+    lib.dsa_indexer_error_string.restype = ctypes.c_char_p
+    lib.dsa_indexer_last_error.argtypes = []
+    lib.dsa_indexer_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class IndexerError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        super().__init__(f"{ERR.get(code, code)}: {detail}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        raise IndexerError(rc, lib.dsa_indexer_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_inputs_struct(q, k, w, positions, q_scale=None, k_scale=None, *, heads=None, head_dim=None) -> Inputs:
+    """Build the C inputs struct from device tensors.
+
+    q [B,Q,H,d] (bf16 or float8_e4m3fn), k [B,N,d], w [B,Q,H] fp32,
+    positions [B,Q] int32, q_scale [B,Q] / k_scale [B,N] fp32 (fp8 only).
+    """
+    if q.dtype == torch.bfloat16:
+        dt = DSA_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dt = DSA_FP8_E4M3
+    else:
+        raise TypeError(f"unsupported q dtype {q.dtype}")
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must share a dtype")
+    for name, t in (("q", q), ("k", k), ("w", w), ("positions", positions), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if w.dtype != torch.float32 or positions.dtype != torch.int32:
+        raise TypeError("w must be float32 and positions int32")
+    B, Q, H, D = q.shape
+    N = k.shape[1]
+    return Inputs(
+        B,
+        Q,
+        N,
+        H if heads is None else heads,
+        D if head_dim is None else head_dim,
+        dt,
+        _ptr(q),
+        _ptr(k),
+        _ptr(w),
+        _ptr(q_scale),
+        _ptr(k_scale),
+        _ptr(positions),
+    )
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(op: int, inp: Inputs, topk: int = 0, opts: PruneOpts | None = None) -> int:
+    lib = load()
+    n = lib.dsa_indexer_workspace_bytes(op, ctypes.byref(inp), topk, ctypes.byref(opts) if opts else None)
+    if n == 0 and op != DSA_OP_SCORES:
+        detail = lib.dsa_indexer_last_error().decode()
+        if detail:
+            raise IndexerError(1, detail)
+    return n
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte (or better) aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def scores(q, k, w, positions, q_scale=None, k_scale=None) -> torch.Tensor:
+    """[B,Q,N] fp32 index scores, -inf where the key is not visible."""
+    lib = load()
+    inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
+    out = torch.empty((q.shape[0], q.shape[1], k.shape[1]), dtype=torch.float32, device=q.device)
+    _check(lib.dsa_indexer_scores(ctypes.byref(inp), _ptr(out), _stream()))
+    return out
+
+
+def topk(q, k, w, positions, topk: int, q_scale=None, k_scale=None, return_scores: bool = True, workspace=None):
+    """Exact per-row Top-K: (idx [B,Q,topk] int32 with -1 padding, scores or None)."""
+    lib = load()
+    inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
+    nbytes = workspace_bytes(DSA_OP_TOPK, inp, topk)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    B, Q = q.shape[:2]
+    idx = torch.empty((B, Q, topk), dtype=torch.int32, device=q.device)
+    sc = torch.empty((B, Q, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    _check(lib.dsa_indexer_topk(ctypes.byref(inp), topk, _ptr(idx), _ptr(sc), _ptr(ws), ws.numel(), _stream()))
+    return idx, sc
+
+
+def topk_pruned(
+    q,
+    k,
+    w,
+    positions,
+    topk: int,
+    q_scale=None,
+    k_scale=None,
+    *,
+    num_seeds: int = 0,
+    num_retained: int = 0,
+    seed_idx=None,
+    force_recover=None,
+    return_scores: bool = True,
+    stats: bool = False,
+    upper_bound: bool = False,
+    workspace=None,
+):
+    """Exact per-row Top-K with certified pruning; same index set as topk().
+
+    Returns (idx, scores or None, stats dict or None).  stats holds per-row
+    tau, screened, survivors, recovered (and the debug upper bounds if asked).
+    """
+    lib = load()
+    inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
+    opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover))
+    nbytes = workspace_bytes(DSA_OP_TOPK_PRUNED, inp, topk, opts)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    B, Q = q.shape[:2]
+    dev = q.device
+    idx = torch.empty((B, Q, topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, Q, topk), dtype=torch.float32, device=dev) if return_scores else None
+    st = None
+    cst = PruneStats()
+    if stats or upper_bound:
+        st = {
+            "tau": torch.empty((B, Q), dtype=torch.float32, device=dev),
+            "screened": torch.empty((B, Q), dtype=torch.int32, device=dev),
+            "survivors": torch.empty((B, Q), dtype=torch.int32, device=dev),
+            "recovered": torch.empty((B, Q), dtype=torch.uint8, device=dev),
+        }
+        if upper_bound:
+            st["upper_bound"] = torch.empty((B, Q, k.shape[1]), dtype=torch.float32, device=dev)
+        cst = PruneStats(*(_ptr(st.get(n)) for n in ("tau", "screened", "survivors", "recovered", "upper_bound")))
+    _check(
+        lib.dsa_indexer_topk_pruned(
+            ctypes.byref(inp),
+            topk,
+            ctypes.byref(opts),
+            _ptr(idx),
+            _ptr(sc),
+            ctypes.byref(cst),
+            _ptr(ws),
+            ws.numel(),
+            _stream(),
+        )
+    )
+    return idx, sc, st

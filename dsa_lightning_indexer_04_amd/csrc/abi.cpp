@@ -1,0 +1,227 @@
+// abi.cpp -- the C ABI: argument checks, workspace layout, launch order.
+//
+// Nothing here allocates, frees or synchronises; all work goes on the
+// caller's stream.  See include/dsa_indexer.h for the contract.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/dsa_indexer.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == DSA_BF16 ? 2 : 1; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + bytes};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_inputs(const dsa_indexer_inputs* in) {
+  if (!in) return fail(DSA_ERR_INVALID_ARG, "inputs struct is NULL");
+  if (in->batch < 1 || in->num_q < 1 || in->num_k < 1)
+    return fail(DSA_ERR_INVALID_ARG, "batch, num_q and num_k must be >= 1");
+  if (in->heads != 64) return fail(DSA_ERR_UNSUPPORTED, "heads must be 64");
+  if (in->head_dim != 128) return fail(DSA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (in->dtype != DSA_BF16 && in->dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "unknown dtype");
+  if (!in->q || !in->k || !in->w || !in->positions) return fail(DSA_ERR_INVALID_ARG, "q, k, w, positions required");
+  if (in->dtype == DSA_FP8_E4M3) {
+    if (!in->q_scale || !in->k_scale) return fail(DSA_ERR_INVALID_ARG, "fp8 inputs need q_scale and k_scale");
+  } else if (in->q_scale || in->k_scale) {
+    return fail(DSA_ERR_INVALID_ARG, "bf16 inputs take no scales");
+  }
+  const void* ptrs[] = {in->q, in->k, in->w, in->positions, in->q_scale, in->k_scale};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "input pointers must be 16-byte aligned");
+  const uint64_t rows = (uint64_t)in->batch * in->num_q;
+  if (rows > (1ull << 31) || (uint64_t)in->batch * in->num_k > (1ull << 40))
+    return fail(DSA_ERR_INVALID_ARG, "problem too large");
+  return DSA_OK;
+}
+
+dsa::Problem problem_of(const dsa_indexer_inputs* in) {
+  return dsa::Problem{in->batch,
+                      in->num_q,
+                      in->num_k,
+                      in->dtype,
+                      static_cast<const uint8_t*>(in->q),
+                      static_cast<const uint8_t*>(in->k),
+                      in->w,
+                      in->q_scale,
+                      in->k_scale,
+                      in->positions};
+}
+
+// Input byte ranges, for output-aliasing checks.
+int check_no_alias(const dsa_indexer_inputs* in, Range out) {
+  const size_t eb = elem_bytes(in->dtype);
+  const uint64_t B = in->batch, Q = in->num_q, N = in->num_k;
+  Range r[] = {span(in->q, B * Q * 64 * 128 * eb), span(in->k, B * N * 128 * eb), span(in->w, B * Q * 64 * 4),
+               span(in->positions, B * Q * 4)};
+  for (const Range& x : r)
+    if (overlaps(x, out)) return fail(DSA_ERR_INVALID_ARG, "an output aliases an input");
+  if (in->q_scale && overlaps(span(in->q_scale, B * Q * 4), out))
+    return fail(DSA_ERR_INVALID_ARG, "an output aliases an input");
+  if (in->k_scale && overlaps(span(in->k_scale, B * N * 4), out))
+    return fail(DSA_ERR_INVALID_ARG, "an output aliases an input");
+  return DSA_OK;
+}
+
+int check_topk(int32_t topk) {
+  if (topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1");
+  if (topk > 4096) return fail(DSA_ERR_UNSUPPORTED, "topk must be <= 4096");
+  return DSA_OK;
+}
+
+// Few query-row groups cannot fill the GPU with one workgroup per 8 rows:
+// such calls (decode) score rows split across the key axis into a stored
+// [B*Q, N] row block and select from it.
+bool use_split_rows(const dsa_indexer_inputs* in) {
+  // DSA_INDEXER_TOPK_PATH=split|stream pins the choice (tests cover both on small shapes)
+  if (const char* f = std::getenv("DSA_INDEXER_TOPK_PATH")) {
+    if (std::strcmp(f, "split") == 0) return true;
+    if (std::strcmp(f, "stream") == 0) return false;
+  }
+  const uint64_t groups = (uint64_t)in->batch * ((in->num_q + 7) / 8);
+  const uint64_t row_bytes = (uint64_t)in->batch * in->num_q * in->num_k * 4;
+  return groups < 256 && row_bytes <= (8ull << 30);
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t topk_workspace(const dsa_indexer_inputs* in, int32_t topk) {
+  const uint64_t rows = (uint64_t)in->batch * in->num_q;
+  if (use_split_rows(in)) return round_up(rows * in->num_k * 4, 256);
+  return round_up(rows * (uint64_t)dsa::stream_capacity(topk) * 8, 256);
+}
+
+int hip_status(hipError_t e) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+  return DSA_OK;
+}
+
+int run_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float* out_score, void* workspace,
+             hipStream_t st) {
+  const dsa::Problem p = problem_of(in);
+  if (use_split_rows(in)) {
+    float* rows = static_cast<float*>(workspace);
+    int rc = hip_status(dsa::launch_scores(p, rows, st));
+    if (rc) return rc;
+    return hip_status(dsa::launch_select_rows(p, rows, topk, out_idx, out_score, st));
+  }
+  return hip_status(dsa::launch_topk_stream(p, topk, dsa::stream_capacity(topk), static_cast<uint64_t*>(workspace),
+                                            out_idx, out_score, st));
+}
+
+int check_topk_outputs(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float* out_score,
+                       void* workspace, size_t workspace_bytes, size_t need) {
+  if (!out_idx) return fail(DSA_ERR_INVALID_ARG, "out_idx is required");
+  if (!aligned16(out_idx) || (out_score && !aligned16(out_score)))
+    return fail(DSA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  const uint64_t n = (uint64_t)in->batch * in->num_q * topk;
+  int rc = check_no_alias(in, span(out_idx, n * 4));
+  if (rc) return rc;
+  if (out_score) {
+    if ((rc = check_no_alias(in, span(out_score, n * 4)))) return rc;
+    if (overlaps(span(out_idx, n * 4), span(out_score, n * 4)))
+      return fail(DSA_ERR_INVALID_ARG, "out_idx and out_score overlap");
+  }
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(DSA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (need && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (need) {
+    Range ws = span(workspace, need);
+    if ((rc = check_no_alias(in, ws))) return rc;
+    if (overlaps(ws, span(out_idx, n * 4)) || (out_score && overlaps(ws, span(out_score, n * 4))))
+      return fail(DSA_ERR_INVALID_ARG, "workspace overlaps an output");
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_indexer_scores(const dsa_indexer_inputs* in, float* scores, void* stream) {
+  int rc = check_inputs(in);
+  if (rc) return rc;
+  if (!scores) return fail(DSA_ERR_INVALID_ARG, "scores output is required");
+  if (!aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "scores must be 16-byte aligned");
+  if ((rc = check_no_alias(in, span(scores, (uint64_t)in->batch * in->num_q * in->num_k * 4)))) return rc;
+  return hip_status(dsa::launch_scores(problem_of(in), scores, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float* out_score,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_inputs(in);
+  if (rc) return rc;
+  if ((rc = check_topk(topk))) return rc;
+  const size_t need = topk_workspace(in, topk);
+  if ((rc = check_topk_outputs(in, topk, out_idx, out_score, workspace, workspace_bytes, need))) return rc;
+  return run_topk(in, topk, out_idx, out_score, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t topk, const dsa_prune_opts* opts) {
+  (void)opts;
+  if (check_inputs(in)) return 0;
+  if (op == DSA_OP_SCORES) return 0;
+  if (check_topk(topk)) return 0;
+  if (op == DSA_OP_TOPK) return topk_workspace(in, topk);
+  fail(DSA_ERR_INVALID_ARG, "unknown op");
+  return 0;
+}
+
+int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const dsa_prune_opts* opts,
+                            int32_t* out_idx, float* out_score, const dsa_prune_stats* stats, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  (void)opts;
+  (void)stats;
+  (void)in;
+  (void)topk;
+  (void)out_idx;
+  (void)out_score;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  return fail(DSA_ERR_UNSUPPORTED, "pruned path not built yet");
+}
+
+const char* dsa_indexer_error_string(int code) {
+  switch (code) {
+    case DSA_OK:
+      return "ok";
+    case DSA_ERR_INVALID_ARG:
+      return "invalid argument";
+    case DSA_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case DSA_ERR_WORKSPACE:
+      return "workspace too small";
+    case DSA_ERR_HIP:
+      return "HIP error";
+    default:
+      return "unknown error";
+  }
+}
+
+const char* dsa_indexer_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

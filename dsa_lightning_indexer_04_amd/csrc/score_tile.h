@@ -1,0 +1,187 @@
+// score_tile.h -- the one device routine that scores (query, key) pairs.
+//
+// Index score (DeepSeek DSA FLOPs notes, section "Lightning Indexer FLOPs",
+// the index-score equation):  I[t,s] = sum_j w[t,j] ReLU(q[t,j,:] . k[s,:]),
+// 64 heads of 128, one key row shared by every head.
+//
+// Every path of the library (full score matrix, streaming Top-K, seed
+// rescoring, survivor refinement) computes a pair's score with the code in
+// this file, so a pair's fp32 score is bit-identical whichever path, tile or
+// column position produced it.  That is what lets the pruned Top-K return
+// exactly the unpruned index set.
+//
+// MFMA mapping (gfx950, wave64):
+//   rows (M) = heads: two 32-row blocks per query (heads 0..31, 32..63)
+//   cols (N) = 32 keys
+//   K        = the 128 feature dims.  Both operands use the same lane->dim
+//              permutation: lane l (half h = l/32) feeds dims 64h..64h+63,
+//              so each lane reads one contiguous run of its row.
+// bf16: v_mfma_f32_32x32x16_bf16, 8 k-steps of 16 (lane: 8 dims per step).
+// fp8 : v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales, 2 k-steps of 64
+//       (lane: 32 dims per step), OCP e4m3 operands.
+// Accumulator layout (32x32 blocks): lane l, register v holds
+//   row 8*(v/4) + 4*(l/32) + (v%4), column l%32.
+// So each lane holds 16 heads of each block for one key; the head sum is
+// lane-local over 32 heads, then one cross-half exchange adds the other 32.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kHeads = 64;
+constexpr int kDim = 128;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+enum : int { kBF16 = 0, kFP8 = 1 };
+
+template <int DT>
+struct Frag;  // per-lane operand fragment of one 32-row (or 32-key) block, K = 128
+
+template <>
+struct Frag<kBF16> {
+  static constexpr int kSteps = 8;        // 8 x (32x32x16)
+  static constexpr int kRowBytes = 256;   // 128 bf16
+  static constexpr int kLaneBytes = 128;  // contiguous bytes one lane feeds
+  u32x4 v[8];
+};
+
+template <>
+struct Frag<kFP8> {
+  static constexpr int kSteps = 2;        // 2 x (32x32x64)
+  static constexpr int kRowBytes = 128;   // 128 e4m3 codes
+  static constexpr int kLaneBytes = 64;
+  i32x8 v[2];
+};
+
+// Load one lane's fragment of a row (query head row or key row) from any
+// address space: `row` points at the start of the row (kRowBytes long).
+template <int DT>
+__device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* row, int lane) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(row + (lane >> 5) * Frag<DT>::kLaneBytes);
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = p[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32x4 lo = p[2 * i], hi = p[2 * i + 1];
+      f.v[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  }
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// acc += A(32 rows) x B(32 keys)^T over K = 128.
+template <int DT>
+__device__ __forceinline__ f32x16 mma_block(const Frag<DT>& a, const Frag<DT>& b, f32x16 acc) {
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[i]),
+                                                     __builtin_bit_cast(bf16x8, b.v[i]), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v[i], b.v[i], acc, 0, 0, 0, 127, 0, 127);
+  }
+  return acc;
+}
+
+// The query side of a score: 64 head rows as two A fragments plus this
+// lane's 32 head weights, wl[blk][v] = w[32*blk + 8*(v/4) + 4*(lane/32) + v%4].
+template <int DT>
+struct QuerySide {
+  Frag<DT> a[2];
+  float wl[2][16];
+};
+
+// q_heads: the query's [64][128] rows; w_row: its 64 weights.
+template <int DT>
+__device__ __forceinline__ void load_query(QuerySide<DT>& qs, const uint8_t* q_heads, const float* w_row,
+                                           int lane) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+    load_frag<DT>(qs.a[blk], q_heads + (size_t)(32 * blk + r) * Frag<DT>::kRowBytes, lane);
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) qs.wl[blk][v] = w_row[32 * blk + 8 * (v >> 2) + 4 * h + (v & 3)];
+}
+
+// This lane's share of the head sum for its key column: 32 of the 64 heads,
+// in a fixed order (four chains of eight, then a fixed pairing).
+__device__ __forceinline__ float head_partial(const f32x16& s0, const f32x16& s1, const float (&wl)[2][16]) {
+  float c[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__builtin_fmaxf(s0[4 * g + e], 0.0f), wl[0][4 * g + e], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__builtin_fmaxf(s1[4 * g + e], 0.0f), wl[1][4 * g + e], acc);
+    c[g] = acc;
+  }
+  return (c[0] + c[1]) + (c[2] + c[3]);
+}
+
+// Full-head partial for one query against one 32-key block.
+template <int DT>
+__device__ __forceinline__ float query_partial(const QuerySide<DT>& qs, const Frag<DT>& kb) {
+  f32x16 s0 = mma_block<DT>(qs.a[0], kb, zero16());
+  f32x16 s1 = mma_block<DT>(qs.a[1], kb, zero16());
+  return head_partial(s0, s1, qs.wl);
+}
+
+// Cross-half exchange.  Lanes 0..31 hold partials (p0 of query A, p1 of
+// query B) over heads with (row/4) even, lanes 32..63 the other heads, for
+// key column l%32.  Returns, in lanes 0..31, A's full sum for key l; in
+// lanes 32..63, B's full sum for key l-32.  Each lane adds its own partial
+// and its partner's (lane^32); fp32 addition is commutative, so every path
+// gets the same bits for a (query, key) pair.
+// (The exchange goes through ds_bpermute: at -O3 this compiler folds the two
+// results of the gfx950 permlane32 swap builtin into one.)
+__device__ __forceinline__ float combine_halves(float p0, float p1, int lane) {
+  const bool lo = lane < 32;
+  const float own = lo ? p0 : p1;
+  const float send = lo ? p1 : p0;
+  return own + __shfl_xor(send, 32, 64);
+}
+
+// Single query: the full sum for key l%32 in every lane.
+__device__ __forceinline__ float combine_single(float p) { return p + __shfl_xor(p, 32, 64); }
+
+// Dequantisation of fp8 scores: (q_scale * k_scale) * head_sum, same order everywhere.
+__device__ __forceinline__ float apply_scales(float sum, float qscale, float kscale) {
+  return sum * (qscale * kscale);
+}
+
+// Monotone 32-bit code of a finite fp32 score (larger score -> larger code);
+// -0 maps like +0.
+__device__ __forceinline__ uint32_t mono_code(float s) {
+  uint32_t u = __builtin_bit_cast(uint32_t, s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float mono_decode(uint32_t c) {
+  uint32_t u = (c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c;
+  return __builtin_bit_cast(float, u);
+}
+// 64-bit record: larger record = larger score, then smaller key index.
+__device__ __forceinline__ uint64_t make_record(float s, uint32_t key) {
+  return ((uint64_t)mono_code(s) << 32) | (uint64_t)(0xFFFFFFFFu - key);
+}
+__device__ __forceinline__ uint32_t record_key(uint64_t r) { return 0xFFFFFFFFu - (uint32_t)r; }
+__device__ __forceinline__ float record_score(uint64_t r) { return mono_decode((uint32_t)(r >> 32)); }
+
+}  // namespace dsa

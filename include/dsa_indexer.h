@@ -1,0 +1,161 @@
+/*
+ * dsa_indexer.h -- C ABI of the MI355X (gfx950) lightning indexer with exact
+ * per-query Top-K and certified (DoSA) pruning.
+ *
+ * What is computed (DeepSeek DSA FLOPs notes, section "Lightning Indexer
+ * FLOPs", the index-score equation; query t, key s):
+ *
+ *     I[t,s] = sum_{j<H} w[t,j] * ReLU(q[t,j,:] . k[s,:])
+ *
+ * with H = 64 indexer heads of d = 128, one key row shared by all heads
+ * (section "Notation", indexer tensors Q^I (T,H^I,d^I), K^I (T,d^I),
+ * W^I (T,H^I)).  Key s is visible to query row t iff s <= positions[t]
+ * (section "Causal token-pair 数": the diagonal counts), and each row keeps
+ * the min(k, visible) best visible keys (the N_sel equation there).
+ * The pages fix no tie rule; this library orders by score descending, then
+ * key index ascending, in every path.
+ *
+ * For fp8 inputs (OCP e4m3fn codes), q_scale[t] (one per query token, shared
+ * by its heads) and k_scale[s] (one per key row) are the dequantisation
+ * scales: the score is the equation above on scale * code values, computed as
+ * (q_scale[t] * k_scale[s]) * sum_j w[t,j] ReLU(q8[t,j,:] . k8[s,:]),
+ * exact for positive scales.
+ *
+ * Conventions shared by all entry points
+ *  - Every array pointer is DEVICE memory owned by the caller, row-major and
+ *    contiguous, innermost dimension last, 16-byte aligned.  The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream`
+ *    (a hipStream_t; NULL is the default stream) and returns at once.
+ *  - Scores are fp32 computed with fp32 accumulation; every path uses the
+ *    same instruction sequence for a (t, s) pair, so a score is bit-identical
+ *    whichever entry point or tile produced it.
+ *  - Return value: DSA_OK (0) or an error code; the call enqueues nothing
+ *    when it returns an argument, support or workspace error.
+ *    dsa_indexer_last_error() gives a thread-local detail string.
+ *  - Device data (positions, finiteness of inputs) are preconditions and are
+ *    not inspected on the host.  Inputs must be finite.
+ *  - Calls on one stream are ordered; calls that share a workspace must not
+ *    run concurrently on different streams.
+ */
+#ifndef DSA_INDEXER_H_
+#define DSA_INDEXER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { DSA_BF16 = 0, DSA_FP8_E4M3 = 1 };
+
+enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, scales wrong for dtype */
+  DSA_ERR_UNSUPPORTED = 2, /* heads != 64, head_dim != 128, unknown dtype, topk out of range */
+  DSA_ERR_WORKSPACE = 3,   /* workspace smaller than dsa_indexer_workspace_bytes() */
+  DSA_ERR_HIP = 4          /* a HIP launch reported an error */
+};
+
+/* Shared inputs.  B = batch (independent sequences), Q = query rows per
+ * sequence, N = keys per sequence.
+ *   q          [B,Q,H,d]  bf16 bits (uint16) or e4m3fn codes (uint8)
+ *   k          [B,N,d]    same dtype as q
+ *   w          [B,Q,H]    fp32 head weights, any sign
+ *   q_scale    [B,Q]      fp32 > 0, fp8 only (must be NULL for bf16)
+ *   k_scale    [B,N]      fp32 > 0, fp8 only (must be NULL for bf16)
+ *   positions  [B,Q]      int32 absolute position of each query row; the
+ *                         row sees keys 0..min(positions, N-1); a negative
+ *                         position sees no key.                            */
+typedef struct dsa_indexer_inputs {
+  int32_t batch, num_q, num_k, heads, head_dim, dtype;
+  const void* q;
+  const void* k;
+  const float* w;
+  const float* q_scale;
+  const float* k_scale;
+  const int32_t* positions;
+} dsa_indexer_inputs;
+
+/* Full score matrix (the index-score equation for every pair).
+ *   scores [B,Q,N] fp32 out; -inf where the key is not visible.
+ * Intended for checking and small shapes: it writes B*Q*N floats.          */
+int dsa_indexer_scores(const dsa_indexer_inputs* in, float* scores, void* stream);
+
+/* Exact Top-K per query row without forming the score matrix in HBM.
+ *   topk       1..4096
+ *   out_idx    [B,Q,topk] int32 out: the min(topk, visible) selected key
+ *              indices first (in no particular order), then -1 padding
+ *   out_score  [B,Q,topk] fp32 out (score of each index; -inf at padding),
+ *              or NULL
+ *   workspace  device scratch of at least
+ *              dsa_indexer_workspace_bytes(DSA_OP_TOPK, in, topk, NULL) bytes,
+ *              256-byte aligned; contents on entry are ignored.
+ * Selection ties are broken by the smaller key index.                       */
+int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx,
+                     float* out_score, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of the pruned path (host struct; pass NULL for defaults).
+ *   num_seeds     seeds per sequence (0 -> 12288), clamped to the common
+ *                 visible prefix; seeds rescored with all heads fix the
+ *                 starting threshold tau (DoSA reading notes, annotation
+ *                 LBKERZAW, step 1)
+ *   num_retained  heads scored exactly when bounding (0 -> 15, at most 31);
+ *                 the bound also uses one folded negative-head row
+ *   seed_idx      [B,num_seeds] int32 device array of ascending, distinct
+ *                 key indices, or NULL for evenly spaced seeds
+ *                 floor(i*(p0+1)/S) over the common prefix 0..p0
+ *   force_recover [B,Q] uint8 device mask, or NULL: rows marked non-zero
+ *                 take the recovery (unpruned) path; for tests             */
+typedef struct dsa_prune_opts {
+  int32_t num_seeds;
+  int32_t num_retained;
+  const int32_t* seed_idx;
+  const uint8_t* force_recover;
+} dsa_prune_opts;
+
+/* Optional per-row statistics of the pruned path (device pointers, each may
+ * be NULL):
+ *   tau        [B,Q] fp32  threshold from the seeds (K-th seed score)
+ *   screened   [B,Q] int32 non-seed visible keys that were bounded
+ *   survivors  [B,Q] int32 keys whose bound reached the running threshold
+ *   recovered  [B,Q] uint8 1 if the row was recomputed by the unpruned path
+ *   upper_bound [B,Q,N] fp32 debug: the bound of every non-seed visible key
+ *              (NaN elsewhere); small shapes only, costs one extra pass    */
+typedef struct dsa_prune_stats {
+  float* tau;
+  int32_t* screened;
+  int32_t* survivors;
+  uint8_t* recovered;
+  float* upper_bound;
+} dsa_prune_stats;
+
+/* Exact Top-K with certified pruning (DoSA reading notes, annotation
+ * LBKERZAW; 机器之心 DoSA article, sections 03-04): seeds fix a threshold,
+ * a per-key upper bound from a few retained heads, projected positive heads
+ * with a residual term and a folded negative-head penalty excludes keys that
+ * cannot reach the Top-K, and survivors are rescored with all heads.
+ * Returns the same index set as dsa_indexer_topk, bit for bit.  Rows whose
+ * seeds are invalid (not ascending or duplicated), whose plan is not finite,
+ * or that are forced by opts->force_recover are recomputed by the unpruned
+ * path on the device.  Arguments as for dsa_indexer_topk, plus opts and
+ * stats; workspace from dsa_indexer_workspace_bytes(DSA_OP_TOPK_PRUNED, ...). */
+int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const dsa_prune_opts* opts,
+                            int32_t* out_idx, float* out_score, const dsa_prune_stats* stats,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+enum { DSA_OP_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_TOPK_PRUNED = 2 };
+
+/* Workspace bytes an entry point needs for these inputs (0 for scores).
+ * Returns 0 and sets the last error if the arguments are invalid.          */
+size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t topk,
+                                   const dsa_prune_opts* opts);
+
+/* Static name of an error code, and the calling thread's last error detail. */
+const char* dsa_indexer_error_string(int code);
+const char* dsa_indexer_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_INDEXER_H_ */

@@ -1,0 +1,95 @@
+"""Shared helpers of the tests: device transfer, oracle rows, checks."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_lightning_indexer_04_amd import inputs
+from oracle import indexer
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def to_device(d: dict, dev="cuda") -> dict:
+    out = {}
+    for key, v in d.items():
+        out[key] = v.to(dev) if isinstance(v, torch.Tensor) else v
+    return out
+
+
+def call_args(dd: dict):
+    return (dd["q"], dd["k"], dd["w"], dd["pos"]), dict(q_scale=dd["q_scale"], k_scale=dd["k_scale"])
+
+
+class OracleRows:
+    """Float64 oracle scores of selected rows of one CPU input set."""
+
+    def __init__(self, d: dict):
+        self.d = d
+        self.dtype = d["dtype"]
+        self.qbits = inputs.to_bits(d["q"])
+        self.kbits = inputs.to_bits(d["k"])
+        self.w = d["w"].numpy().astype(np.float64)
+        self.pos = d["pos"].numpy()
+        self.qs = None if d["q_scale"] is None else d["q_scale"].numpy()
+        self.ks = None if d["k_scale"] is None else d["k_scale"].numpy()
+        self.N = self.kbits.shape[1]
+        self._kf = {}
+
+    def keys(self, b: int) -> np.ndarray:
+        if b not in self._kf:
+            if self.dtype == "bf16":
+                self._kf[b] = indexer.decode_bf16(self.kbits[b])
+            else:
+                self._kf[b] = indexer.decode_e4m3fn(self.kbits[b]) * self.ks[b].astype(np.float64)[:, None]
+        return self._kf[b]
+
+    def visible(self, b: int, t: int) -> int:
+        return int(indexer.visible_count(self.pos[b, t], self.N))
+
+    def row(self, b: int, t: int) -> np.ndarray:
+        """Visible scores of row (b, t), float64."""
+        v = self.visible(b, t)
+        if self.dtype == "bf16":
+            q = indexer.decode_bf16(self.qbits[b, t])
+        else:
+            q = indexer.decode_e4m3fn(self.qbits[b, t]) * float(self.qs[b, t])
+        return indexer.index_score_row(q, self.keys(b)[:v], self.w[b, t])
+
+
+def tol(dtype: str):
+    return indexer.tolerance(dtype)
+
+
+def assert_rows_ok(orc: OracleRows, idx: np.ndarray, sc: np.ndarray | None, rows, k: int):
+    rtol, atol = tol(orc.dtype)
+    for b, t in rows:
+        ref = orc.row(b, t)
+        errs = indexer.check_topk_row(idx[b, t], ref, k, rtol, atol, None if sc is None else sc[b, t])
+        assert not errs, f"row ({b},{t}): {errs}"
+
+
+def lexsort_topk_of_scores(S_row: np.ndarray, vis: int, k: int) -> np.ndarray:
+    """Exact Top-K by sort over one row of (GPU) scores; total order score desc, idx asc."""
+    s = S_row[:vis].astype(np.float64)
+    order = np.lexsort((np.arange(vis), -s))
+    return np.sort(order[: min(k, vis)])
+
+
+def set_path(path: str | None):
+    if path is None:
+        os.environ.pop("DSA_INDEXER_TOPK_PATH", None)
+    else:
+        os.environ["DSA_INDEXER_TOPK_PATH"] = path

@@ -1,0 +1,95 @@
+"""The C-ABI library builds, loads and exports every declared symbol, and
+rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+LIB = os.path.join(ROOT, "dsa_lightning_indexer_04_amd", "libdsa_indexer.so")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdsa_indexer.so not built (run __graft_entry__.build())")
+    import torch  # noqa: F401  (share torch's HIP runtime)
+    from dsa_lightning_indexer_04_amd import _lib
+
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dsa_indexer_scores", "dsa_indexer_topk", "dsa_indexer_topk_pruned", "dsa_indexer_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\S+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every case below fails validation first
+
+
+def _inputs(_lib, **kw):
+    d = dict(batch=1, num_q=4, num_k=64, heads=64, head_dim=128, dtype=0, q=FAKE, k=FAKE * 2, w=FAKE * 3,
+             q_scale=None, k_scale=None, positions=FAKE * 4)
+    d.update(kw)
+    return _lib.Inputs(**d)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(heads=32), 2),
+        (dict(head_dim=64), 2),
+        (dict(dtype=7), 2),
+        (dict(num_q=0), 1),
+        (dict(batch=-1), 1),
+        (dict(q=None), 1),
+        (dict(q=FAKE + 4), 1),
+        (dict(dtype=1), 1),  # fp8 without scales
+        (dict(q_scale=FAKE * 5), 1),  # bf16 with a scale
+    ],
+)
+def test_invalid_inputs_are_rejected(lib, kw, code):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _inputs(_lib, **kw)
+    rc = lib.dsa_indexer_scores(ctypes.byref(inp), ctypes.c_void_p(FAKE * 8), None)
+    assert rc == code
+    assert lib.dsa_indexer_last_error()
+    rc = lib.dsa_indexer_topk(ctypes.byref(inp), 16, ctypes.c_void_p(FAKE * 8), None, None, 0, None)
+    assert rc == code
+
+
+def test_topk_argument_errors(lib):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _inputs(_lib)
+    out = ctypes.c_void_p(FAKE * 8)
+    assert lib.dsa_indexer_topk(ctypes.byref(inp), 0, out, None, None, 0, None) == 1
+    assert lib.dsa_indexer_topk(ctypes.byref(inp), 5000, out, None, None, 0, None) == 2
+    assert lib.dsa_indexer_topk(ctypes.byref(inp), 16, None, None, None, 0, None) == 1
+    # workspace too small
+    need = lib.dsa_indexer_workspace_bytes(1, ctypes.byref(inp), 16, None)
+    assert need > 0
+    assert lib.dsa_indexer_topk(ctypes.byref(inp), 16, out, None, ctypes.c_void_p(FAKE * 64), need - 1, None) == 3
+    # an output aliasing an input
+    assert lib.dsa_indexer_topk(ctypes.byref(inp), 16, ctypes.c_void_p(FAKE * 3), None, None, need, None) == 1
+    assert lib.dsa_indexer_error_string(3) == b"workspace too small"
