@@ -1,0 +1,260 @@
+"""Benchmark of the indexer hot path on one MI355X.
+
+A step is one call of the exact Top-K entry point (all kernels of the path)
+over one synthetic input batch that is already resident in HBM.  The timed
+region is bracketed by device synchronisation; throughput counts visible
+(query, key) pairs: key s is visible to a row at position p iff s <= p.
+
+Prints ONE JSON line.  Default workload: the 128K chunked prefill block
+(8192 rows at positions 122880..131071, 131072 keys, top-2048, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0
+PAIR_FLOPS = 2 * 64 * 128  # matrix-product FLOPs per scored pair
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="chunked_prefill_128k")
+    ap.add_argument("--path", choices=["auto", "topk", "pruned"], default="auto")
+    ap.add_argument("--also", default="context_1m_fp8", help="comma list of extra workloads to time (or 'none')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0: sized to ~15 s)")
+    return ap.parse_args()
+
+
+def run_workload(name, path, steps, warmup):
+    import torch
+
+    import dsa_lightning_indexer_04_amd as dsa
+    from dsa_lightning_indexer_04_amd import inputs
+
+    wl = inputs.WORKLOADS[name]
+    t0 = time.time()
+    d = inputs.make_workload(wl)
+    log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    q, k, w, pos = (d[n].to(dev) for n in ("q", "k", "w", "pos"))
+    qs = None if d["q_scale"] is None else d["q_scale"].to(dev)
+    ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
+    use_pruned = path == "pruned" or (path == "auto" and wl.pruned and _pruned_available())
+    if use_pruned:
+        call = lambda: dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False)
+    else:
+        from dsa_lightning_indexer_04_amd import _lib
+
+        inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
+        ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK, inp, wl.topk), dtype=torch.uint8, device=dev)
+        call = lambda: dsa.topk(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [a.elapsed_time(b) for a, b in evs]
+    pairs = wl.visible_pairs
+    res = {
+        "workload": name,
+        "path": "pruned" if use_pruned else "unpruned",
+        "dtype": wl.dtype,
+        "pairs": pairs,
+        "ms_per_step": wall * 1e3 / steps,
+        "event_ms_median": float(np.median(per_call_ms)),
+        "event_ms_min": float(np.min(per_call_ms)),
+    }
+    res["pairs_per_s"] = pairs / (wall / steps)
+    res["effective_tflops"] = pairs * PAIR_FLOPS / (res["event_ms_median"] * 1e-3) / 1e12
+    res["mfma_frac"] = res["effective_tflops"] / PEAK_TFLOPS[wl.dtype]
+    log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s, "
+        f"{res['effective_tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of {wl.dtype} peak)")
+    del q, k, w, pos, qs, ks
+    torch.cuda.empty_cache()
+    return res
+
+
+def _pruned_available():
+    return os.environ.get("DSA_BENCH_PRUNED", "1") == "1" and _probe_pruned()
+
+
+_PRUNED_OK = None
+
+
+def _probe_pruned():
+    global _PRUNED_OK
+    if _PRUNED_OK is None:
+        import torch
+
+        import dsa_lightning_indexer_04_amd as dsa
+        from dsa_lightning_indexer_04_amd import inputs
+
+        d = inputs.make_inputs(1, 8, 256, "bf16", "clustered", seed=0)
+        try:
+            dsa.topk_pruned(*(d[n].cuda() for n in ("q", "k", "w", "pos")), 16)
+            torch.cuda.synchronize()
+            _PRUNED_OK = True
+        except Exception:
+            _PRUNED_OK = False
+    return _PRUNED_OK
+
+
+def cpu_baseline(name, rows_wanted):
+    """Time the float64 oracle (scores + sort Top-K) on a bounded row sample."""
+    from dsa_lightning_indexer_04_amd import inputs
+    from oracle import indexer
+
+    wl = inputs.WORKLOADS[name]
+    d = inputs.make_workload(wl)
+    qb, kb = inputs.to_bits(d["q"]), inputs.to_bits(d["k"])
+    w = d["w"].numpy().astype(np.float64)
+    pos = d["pos"].numpy()
+    if wl.dtype == "bf16":
+        kf = indexer.decode_bf16(kb[0])
+    else:
+        kf = indexer.decode_e4m3fn(kb[0]) * d["k_scale"].numpy()[0].astype(np.float64)[:, None]
+    rng = np.random.default_rng(0)
+    Q = wl.num_q
+    threads = _blas_threads()
+    # one row first, to size the sample to ~15 s of CPU work
+    order = [Q - 1, 0] + list(rng.permutation(Q))
+    done_pairs, t_total, rows = 0, 0.0, 0
+    for t in order:
+        if rows_wanted and rows >= rows_wanted:
+            break
+        if not rows_wanted and t_total > 15.0:
+            break
+        t0 = time.perf_counter()
+        if wl.dtype == "bf16":
+            qf = indexer.decode_bf16(qb[0, t])
+        else:
+            qf = indexer.decode_e4m3fn(qb[0, t]) * float(d["q_scale"].numpy()[0, t])
+        v = int(indexer.visible_count(pos[0, t], wl.num_k))
+        s = indexer.index_score_row(qf, kf[:v], w[0, t])
+        indexer.topk_row(s, wl.topk)
+        t_total += time.perf_counter() - t0
+        done_pairs += v
+        rows += 1
+    return {
+        "value": done_pairs / t_total,
+        "unit": "pairs/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows} of {Q} query rows of {name} (first, last, then random by rng(0)); "
+        f"float64 numpy scores + lexsort Top-K; {done_pairs} visible pairs in {t_total:.1f}s, "
+        "rate scaled by visible pairs",
+    }
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = threadpool_info()
+        n = [i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(
+            json.dumps({"error": "this build measures one GPU only; the indexer is sharded by query rows "
+                        "across GPUs with no collective, see the design notes", "n_gpus": args.gpus}),
+            flush=True,
+        )
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    main_res = run_workload(args.workload, args.path, args.steps, args.warmup)
+    extra = {}
+    if args.also and args.also != "none":
+        for name in args.also.split(","):
+            if name and name != args.workload:
+                extra[name] = run_workload(name, args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
+    kt = main_res["event_ms_median"]
+    peak = PEAK_TFLOPS[main_res["dtype"]]
+    roofline = {
+        "bound": "mfma",
+        "achieved": main_res["effective_tflops"],
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": main_res["effective_tflops"] / peak,
+        "traffic": None,
+        "kernel": "k_topk_stream" if main_res["path"] == "unpruned" else "pruned path (all kernels)",
+        "per_launch_flops": main_res["pairs"] * PAIR_FLOPS,
+        "launch_ms": kt,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores ...")
+        cpu = cpu_baseline(args.workload, args.cpu_rows)
+        log(f"[bench] oracle: {cpu['value']:.3e} pairs/s on {cpu['cores']} threads")
+    from dsa_lightning_indexer_04_amd import inputs
+
+    wl = inputs.WORKLOADS[args.workload]
+    line = {
+        "metric": "indexer scored query-key pairs/s (+Top-K)",
+        "value": main_res["pairs_per_s"],
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "batch": wl.batch,
+            "query_rows": wl.num_q,
+            "keys": wl.num_k,
+            "positions": f"{wl.pos_start}..{wl.pos_start + wl.num_q - 1}",
+            "topk": wl.topk,
+            "heads": 64,
+            "head_dim": 128,
+            "path": main_res["path"],
+            "visible_pairs": main_res["pairs"],
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "also": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

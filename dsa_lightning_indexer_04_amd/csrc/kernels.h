@@ -29,6 +29,6 @@ hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* can
                               float* out_score, hipStream_t st);
 
 // Candidate capacity (records per row) used by the streaming Top-K.
-inline int stream_capacity(int topk) { return ((2 * topk + 64) + 63) / 64 * 64; }
+inline int stream_capacity(int topk) { return 4 * topk + 128; }
 
 }  // namespace dsa

@@ -1,30 +1,39 @@
-// select.h -- exact selection of the best records by radix select.
+// select.h -- exact selection of the best records by radix select (one wave).
 //
 // A record is the 64-bit key (monotone score code << 32) | (~key index), so
 // ordering records descending orders by score descending, then key index
 // ascending.  Records are distinct (one per key), so "the `need` largest
 // records" is a unique set.
 //
-// The select finds (prefix, mask): the `need` largest records are exactly
-// those r with (r & mask) >= prefix.  Digits are taken from the top, 11/11/10
-// bits of the score code and then of the key part; it stops as soon as the
-// digit bin holding the boundary is taken whole.  `prefix` is also a valid
-// running threshold: every record below it is beaten by at least `need`
-// records.
+// A selection is (prefix, mask): the kept records are those r with
+// (r & mask) >= prefix.  Digits come from the top: bits 63..53 first, then
+// 11/10/11/11/10 more bits; it stops as soon as the digit bin holding the
+// boundary is taken whole (exact), or -- for a mid-scan cut of a candidate
+// buffer -- as soon as the kept count is small enough.  `prefix` is always a
+// valid running threshold: every record below it is beaten by at least
+// `need` kept records.
+//
+// The first digit's histogram (H1, 2048 bins over bits 63..53) is kept up to
+// date by the caller as records are appended, so the first pass costs no
+// buffer read.  Later passes read the buffer 8 records per lane at a time so
+// that many loads are in flight.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dsa {
 
+constexpr int kH1Shift = 53;
+constexpr uint32_t kH1Bins = 2048;
+
 struct SelectResult {
   uint64_t prefix;
   uint64_t mask;
+  uint32_t kept;  // number of records with (r & mask) >= prefix
 };
 
 __device__ __forceinline__ int digit_shift(int pass) {
-  const int s[6] = {53, 42, 32, 21, 10, 0};
-  return s[pass];
+  return pass == 0 ? 53 : pass == 1 ? 42 : pass == 2 ? 32 : pass == 3 ? 21 : pass == 4 ? 10 : 0;
 }
 __device__ __forceinline__ int digit_width(int pass) { return (pass == 2 || pass == 5) ? 10 : 11; }
 
@@ -39,54 +48,110 @@ __device__ __forceinline__ uint32_t wave_suffix_excl(uint32_t x, int lane) {
   return incl - x;
 }
 
-// One wave selects among `cnt` records at `buf` (global memory).  hist is a
-// 2048-entry LDS scratch private to the wave.  Requires 1 <= need <= cnt.
-__device__ __noinline__ SelectResult wave_radix_select(const uint64_t* buf, int cnt, int need, uint32_t* hist,
-                                                       int lane) {
-  uint64_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)need;
-  for (int pass = 0; pass < 6; ++pass) {
-    const int S = digit_shift(pass), W = digit_width(pass);
-    const uint32_t nb = 1u << W, bpl = nb / 64;
-    for (uint32_t i = lane; i < nb; i += 64) hist[i] = 0;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    for (int i = lane; i < cnt; i += 64) {
-      uint64_t r = buf[i];
-      if ((r & mask) == prefix) atomicAdd(&hist[(uint32_t)(r >> S) & (nb - 1)], 1u);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    uint32_t local = 0;
-    for (uint32_t j = 0; j < bpl; ++j) local += hist[lane * bpl + j];
-    uint32_t above = wave_suffix_excl(local, lane);
-    bool mine = above < remaining && remaining <= above + local;
-    uint64_t bal = __ballot(mine);
-    int src = __builtin_ctzll(bal);
-    uint32_t dsel = 0, dabove = 0, dcount = 0;
-    if (lane == src) {
-      uint32_t acc = above;
-      for (int j = (int)bpl - 1; j >= 0; --j) {
-        uint32_t h = hist[lane * bpl + j];
-        if (acc + h >= remaining) {
-          dsel = lane * bpl + j;
-          dabove = acc;
-          dcount = h;
-          break;
-        }
-        acc += h;
+// Boundary bin of an nb-bin histogram: the highest bin b with
+// count(bins >= b) >= remaining.  Returns b, the count strictly above it and
+// its own count, in every lane.
+__device__ __forceinline__ void find_boundary(const uint32_t* hist, uint32_t nb, uint32_t remaining, int lane,
+                                              uint32_t& bin, uint32_t& above, uint32_t& count) {
+  const uint32_t bpl = nb / 64;
+  uint32_t local = 0;
+  for (uint32_t j = 0; j < bpl; ++j) local += hist[lane * bpl + j];
+  const uint32_t sfx = wave_suffix_excl(local, lane);
+  const bool mine = sfx < remaining && remaining <= sfx + local;
+  const uint64_t bal = __ballot(mine);
+  const int src = __builtin_ctzll(bal);
+  uint32_t b = 0, a = 0, c = 0;
+  if (lane == src) {
+    uint32_t acc = sfx;
+    for (int j = (int)bpl - 1; j >= 0; --j) {
+      const uint32_t h = hist[lane * bpl + j];
+      if (acc + h >= remaining) {
+        b = lane * bpl + j;
+        a = acc;
+        c = h;
+        break;
       }
+      acc += h;
     }
-    dsel = __shfl(dsel, src, 64);
-    dabove = __shfl(dabove, src, 64);
-    dcount = __shfl(dcount, src, 64);
-    prefix |= (uint64_t)dsel << S;
-    mask |= (uint64_t)(nb - 1) << S;
-    remaining -= dabove;
-    __builtin_amdgcn_wave_barrier();
-    if (dcount == remaining) break;
   }
-  return {prefix, mask};
+  bin = __shfl(b, src, 64);
+  above = __shfl(a, src, 64);
+  count = __shfl(c, src, 64);
+}
+
+// Histogram of digit (S, nb) over the records of buf[0, cnt) that match
+// (prefix, mask).  hist must be cleared by the caller.
+__device__ __forceinline__ void hist_pass(const uint64_t* buf, int cnt, uint64_t prefix, uint64_t mask, int S,
+                                          uint32_t nb, uint32_t* hist, int lane) {
+  for (int i0 = 0; i0 < cnt; i0 += 512) {
+    uint64_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      r[j] = i < cnt ? buf[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      if (i < cnt && (r[j] & mask) == prefix) atomicAdd(&hist[(uint32_t)(r[j] >> S) & (nb - 1)], 1u);
+    }
+  }
+}
+
+// Select the `need` best of the cnt records in buf (1 <= need <= cnt).
+// On entry hist holds H1 of exactly these records; it is clobbered.
+// exact = false stops once kept <= goal.
+__device__ __noinline__ SelectResult select_records(const uint64_t* buf, int cnt, uint32_t need, uint32_t* hist,
+                                                    bool exact, uint32_t goal, int lane) {
+  uint32_t bin, above, count;
+  find_boundary(hist, kH1Bins, need, lane, bin, above, count);
+  uint64_t prefix = (uint64_t)bin << kH1Shift;
+  uint64_t mask = (uint64_t)(kH1Bins - 1) << kH1Shift;
+  uint32_t remaining = need - above;
+  uint32_t kept = need - remaining + count;
+  for (int pass = 1; pass < 6; ++pass) {
+    if (count == remaining) break;  // boundary bin taken whole: exact
+    if (!exact && kept <= goal) break;
+    const int S = digit_shift(pass);
+    const uint32_t nb = 1u << digit_width(pass);
+    for (uint32_t i = lane; i < nb; i += 64) hist[i] = 0;
+    hist_pass(buf, cnt, prefix, mask, S, nb, hist, lane);
+    find_boundary(hist, nb, remaining, lane, bin, above, count);
+    prefix |= (uint64_t)bin << S;
+    mask |= (uint64_t)(nb - 1) << S;
+    remaining -= above;
+    kept = need - remaining + count;
+  }
+  return {prefix, mask, kept};
+}
+
+// In place: keep records with (r & mask) >= prefix, in their order, and
+// rebuild H1 over the kept ones.  Returns the kept count.
+__device__ __noinline__ int compact_records(uint64_t* buf, int cnt, SelectResult sel, uint32_t* hist, int lane) {
+  for (uint32_t i = lane; i < kH1Bins; i += 64) hist[i] = 0;
+  int base = 0;
+  for (int i0 = 0; i0 < cnt; i0 += 512) {
+    uint64_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      r[j] = i < cnt ? buf[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      const bool keep = i < cnt && (r[j] & sel.mask) >= sel.prefix;
+      const uint64_t bal = __ballot(keep);
+      const uint32_t before =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep) {
+        buf[base + before] = r[j];
+        atomicAdd(&hist[(uint32_t)(r[j] >> kH1Shift)], 1u);
+      }
+      base += __popcll(bal);
+    }
+  }
+  return base;
 }
 
 }  // namespace dsa
