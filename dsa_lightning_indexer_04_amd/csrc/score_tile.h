@@ -120,6 +120,14 @@ __device__ __forceinline__ void load_query(QuerySide<DT>& qs, const uint8_t* q_h
     for (int v = 0; v < 16; ++v) qs.wl[blk][v] = w_row[32 * blk + 8 * (v >> 2) + 4 * h + (v & 3)];
 }
 
+// ReLU of a finite fp32 value as one integer max on its bits: non-negative
+// floats are non-negative int32 patterns, negative floats (and -0) negative
+// ones, so max(bits, 0) is the bit pattern of max(x, +0).  (fmaxf would add
+// a NaN-canonicalising max per element.)
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // This lane's share of the head sum for its key column: 32 of the 64 heads,
 // in a fixed order (four chains of eight, then a fixed pairing).
 __device__ __forceinline__ float head_partial(const f32x16& s0, const f32x16& s1, const float (&wl)[2][16]) {
@@ -128,9 +136,9 @@ __device__ __forceinline__ float head_partial(const f32x16& s0, const f32x16& s1
   for (int g = 0; g < 4; ++g) {
     float acc = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__builtin_fmaxf(s0[4 * g + e], 0.0f), wl[0][4 * g + e], acc);
+    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(relu_bits(s0[4 * g + e]), wl[0][4 * g + e], acc);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__builtin_fmaxf(s1[4 * g + e], 0.0f), wl[1][4 * g + e], acc);
+    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(relu_bits(s1[4 * g + e]), wl[1][4 * g + e], acc);
     c[g] = acc;
   }
   return (c[0] + c[1]) + (c[2] + c[3]);
