@@ -157,6 +157,68 @@ int check_topk_outputs(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_
   return DSA_OK;
 }
 
+
+// ---------------------------------------------------------------- pruned path
+
+struct PruneConfig {
+  int num_seeds;
+  int num_retained;
+  const int32_t* seed_idx;
+  const uint8_t* force_recover;
+};
+
+int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
+  pc->num_seeds = (o && o->num_seeds) ? o->num_seeds : 12288;
+  pc->num_retained = (o && o->num_retained) ? o->num_retained : 14;
+  pc->seed_idx = o ? o->seed_idx : nullptr;
+  pc->force_recover = o ? o->force_recover : nullptr;
+  if (pc->num_seeds < 1 || pc->num_seeds > (1 << 26)) return fail(DSA_ERR_INVALID_ARG, "num_seeds out of range");
+  if (o && o->seed_idx && o->num_seeds < 1) return fail(DSA_ERR_INVALID_ARG, "seed_idx needs num_seeds > 0");
+  if (pc->num_retained < 1 || pc->num_retained > 14)
+    return fail(DSA_ERR_UNSUPPORTED, "num_retained must be in 1..14");
+  if (pc->seed_idx && !aligned16(pc->seed_idx)) return fail(DSA_ERR_INVALID_ARG, "seed_idx must be 16-byte aligned");
+  return DSA_OK;
+}
+
+// Workspace carve-up of the pruned path; returns the total bytes.  With a
+// base pointer it also fills the buffer pointers.
+size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConfig& pc, uint8_t* base,
+                     dsa::PrunedBuffers* pb, uint64_t** cand = nullptr) {
+  const uint64_t R = (uint64_t)in->batch * in->num_q, B = in->batch, N = in->num_k;
+  const uint64_t words = (N + 31) / 32;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return base ? base + o : nullptr;
+  };
+  uint8_t* c = take(R * (uint64_t)dsa::stream_capacity(topk) * 8);
+  uint8_t* rows = take(R * 16 * 128 * elem_bytes(in->dtype));
+  uint8_t* coef = take(R * 16 * 4);
+  uint8_t* misc = take(R * 4 * 4);
+  uint8_t* flag = take(R * 4);
+  uint8_t* kn = take(B * N * 4);
+  uint8_t* seeds = take(B * (uint64_t)pc.num_seeds * 4);
+  uint8_t* scount = take(B * 4);
+  uint8_t* bits = take(B * words * 4);
+  uint8_t* bflag = take(B * 4);
+  if (base && pb) {
+    if (cand) *cand = reinterpret_cast<uint64_t*>(c);
+    pb->plan_rows = rows;
+    pb->plan_coef = reinterpret_cast<float*>(coef);
+    pb->plan_misc = reinterpret_cast<float*>(misc);
+    pb->plan_flag = reinterpret_cast<int32_t*>(flag);
+    pb->knorm = reinterpret_cast<float*>(kn);
+    pb->seeds = reinterpret_cast<int32_t*>(seeds);
+    pb->seed_count = reinterpret_cast<int32_t*>(scount);
+    pb->seed_stride = pc.num_seeds;
+    pb->seed_bits = reinterpret_cast<uint32_t*>(bits);
+    pb->bits_stride = (int)words;
+    pb->batch_flag = reinterpret_cast<int32_t*>(bflag);
+  }
+  return off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,11 +243,16 @@ int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_id
 }
 
 size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t topk, const dsa_prune_opts* opts) {
-  (void)opts;
+  g_last_error.clear();
   if (check_inputs(in)) return 0;
   if (op == DSA_OP_SCORES) return 0;
   if (check_topk(topk)) return 0;
   if (op == DSA_OP_TOPK) return topk_workspace(in, topk);
+  if (op == DSA_OP_TOPK_PRUNED) {
+    PruneConfig pc;
+    if (prune_config(opts, &pc)) return 0;
+    return pruned_layout(in, topk, pc, nullptr, nullptr);
+  }
   fail(DSA_ERR_INVALID_ARG, "unknown op");
   return 0;
 }
@@ -193,16 +260,47 @@ size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t
 int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const dsa_prune_opts* opts,
                             int32_t* out_idx, float* out_score, const dsa_prune_stats* stats, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  (void)opts;
-  (void)stats;
-  (void)in;
-  (void)topk;
-  (void)out_idx;
-  (void)out_score;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
-  return fail(DSA_ERR_UNSUPPORTED, "pruned path not built yet");
+  int rc = check_inputs(in);
+  if (rc) return rc;
+  if ((rc = check_topk(topk))) return rc;
+  PruneConfig pc;
+  if ((rc = prune_config(opts, &pc))) return rc;
+  const size_t need = pruned_layout(in, topk, pc, nullptr, nullptr);
+  if ((rc = check_topk_outputs(in, topk, out_idx, out_score, workspace, workspace_bytes, need))) return rc;
+  if (stats) {
+    const uint64_t rows = (uint64_t)in->batch * in->num_q;
+    const Range outs[] = {span(stats->tau, rows * 4), span(stats->screened, rows * 4),
+                          span(stats->survivors, rows * 4), span(stats->recovered, rows),
+                          span(stats->upper_bound, rows * in->num_k * 4)};
+    const void* ptrs[] = {stats->tau, stats->screened, stats->survivors, stats->recovered, stats->upper_bound};
+    for (int i = 0; i < 5; ++i) {
+      if (!ptrs[i]) continue;
+      if ((rc = check_no_alias(in, outs[i]))) return rc;
+      if (overlaps(outs[i], span(workspace, need))) return fail(DSA_ERR_INVALID_ARG, "stats overlap the workspace");
+    }
+  }
+  dsa::PrunedBuffers pb{};
+  uint64_t* cand = nullptr;
+  pruned_layout(in, topk, pc, static_cast<uint8_t*>(workspace), &pb, &cand);
+  if (stats) {
+    pb.st_tau = stats->tau;
+    pb.st_screened = stats->screened;
+    pb.st_surv = stats->survivors;
+    pb.st_rec = stats->recovered;
+    pb.st_ub = stats->upper_bound;
+  }
+  const dsa::Problem p = problem_of(in);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(dsa::launch_seed_prep(p, pc.num_seeds, pc.seed_idx, pb.seeds, pb.seed_count, pb.seed_bits,
+                                             pb.batch_flag, st))))
+    return rc;
+  if ((rc = hip_status(dsa::launch_key_norms(p, pb.knorm, st)))) return rc;
+  if ((rc = hip_status(dsa::launch_plan(p, pc.num_retained, pb.seeds, pb.seed_count, pb.seed_stride, pb.batch_flag,
+                                        pc.force_recover, pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag,
+                                        st))))
+    return rc;
+  return hip_status(
+      dsa::launch_topk_pruned(p, topk, dsa::stream_capacity(topk), cand, out_idx, out_score, pb, st));
 }
 
 const char* dsa_indexer_error_string(int code) {

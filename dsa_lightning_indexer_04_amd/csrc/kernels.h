@@ -28,6 +28,37 @@ hipError_t launch_select_rows(const Problem& p, const float* scores, int topk, i
 hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
                               float* out_score, hipStream_t st);
 
+// ---------------------------------------------------------------- pruned path
+
+// Device buffers of the pruned Top-K (workspace carve-up and optional stats).
+struct PrunedBuffers {
+  uint8_t* plan_rows;  // [B*Q][16][128] dtype
+  float* plan_coef;    // [B*Q][16]
+  float* plan_misc;    // [B*Q][4]
+  int32_t* plan_flag;  // [B*Q]
+  float* knorm;        // [B][N]
+  int32_t* seeds;      // [B][seed_stride]
+  int32_t* seed_count; // [B]
+  int seed_stride;
+  uint32_t* seed_bits; // [B][bits_stride]
+  int bits_stride;
+  int32_t* batch_flag; // [B]
+  float* st_tau;
+  int32_t* st_screened;
+  int32_t* st_surv;
+  uint8_t* st_rec;
+  float* st_ub;
+};
+
+hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, int32_t* seeds, int32_t* seed_count,
+                            uint32_t* bits, int32_t* batch_flag, hipStream_t st);
+hipError_t launch_key_norms(const Problem& p, float* knorm, hipStream_t st);
+hipError_t launch_plan(const Problem& p, int nret, const int32_t* seeds, const int32_t* seed_count, int seed_stride,
+                       const int32_t* batch_flag, const uint8_t* force_recover, uint8_t* plan_rows, float* plan_coef,
+                       float* plan_misc, int32_t* plan_flag, hipStream_t st);
+hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx, float* out_score,
+                              const PrunedBuffers& pb, hipStream_t st);
+
 // Candidate capacity (records per row) used by the streaming Top-K.
 inline int stream_capacity(int topk) { return 4 * topk + 128; }
 

@@ -101,7 +101,7 @@ __device__ __forceinline__ void hist_pass(const uint64_t* buf, int cnt, uint64_t
 // Select the `need` best of the cnt records in buf (1 <= need <= cnt).
 // On entry hist holds H1 of exactly these records; it is clobbered.
 // exact = false stops once kept <= goal.
-__device__ __noinline__ SelectResult select_records(const uint64_t* buf, int cnt, uint32_t need, uint32_t* hist,
+static __device__ __noinline__ SelectResult select_records(const uint64_t* buf, int cnt, uint32_t need, uint32_t* hist,
                                                     bool exact, uint32_t goal, int lane) {
   uint32_t bin, above, count;
   find_boundary(hist, kH1Bins, need, lane, bin, above, count);
@@ -127,7 +127,8 @@ __device__ __noinline__ SelectResult select_records(const uint64_t* buf, int cnt
 
 // In place: keep records with (r & mask) >= prefix, in their order, and
 // rebuild H1 over the kept ones.  Returns the kept count.
-__device__ __noinline__ int compact_records(uint64_t* buf, int cnt, SelectResult sel, uint32_t* hist, int lane) {
+static __device__ __noinline__ int compact_records(uint64_t* buf, int cnt, SelectResult sel, uint32_t* hist,
+                                                   int lane) {
   for (uint32_t i = lane; i < kH1Bins; i += 64) hist[i] = 0;
   int base = 0;
   for (int i0 = 0; i0 < cnt; i0 += 512) {
@@ -152,6 +153,18 @@ __device__ __noinline__ int compact_records(uint64_t* buf, int cnt, SelectResult
     }
   }
   return base;
+}
+
+// Smallest of the cnt records in buf (all lanes get it; ~0 if cnt == 0).
+static __device__ __noinline__ uint64_t min_record(const uint64_t* buf, int cnt, int lane) {
+  uint64_t mn = ~0ull;
+  for (int i = lane; i < cnt; i += 64) mn = buf[i] < mn ? buf[i] : mn;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint64_t o = __shfl_xor(mn, d, 64);
+    mn = o < mn ? o : mn;
+  }
+  return mn;
 }
 
 }  // namespace dsa

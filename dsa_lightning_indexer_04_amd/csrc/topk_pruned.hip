@@ -1,0 +1,351 @@
+// topk_pruned.hip -- exact Top-K with certified (DoSA) pruning, fused.
+//
+// Flow per query row (DoSA reading notes, annotation LBKERZAW, steps 1-3;
+// 机器之心 DoSA article, sections 03-04, Fig. 2-3):
+//   1. seeds: the seed keys are scored with all heads by the same routine as
+//      every other path and go into the row's candidate buffer; the K-th best
+//      seed record is the threshold tau (K distinct visible keys reach it, so
+//      it cannot exceed the true K-th score);
+//   2. screen: every other visible key gets the certified upper bound U from
+//      16 plan rows (14 retained heads, the folded negative-head row, the
+//      linear row; see prune_prep.hip) -- one 16x16 MFMA block per 16 keys --
+//      and survives iff its record (U, key) is not below the row's running
+//      threshold; a 64-lane ballot packs the survivors into a bitmask;
+//   3. compact + refine: survivors are queued per row and rescored with all
+//      heads in batches of 32 (keys gathered by index, same score routine),
+//      and only records not below the threshold are written as candidates;
+//   4. select: the row's candidates (seed Top-K and refined survivors) are cut
+//      to the exact Top-K by score, then key index.
+// The running threshold starts at tau and only rises when the candidate
+// buffer is cut (the K-th best exact score found so far), which is valid for
+// the same reason as tau.  The bounds never rank: only exact scores do.
+// Recovery: a row flagged by the planner (non-finite plan, forced, invalid
+// seeds) lets every key survive, i.e. runs the unpruned computation.
+#include <math.h>
+
+#include "kernels.h"
+#include "stream_common.h"
+
+namespace dsa {
+
+constexpr int kPlanRowsK = 16;
+constexpr int kLinRowK = 15;
+constexpr int kAuxRowK = 14;
+constexpr int kRetainedK = 14;
+
+// ---------------------------------------------------------------- screen MFMA
+// 16x16 blocks: lane l feeds row (or key) l%16 with dims 32*(l/16)..+31
+// (bf16: v_mfma_f32_16x16x32_bf16 x 4; fp8: v_mfma_scale_f32_16x16x128_f8f6f4
+// with unit scales).  Output: lane l holds key l%16, rows 4*(l/16)+v.
+template <int DT>
+struct SFrag;
+template <>
+struct SFrag<kBF16> {
+  u32x4 v[4];
+};
+template <>
+struct SFrag<kFP8> {
+  i32x8 v;
+};
+
+template <int DT>
+__device__ __forceinline__ void load_sfrag(SFrag<DT>& f, const uint8_t* row, int lane) {
+  constexpr int LB = DT == kBF16 ? 64 : 32;  // bytes per lane
+  const u32x4* p = reinterpret_cast<const u32x4*>(row + (lane >> 4) * LB);
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = p[i];
+  } else {
+    const u32x4 lo = p[0], hi = p[1];
+    f.v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void load_sfrag_lds(SFrag<DT>& f, const u32x4* tile, int key, int lane) {
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = tile[swz_chunk<DT>(key, 4 * (lane >> 4) + i)];
+  } else {
+    const u32x4 lo = tile[swz_chunk<DT>(key, 2 * (lane >> 4))], hi = tile[swz_chunk<DT>(key, 2 * (lane >> 4) + 1)];
+    f.v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mma16(const SFrag<DT>& a, const SFrag<DT>& b) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[i]),
+                                                     __builtin_bit_cast(bf16x8, b.v[i]), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, acc, 0, 0, 0, 127, 0, 127);
+  }
+  return acc;
+}
+
+struct PrunePlan {
+  const uint8_t* rows;       // [R][16][128] dtype: bound rows
+  const float* coef;         // [R][16]: c_0..c_13, aux multiplier, linear multiplier
+  const float* misc;         // [R][4]: kappa, e_neg
+  const int32_t* flag;       // [R]: 1 = recover (no pruning)
+  const float* knorm;        // [B][N]: |k|, rounded up
+  const int32_t* seeds;      // [B][seed_stride] ascending
+  const int32_t* seed_count; // [B]
+  int seed_stride;
+  const uint32_t* seed_bits; // [B][bits_stride]
+  int bits_stride;
+  float* st_tau;
+  int32_t* st_screened;
+  int32_t* st_surv;
+  uint8_t* st_rec;
+  float* st_ub;              // [R][N] debug bounds or null
+};
+
+// Append state of one row (all wave-uniform except `rec`/`live`).
+struct RowState {
+  uint64_t* buf;
+  int cnt, nst;
+  uint64_t thr;
+};
+
+__device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live, uint64_t* stage, uint32_t* hist,
+                                           int topk, int cap, int lane) {
+  uint64_t bal = __ballot(live && rec >= rs.thr);
+  if (bal) {
+    if (rs.cnt + rs.nst + __popcll(bal) > cap) {
+      const Cut c = cut_candidates(rs.buf, rs.cnt, stage, rs.nst, hist, topk, cap, lane);
+      rs.cnt = c.cnt;
+      rs.thr = c.thr;
+      rs.nst = 0;
+      bal = __ballot(live && rec >= rs.thr);
+    }
+    if (live && rec >= rs.thr) {
+      stage[rs.nst + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+          rec;
+      atomicAdd(&hist[(uint32_t)(rec >> kH1Shift)], 1u);
+    }
+    rs.nst += __popcll(bal);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_topk_pruned(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
+    const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
+    int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
+    PrunePlan pp) {
+  constexpr int RB = Frag<DT>::kRowBytes;
+  constexpr int KT = kTileBytes / RB;
+  constexpr int NSB = KT / 32;
+  __shared__ u32x4 ktile[2][kTileBytes / 16];
+  __shared__ float kscale_tile[2][KT];
+  __shared__ uint32_t hist[kWaves][kH1Bins];
+  __shared__ uint64_t stage[kWaves][KT + 32];
+  __shared__ int32_t squeue[kWaves][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int group = gridDim.x - 1 - blockIdx.x;
+  const int b = blockIdx.y;
+  const int t = group * kWaves + wave;
+  const bool valid = t < Q;
+  const size_t row = (size_t)b * Q + min(t, Q - 1);
+  const int vis = valid ? min(max(pos[row] + 1, 0), N) : 0;
+  int wg_vis = 0;
+  for (int j = 0; j < kWaves; ++j) {
+    const int tj = group * kWaves + j;
+    if (tj < Q) wg_vis = max(wg_vis, min(max(pos[(size_t)b * Q + tj] + 1, 0), N));
+  }
+
+  QuerySide<DT> qs;
+  load_query<DT>(qs, q + row * kHeads * RB, w + row * kHeads, lane);
+  const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
+
+  // screen side: plan row (lane % 16), coefficients of this lane's 4 rows
+  SFrag<DT> sa;
+  load_sfrag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 15)) * RB, lane);
+  const float* co = pp.coef + row * kPlanRowsK;
+  float cl[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * (lane >> 4) + v;
+    cl[v] = r < kRetainedK ? co[r] : 0.0f;
+  }
+  const float m_aux = co[kAuxRowK], m_lin = co[kLinRowK];
+  const float kappa = pp.misc[row * 4 + 0], e_neg = pp.misc[row * 4 + 1];
+  const bool special = (lane >> 4) == 3;  // holds rows 14 (aux) and 15 (linear)
+  const bool recover = pp.flag[row] != 0;
+
+  uint32_t* my_hist = hist[wave];
+  uint64_t* my_stage = stage[wave];
+  int32_t* my_q = squeue[wave];
+  for (uint32_t i = lane; i < kH1Bins; i += 64) my_hist[i] = 0;
+  RowState rs{cand + row * (size_t)cap, 0, 0, 0};
+  const uint8_t* kbase = k + (size_t)b * N * RB;
+  const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
+  const float* knb = pp.knorm + (size_t)b * N;
+  const int nseed = pp.seed_count[b];
+  const int32_t* sd = pp.seeds + (size_t)b * pp.seed_stride;
+  const uint32_t* sbits = pp.seed_bits + (size_t)b * pp.bits_stride;
+  TileFetch<DT> tf;
+
+  // ---------------------------------------------------------------- 1. seeds
+  {
+    const int ntiles = (nseed + KT - 1) / KT;
+    if (ntiles > 0) {
+      tf.fetch(kbase, kscb, 0, N, tid, sd, nseed);
+      tf.commit(ktile[0], kscale_tile[0], tid);
+    }
+    __syncthreads();
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const int cur = ti & 1;
+      const int ts = ti * KT;
+      if (rs.nst) {
+        rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+        rs.nst = 0;
+      }
+      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, sd, nseed);
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int s0 = ts + 32 * sb;
+        if (s0 < nseed && sd[s0] < vis) {  // seeds ascend: wave-uniform test
+          const int si = s0 + (lane & 31);
+          const int key = sd[min(si, nseed - 1)];
+          Frag<DT> f;
+          load_frag_lds<DT>(f, ktile[cur], 32 * sb + (lane & 31), lane);
+          float s = combine_single(query_partial<DT>(qs, f));
+          if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[cur][32 * sb + (lane & 31)]);
+          append_rec(rs, make_record(s, (uint32_t)key), lane < 32 && si < nseed && key < vis, my_stage, my_hist,
+                     topk, cap, lane);
+        }
+      }
+      if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid);
+      __syncthreads();
+    }
+  }
+  // tau: the exact K-th seed record (records below it can never be selected)
+  if (rs.nst) {
+    rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+    rs.nst = 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  float tau = -INFINITY;
+  if (rs.cnt >= topk) {
+    const SelectResult sel = select_records(rs.buf, rs.cnt, (uint32_t)topk, my_hist, true, 0, lane);
+    rs.cnt = compact_records(rs.buf, rs.cnt, sel, my_hist, lane);
+    rs.thr = min_record(rs.buf, rs.cnt, lane);
+    tau = record_score(rs.thr);
+  }
+
+  // ---------------------------------------------------------------- 2-3. screen + refine
+  int nq = 0, screened = 0, survived = 0;
+  auto refine = [&](int n) {
+    const int slot = lane & 31;
+    const int key = my_q[slot < n ? slot : 0];
+    Frag<DT> f;
+    load_frag<DT>(f, kbase + (size_t)key * RB, lane);
+    float s = combine_single(query_partial<DT>(qs, f));
+    if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscb[key]);
+    append_rec(rs, make_record(s, (uint32_t)key), lane < 32 && slot < n, my_stage, my_hist, topk, cap, lane);
+    const int rest = nq - n;  // < 32 <= n, so the move below never overlaps
+    const int moved = lane < rest ? my_q[n + lane] : 0;
+    if (lane < rest) my_q[lane] = moved;
+    nq = rest;
+  };
+  {
+    const int ntiles = (wg_vis + KT - 1) / KT;
+    if (ntiles > 0) {
+      tf.fetch(kbase, kscb, 0, N, tid);
+      tf.commit(ktile[0], kscale_tile[0], tid);
+    }
+    __syncthreads();
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const int cur = ti & 1;
+      const int ts = ti * KT;
+      if (rs.nst) {
+        rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+        rs.nst = 0;
+      }
+      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid);
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int kb = ts + 32 * sb;
+        if (kb < vis) {  // wave-uniform
+          const uint32_t seedw = sbits[kb >> 5];
+          uint32_t mask = 0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            SFrag<DT> kf;
+            const int tk = 32 * sb + 16 * j + (lane & 15);
+            load_sfrag_lds<DT>(kf, ktile[cur], tk, lane);
+            const f32x4 d = mma16<DT>(sa, kf);
+            const int key = kb + 16 * j + (lane & 15);
+            const float kn = knb[min(key, N - 1)];
+            float part = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part = __builtin_fmaf(__builtin_fabsf(d[v]), cl[v], part);
+            const float pen = __builtin_fmaf(m_aux, d[2], -e_neg * kn);
+            part += special ? __builtin_fmaf(m_lin, d[3], -relu_bits(pen)) : 0.0f;
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            float U = __builtin_fmaf(kappa, kn, part);
+            if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][tk]);
+            const bool cand_key = key < vis && !((seedw >> (16 * j + (lane & 15))) & 1u);
+            const bool surv = cand_key && (recover || make_record(U, (uint32_t)key) >= rs.thr);
+            if (pp.st_ub && lane < 16 && cand_key) pp.st_ub[row * (size_t)N + key] = U;
+            screened += __popcll(__ballot(cand_key) & 0xFFFFull);
+            mask |= (uint32_t)(__ballot(surv) & 0xFFFFull) << (16 * j);
+          }
+          if (mask) {
+            if (lane < 32 && ((mask >> lane) & 1u)) my_q[nq + __popc(mask & ((1u << lane) - 1u))] = kb + lane;
+            nq += __popc(mask);
+            survived += __popc(mask);
+            if (nq >= 32) refine(32);
+          }
+        }
+      }
+      if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid);
+      __syncthreads();
+    }
+  }
+  if (nq > 0) refine(nq);
+
+  // ---------------------------------------------------------------- 4. select
+  if (!valid) return;
+  emit_topk(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
+            out_score ? out_score + row * (size_t)topk : nullptr, lane);
+  if (lane == 0) {
+    if (pp.st_tau) pp.st_tau[row] = tau;
+    if (pp.st_screened) pp.st_screened[row] = screened;
+    if (pp.st_surv) pp.st_surv[row] = survived;
+    if (pp.st_rec) pp.st_rec[row] = recover ? 1 : 0;
+  }
+}
+
+__global__ void k_fill_nan(float* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = __builtin_nanf("");
+}
+
+hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx, float* out_score,
+                              const PrunedBuffers& pb, hipStream_t st) {
+  if (pb.st_ub) {
+    const size_t n = (size_t)p.B * p.Q * p.N;
+    hipLaunchKernelGGL(k_fill_nan, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pb.st_ub, n);
+  }
+  PrunePlan pp{pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag, pb.knorm, pb.seeds, pb.seed_count,
+               pb.seed_stride, pb.seed_bits, pb.bits_stride, pb.st_tau, pb.st_screened, pb.st_surv, pb.st_rec,
+               pb.st_ub};
+  dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
+  if (p.dtype == kBF16)
+    hipLaunchKernelGGL(k_topk_pruned<kBF16>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
+                       p.pos, p.Q, p.N, topk, cap, cand, out_idx, out_score, pp);
+  else
+    hipLaunchKernelGGL(k_topk_pruned<kFP8>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
+                       p.pos, p.Q, p.N, topk, cap, cand, out_idx, out_score, pp);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
