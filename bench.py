@@ -58,8 +58,22 @@ def run_workload(name, path, steps, warmup):
     qs = None if d["q_scale"] is None else d["q_scale"].to(dev)
     ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
     use_pruned = path == "pruned" or (path == "auto" and wl.pruned and _pruned_available())
+    stats = None
     if use_pruned:
-        call = lambda: dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False)
+        from dsa_lightning_indexer_04_amd import _lib
+
+        inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
+        opts = _lib.PruneOpts(0, 0, None, None)
+        ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
+                         device=dev)
+        call = lambda: dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False,
+                                       workspace=ws)
+        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False,
+                                   workspace=ws, stats=True)
+        scr = int(st["screened"].sum().item())
+        sur = int(st["survivors"].sum().item())
+        stats = {"screened": scr, "survivors": sur, "filter_rate": 1.0 - sur / max(1, scr),
+                 "recovered_rows": int(st["recovered"].sum().item())}
     else:
         from dsa_lightning_indexer_04_amd import _lib
 
@@ -91,10 +105,13 @@ def run_workload(name, path, steps, warmup):
         "event_ms_min": float(np.min(per_call_ms)),
     }
     res["pairs_per_s"] = pairs / (wall / steps)
+    if stats:
+        res["prune"] = stats
     res["effective_tflops"] = pairs * PAIR_FLOPS / (res["event_ms_median"] * 1e-3) / 1e12
     res["mfma_frac"] = res["effective_tflops"] / PEAK_TFLOPS[wl.dtype]
     log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s, "
-        f"{res['effective_tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of {wl.dtype} peak)")
+        f"{res['effective_tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of {wl.dtype} peak)"
+        + (f", filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
     del q, k, w, pos, qs, ks
     torch.cuda.empty_cache()
     return res
@@ -200,9 +217,11 @@ def main():
     main_res = run_workload(args.workload, args.path, args.steps, args.warmup)
     extra = {}
     if args.also and args.also != "none":
-        for name in args.also.split(","):
-            if name and name != args.workload:
-                extra[name] = run_workload(name, args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
+        for item in args.also.split(","):
+            if not item:
+                continue
+            name, _, pth = item.partition(":")
+            extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
     kt = main_res["event_ms_median"]
     peak = PEAK_TFLOPS[main_res["dtype"]]
     roofline = {

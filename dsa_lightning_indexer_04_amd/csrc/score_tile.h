@@ -145,6 +145,49 @@ __device__ __forceinline__ float head_partial(const f32x16& s0, const f32x16& s1
   return (c[0] + c[1]) + (c[2] + c[3]);
 }
 
+// Head weights of this lane's 32 heads from a row of 64 weights (any address
+// space): the same order as QuerySide::wl.
+__device__ __forceinline__ void load_wl(float (&wl)[2][16], const float* w_row, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) wl[blk][v] = w_row[32 * blk + 8 * (v >> 2) + 4 * h + (v & 3)];
+}
+
+// head_partial with the weights read from a 64-float row four at a time
+// (exactly the same FMA sequence, so the same bits).
+__device__ __forceinline__ float head_partial_w(const f32x16& s0, const f32x16& s1, const float* w_row, int lane) {
+  const int h = lane >> 5;
+  float c[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float4 w0 = *reinterpret_cast<const float4*>(w_row + 8 * g + 4 * h);
+    const float4 w1 = *reinterpret_cast<const float4*>(w_row + 32 + 8 * g + 4 * h);
+    float acc = 0.0f;
+    acc = __builtin_fmaf(relu_bits(s0[4 * g + 0]), w0.x, acc);
+    acc = __builtin_fmaf(relu_bits(s0[4 * g + 1]), w0.y, acc);
+    acc = __builtin_fmaf(relu_bits(s0[4 * g + 2]), w0.z, acc);
+    acc = __builtin_fmaf(relu_bits(s0[4 * g + 3]), w0.w, acc);
+    acc = __builtin_fmaf(relu_bits(s1[4 * g + 0]), w1.x, acc);
+    acc = __builtin_fmaf(relu_bits(s1[4 * g + 1]), w1.y, acc);
+    acc = __builtin_fmaf(relu_bits(s1[4 * g + 2]), w1.z, acc);
+    acc = __builtin_fmaf(relu_bits(s1[4 * g + 3]), w1.w, acc);
+    c[g] = acc;
+  }
+  return (c[0] + c[1]) + (c[2] + c[3]);
+}
+
+// Full-head partial for one query against one 32-key block, with the head
+// weights read from a row of 64 floats (same arithmetic as query_partial).
+template <int DT>
+__device__ __forceinline__ float query_partial_w(const Frag<DT> (&a)[2], const Frag<DT>& kb, const float* w_row,
+                                                 int lane) {
+  f32x16 s0 = mma_block<DT>(a[0], kb, zero16());
+  f32x16 s1 = mma_block<DT>(a[1], kb, zero16());
+  return head_partial_w(s0, s1, w_row, lane);
+}
+
 // Full-head partial for one query against one 32-key block.
 template <int DT>
 __device__ __forceinline__ float query_partial(const QuerySide<DT>& qs, const Frag<DT>& kb) {

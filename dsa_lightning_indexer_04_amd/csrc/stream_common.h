@@ -105,12 +105,17 @@ struct TileFetch {
   static constexpr int PER_THREAD = CHUNKS / (kWaves * 64);
   static constexpr int KT = kTileBytes / Frag<DT>::kRowBytes;
   u32x4 v[PER_THREAD];
-  float ks;
+  float ks;   // fp8 key scale of tile row tid (tid < KT)
+  float kn;   // key norm of tile row tid (pruned path, tid < KT)
+  uint32_t sbw;  // seed-bitmap word tid (pruned path, tid < KT / 32)
 
   // Tile rows ts..ts+KT-1 of the key sequence; with `gidx`, tile row r is key
   // gidx[min(ts + r, nidx - 1)] (a gathered tile), else key min(ts + r, N - 1).
+  // `knorm` / `sbits` (pruned path) also stage each row's |k| and the seed
+  // bitmap words of a contiguous tile.
   __device__ __forceinline__ void fetch(const uint8_t* kbase, const float* kscb, int ts, int N, int tid,
-                                        const int32_t* gidx = nullptr, int nidx = 0) {
+                                        const int32_t* gidx = nullptr, int nidx = 0, const float* knorm = nullptr,
+                                        const uint32_t* sbits = nullptr) {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int c = tid + j * kWaves * 64;
@@ -118,19 +123,25 @@ struct TileFetch {
       const int gk = gidx ? gidx[min(ts + key, nidx - 1)] : min(ts + key, N - 1);
       v[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)gk * Frag<DT>::kRowBytes + ch * 16);
     }
-    if constexpr (DT == kFP8) {
-      if (tid < KT) ks = kscb[gidx ? gidx[min(ts + tid, nidx - 1)] : min(ts + tid, N - 1)];
+    if (tid < KT) {
+      const int gk = gidx ? gidx[min(ts + tid, nidx - 1)] : min(ts + tid, N - 1);
+      if constexpr (DT == kFP8) ks = kscb[gk];
+      if (knorm) kn = knorm[gk];
     }
+    if (sbits && tid < KT / 32) sbw = sbits[min(ts / 32 + tid, (N - 1) / 32)];
   }
-  __device__ __forceinline__ void commit(u32x4* tile, float* kst, int tid) const {
+  __device__ __forceinline__ void commit(u32x4* tile, float* kst, int tid, float* knt = nullptr,
+                                         uint32_t* sbt = nullptr) const {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int c = tid + j * kWaves * 64;
       tile[swz_chunk<DT>(c / CPR, c % CPR)] = v[j];
     }
-    if constexpr (DT == kFP8) {
-      if (tid < KT) kst[tid] = ks;
+    if (tid < KT) {
+      if constexpr (DT == kFP8) kst[tid] = ks;
+      if (knt) knt[tid] = kn;
     }
+    if (sbt && tid < KT / 32) sbt[tid] = sbw;
   }
 };
 

@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ uint32_t hist[kWaves][kH1Bins];
   __shared__ uint64_t stage[kWaves][KT + 32];
   __shared__ int32_t squeue[kWaves][64];
+  __shared__ float knorm_tile[2][KT];
+  __shared__ uint32_t sbits_tile[2][KT / 32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = gridDim.x - 1 - blockIdx.x;
@@ -159,8 +161,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     if (tj < Q) wg_vis = max(wg_vis, min(max(pos[(size_t)b * Q + tj] + 1, 0), N));
   }
 
-  QuerySide<DT> qs;
-  load_query<DT>(qs, q + row * kHeads * RB, w + row * kHeads, lane);
+  // query rows in registers; head weights in LDS (read at each full epilogue)
+  __shared__ __align__(16) float wrow[kWaves][kHeads];
+  Frag<DT> qa[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], q + (row * kHeads + 32 * blk + (lane & 31)) * RB, lane);
+  wrow[wave][lane] = w[row * kHeads + lane];
+  const float* my_w = wrow[wave];
   const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
 
   // screen side: plan row (lane % 16), coefficients of this lane's 4 rows
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
           const int key = sd[min(si, nseed - 1)];
           Frag<DT> f;
           load_frag_lds<DT>(f, ktile[cur], 32 * sb + (lane & 31), lane);
-          float s = combine_single(query_partial<DT>(qs, f));
+          float s = combine_single(query_partial_w<DT>(qa, f, my_w, lane));
           if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[cur][32 * sb + (lane & 31)]);
           append_rec(rs, make_record(s, (uint32_t)key), lane < 32 && si < nseed && key < vis, my_stage, my_hist,
                      topk, cap, lane);
@@ -240,27 +247,33 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---------------------------------------------------------------- 2-3. screen + refine
+  // Survivor queue: 32 slots held in registers.  Slot s is lanes s and s+32,
+  // which hold the MFMA B fragment of the queued key (each its half of the
+  // row) -- loaded from the LDS tile the moment the key survives, so the
+  // refine never reads HBM.  A full queue is scored with all heads at once.
   int nq = 0, screened = 0, survived = 0;
-  auto refine = [&](int n) {
-    const int slot = lane & 31;
-    const int key = my_q[slot < n ? slot : 0];
-    Frag<DT> f;
-    load_frag<DT>(f, kbase + (size_t)key * RB, lane);
-    float s = combine_single(query_partial<DT>(qs, f));
-    if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscb[key]);
-    append_rec(rs, make_record(s, (uint32_t)key), lane < 32 && slot < n, my_stage, my_hist, topk, cap, lane);
-    const int rest = nq - n;  // < 32 <= n, so the move below never overlaps
-    const int moved = lane < rest ? my_q[n + lane] : 0;
-    if (lane < rest) my_q[lane] = moved;
-    nq = rest;
+  Frag<DT> fr;
+  int fr_key = 0;
+  float fr_ks = 1.0f;
+  auto refine_run = [&]() {
+    float s = combine_single(query_partial_w<DT>(qa, fr, my_w, lane));
+    if constexpr (DT == kFP8) s = apply_scales(s, qscale, fr_ks);
+    append_rec(rs, make_record(s, (uint32_t)fr_key), lane < 32 && (lane & 31) < nq, my_stage, my_hist, topk, cap,
+               lane);
+    nq = 0;
   };
   {
     const int ntiles = (wg_vis + KT - 1) / KT;
     if (ntiles > 0) {
-      tf.fetch(kbase, kscb, 0, N, tid);
-      tf.commit(ktile[0], kscale_tile[0], tid);
+      tf.fetch(kbase, kscb, 0, N, tid, nullptr, 0, knb, sbits);
+      tf.commit(ktile[0], kscale_tile[0], tid, knorm_tile[0], sbits_tile[0]);
     }
     __syncthreads();
+    // Lane l reports key slot ks = (l & 15) + 16 * (l >> 5) of a 32-key block
+    // after the butterfly below (lanes 16..31 and 48..63 repeat 0..15/32..47).
+    const int kslot = (lane & 15) + 16 * (lane >> 5);
+    const bool g_lo = ((lane >> 5) & 1) == 0;   // lane groups 0,1 vs 2,3
+    const bool g_even = ((lane >> 4) & 1) == 0;  // lane groups 0,2 vs 1,3
     for (int ti = 0; ti < ntiles; ++ti) {
       const int cur = ti & 1;
       const int ts = ti * KT;
@@ -268,49 +281,84 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
         rs.nst = 0;
       }
-      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid);
+      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, nullptr, 0, knb, sbits);
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         const int kb = ts + 32 * sb;
         if (kb < vis) {  // wave-uniform
-          const uint32_t seedw = sbits[kb >> 5];
-          uint32_t mask = 0;
+          // -- bound of 32 keys: two 16x16 blocks (keys kb..kb+15, kb+16..kb+31)
+          SFrag<DT> kf0, kf1;
+          load_sfrag_lds<DT>(kf0, ktile[cur], 32 * sb + (lane & 15), lane);
+          load_sfrag_lds<DT>(kf1, ktile[cur], 32 * sb + 16 + (lane & 15), lane);
+          const f32x4 d0 = mma16<DT>(sa, kf0);
+          const f32x4 d1 = mma16<DT>(sa, kf1);
+          const float kn0 = knorm_tile[cur][32 * sb + (lane & 15)];
+          const float kn1 = knorm_tile[cur][32 * sb + 16 + (lane & 15)];
+          float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            SFrag<DT> kf;
-            const int tk = 32 * sb + 16 * j + (lane & 15);
-            load_sfrag_lds<DT>(kf, ktile[cur], tk, lane);
-            const f32x4 d = mma16<DT>(sa, kf);
-            const int key = kb + 16 * j + (lane & 15);
-            const float kn = knb[min(key, N - 1)];
-            float part = 0.0f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) part = __builtin_fmaf(__builtin_fabsf(d[v]), cl[v], part);
-            const float pen = __builtin_fmaf(m_aux, d[2], -e_neg * kn);
-            part += special ? __builtin_fmaf(m_lin, d[3], -relu_bits(pen)) : 0.0f;
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            float U = __builtin_fmaf(kappa, kn, part);
-            if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][tk]);
-            const bool cand_key = key < vis && !((seedw >> (16 * j + (lane & 15))) & 1u);
-            const bool surv = cand_key && (recover || make_record(U, (uint32_t)key) >= rs.thr);
-            if (pp.st_ub && lane < 16 && cand_key) pp.st_ub[row * (size_t)N + key] = U;
-            screened += __popcll(__ballot(cand_key) & 0xFFFFull);
-            mask |= (uint32_t)(__ballot(surv) & 0xFFFFull) << (16 * j);
+          for (int v = 0; v < 4; ++v) {
+            p0 = __builtin_fmaf(__builtin_fabsf(d0[v]), cl[v], p0);
+            p1 = __builtin_fmaf(__builtin_fabsf(d1[v]), cl[v], p1);
           }
+          if (special) {  // lanes 48..63 hold the aux (14) and linear (15) rows
+            p0 += __builtin_fmaf(m_lin, d0[3], -relu_bits(__builtin_fmaf(m_aux, d0[2], -e_neg * kn0)));
+            p1 += __builtin_fmaf(m_lin, d1[3], -relu_bits(__builtin_fmaf(m_aux, d1[2], -e_neg * kn1)));
+          }
+          // butterfly over the four lane groups: groups 0,1 end with block 0's
+          // sum, groups 2,3 with block 1's (2 exchanges for both blocks)
+          const float a = (g_lo ? p0 : p1) + __shfl_xor(g_lo ? p1 : p0, 32, 64);
+          const float bsum = a + __shfl_xor(a, 16, 64);
+          const float kn = g_lo ? kn0 : kn1;
+          float U = __builtin_fmaf(kappa, kn, bsum);
+          if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][32 * sb + kslot]);
+          const int key = kb + kslot;
+          const uint32_t seedw = sbits_tile[cur][sb];
+          const bool ck = g_even & (key < vis) & !((seedw >> kslot) & 1u);
+          const bool sv = ck & (recover | (make_record(U, (uint32_t)key) >= rs.thr));
+          if (pp.st_ub && ck) pp.st_ub[row * (size_t)N + key] = U;
+          const uint64_t bck = __ballot(ck), bsv = __ballot(sv);
+          screened += __popcll(bck);
+          // survivor bits in key order: bits 0..15 <- lanes 0..15, 16..31 <- lanes 32..47
+          uint32_t mask = (uint32_t)(bsv & 0xFFFFull) | ((uint32_t)((bsv >> 32) & 0xFFFFull) << 16);
+          survived += __popc(mask);
+          // -- enqueue survivors into register slots (rank order), scoring a
+          //    full queue; a block fills at most one queue, so two rounds
           if (mask) {
-            if (lane < 32 && ((mask >> lane) & 1u)) my_q[nq + __popc(mask & ((1u << lane) - 1u))] = kb + lane;
-            nq += __popc(mask);
-            survived += __popc(mask);
-            if (nq >= 32) refine(32);
+            mask = __builtin_amdgcn_readfirstlane(mask);
+            const int m = __popc(mask);
+            const int take = min(m, 32 - nq);
+            const bool mine = lane < 32 && ((mask >> lane) & 1u);
+            const int rank = __popc(mask & ((1u << (lane & 31)) - 1u));
+            if (mine && rank < take) my_q[nq + rank] = lane;
+            const int slot = lane & 31;
+            if (slot >= nq && slot < nq + take) {
+              const int off = my_q[slot];
+              load_frag_lds<DT>(fr, ktile[cur], 32 * sb + off, lane);
+              fr_key = kb + off;
+              if constexpr (DT == kFP8) fr_ks = kscale_tile[cur][32 * sb + off];
+            }
+            nq = __builtin_amdgcn_readfirstlane(nq + take);
+            if (nq == 32) {
+              refine_run();
+              if (take < m) {
+                if (mine && rank >= take) my_q[rank - take] = lane;
+                if (slot < m - take) {
+                  const int off = my_q[slot];
+                  load_frag_lds<DT>(fr, ktile[cur], 32 * sb + off, lane);
+                  fr_key = kb + off;
+                  if constexpr (DT == kFP8) fr_ks = kscale_tile[cur][32 * sb + off];
+                }
+                nq = m - take;
+              }
+            }
           }
         }
       }
-      if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid);
+      if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid, knorm_tile[cur ^ 1], sbits_tile[cur ^ 1]);
       __syncthreads();
     }
   }
-  if (nq > 0) refine(nq);
+  if (nq > 0) refine_run();
 
   // ---------------------------------------------------------------- 4. select
   if (!valid) return;
