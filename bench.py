@@ -1,12 +1,20 @@
 """Benchmark of the indexer hot path on one MI355X.
 
-A step is one call of the exact Top-K entry point (all kernels of the path)
-over one synthetic input batch that is already resident in HBM.  The timed
-region is bracketed by device synchronisation; throughput counts visible
-(query, key) pairs: key s is visible to a row at position p iff s <= p.
+A step is one call of an exact Top-K entry point (every kernel of the path)
+over one synthetic input batch already resident in HBM.  The timed region is
+bracketed by device synchronisation; throughput counts visible (query, key)
+pairs: key s is visible to a row at position p iff s <= p.
 
-Prints ONE JSON line.  Default workload: the 128K chunked prefill block
-(8192 rows at positions 122880..131071, 131072 keys, top-2048, bf16).
+Prints ONE JSON line.  Default workload: the 128K chunked-prefill block (8192
+rows at positions 122880..131071, 131072 keys, top-2048, bf16) through the
+certified-pruning path (all steps: seeds, plan, screen, refine, select), with
+the unpruned path and the 1M-key fp8 block reported beside it.
+
+The roofline object describes the dominant kernel of the timed path: its
+duration is the mean of HIP events the library records around each launch
+on the launch stream during the timed steps; its work is the matrix-product
+FLOPs one launch executes (2*64*128 per fully scored pair, 2*128*16 per
+screened pair), against MI355X's published dense MFMA peak for the dtype.
 """
 from __future__ import annotations
 
@@ -22,8 +30,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
-PEAK_HBM_GBS = 8000.0
-PAIR_FLOPS = 2 * 64 * 128  # matrix-product FLOPs per scored pair
+# HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
+# dispatch, mean over dispatches), scaled by what the same counters read for a
+# 1 GiB device copy (FETCH x2.000, WRITE x1.000).  Valid only for the kernel
+# sources they were taken on: reported as null once the sources change.
+FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
+MEASURED_KIB = {
+    # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    ("chunked_prefill_128k", "k_topk_stream"): ("8f67374fd62d8d9e", 1700319, 2010090),
+    ("chunked_prefill_128k", "k_topk_pruned"): ("8f67374fd62d8d9e", 6424360, 1968081),
+}
+PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
+SCREEN_FLOPS = 2 * 128 * 16  # 16-row bound of one pair
 
 
 def log(msg):
@@ -37,17 +55,56 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunked_prefill_128k")
     ap.add_argument("--path", choices=["auto", "topk", "pruned"], default="auto")
-    ap.add_argument("--also", default="context_1m_fp8", help="comma list of extra workloads to time (or 'none')")
+    ap.add_argument(
+        "--also",
+        default="chunked_prefill_128k:topk,context_1m_fp8:pruned,context_1m_fp8:topk",
+        help="comma list of extra workload[:path] runs (or 'none')",
+    )
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0: sized to ~15 s)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (counter calibration) and exit")
     return ap.parse_args()
+
+
+def source_digest():
+    """Digest of the HIP kernel sources (the key of MEASURED_KIB)."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dsa_lightning_indexer_04_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    m = MEASURED_KIB.get((workload, kernel))
+    if m is None or m[0] != source_digest():
+        return None
+    return (m[1] * FETCH_SCALE + m[2] * WRITE_SCALE) * 1024
+
+
+def copy_calibration(mib):
+    """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": mib << 20, "copy_bytes_written": mib << 20, "launches": 3}), flush=True)
 
 
 def run_workload(name, path, steps, warmup):
     import torch
 
     import dsa_lightning_indexer_04_amd as dsa
-    from dsa_lightning_indexer_04_amd import inputs
+    from dsa_lightning_indexer_04_amd import _lib, inputs
 
     wl = inputs.WORKLOADS[name]
     t0 = time.time()
@@ -57,89 +114,71 @@ def run_workload(name, path, steps, warmup):
     q, k, w, pos = (d[n].to(dev) for n in ("q", "k", "w", "pos"))
     qs = None if d["q_scale"] is None else d["q_scale"].to(dev)
     ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
-    use_pruned = path == "pruned" or (path == "auto" and wl.pruned and _pruned_available())
+    del d
+    use_pruned = path == "pruned" or (path == "auto" and wl.pruned)
+    inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
     stats = None
     if use_pruned:
-        from dsa_lightning_indexer_04_amd import _lib
-
-        inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
         opts = _lib.PruneOpts(0, 0, None, None)
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                          device=dev)
-        call = lambda: dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False,
-                                       workspace=ws)
+
+        def call():
+            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False, workspace=ws)
+
         _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False,
                                    workspace=ws, stats=True)
         scr = int(st["screened"].sum().item())
         sur = int(st["survivors"].sum().item())
-        stats = {"screened": scr, "survivors": sur, "filter_rate": 1.0 - sur / max(1, scr),
-                 "recovered_rows": int(st["recovered"].sum().item())}
+        seeds = min(12288, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced seeds, visible to every row
+        stats = {"screened_pairs": scr, "survivor_pairs": sur, "seed_pairs": seeds,
+                 "filter_rate": 1.0 - sur / max(1, scr), "recovered_rows": int(st["recovered"].sum().item())}
     else:
-        from dsa_lightning_indexer_04_amd import _lib
-
-        inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK, inp, wl.topk), dtype=torch.uint8, device=dev)
-        call = lambda: dsa.topk(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False, workspace=ws)
+
+        def call():
+            return dsa.topk(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False, workspace=ws)
+
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    _lib.profile_begin()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(stream)
+    for _ in range(steps):
         call()
-        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call_ms = [a.elapsed_time(b) for a, b in evs]
+    kernels = _lib.profile_end()
     pairs = wl.visible_pairs
     res = {
         "workload": name,
         "path": "pruned" if use_pruned else "unpruned",
         "dtype": wl.dtype,
-        "pairs": pairs,
+        "visible_pairs": pairs,
         "ms_per_step": wall * 1e3 / steps,
-        "event_ms_median": float(np.median(per_call_ms)),
-        "event_ms_min": float(np.min(per_call_ms)),
+        "pairs_per_s": pairs / (wall / steps),
+        "kernels_ms": {n: round(ms, 4) for n, (c, ms) in kernels.items()},
     }
-    res["pairs_per_s"] = pairs / (wall / steps)
-    if stats:
+    dom = max(kernels.items(), key=lambda kv: kv[1][1])
+    if use_pruned:
+        flops = stats["seed_pairs"] * PAIR_FLOPS + stats["screened_pairs"] * SCREEN_FLOPS
+        flops += stats["survivor_pairs"] * PAIR_FLOPS
         res["prune"] = stats
-    res["effective_tflops"] = pairs * PAIR_FLOPS / (res["event_ms_median"] * 1e-3) / 1e12
-    res["mfma_frac"] = res["effective_tflops"] / PEAK_TFLOPS[wl.dtype]
-    log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s, "
-        f"{res['effective_tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of {wl.dtype} peak)"
-        + (f", filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
-    del q, k, w, pos, qs, ks
+    else:
+        flops = pairs * PAIR_FLOPS
+    res["dominant_kernel"] = dom[0]
+    res["dominant_ms"] = dom[1][1]
+    res["executed_flops"] = flops
+    res["achieved_tflops"] = flops / (dom[1][1] * 1e-3) / 1e12
+    res["effective_tflops"] = pairs * PAIR_FLOPS / (res["ms_per_step"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s; "
+        f"{dom[0]} {dom[1][1]:.3f} ms at {res['achieved_tflops']:.0f} TFLOP/s ({100 * res['achieved_tflops'] / peak:.1f}%"
+        f" of {wl.dtype} peak)" + (f"; filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
+    del q, k, w, pos, qs, ks, ws
     torch.cuda.empty_cache()
     return res
-
-
-def _pruned_available():
-    return os.environ.get("DSA_BENCH_PRUNED", "1") == "1" and _probe_pruned()
-
-
-_PRUNED_OK = None
-
-
-def _probe_pruned():
-    global _PRUNED_OK
-    if _PRUNED_OK is None:
-        import torch
-
-        import dsa_lightning_indexer_04_amd as dsa
-        from dsa_lightning_indexer_04_amd import inputs
-
-        d = inputs.make_inputs(1, 8, 256, "bf16", "clustered", seed=0)
-        try:
-            dsa.topk_pruned(*(d[n].cuda() for n in ("q", "k", "w", "pos")), 16)
-            torch.cuda.synchronize()
-            _PRUNED_OK = True
-        except Exception:
-            _PRUNED_OK = False
-    return _PRUNED_OK
 
 
 def cpu_baseline(name, rows_wanted):
@@ -159,7 +198,6 @@ def cpu_baseline(name, rows_wanted):
     rng = np.random.default_rng(0)
     Q = wl.num_q
     threads = _blas_threads()
-    # one row first, to size the sample to ~15 s of CPU work
     order = [Q - 1, 0] + list(rng.permutation(Q))
     done_pairs, t_total, rows = 0, 0.0, 0
     for t in order:
@@ -183,9 +221,9 @@ def cpu_baseline(name, rows_wanted):
         "unit": "pairs/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{rows} of {Q} query rows of {name} (first, last, then random by rng(0)); "
-        f"float64 numpy scores + lexsort Top-K; {done_pairs} visible pairs in {t_total:.1f}s, "
-        "rate scaled by visible pairs",
+        "sample": f"{rows} of {Q} query rows of {name} (last, first, then random by rng(0)); "
+        f"float64 numpy scores + lexsort Top-K; {done_pairs} visible pairs in {t_total:.1f}s; "
+        "pairs/s of the sample",
     }
 
 
@@ -193,8 +231,7 @@ def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
 
-        info = threadpool_info()
-        n = [i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"]
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
         if n:
             return int(max(n))
     except Exception:
@@ -204,16 +241,19 @@ def _blas_threads():
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
-        print(
-            json.dumps({"error": "this build measures one GPU only; the indexer is sharded by query rows "
-                        "across GPUs with no collective, see the design notes", "n_gpus": args.gpus}),
-            flush=True,
-        )
+        print(json.dumps({"error": "this benchmark measures one GPU; rows shard across GPUs with no "
+                          "collective (see the design notes), so no multi-GPU figure is produced",
+                          "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
 
     assert torch.cuda.is_available(), "bench needs a GPU"
+    from dsa_lightning_indexer_04_amd import inputs
+
     main_res = run_workload(args.workload, args.path, args.steps, args.warmup)
     extra = {}
     if args.also and args.also != "none":
@@ -222,26 +262,24 @@ def main():
                 continue
             name, _, pth = item.partition(":")
             extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
-    kt = main_res["event_ms_median"]
     peak = PEAK_TFLOPS[main_res["dtype"]]
     roofline = {
         "bound": "mfma",
-        "achieved": main_res["effective_tflops"],
+        "achieved": main_res["achieved_tflops"],
         "peak": peak,
         "unit": "TFLOP/s",
-        "frac": main_res["effective_tflops"] / peak,
-        "traffic": None,
-        "kernel": "k_topk_stream" if main_res["path"] == "unpruned" else "pruned path (all kernels)",
-        "per_launch_flops": main_res["pairs"] * PAIR_FLOPS,
-        "launch_ms": kt,
+        "frac": main_res["achieved_tflops"] / peak,
+        "traffic": measured_traffic(args.workload, main_res["dominant_kernel"]),
+        "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+        "kernel": main_res["dominant_kernel"],
+        "launch_ms": main_res["dominant_ms"],
+        "flops_per_launch": main_res["executed_flops"],
     }
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores ...")
         cpu = cpu_baseline(args.workload, args.cpu_rows)
         log(f"[bench] oracle: {cpu['value']:.3e} pairs/s on {cpu['cores']} threads")
-    from dsa_lightning_indexer_04_amd import inputs
-
     wl = inputs.WORKLOADS[args.workload]
     line = {
         "metric": "indexer scored query-key pairs/s (+Top-K)",
@@ -266,10 +304,11 @@ def main():
             "heads": 64,
             "head_dim": 128,
             "path": main_res["path"],
-            "visible_pairs": main_res["pairs"],
+            "visible_pairs": main_res["visible_pairs"],
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "detail": main_res,
         "also": extra,
     }
     print(json.dumps(line), flush=True)

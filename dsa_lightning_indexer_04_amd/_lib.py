@@ -63,6 +63,8 @@ EXPORTED = [
     "dsa_indexer_workspace_bytes",
     "dsa_indexer_error_string",
     "dsa_indexer_last_error",
+    "dsa_indexer_profile_begin",
+    "dsa_indexer_profile_end",
 ]
 
 _lib = None
@@ -102,6 +104,11 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_error_string.restype = ctypes.c_char_p
     lib.dsa_indexer_last_error.argtypes = []
     lib.dsa_indexer_last_error.restype = ctypes.c_char_p
+    lib.dsa_indexer_profile_begin.argtypes = []
+    lib.dsa_indexer_profile_begin.restype = ctypes.c_int
+    lib.dsa_indexer_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(I32),
+                                            ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    lib.dsa_indexer_profile_end.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -258,3 +265,20 @@ def topk_pruned(
         )
     )
     return idx, sc, st
+
+
+def profile_begin():
+    """Open a per-kernel timing window (events on the launch stream)."""
+    load().dsa_indexer_profile_begin()
+
+
+def profile_end(max_kernels: int = 16) -> dict:
+    """Close the window: {kernel name: (launches, mean ms)}."""
+    lib = load()
+    names = (ctypes.c_char_p * max_kernels)()
+    counts = (ctypes.c_int32 * max_kernels)()
+    means = (ctypes.c_double * max_kernels)()
+    n = lib.dsa_indexer_profile_end(names, counts, means, max_kernels)
+    if n < 0:
+        raise IndexerError(4, "profile window: HIP error")
+    return {names[i].decode(): (int(counts[i]), float(means[i])) for i in range(min(n, max_kernels))}

@@ -6,6 +6,11 @@
 
 namespace dsa {
 
+// Optional per-kernel event timing (see dsa_indexer_profile.h): a launcher
+// brackets its launch with prof_open / prof_close on the launch stream.
+int prof_open(const char* name, hipStream_t st);
+void prof_close(int slot, hipStream_t st);
+
 struct Problem {
   int B, Q, N, dtype;
   const uint8_t* q;

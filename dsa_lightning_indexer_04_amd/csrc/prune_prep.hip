@@ -400,25 +400,30 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
 
 hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, int32_t* seeds, int32_t* seed_count,
                             uint32_t* bits, int32_t* batch_flag, hipStream_t st) {
+  const int prof_slot = prof_open("k_seed_prep", st);
   const int words = (p.N + 31) / 32;
   hipLaunchKernelGGL(k_seed_prep, dim3(p.B), dim3(256), 0, st, p.pos, p.Q, p.N, S, user_seeds, seeds, seed_count,
                      bits, words, batch_flag);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 
 hipError_t launch_key_norms(const Problem& p, float* knorm, hipStream_t st) {
+  const int prof_slot = prof_open("k_key_norms", st);
   const size_t n = (size_t)p.B * p.N;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_key_norms<kBF16>, grid, dim3(256), 0, st, p.k, n, knorm);
   else
     hipLaunchKernelGGL(k_key_norms<kFP8>, grid, dim3(256), 0, st, p.k, n, knorm);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 
 hipError_t launch_plan(const Problem& p, int nret, const int32_t* seeds, const int32_t* seed_count, int seed_stride,
                        const int32_t* batch_flag, const uint8_t* force_recover, uint8_t* plan_rows, float* plan_coef,
                        float* plan_misc, int32_t* plan_flag, hipStream_t st) {
+  const int prof_slot = prof_open("k_plan", st);
   const dim3 grid((unsigned)((size_t)p.B * p.Q));
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_plan<kBF16>, grid, dim3(64), 0, st, p.q, p.k, p.w, p.pos, p.Q, p.N, nret, seeds,
@@ -426,6 +431,7 @@ hipError_t launch_plan(const Problem& p, int nret, const int32_t* seeds, const i
   else
     hipLaunchKernelGGL(k_plan<kFP8>, grid, dim3(64), 0, st, p.q, p.k, p.w, p.pos, p.Q, p.N, nret, seeds, seed_count,
                        seed_stride, batch_flag, force_recover, plan_rows, plan_coef, plan_misc, plan_flag);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void k_scores(const uint8_t* __restrict__ q, c
 }
 
 hipError_t launch_scores(const Problem& p, float* scores, hipStream_t st) {
+  const int prof_slot = prof_open("k_scores", st);
   const int kpw = 2048;
   dim3 grid((unsigned)(p.B * p.Q), (p.N + kpw - 1) / kpw);
   if (p.dtype == kBF16)
@@ -59,6 +60,7 @@ hipError_t launch_scores(const Problem& p, float* scores, hipStream_t st) {
   else
     hipLaunchKernelGGL(k_scores<kFP8>, grid, dim3(256), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
                        scores, p.Q, p.N, kpw);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 
@@ -161,8 +163,10 @@ __global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ 
 
 hipError_t launch_select_rows(const Problem& p, const float* scores, int topk, int32_t* out_idx, float* out_score,
                               hipStream_t st) {
+  const int prof_slot = prof_open("k_select_rows", st);
   hipLaunchKernelGGL(k_select_rows, dim3(p.B * p.Q), dim3(1024), 0, st, scores, p.pos, p.N, topk, out_idx,
                      out_score);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 

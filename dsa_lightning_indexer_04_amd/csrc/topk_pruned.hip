@@ -387,12 +387,14 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
                pb.seed_stride, pb.seed_bits, pb.bits_stride, pb.st_tau, pb.st_screened, pb.st_surv, pb.st_rec,
                pb.st_ub};
   dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
+  const int prof_slot = prof_open("k_topk_pruned", st);
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_topk_pruned<kBF16>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
                        p.pos, p.Q, p.N, topk, cap, cand, out_idx, out_score, pp);
   else
     hipLaunchKernelGGL(k_topk_pruned<kFP8>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
                        p.pos, p.Q, p.N, topk, cap, cand, out_idx, out_score, pp);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 

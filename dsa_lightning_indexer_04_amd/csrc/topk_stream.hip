@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
 hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
                               float* out_score, hipStream_t st) {
+  const int prof_slot = prof_open("k_topk_stream", st);
   dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_topk_stream<kBF16>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
@@ -126,6 +127,7 @@ hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* can
   else
     hipLaunchKernelGGL(k_topk_stream<kFP8>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
                        p.Q, p.N, topk, cap, cand, out_idx, out_score);
+  prof_close(prof_slot, st);
   return hipGetLastError();
 }
 
