@@ -25,6 +25,7 @@
 // lane-local over 32 heads, then one cross-half exchange adds the other 32.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace dsa {
@@ -76,6 +77,13 @@ __device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* row, int l
   }
 }
 
+// Wait for every outstanding vector-memory load of this wave (s_waitcnt
+// vmcnt(0), other counters untouched).  Issued once after the loop-invariant
+// loads (query fragments, weights): without it the compiler cannot tell at
+// the loop head that they have landed and waits for vmcnt(0) inside the key
+// loop, which also waits for the next tile's prefetch.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -83,19 +91,22 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// One k-step of a 32x32 block: acc += A(32 rows) x B(32 keys)^T over the
+// step's slice of the 128 dims.
+template <int DT>
+__device__ __forceinline__ f32x16 mma_step(const Frag<DT>& a, const Frag<DT>& b, int i, f32x16 acc) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[i]), __builtin_bit_cast(bf16x8, b.v[i]),
+                                                   acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v[i], b.v[i], acc, 0, 0, 0, 127, 0, 127);
+}
+
 // acc += A(32 rows) x B(32 keys)^T over K = 128.
 template <int DT>
 __device__ __forceinline__ f32x16 mma_block(const Frag<DT>& a, const Frag<DT>& b, f32x16 acc) {
-  if constexpr (DT == kBF16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[i]),
-                                                     __builtin_bit_cast(bf16x8, b.v[i]), acc, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v[i], b.v[i], acc, 0, 0, 0, 127, 0, 127);
-  }
+  for (int i = 0; i < Frag<DT>::kSteps; ++i) acc = mma_step<DT>(a, b, i, acc);
   return acc;
 }
 
@@ -196,6 +207,40 @@ __device__ __forceinline__ float query_partial(const QuerySide<DT>& qs, const Fr
   return head_partial(s0, s1, qs.wl);
 }
 
+// One software-pipelined step of a key scan: the MFMAs of a new 32-key block
+// (into n0/n1, the same k-step sequence as mma_block from zero) issued one by
+// one, each followed by its share of the previous block's head sum (p0/p1),
+// so one wave keeps the matrix core and the vector ALU busy together.  The
+// head sum is head_partial's, operation for operation: chain g starts at +0
+// and takes relu(p0[4g+e]) * wl[0][4g+e] for e = 0..3, then the same over
+// p1 and wl[1]; only the four chains are interleaved with each other.
+template <int DT>
+__device__ __forceinline__ float pipelined_partial(const QuerySide<DT>& qs, const Frag<DT>& kb, const f32x16& p0,
+                                                   const f32x16& p1, f32x16& n0, f32x16& n1) {
+  constexpr int kMfma = 2 * Frag<DT>::kSteps;
+  constexpr int kUnits = 32 / kMfma;  // (relu, fma) pairs after each MFMA
+  float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  n0 = zero16();
+  n1 = zero16();
+#pragma unroll
+  for (int m = 0; m < kMfma; ++m) {
+    if ((m & 1) == 0)
+      n0 = mma_step<DT>(qs.a[0], kb, m >> 1, n0);
+    else
+      n1 = mma_step<DT>(qs.a[1], kb, m >> 1, n1);
+#pragma unroll
+    for (int u = m * kUnits; u < (m + 1) * kUnits; ++u) {
+      const int e = u >> 2, g = u & 3;
+      const float x = e < 4 ? p0[4 * g + e] : p1[4 * g + e - 4];
+      const float wv = e < 4 ? qs.wl[0][4 * g + e] : qs.wl[1][4 * g + e - 4];
+      c[g] = __builtin_fmaf(relu_bits(x), wv, c[g]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // this MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kUnits, 0);  // then its VALU share
+  }
+  return (c[0] + c[1]) + (c[2] + c[3]);
+}
+
 // Cross-half exchange.  Lanes 0..31 hold partials (p0 of query A, p1 of
 // query B) over heads with (row/4) even, lanes 32..63 the other heads, for
 // key column l%32.  Returns, in lanes 0..31, A's full sum for key l; in
@@ -235,5 +280,13 @@ __device__ __forceinline__ uint64_t make_record(float s, uint32_t key) {
 }
 __device__ __forceinline__ uint32_t record_key(uint64_t r) { return 0xFFFFFFFFu - (uint32_t)r; }
 __device__ __forceinline__ float record_score(uint64_t r) { return mono_decode((uint32_t)(r >> 32)); }
+
+// A float that every score whose record is >= thr reaches (s >= it), for a
+// cheap pre-test before building records: the decoded high half of thr, or
+// -inf when that half lies below every finite score's code.
+__device__ __forceinline__ float record_floor(uint64_t thr) {
+  const uint32_t c = (uint32_t)(thr >> 32);
+  return c < 0x00800000u ? -INFINITY : mono_decode(c);
+}
 
 }  // namespace dsa

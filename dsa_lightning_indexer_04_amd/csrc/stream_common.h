@@ -11,24 +11,33 @@ namespace dsa {
 constexpr int kWaves = 8;           // query rows per workgroup, one per wave
 constexpr int kTileBytes = 16384;   // one LDS key tile (64 bf16 or 128 fp8 keys)
 
+// LDS key tile layout: chunk-major with one chunk of padding per chunk row.
+// 16-byte chunk c of tile key r lives at chunk index c * (KT + 1) + r, so
+//  - the 32 (or 16) lanes that read chunk c of consecutive keys read one
+//    contiguous run (conflict-free), and a lane's successive chunks are a
+//    constant stride apart (immediate ds_read offsets from one base address);
+//  - the 16 (bf16) / 8 (fp8) threads that store the chunks of one key hit
+//    different banks, the row pitch being (KT + 1) * 16 bytes.
+constexpr int kTileChunks = 1040;  // max over dtypes of (chunks per key) * (KT + 1)
+
 template <int DT>
-__device__ __forceinline__ int swz_chunk(int key, int c) {
-  constexpr int CPR = Frag<DT>::kRowBytes / 16;  // 16-byte chunks per row
-  return key * CPR + (c ^ (key & (CPR - 1)));
+__device__ __forceinline__ int tile_chunk(int key, int c) {
+  constexpr int KT = kTileBytes / Frag<DT>::kRowBytes;
+  return c * (KT + 1) + key;
 }
 
-// Fragment of key `key` (tile-relative) from the swizzled LDS tile.
+// Fragment of key `key` (tile-relative) from an LDS tile.
 template <int DT>
 __device__ __forceinline__ void load_frag_lds(Frag<DT>& f, const u32x4* tile, int key, int lane) {
   constexpr int CPL = Frag<DT>::kLaneBytes / 16;  // chunks per lane
   const int c0 = (lane >> 5) * CPL;
   if constexpr (DT == kBF16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.v[i] = tile[swz_chunk<DT>(key, c0 + i)];
+    for (int i = 0; i < 8; ++i) f.v[i] = tile[tile_chunk<DT>(key, c0 + i)];
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      u32x4 lo = tile[swz_chunk<DT>(key, c0 + 2 * i)], hi = tile[swz_chunk<DT>(key, c0 + 2 * i + 1)];
+      u32x4 lo = tile[tile_chunk<DT>(key, c0 + 2 * i)], hi = tile[tile_chunk<DT>(key, c0 + 2 * i + 1)];
       f.v[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   }
@@ -135,7 +144,7 @@ struct TileFetch {
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       const int c = tid + j * kWaves * 64;
-      tile[swz_chunk<DT>(c / CPR, c % CPR)] = v[j];
+      tile[tile_chunk<DT>(c / CPR, c % CPR)] = v[j];
     }
     if (tid < KT) {
       if constexpr (DT == kFP8) kst[tid] = ks;

@@ -65,9 +65,9 @@ template <int DT>
 __device__ __forceinline__ void load_sfrag_lds(SFrag<DT>& f, const u32x4* tile, int key, int lane) {
   if constexpr (DT == kBF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = tile[swz_chunk<DT>(key, 4 * (lane >> 4) + i)];
+    for (int i = 0; i < 4; ++i) f.v[i] = tile[tile_chunk<DT>(key, 4 * (lane >> 4) + i)];
   } else {
-    const u32x4 lo = tile[swz_chunk<DT>(key, 2 * (lane >> 4))], hi = tile[swz_chunk<DT>(key, 2 * (lane >> 4) + 1)];
+    const u32x4 lo = tile[tile_chunk<DT>(key, 2 * (lane >> 4))], hi = tile[tile_chunk<DT>(key, 2 * (lane >> 4) + 1)];
     f.v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 }
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int RB = Frag<DT>::kRowBytes;
   constexpr int KT = kTileBytes / RB;
   constexpr int NSB = KT / 32;
-  __shared__ u32x4 ktile[2][kTileBytes / 16];
+  __shared__ u32x4 ktile[2][kTileChunks];
   __shared__ float kscale_tile[2][KT];
   __shared__ uint32_t hist[kWaves][kH1Bins];
   __shared__ uint64_t stage[kWaves][KT + 32];
@@ -205,6 +205,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       tf.fetch(kbase, kscb, 0, N, tid, sd, nseed);
       tf.commit(ktile[0], kscale_tile[0], tid);
     }
+    wait_vmem_all();
     __syncthreads();
     for (int ti = 0; ti < ntiles; ++ti) {
       const int cur = ti & 1;
@@ -268,6 +269,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       tf.fetch(kbase, kscb, 0, N, tid, nullptr, 0, knb, sbits);
       tf.commit(ktile[0], kscale_tile[0], tid, knorm_tile[0], sbits_tile[0]);
     }
+    wait_vmem_all();
     __syncthreads();
     // Lane l reports key slot ks = (l & 15) + 16 * (l >> 5) of a 32-key block
     // after the butterfly below (lanes 16..31 and 48..63 repeat 0..15/32..47).
