@@ -169,13 +169,13 @@ struct PruneConfig {
 
 int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
   pc->num_seeds = (o && o->num_seeds) ? o->num_seeds : 12288;
-  pc->num_retained = (o && o->num_retained) ? o->num_retained : 14;
+  pc->num_retained = (o && o->num_retained) ? o->num_retained : 30;
   pc->seed_idx = o ? o->seed_idx : nullptr;
   pc->force_recover = o ? o->force_recover : nullptr;
   if (pc->num_seeds < 1 || pc->num_seeds > (1 << 26)) return fail(DSA_ERR_INVALID_ARG, "num_seeds out of range");
   if (o && o->seed_idx && o->num_seeds < 1) return fail(DSA_ERR_INVALID_ARG, "seed_idx needs num_seeds > 0");
-  if (pc->num_retained < 1 || pc->num_retained > 14)
-    return fail(DSA_ERR_UNSUPPORTED, "num_retained must be in 1..14");
+  if (pc->num_retained < 1 || pc->num_retained > 30)
+    return fail(DSA_ERR_UNSUPPORTED, "num_retained must be in 1..30");
   if (pc->seed_idx && !aligned16(pc->seed_idx)) return fail(DSA_ERR_INVALID_ARG, "seed_idx must be 16-byte aligned");
   return DSA_OK;
 }
@@ -193,8 +193,8 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
     return base ? base + o : nullptr;
   };
   uint8_t* c = take(R * (uint64_t)dsa::stream_capacity(topk) * 8);
-  uint8_t* rows = take(R * 16 * 128 * elem_bytes(in->dtype));
-  uint8_t* coef = take(R * 16 * 4);
+  uint8_t* rows = take(R * 32 * 128 * elem_bytes(in->dtype));
+  uint8_t* coef = take(R * 32 * 4);
   uint8_t* misc = take(R * 4 * 4);
   uint8_t* flag = take(R * 4);
   uint8_t* kn = take(B * N * 4);

@@ -37,8 +37,8 @@ hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* can
 
 // Device buffers of the pruned Top-K (workspace carve-up and optional stats).
 struct PrunedBuffers {
-  uint8_t* plan_rows;  // [B*Q][16][128] dtype
-  float* plan_coef;    // [B*Q][16]
+  uint8_t* plan_rows;  // [B*Q][32][128] dtype
+  float* plan_coef;    // [B*Q][32]
   float* plan_misc;    // [B*Q][4]
   int32_t* plan_flag;  // [B*Q]
   float* knorm;        // [B][N]

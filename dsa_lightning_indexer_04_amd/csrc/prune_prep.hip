@@ -4,20 +4,23 @@
 // The bound (DoSA reading notes, annotation LBKERZAW, step 2; 机器之心 DoSA
 // article, section 03), for one query row with heads j, weights w_j and the
 // shared key k, with d_i = q_i . k:
-//   * retained heads R (scored exactly);
-//   * omitted positive-weight heads P: least-squares projection
-//     q_j = sum_{i in R} C_ji q_i + r_j, so with ReLU subadditive and
-//     positively homogeneous,
+//   * retained heads R (scored exactly): up to 30 positive-weight heads;
+//   * omitted positive-weight heads P: projection onto the retained rows
+//     q_j = sum_{i in R} C_ji q_i + r_j with nonnegative C (approximate
+//     nonnegative least squares), so with ReLU subadditive and positively
+//     homogeneous,
 //       w_j ReLU(q_j.k) <= w_j sum_i [C_ji^+ ReLU(d_i) + C_ji^- ReLU(-d_i)]
 //                          + w_j |r_j| |k|;
-//   * omitted negative-weight heads: the selected subset N' folded by |w|
-//     into one row q_neg; sum |w_j| ReLU(q_j.k) >= ReLU(q_neg . k).
+//   * negative-weight heads (none is retained): the selected subset N'
+//     folded by |w| into one row q_neg; sum |w_j| ReLU(q_j.k) >= ReLU(q_neg . k).
 // Summing:  I <= sum_{i in R} [a_i ReLU(d_i) + b_i ReLU(-d_i)] + rho |k|
 //                - ReLU(q_neg . k),
 // a_i = w_i + sum_P w_j C_ji^+,  b_i = sum_P w_j C_ji^-,  rho = sum_P w_j |r_j|.
 // With c_i = (a_i + b_i)/2 and e_i = (a_i - b_i)/2 the retained part is
 // sum_i c_i |d_i| + E . k, E = sum_i e_i q_i, so the GPU screen needs one
-// fp32 FMA per retained row plus one extra "linear" row E.  E and q_neg are
+// fp32 FMA per retained row plus one extra "linear" row E.  With C >= 0,
+// b_i = 0 and c_i = e_i = a_i / 2 >= 0, and the fold is tight whenever the
+// retained dots share a sign (no cancellation inside a projection).  E and q_neg are
 // rounded to the input dtype; their rounding errors (measured here in fp64)
 // and a guard for every fp32 rounding of the score and of the bound are
 // added to the |k| coefficient, so the computed bound dominates the computed
@@ -119,10 +122,11 @@ __global__ __launch_bounds__(256) void k_key_norms(const uint8_t* __restrict__ k
 
 // ---------------------------------------------------------------- planner
 
-constexpr int kRetained = 14;   // retained heads: plan rows 0..13
-constexpr int kAuxRow = 14;     // folded negative-head row
-constexpr int kLinRow = 15;     // linear row E
-constexpr int kPlanRows = 16;
+constexpr int kRetained = 30;   // retained heads: plan rows 0..29
+constexpr int kAuxRow = 30;     // folded negative-head row
+constexpr int kLinRow = 31;     // linear row E
+constexpr int kPlanRows = 32;
+constexpr int kSweeps = 20;     // coordinate-descent sweeps of the projection
 constexpr int kSamples = 128;   // sample keys for the activation statistics
 constexpr int kQPad = kDim + 1; // padded LDS row (conflict-free column reads)
 
@@ -165,8 +169,8 @@ __device__ __forceinline__ double round_to_dtype(double v, uint32_t* code) {
   }
 }
 
-// One wave per query row.  Writes the 16 bound rows (dtype), the per-row
-// coefficients (c_0..c_13, aux-row multiplier, linear-row multiplier), the
+// One wave per query row.  Writes the 32 bound rows (dtype), the per-row
+// coefficients (c_0..c_29, aux-row multiplier, linear-row multiplier), the
 // |k| coefficient kappa and the aux rounding bound e_neg, and the recovery
 // flag (non-finite plan, forced, or invalid seeds for the sequence).
 template <int DT>
@@ -181,7 +185,8 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
   constexpr int RB = Frag<DT>::kRowBytes;
   __shared__ float qs[kHeads][kQPad];
   __shared__ float kk[kDim];
-  __shared__ double G[kRetained][kRetained];
+  __shared__ float G[kRetained][kRetained];
+  __shared__ double cch[kRetained];  // c_i = e_i (folded retained coefficients)
   __shared__ int ridx[kRetained];
   __shared__ double vec[2][kDim];  // E, q_neg (fp64)
   const int lane = threadIdx.x;
@@ -220,60 +225,66 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
     npos += x > 0.0f;
   }
 
-  // 3. retained set: the nret heads with the largest |w_j| * activation
-  const float key_j = fabsf((float)wj) * act;
+  // 3. retained set: the (at most nret) positive-weight heads with the
+  //    largest w_j * activation
+  const float key_j = wj > 0.0 ? (float)wj * act : -1.0f;
   int rank = 0;
   for (int i = 0; i < kHeads; ++i) {
     const float ki = __shfl(key_j, i, 64);
     rank += (ki > key_j) || (ki == key_j && i < lane);
   }
-  const bool retained = rank < nret;
+  const int npos_heads = __popcll(__ballot(wj > 0.0));
+  nret = min(nret, npos_heads);
+  const bool retained = wj > 0.0 && rank < nret;
   if (retained) ridx[rank] = lane;
   __syncthreads();
 
-  // 4. Gram matrix of the retained rows (fp64), slightly regularised: any
-  //    coefficients give a valid bound, so the ridge only keeps the solve sane
+  // 4. Gram matrix of the retained rows (fp64 sums, kept in fp32: it only
+  //    steers the projection, whose residual is measured exactly below)
   for (int e = lane; e < nret * nret; e += 64) {
     const int a = e / nret, c = e % nret;
     double g = 0.0;
     for (int d = 0; d < kDim; ++d) g = fma((double)qs[ridx[a]][d], (double)qs[ridx[c]][d], g);
-    G[a][c] = g;
+    G[a][c] = (float)g;
   }
   __syncthreads();
-  double diag_max = 0.0;
-  for (int a = 0; a < nret; ++a) diag_max = fmax(diag_max, G[a][a]);
-  const double ridge = 1e-9 * diag_max + 1e-300;
 
-  // 5. each omitted positive head (lane) projects onto the retained rows:
-  //    Cholesky of (G + ridge I) once (lane 0, into LDS), then every lane
-  //    solves for its own coefficients C; residual norm in fp64
-  __shared__ double Lf[kRetained][kRetained];
-  if (lane == 0) {
-    for (int a = 0; a < nret; ++a) {
-      for (int c = 0; c <= a; ++c) {
-        double s = G[a][c] + (a == c ? ridge : 0.0);
-        for (int m = 0; m < c; ++m) s -= Lf[a][m] * Lf[c][m];
-        Lf[a][c] = (a == c) ? sqrt(fmax(s, ridge)) : s / Lf[c][c];
+  // 5. each omitted positive head (lane) projects onto the retained rows
+  //    with nonnegative coefficients: coordinate descent on
+  //    min |q_j - C Q_R|^2, C >= 0, from C = 0, a fixed number of sweeps.
+  //    Any C >= 0 gives a valid bound (convergence only tightens it); the
+  //    residual is then measured in fp64 from the C actually used.
+  const bool in_P = !retained && wj > 0.0;
+  float C[kRetained];
+  float bq[kRetained];
+  double rnorm = 0.0;
+#pragma unroll
+  for (int a = 0; a < kRetained; ++a) {
+    C[a] = 0.0f;
+    bq[a] = 0.0f;
+  }
+  if (in_P && nret > 0) {
+#pragma unroll
+    for (int a = 0; a < kRetained; ++a) {
+      if (a < nret) {
+        float bsum = 0.0f;
+        for (int d = 0; d < kDim; ++d) bsum = fmaf(qs[ridx[a]][d], qs[lane][d], bsum);
+        bq[a] = bsum;
       }
     }
-  }
-  __syncthreads();
-  const bool in_P = !retained && wj > 0.0;
-  double C[kRetained];
-  double rnorm = 0.0;
-  for (int a = 0; a < kRetained; ++a) C[a] = 0.0;
-  if (in_P && nret > 0) {
-    double y[kRetained];
-    for (int a = 0; a < nret; ++a) {
-      double bsum = 0.0;
-      for (int d = 0; d < kDim; ++d) bsum = fma((double)qs[ridx[a]][d], (double)qs[lane][d], bsum);
-      for (int m = 0; m < a; ++m) bsum -= Lf[a][m] * y[m];
-      y[a] = bsum / Lf[a][a];
-    }
-    for (int a = nret - 1; a >= 0; --a) {
-      double s = y[a];
-      for (int m = a + 1; m < nret; ++m) s -= Lf[m][a] * C[m];
-      C[a] = s / Lf[a][a];
+    for (int sw = 0; sw < kSweeps; ++sw) {
+      // re-read G from LDS each sweep (keeps its 900 entries out of registers)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < kRetained; ++i) {
+        if (i < nret && G[i][i] > 0.0f) {
+          float g = -bq[i];
+#pragma unroll
+          for (int m = 0; m < kRetained; ++m)
+            if (m < nret) g = fmaf(C[m], G[m][i], g);
+          C[i] = fmaxf(0.0f, C[i] - g / G[i][i]);
+        }
+      }
     }
   }
   if (in_P) {
@@ -281,9 +292,12 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
     for (int d = 0; d < kDim; ++d) {
       double r = qs[lane][d];
       double m = fabs(r);
-      for (int a = 0; a < nret; ++a) {
-        r = fma(-C[a], (double)qs[ridx[a]][d], r);
-        m += fabs(C[a] * qs[ridx[a]][d]);
+#pragma unroll
+      for (int a = 0; a < kRetained; ++a) {
+        if (a < nret) {
+          r = fma(-(double)C[a], (double)qs[ridx[a]][d], r);
+          m += fabs((double)C[a] * qs[ridx[a]][d]);
+        }
       }
       r2 = fma(r, r, r2);
       rmag = fmax(rmag, m);
@@ -292,20 +306,23 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
     rnorm = sqrt(r2) + 32.0 * (nret + 2) * 1.1102230246251565e-16 * rmag * sqrt((double)kDim);
   }
 
-  // 6. folded coefficients a_i, b_i (sums over P), rho
+  // 6. folded coefficients (C >= 0, so b_i = 0): a_i = w_i + sum_P w_j C_ji,
+  //    c_i = e_i = a_i / 2 (wave-uniform, kept in LDS); rho = sum_P w_j |r_j|
   const double rho = wave_sum_d(in_P ? wj * rnorm : 0.0);
-  double cc[kRetained], ee[kRetained];
+#pragma unroll
   for (int a = 0; a < kRetained; ++a) {
-    const double ap = wave_sum_d(in_P ? wj * fmax(C[a], 0.0) : 0.0);
-    const double bp = wave_sum_d(in_P ? wj * fmax(-C[a], 0.0) : 0.0);
-    const double wa = a < nret ? __shfl(wj, ridx[a], 64) : 0.0;
-    const double alpha = wa + ap, beta = bp;
-    cc[a] = a < nret ? 0.5 * (alpha + beta) : 0.0;
-    ee[a] = a < nret ? 0.5 * (alpha - beta) : 0.0;
+    if (a < nret) {
+      const double ap = wave_sum_d(in_P ? wj * (double)C[a] : 0.0);
+      const double wa = __shfl(wj, ridx[a], 64);
+      if (lane == 0) cch[a] = 0.5 * (wa + ap);
+    } else if (lane == 0) {
+      cch[a] = 0.0;
+    }
   }
+  __syncthreads();
 
-  // 7. folded negative row: omitted negative heads active on >= half the
-  //    samples (all omitted negative heads if none is)
+  // 7. folded negative row: negative heads active on >= half the samples
+  //    (all negative heads if none is)
   const bool negom = !retained && wj < 0.0;
   const bool act_half = negom && 2 * npos >= nsamp && nsamp > 0;
   const bool use_half = __ballot(act_half) != 0;
@@ -314,7 +331,9 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
   // 8. E and q_neg in fp64 (lanes over dims), rounded to the dtype
   for (int d = lane; d < kDim; d += 64) {
     double e = 0.0;
-    for (int a = 0; a < nret; ++a) e = fma(ee[a], (double)qs[ridx[a]][d], e);
+#pragma unroll
+    for (int a = 0; a < kRetained; ++a)
+      if (a < nret) e = fma(cch[a], (double)qs[ridx[a]][d], e);
     vec[0][d] = e;
     double n = 0.0;
     for (int j = 0; j < kHeads; ++j) {
@@ -369,21 +388,25 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
   //    (g_128 + 2 g_64) W1 |k| (128-term dots, 64-term head sum, final
   //    combine), and the fp32 bound from its exact value by at most
   //    (g_128 + g_24) Wb |k| + g_24 (e_neg + rho + e_lin) |k|, where
-  //    g_n = n u / (1 - n u), u = 2^-24.  Doubled for margin.
+  //    g_n = n u / (1 - n u), u = 2^-24 (the screen adds each lane's 16
+  //    rows in one chain, then the other half's sum and the |k| term: at
+  //    most 20 roundings per term, within g_24).  Doubled for margin.
   const double u = 5.9604644775390625e-08;
   auto gam = [u](double n) { return n * u / (1.0 - n * u); };
   const double W1 = wave_sum_d(fabs(wj) * qnorm);
   double Wb = n_lin + n_neg;
-  for (int a = 0; a < nret; ++a) Wb += fabs(cc[a]) * __shfl(qnorm, ridx[a], 64);
+#pragma unroll
+  for (int a = 0; a < kRetained; ++a)
+    if (a < nret) Wb += fabs(cch[a]) * __shfl(qnorm, ridx[a], 64);
   const double guard =
       2.0 * ((gam(128) + 2.0 * gam(64) + gam(4)) * W1 + (gam(128) + gam(24)) * Wb + gam(24) * (e_neg + rho + e_lin));
   const double kappa = (rho + e_lin + guard) * (1.0 + 1e-9);
 
   bool finite = isfinite(kappa) && isfinite(e_neg) && isfinite(mult[0]) && isfinite(mult[1]);
-  for (int a = 0; a < kRetained; ++a) finite = finite && isfinite(cc[a]);
+  for (int a = 0; a < kRetained; ++a) finite = finite && isfinite(cch[a]);
   if (lane == 0) {
     float* co = plan_coef + row * kPlanRows;
-    for (int a = 0; a < kRetained; ++a) co[a] = __double2float_ru(cc[a]);
+    for (int a = 0; a < kRetained; ++a) co[a] = __double2float_ru(cch[a]);
     co[kAuxRow] = (float)mult[1];
     co[kLinRow] = (float)mult[0];
     float* mi = plan_misc + row * 4;

@@ -60,14 +60,14 @@ struct Cut {
   uint64_t thr;
 };
 
-// Cut the row's candidates (buffer + stage) back towards `topk` and raise
-// the threshold.  Rare: called when the buffer would overflow.
+// Cut the row's candidates (buffer + stage) back to at most `goal` (>= topk)
+// records and raise the threshold to the cut's boundary; goal == topk keeps
+// exactly the best topk, so the threshold becomes the K-th best record seen.
 static __device__ __noinline__ Cut cut_candidates(uint64_t* buf, int cnt, const uint64_t* stage, int nst, uint32_t* hist,
-                                           int topk, int cap, int lane) {
+                                           int topk, int goal, int lane) {
   cnt = flush_stage(buf, cnt, stage, nst, lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
-  const SelectResult sel =
-      select_records(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)(topk + (cap - topk) / 2), lane);
+  const SelectResult sel = select_records(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)goal, lane);
   return {compact_records(buf, cnt, sel, hist, lane), sel.prefix};
 }
 

@@ -28,67 +28,15 @@
 
 namespace dsa {
 
-constexpr int kPlanRowsK = 16;
-constexpr int kLinRowK = 15;
-constexpr int kAuxRowK = 14;
-constexpr int kRetainedK = 14;
-
-// ---------------------------------------------------------------- screen MFMA
-// 16x16 blocks: lane l feeds row (or key) l%16 with dims 32*(l/16)..+31
-// (bf16: v_mfma_f32_16x16x32_bf16 x 4; fp8: v_mfma_scale_f32_16x16x128_f8f6f4
-// with unit scales).  Output: lane l holds key l%16, rows 4*(l/16)+v.
-template <int DT>
-struct SFrag;
-template <>
-struct SFrag<kBF16> {
-  u32x4 v[4];
-};
-template <>
-struct SFrag<kFP8> {
-  i32x8 v;
-};
-
-template <int DT>
-__device__ __forceinline__ void load_sfrag(SFrag<DT>& f, const uint8_t* row, int lane) {
-  constexpr int LB = DT == kBF16 ? 64 : 32;  // bytes per lane
-  const u32x4* p = reinterpret_cast<const u32x4*>(row + (lane >> 4) * LB);
-  if constexpr (DT == kBF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = p[i];
-  } else {
-    const u32x4 lo = p[0], hi = p[1];
-    f.v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ void load_sfrag_lds(SFrag<DT>& f, const u32x4* tile, int key, int lane) {
-  if constexpr (DT == kBF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = tile[tile_chunk<DT>(key, 4 * (lane >> 4) + i)];
-  } else {
-    const u32x4 lo = tile[tile_chunk<DT>(key, 2 * (lane >> 4))], hi = tile[tile_chunk<DT>(key, 2 * (lane >> 4) + 1)];
-    f.v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ f32x4 mma16(const SFrag<DT>& a, const SFrag<DT>& b) {
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (DT == kBF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[i]),
-                                                     __builtin_bit_cast(bf16x8, b.v[i]), acc, 0, 0, 0);
-  } else {
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, acc, 0, 0, 0, 127, 0, 127);
-  }
-  return acc;
-}
+constexpr int kPlanRowsK = 32;
+constexpr int kLinRowK = 31;
+constexpr int kAuxRowK = 30;
+constexpr int kRetainedK = 30;
+constexpr int kCutSlack = 1024;  // records kept beyond topk before the threshold is raised
 
 struct PrunePlan {
-  const uint8_t* rows;       // [R][16][128] dtype: bound rows
-  const float* coef;         // [R][16]: c_0..c_13, aux multiplier, linear multiplier
+  const uint8_t* rows;       // [R][32][128] dtype: bound rows
+  const float* coef;         // [R][32]: c_0..c_29, aux multiplier, linear multiplier
   const float* misc;         // [R][4]: kappa, e_neg
   const int32_t* flag;       // [R]: 1 = recover (no pruning)
   const float* knorm;        // [B][N]: |k|, rounded up
@@ -116,7 +64,7 @@ __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live
   uint64_t bal = __ballot(live && rec >= rs.thr);
   if (bal) {
     if (rs.cnt + rs.nst + __popcll(bal) > cap) {
-      const Cut c = cut_candidates(rs.buf, rs.cnt, stage, rs.nst, hist, topk, cap, lane);
+      const Cut c = cut_candidates(rs.buf, rs.cnt, stage, rs.nst, hist, topk, topk, lane);
       rs.cnt = c.cnt;
       rs.thr = c.thr;
       rs.nst = 0;
@@ -170,19 +118,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const float* my_w = wrow[wave];
   const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
 
-  // screen side: plan row (lane % 16), coefficients of this lane's 4 rows
-  SFrag<DT> sa;
-  load_sfrag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 15)) * RB, lane);
+  // screen side: the 32 plan rows as one 32x32 MFMA A operand; lane l holds
+  // rows 8*(v/4) + 4*(l/32) + v%4 of the result (v = 0..15), with their
+  // coefficients in cl[v].  Rows 30 (aux) and 31 (linear) land in lanes
+  // 32..63 at v = 14, 15; the other lanes get zero multipliers for them.
+  Frag<DT> sa;
+  load_frag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 31)) * RB, lane);
   const float* co = pp.coef + row * kPlanRowsK;
-  float cl[4];
+  float cl[16];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int r = 4 * (lane >> 4) + v;
+  for (int v = 0; v < 16; ++v) {
+    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     cl[v] = r < kRetainedK ? co[r] : 0.0f;
   }
-  const float m_aux = co[kAuxRowK], m_lin = co[kLinRowK];
-  const float kappa = pp.misc[row * 4 + 0], e_neg = pp.misc[row * 4 + 1];
-  const bool special = (lane >> 4) == 3;  // holds rows 14 (aux) and 15 (linear)
+  const bool hi_half = lane >= 32;
+  const float m_aux = hi_half ? co[kAuxRowK] : 0.0f, m_lin = hi_half ? co[kLinRowK] : 0.0f;
+  const float kappa = pp.misc[row * 4 + 0], e_neg = hi_half ? pp.misc[row * 4 + 1] : 0.0f;
   const bool recover = pp.flag[row] != 0;
 
   uint32_t* my_hist = hist[wave];
@@ -271,11 +222,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
     wait_vmem_all();
     __syncthreads();
-    // Lane l reports key slot ks = (l & 15) + 16 * (l >> 5) of a 32-key block
-    // after the butterfly below (lanes 16..31 and 48..63 repeat 0..15/32..47).
-    const int kslot = (lane & 15) + 16 * (lane >> 5);
-    const bool g_lo = ((lane >> 5) & 1) == 0;   // lane groups 0,1 vs 2,3
-    const bool g_even = ((lane >> 4) & 1) == 0;  // lane groups 0,2 vs 1,3
+    const int lk = lane & 31;
     for (int ti = 0; ti < ntiles; ++ti) {
       const int cur = ti & 1;
       const int ts = ti * KT;
@@ -283,45 +230,38 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
         rs.nst = 0;
       }
+      // Keep the survivor threshold near the K-th best exact record seen so
+      // far: cut back to exactly topk records whenever kCutSlack more have
+      // been kept (a short radix select over ~topk + kCutSlack records).
+      if (rs.cnt >= topk + kCutSlack) {
+        const Cut c = cut_candidates(rs.buf, rs.cnt, my_stage, 0, my_hist, topk, topk, lane);
+        rs.cnt = c.cnt;
+        rs.thr = c.thr;
+      }
       if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, nullptr, 0, knb, sbits);
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         const int kb = ts + 32 * sb;
         if (kb < vis) {  // wave-uniform
-          // -- bound of 32 keys: two 16x16 blocks (keys kb..kb+15, kb+16..kb+31)
-          SFrag<DT> kf0, kf1;
-          load_sfrag_lds<DT>(kf0, ktile[cur], 32 * sb + (lane & 15), lane);
-          load_sfrag_lds<DT>(kf1, ktile[cur], 32 * sb + 16 + (lane & 15), lane);
-          const f32x4 d0 = mma16<DT>(sa, kf0);
-          const f32x4 d1 = mma16<DT>(sa, kf1);
-          const float kn0 = knorm_tile[cur][32 * sb + (lane & 15)];
-          const float kn1 = knorm_tile[cur][32 * sb + 16 + (lane & 15)];
-          float p0 = 0.0f, p1 = 0.0f;
+          // -- bound of 32 keys: one 32x32 block (32 plan rows x 32 keys);
+          //    each lane sums its 16 rows, the cross-half exchange the rest
+          Frag<DT> kf;
+          load_frag_lds<DT>(kf, ktile[cur], 32 * sb + lk, lane);
+          const f32x16 dd = mma_block<DT>(sa, kf, zero16());
+          const float kn = knorm_tile[cur][32 * sb + lk];
+          float p = 0.0f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            p0 = __builtin_fmaf(__builtin_fabsf(d0[v]), cl[v], p0);
-            p1 = __builtin_fmaf(__builtin_fabsf(d1[v]), cl[v], p1);
-          }
-          if (special) {  // lanes 48..63 hold the aux (14) and linear (15) rows
-            p0 += __builtin_fmaf(m_lin, d0[3], -relu_bits(__builtin_fmaf(m_aux, d0[2], -e_neg * kn0)));
-            p1 += __builtin_fmaf(m_lin, d1[3], -relu_bits(__builtin_fmaf(m_aux, d1[2], -e_neg * kn1)));
-          }
-          // butterfly over the four lane groups: groups 0,1 end with block 0's
-          // sum, groups 2,3 with block 1's (2 exchanges for both blocks)
-          const float a = (g_lo ? p0 : p1) + __shfl_xor(g_lo ? p1 : p0, 32, 64);
-          const float bsum = a + __shfl_xor(a, 16, 64);
-          const float kn = g_lo ? kn0 : kn1;
-          float U = __builtin_fmaf(kappa, kn, bsum);
-          if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][32 * sb + kslot]);
-          const int key = kb + kslot;
+          for (int v = 0; v < 16; ++v) p = __builtin_fmaf(__builtin_fabsf(dd[v]), cl[v], p);
+          p += __builtin_fmaf(m_lin, dd[15], -relu_bits(__builtin_fmaf(m_aux, dd[14], -e_neg * kn)));
+          float U = __builtin_fmaf(kappa, kn, combine_single(p));
+          if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][32 * sb + lk]);
+          const int key = kb + lk;
           const uint32_t seedw = sbits_tile[cur][sb];
-          const bool ck = g_even & (key < vis) & !((seedw >> kslot) & 1u);
+          const bool ck = (lane < 32) & (key < vis) & !((seedw >> lk) & 1u);
           const bool sv = ck & (recover | (make_record(U, (uint32_t)key) >= rs.thr));
           if (pp.st_ub && ck) pp.st_ub[row * (size_t)N + key] = U;
-          const uint64_t bck = __ballot(ck), bsv = __ballot(sv);
-          screened += __popcll(bck);
-          // survivor bits in key order: bits 0..15 <- lanes 0..15, 16..31 <- lanes 32..47
-          uint32_t mask = (uint32_t)(bsv & 0xFFFFull) | ((uint32_t)((bsv >> 32) & 0xFFFFull) << 16);
+          screened += __popcll(__ballot(ck));
+          uint32_t mask = (uint32_t)__ballot(sv);  // bit i: key kb + i survives
           survived += __popc(mask);
           // -- enqueue survivors into register slots (rank order), scoring a
           //    full queue; a block fills at most one queue, so two rounds

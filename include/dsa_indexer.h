@@ -100,10 +100,11 @@ int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_id
  *                 visible prefix; seeds rescored with all heads fix the
  *                 starting threshold tau (DoSA reading notes, annotation
  *                 LBKERZAW, step 1)
- *   num_retained  heads whose dot products the bound uses directly (0 -> 14,
- *                 range 1..14, else DSA_ERR_UNSUPPORTED); the bound also
+ *   num_retained  positive-weight heads whose dot products the bound uses
+ *                 directly (0 -> 30, range 1..30, else DSA_ERR_UNSUPPORTED;
+ *                 fewer if the row has fewer positive heads); the bound also
  *                 uses one folded negative-head row and one linear row that
- *                 carries the projected positive heads (16 rows in all)
+ *                 carries the projected positive heads (32 rows in all)
  *   seed_idx      [B,num_seeds] int32 device array of ascending, distinct
  *                 key indices, or NULL for evenly spaced seeds
  *                 floor(i*(p0+1)/S) over the common prefix 0..p0
