@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
                                              float* __restrict__ plan_misc, int32_t* __restrict__ plan_flag) {
   constexpr int RB = Frag<DT>::kRowBytes;
   __shared__ float qs[kHeads][kQPad];
-  __shared__ float kk[kDim];
+  __shared__ float red[kHeads][33];   // per-head staging of MFMA results
   __shared__ float G[kRetained][kRetained];
   __shared__ double cch[kRetained];  // c_i = e_i (folded retained coefficients)
   __shared__ int ridx[kRetained];
@@ -204,25 +204,56 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
   for (int d = 0; d < kDim; ++d) qn2 = fma((double)qs[lane][d], (double)qs[lane][d], qn2);
   const double qnorm = sqrt(qn2);
 
-  // 2. activation statistics of each head (lane = head) over sample keys
+  // 2. activation statistics of each head over 128 sample keys (seeds, or
+  //    evenly spaced visible keys): X = Q K_s^T by MFMA, 32 samples at a
+  //    time (dtype code units for fp8: the scales are positive, so signs and
+  //    the head ranking are those of the real values).  Lane l holds sample
+  //    l % 32 for heads 32*blk + 8*(v/4) + 4*(l/32) + v%4; the per-head sums
+  //    over the 32 sample columns go through LDS.
   const int nseed = seed_count[b];
   const int32_t* sb = seeds + (size_t)b * seed_stride;
   const int nsamp = min(kSamples, nseed > 0 ? nseed : vis);
+  Frag<DT> qa[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], qrow + (size_t)(32 * blk + (lane & 31)) * RB, lane);
+  float pa[2][16], pn[2][16];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pa[blk][v] = pn[blk][v] = 0.0f;
+  for (int s0 = 0; s0 < nsamp; s0 += 32) {
+    const int si = s0 + (lane & 31);
+    const bool okc = si < nsamp;
+    const int key = !okc ? 0 : nseed > 0 ? sb[(int)(((int64_t)si * nseed) / nsamp)] : (int)(((int64_t)si * vis) / nsamp);
+    Frag<DT> f;
+    load_frag<DT>(f, k + ((size_t)b * N + key) * RB, lane);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const f32x16 x = mma_block<DT>(qa[blk], f, zero16());
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        pa[blk][v] += okc ? relu_bits(x[v]) : 0.0f;
+        pn[blk][v] += (okc && x[v] > 0.0f) ? 1.0f : 0.0f;
+      }
+    }
+  }
   float act = 0.0f;
   int npos = 0;
-  for (int s = 0; s < nsamp; ++s) {
-    int key;
-    if (nseed > 0)
-      key = sb[(int)(((int64_t)s * nseed) / nsamp)];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = pass ? pn[blk][v] : pa[blk][v];
+    __syncthreads();
+    float sum = 0.0f;
+    for (int c = 0; c < 32; ++c) sum += red[lane][c];
+    if (pass)
+      npos = (int)sum;
     else
-      key = (int)(((int64_t)s * vis) / nsamp);
+      act = sum;
     __syncthreads();
-    for (int d = lane; d < kDim; d += 64) kk[d] = elem<DT>(k + ((size_t)b * N + key) * RB, d);
-    __syncthreads();
-    float x = 0.0f;
-    for (int d = 0; d < kDim; ++d) x = fmaf(qs[lane][d], kk[d], x);
-    act += fmaxf(x, 0.0f);
-    npos += x > 0.0f;
   }
 
   // 3. retained set: the (at most nret) positive-weight heads with the
@@ -239,13 +270,30 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
   if (retained) ridx[rank] = lane;
   __syncthreads();
 
-  // 4. Gram matrix of the retained rows (fp64 sums, kept in fp32: it only
-  //    steers the projection, whose residual is measured exactly below)
+  // 4. dots of every head with every retained row, G_full = Q Q_R^T, by one
+  //    MFMA pass (fp32: these only steer the projection, whose residual is
+  //    measured exactly below).  G = rows ridx of G_full; head j's
+  //    right-hand side b_j = row j of G_full.
+  {
+    Frag<DT> fr;
+    const int ri = (lane & 31) < nret ? ridx[lane & 31] : -1;
+    if (ri >= 0) {
+      load_frag<DT>(fr, qrow + (size_t)ri * RB, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Frag<DT>::kSteps; ++i) fr.v[i] = {};
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const f32x16 x = mma_block<DT>(qa[blk], fr, zero16());
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = x[v];
+    }
+  }
+  __syncthreads();
   for (int e = lane; e < nret * nret; e += 64) {
     const int a = e / nret, c = e % nret;
-    double g = 0.0;
-    for (int d = 0; d < kDim; ++d) g = fma((double)qs[ridx[a]][d], (double)qs[ridx[c]][d], g);
-    G[a][c] = (float)g;
+    G[a][c] = red[ridx[a]][c];
   }
   __syncthreads();
 
@@ -265,13 +313,8 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
   }
   if (in_P && nret > 0) {
 #pragma unroll
-    for (int a = 0; a < kRetained; ++a) {
-      if (a < nret) {
-        float bsum = 0.0f;
-        for (int d = 0; d < kDim; ++d) bsum = fmaf(qs[ridx[a]][d], qs[lane][d], bsum);
-        bq[a] = bsum;
-      }
-    }
+    for (int a = 0; a < kRetained; ++a)
+      if (a < nret) bq[a] = red[lane][a];
     for (int sw = 0; sw < kSweeps; ++sw) {
       // re-read G from LDS each sweep (keeps its 900 entries out of registers)
       asm volatile("" ::: "memory");
@@ -281,7 +324,7 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
           float g = -bq[i];
 #pragma unroll
           for (int m = 0; m < kRetained; ++m)
-            if (m < nret) g = fmaf(C[m], G[m][i], g);
+            if (m < nret) g = fmaf(C[m], G[i][m], g);  // G is symmetric: row i
           C[i] = fmaxf(0.0f, C[i] - g / G[i][i]);
         }
       }

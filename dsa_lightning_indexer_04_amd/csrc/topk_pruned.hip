@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ float kscale_tile[2][KT];
   __shared__ uint32_t hist[kWaves][kH1Bins];
   __shared__ uint64_t stage[kWaves][KT + 32];
-  __shared__ int32_t squeue[kWaves][64];
+  __shared__ int32_t squeue[kWaves][32 + KT];  // survivor list (see below)
   __shared__ float knorm_tile[2][KT];
   __shared__ uint32_t sbits_tile[2][KT / 32];
 
@@ -199,20 +199,41 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---------------------------------------------------------------- 2-3. screen + refine
-  // Survivor queue: 32 slots held in registers.  Slot s is lanes s and s+32,
-  // which hold the MFMA B fragment of the queued key (each its half of the
-  // row) -- loaded from the LDS tile the moment the key survives, so the
-  // refine never reads HBM.  A full queue is scored with all heads at once.
+  // Survivor list: key indices in the wave's LDS slots my_q[0..nq); a
+  // survivor costs the screen one LDS store.  Every 32 of them form a batch
+  // that is rescored with all heads: at a tile start lanes l and l + 32
+  // gather their halves of key my_q[l % 32] from memory into the register
+  // batch `g` (the keys were streamed a few tiles earlier, so mostly cache
+  // hits), and the batch is scored at the start of the next tile, by when
+  // the loads have landed.  After the tile-start drain nq < 32, so a tile
+  // leaves nq < 32 + KT.
   int nq = 0, screened = 0, survived = 0;
-  Frag<DT> fr;
-  int fr_key = 0;
-  float fr_ks = 1.0f;
-  auto refine_run = [&]() {
-    float s = combine_single(query_partial_w<DT>(qa, fr, my_w, lane));
-    if constexpr (DT == kFP8) s = apply_scales(s, qscale, fr_ks);
-    append_rec(rs, make_record(s, (uint32_t)fr_key), lane < 32 && (lane & 31) < nq, my_stage, my_hist, topk, cap,
-               lane);
-    nq = 0;
+  Frag<DT> g;
+  int gkey = 0, gn = 0;
+  float gks = 1.0f;
+  auto gather = [&](int n) {  // take my_q[0..n) (n in 1..32) into the batch; keep the rest
+    gkey = my_q[(lane & 31) < n ? (lane & 31) : 0];
+    load_frag<DT>(g, kbase + (size_t)gkey * RB, lane);
+    if constexpr (DT == kFP8) gks = kscb[gkey];
+    gn = n;
+    const int rest = nq - n;
+    for (int i = lane; i < rest; i += 64) {  // move the tail to the front
+      const int v = my_q[n + i];
+      my_q[i] = v;
+    }
+    nq = rest;
+  };
+  auto score_batch = [&]() {
+    if (gn > 0) {
+      if (rs.nst > KT) {  // the stage holds KT + 32 records: make room for this batch
+        rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+        rs.nst = 0;
+      }
+      float s = combine_single(query_partial_w<DT>(qa, g, my_w, lane));
+      if constexpr (DT == kFP8) s = apply_scales(s, qscale, gks);
+      append_rec(rs, make_record(s, (uint32_t)gkey), lane < gn, my_stage, my_hist, topk, cap, lane);
+      gn = 0;
+    }
   };
   {
     const int ntiles = (wg_vis + KT - 1) / KT;
@@ -237,6 +258,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         const Cut c = cut_candidates(rs.buf, rs.cnt, my_stage, 0, my_hist, topk, topk, lane);
         rs.cnt = c.cnt;
         rs.thr = c.thr;
+      }
+      // refine.  Gathers are issued before the tile prefetch: vector-memory
+      // waits are in issue order, so the tile-end wait for the prefetch also
+      // covers the gather, and a later tile scores the batch without waiting.
+      score_batch();
+      while (nq >= 32) {
+        gather(32);
+        if (nq >= 32) score_batch();  // only when survivors come faster than a batch per tile
       }
       if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, nullptr, 0, knb, sbits);
 #pragma unroll
@@ -263,36 +292,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
           screened += __popcll(__ballot(ck));
           uint32_t mask = (uint32_t)__ballot(sv);  // bit i: key kb + i survives
           survived += __popc(mask);
-          // -- enqueue survivors into register slots (rank order), scoring a
-          //    full queue; a block fills at most one queue, so two rounds
+          // -- append survivors to the list (key order)
           if (mask) {
-            mask = __builtin_amdgcn_readfirstlane(mask);
-            const int m = __popc(mask);
-            const int take = min(m, 32 - nq);
-            const bool mine = lane < 32 && ((mask >> lane) & 1u);
-            const int rank = __popc(mask & ((1u << (lane & 31)) - 1u));
-            if (mine && rank < take) my_q[nq + rank] = lane;
-            const int slot = lane & 31;
-            if (slot >= nq && slot < nq + take) {
-              const int off = my_q[slot];
-              load_frag_lds<DT>(fr, ktile[cur], 32 * sb + off, lane);
-              fr_key = kb + off;
-              if constexpr (DT == kFP8) fr_ks = kscale_tile[cur][32 * sb + off];
-            }
-            nq = __builtin_amdgcn_readfirstlane(nq + take);
-            if (nq == 32) {
-              refine_run();
-              if (take < m) {
-                if (mine && rank >= take) my_q[rank - take] = lane;
-                if (slot < m - take) {
-                  const int off = my_q[slot];
-                  load_frag_lds<DT>(fr, ktile[cur], 32 * sb + off, lane);
-                  fr_key = kb + off;
-                  if constexpr (DT == kFP8) fr_ks = kscale_tile[cur][32 * sb + off];
-                }
-                nq = m - take;
-              }
-            }
+            const int rank = __popc(mask & ((1u << lk) - 1u));
+            if (sv) my_q[nq + rank] = key;
+            nq += __popc(mask);
           }
         }
       }
@@ -300,7 +304,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       __syncthreads();
     }
   }
-  if (nq > 0) refine_run();
+  score_batch();
+  while (nq > 0) {
+    gather(min(nq, 32));
+    score_batch();
+  }
 
   // ---------------------------------------------------------------- 4. select
   if (!valid) return;
