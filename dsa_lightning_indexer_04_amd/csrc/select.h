@@ -155,6 +155,55 @@ static __device__ __noinline__ int compact_records(uint64_t* buf, int cnt, Selec
   return base;
 }
 
+// Variant without the incremental first-digit histogram, for paths that
+// select rarely and cannot spare 8 KB of LDS per row: eight passes of 8-bit
+// digits over a 256-bin histogram, each pass reading the buffer.  Same
+// result contract as select_records.
+static __device__ __noinline__ SelectResult select_records_d8(const uint64_t* buf, int cnt, uint32_t need,
+                                                              uint32_t* hist, bool exact, uint32_t goal, int lane) {
+  uint64_t prefix = 0, mask = 0;
+  uint32_t remaining = need, kept = (uint32_t)cnt;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int S = 56 - 8 * pass;
+    for (uint32_t i = lane; i < 256; i += 64) hist[i] = 0;
+    hist_pass(buf, cnt, prefix, mask, S, 256, hist, lane);
+    uint32_t bin, above, count;
+    find_boundary(hist, 256, remaining, lane, bin, above, count);
+    prefix |= (uint64_t)bin << S;
+    mask |= (uint64_t)0xFF << S;
+    remaining -= above;
+    kept = need - remaining + count;
+    if (count == remaining) break;  // boundary bin taken whole: exact
+    if (!exact && kept <= goal) break;
+  }
+  return {prefix, mask, kept};
+}
+
+// In place: keep records with (r & mask) >= prefix, in their order (no
+// histogram upkeep).  Returns the kept count.
+static __device__ __noinline__ int compact_records_d8(uint64_t* buf, int cnt, SelectResult sel, int lane) {
+  int base = 0;
+  for (int i0 = 0; i0 < cnt; i0 += 512) {
+    uint64_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      r[j] = i < cnt ? buf[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      const bool keep = i < cnt && (r[j] & sel.mask) >= sel.prefix;
+      const uint64_t bal = __ballot(keep);
+      const uint32_t before =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep) buf[base + before] = r[j];
+      base += __popcll(bal);
+    }
+  }
+  return base;
+}
+
 // Smallest of the cnt records in buf (all lanes get it; ~0 if cnt == 0).
 static __device__ __noinline__ uint64_t min_record(const uint64_t* buf, int cnt, int lane) {
   uint64_t mn = ~0ull;

@@ -103,6 +103,46 @@ static __device__ __noinline__ void emit_topk(uint64_t* buf, int cnt, const uint
   }
 }
 
+// The same pair for rows without the incremental histogram (8-bit digits).
+static __device__ __noinline__ Cut cut_candidates_d8(uint64_t* buf, int cnt, const uint64_t* stage, int nst,
+                                                     uint32_t* hist, int topk, int goal, int lane) {
+  cnt = flush_stage(buf, cnt, stage, nst, lane);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  const SelectResult sel = select_records_d8(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)goal, lane);
+  return {compact_records_d8(buf, cnt, sel, lane), sel.prefix};
+}
+
+static __device__ __noinline__ void emit_topk_d8(uint64_t* buf, int cnt, const uint64_t* stage, int nst,
+                                                 uint32_t* hist, int topk, int32_t* oi, float* os, int lane) {
+  cnt = flush_stage(buf, cnt, stage, nst, lane);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  const int need = min(topk, cnt);
+  SelectResult sel = {0, 0, 0};
+  if (need > 0) sel = select_records_d8(buf, cnt, (uint32_t)need, hist, true, 0, lane);
+  int base = 0;
+  for (int i0 = 0; i0 < cnt; i0 += 64) {
+    const int i = i0 + lane;
+    uint64_t r = 0;
+    bool keep = false;
+    if (i < cnt) {
+      r = buf[i];
+      keep = (r & sel.mask) >= sel.prefix;
+    }
+    const uint64_t bal = __ballot(keep);
+    const uint32_t before =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (keep) {
+      oi[base + before] = (int32_t)record_key(r);
+      if (os) os[base + before] = record_score(r);
+    }
+    base += __popcll(bal);
+  }
+  for (int j = need + lane; j < topk; j += 64) {
+    oi[j] = -1;
+    if (os) os[j] = -INFINITY;
+  }
+}
+
 // Next key tile: each thread fetches two 16-byte chunks into registers at the
 // start of a tile and stores them (swizzled) into the other LDS buffer at its
 // end, so the fetch latency hides behind the current tile's MFMAs.  Keys at

@@ -33,6 +33,8 @@ constexpr int kLinRowK = 31;
 constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
 constexpr int kCutSlack = 1024;  // records kept beyond topk before the threshold is raised
+constexpr int kRing = 6;         // LDS key tiles: the screen's, the next one, and four awaiting refinement
+constexpr int kRefineEvery = 4;  // tiles between refine rounds
 
 struct PrunePlan {
   const uint8_t* rows;       // [R][32][128] dtype: bound rows
@@ -64,17 +66,15 @@ __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live
   uint64_t bal = __ballot(live && rec >= rs.thr);
   if (bal) {
     if (rs.cnt + rs.nst + __popcll(bal) > cap) {
-      const Cut c = cut_candidates(rs.buf, rs.cnt, stage, rs.nst, hist, topk, topk, lane);
+      const Cut c = cut_candidates_d8(rs.buf, rs.cnt, stage, rs.nst, hist, topk, topk, lane);
       rs.cnt = c.cnt;
       rs.thr = c.thr;
       rs.nst = 0;
       bal = __ballot(live && rec >= rs.thr);
     }
-    if (live && rec >= rs.thr) {
+    if (live && rec >= rs.thr)
       stage[rs.nst + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
           rec;
-      atomicAdd(&hist[(uint32_t)(rec >> kH1Shift)], 1u);
-    }
     rs.nst += __popcll(bal);
   }
 }
@@ -88,13 +88,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int RB = Frag<DT>::kRowBytes;
   constexpr int KT = kTileBytes / RB;
   constexpr int NSB = KT / 32;
-  __shared__ u32x4 ktile[2][kTileChunks];
-  __shared__ float kscale_tile[2][KT];
-  __shared__ uint32_t hist[kWaves][kH1Bins];
+  __shared__ u32x4 ktile[kRing][kTileChunks];
+  __shared__ float kscale_tile[kRing][KT];
+  __shared__ uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits)
   __shared__ uint64_t stage[kWaves][KT + 32];
-  __shared__ int32_t squeue[kWaves][32 + KT];  // survivor list (see below)
-  __shared__ float knorm_tile[2][KT];
-  __shared__ uint32_t sbits_tile[2][KT / 32];
+  __shared__ int32_t squeue[kWaves][kRefineEvery * KT];  // survivor list (see below)
+  __shared__ float knorm_tile[kRing][KT];
+  __shared__ uint32_t sbits_tile[kRing][KT / 32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = gridDim.x - 1 - blockIdx.x;
@@ -139,7 +139,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   uint32_t* my_hist = hist[wave];
   uint64_t* my_stage = stage[wave];
   int32_t* my_q = squeue[wave];
-  for (uint32_t i = lane; i < kH1Bins; i += 64) my_hist[i] = 0;
   RowState rs{cand + row * (size_t)cap, 0, 0, 0};
   const uint8_t* kbase = k + (size_t)b * N * RB;
   const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
@@ -192,48 +191,37 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
   float tau = -INFINITY;
   if (rs.cnt >= topk) {
-    const SelectResult sel = select_records(rs.buf, rs.cnt, (uint32_t)topk, my_hist, true, 0, lane);
-    rs.cnt = compact_records(rs.buf, rs.cnt, sel, my_hist, lane);
+    const SelectResult sel = select_records_d8(rs.buf, rs.cnt, (uint32_t)topk, my_hist, true, 0, lane);
+    rs.cnt = compact_records_d8(rs.buf, rs.cnt, sel, lane);
     rs.thr = min_record(rs.buf, rs.cnt, lane);
     tau = record_score(rs.thr);
   }
 
   // ---------------------------------------------------------------- 2-3. screen + refine
-  // Survivor list: key indices in the wave's LDS slots my_q[0..nq); a
-  // survivor costs the screen one LDS store.  Every 32 of them form a batch
-  // that is rescored with all heads: at a tile start lanes l and l + 32
-  // gather their halves of key my_q[l % 32] from memory into the register
-  // batch `g` (the keys were streamed a few tiles earlier, so mostly cache
-  // hits), and the batch is scored at the start of the next tile, by when
-  // the loads have landed.  After the tile-start drain nq < 32, so a tile
-  // leaves nq < 32 + KT.
+  // Key tiles stream through a ring of kRing LDS slots (tile ti in slot
+  // ti % kRing).  The screen appends surviving keys to the wave's list
+  // my_q[0..nq) (one LDS store per survivor); every kRefineEvery tiles all
+  // waves rescore their lists together, 32 keys per MFMA batch, with the key
+  // fragments read from the ring (the survivors' tiles are still resident:
+  // a slot is refilled only kRing tiles later).  Refining in the same tiles
+  // keeps the eight waves, which meet at every tile, in step.
   int nq = 0, screened = 0, survived = 0;
-  Frag<DT> g;
-  int gkey = 0, gn = 0;
-  float gks = 1.0f;
-  auto gather = [&](int n) {  // take my_q[0..n) (n in 1..32) into the batch; keep the rest
-    gkey = my_q[(lane & 31) < n ? (lane & 31) : 0];
-    load_frag<DT>(g, kbase + (size_t)gkey * RB, lane);
-    if constexpr (DT == kFP8) gks = kscb[gkey];
-    gn = n;
-    const int rest = nq - n;
-    for (int i = lane; i < rest; i += 64) {  // move the tail to the front
-      const int v = my_q[n + i];
-      my_q[i] = v;
-    }
-    nq = rest;
-  };
-  auto score_batch = [&]() {
-    if (gn > 0) {
+  auto refine_round = [&]() {
+    for (int p0 = 0; p0 < nq; p0 += 32) {
+      const int n = min(32, nq - p0);
+      const int key = my_q[p0 + ((lane & 31) < n ? (lane & 31) : 0)];
+      const int tk = key / KT, r = key - tk * KT, slot = tk % kRing;
+      Frag<DT> f;
+      load_frag_lds<DT>(f, ktile[slot], r, lane);
+      float s = combine_single(query_partial_w<DT>(qa, f, my_w, lane));
+      if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[slot][r]);
       if (rs.nst > KT) {  // the stage holds KT + 32 records: make room for this batch
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
         rs.nst = 0;
       }
-      float s = combine_single(query_partial_w<DT>(qa, g, my_w, lane));
-      if constexpr (DT == kFP8) s = apply_scales(s, qscale, gks);
-      append_rec(rs, make_record(s, (uint32_t)gkey), lane < gn, my_stage, my_hist, topk, cap, lane);
-      gn = 0;
+      append_rec(rs, make_record(s, (uint32_t)key), lane < n, my_stage, my_hist, topk, cap, lane);
     }
+    nq = 0;
   };
   {
     const int ntiles = (wg_vis + KT - 1) / KT;
@@ -245,29 +233,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     __syncthreads();
     const int lk = lane & 31;
     for (int ti = 0; ti < ntiles; ++ti) {
-      const int cur = ti & 1;
+      const int cur = ti % kRing;
       const int ts = ti * KT;
+      // The loop is bound by the latency of the next tile's fetch: issue it
+      // first, so that refine rounds and cuts run in its shadow.
+      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, nullptr, 0, knb, sbits);
+      if (ti > 0 && ti % kRefineEvery == 0) refine_round();
       if (rs.nst) {
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
         rs.nst = 0;
       }
       // Keep the survivor threshold near the K-th best exact record seen so
       // far: cut back to exactly topk records whenever kCutSlack more have
-      // been kept (a short radix select over ~topk + kCutSlack records).
+      // been kept.
       if (rs.cnt >= topk + kCutSlack) {
-        const Cut c = cut_candidates(rs.buf, rs.cnt, my_stage, 0, my_hist, topk, topk, lane);
+        const Cut c = cut_candidates_d8(rs.buf, rs.cnt, my_stage, 0, my_hist, topk, topk, lane);
         rs.cnt = c.cnt;
         rs.thr = c.thr;
       }
-      // refine.  Gathers are issued before the tile prefetch: vector-memory
-      // waits are in issue order, so the tile-end wait for the prefetch also
-      // covers the gather, and a later tile scores the batch without waiting.
-      score_batch();
-      while (nq >= 32) {
-        gather(32);
-        if (nq >= 32) score_batch();  // only when survivors come faster than a batch per tile
-      }
-      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, nullptr, 0, knb, sbits);
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         const int kb = ts + 32 * sb;
@@ -290,29 +273,25 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
           const bool sv = ck & (recover | (make_record(U, (uint32_t)key) >= rs.thr));
           if (pp.st_ub && ck) pp.st_ub[row * (size_t)N + key] = U;
           screened += __popcll(__ballot(ck));
-          uint32_t mask = (uint32_t)__ballot(sv);  // bit i: key kb + i survives
+          const uint32_t mask = (uint32_t)__ballot(sv);  // bit i: key kb + i survives
           survived += __popc(mask);
-          // -- append survivors to the list (key order)
-          if (mask) {
-            const int rank = __popc(mask & ((1u << lk) - 1u));
-            if (sv) my_q[nq + rank] = key;
+          if (mask) {  // append the survivors to the list (key order)
+            if (sv) my_q[nq + __popc(mask & ((1u << lk) - 1u))] = key;
             nq += __popc(mask);
           }
         }
       }
-      if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid, knorm_tile[cur ^ 1], sbits_tile[cur ^ 1]);
+      if (ti + 1 < ntiles)
+        tf.commit(ktile[(ti + 1) % kRing], kscale_tile[(ti + 1) % kRing], tid, knorm_tile[(ti + 1) % kRing],
+                  sbits_tile[(ti + 1) % kRing]);
       __syncthreads();
     }
-  }
-  score_batch();
-  while (nq > 0) {
-    gather(min(nq, 32));
-    score_batch();
+    refine_round();  // the last tiles' survivors (their slots are untouched)
   }
 
   // ---------------------------------------------------------------- 4. select
   if (!valid) return;
-  emit_topk(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
+  emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
             out_score ? out_score + row * (size_t)topk : nullptr, lane);
   if (lane == 0) {
     if (pp.st_tau) pp.st_tau[row] = tau;
