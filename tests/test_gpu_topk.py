@@ -43,6 +43,7 @@ CASES = [
     (1, 9, 3000, 16, "bf16", "iid"),  # many buffer compactions
     (1, 12, 400, 500, "bf16", "iid"),  # fewer visible keys than k
     (2, 10, 1100, 128, "fp8", "clustered"),
+    (2, 7, 1001, 50, "bf16", "iid"),  # odd row length: unaligned score rows on the split path
 ]
 
 
