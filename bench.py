@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 # HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
 # dispatch, mean over dispatches), scaled by what the same counters read for a
 # 1 GiB device copy (FETCH x2.000, WRITE x1.000).  Valid only for the kernel
@@ -37,8 +38,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("chunked_prefill_128k", "k_topk_stream"): ("8f67374fd62d8d9e", 1700319, 2010090),
-    ("chunked_prefill_128k", "k_topk_pruned"): ("8f67374fd62d8d9e", 6424360, 1968081),
+    ("chunked_prefill_128k", "k_topk_stream"): ("e448565d1a79e527", 1702830, 2003118),
+    ("chunked_prefill_128k", "k_topk_pruned"): ("e448565d1a79e527", 3651151, 4044612),
 }
 PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
 SCREEN_FLOPS = 2 * 128 * 16  # 16-row bound of one pair
@@ -54,10 +55,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunked_prefill_128k")
-    ap.add_argument("--path", choices=["auto", "topk", "pruned"], default="auto")
+    ap.add_argument("--path", choices=["auto", "topk", "pruned"], default="topk",
+                    help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one)")
     ap.add_argument(
         "--also",
-        default="chunked_prefill_128k:topk,context_1m_fp8:pruned,context_1m_fp8:topk",
+        default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,prefill_32k:topk,"
+        "decode_64x128k:topk",
         help="comma list of extra workload[:path] runs (or 'none')",
     )
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,6 +176,18 @@ def run_workload(name, path, steps, warmup):
     res["achieved_tflops"] = flops / (dom[1][1] * 1e-3) / 1e12
     res["effective_tflops"] = pairs * PAIR_FLOPS / (res["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
+    if wl.num_q == 1:
+        # one query row per sequence (decode): every key row is read once and
+        # serves 64 heads, far below the MFMA ridge point -> HBM-bound
+        key_bytes = wl.batch * wl.num_k * (256 if wl.dtype == "bf16" else 128 + 4)
+        q_bytes = wl.batch * 64 * (256 if wl.dtype == "bf16" else 128) + wl.batch * 64 * 4
+        alg = key_bytes + q_bytes + wl.batch * wl.num_k * 4  # + the stored score rows
+        res["roofline"] = {"bound": "hbm", "achieved": alg / (dom[1][1] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "kernel": dom[0], "bytes_per_launch": alg}
+    else:
+        res["roofline"] = {"bound": "mfma", "achieved": res["achieved_tflops"], "peak": peak, "unit": "TFLOP/s",
+                           "kernel": dom[0], "flops_per_launch": flops}
+    res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
     log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s; "
         f"{dom[0]} {dom[1][1]:.3f} ms at {res['achieved_tflops']:.0f} TFLOP/s ({100 * res['achieved_tflops'] / peak:.1f}%"
         f" of {wl.dtype} peak)" + (f"; filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
@@ -262,6 +277,12 @@ def main():
                 continue
             name, _, pth = item.partition(":")
             extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
+    for wname in {args.workload} | {k.partition(":")[0] for k in extra}:
+        runs = [r for r in [main_res, *extra.values()] if r["workload"] == wname]
+        t = {r["path"]: r["ms_per_step"] for r in runs}
+        if "pruned" in t and "unpruned" in t:
+            for r in runs:
+                r["pruned_over_unpruned_time"] = t["pruned"] / t["unpruned"]
     peak = PEAK_TFLOPS[main_res["dtype"]]
     roofline = {
         "bound": "mfma",
