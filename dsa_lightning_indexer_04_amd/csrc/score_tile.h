@@ -241,23 +241,26 @@ __device__ __forceinline__ float pipelined_partial(const QuerySide<DT>& qs, cons
   return (c[0] + c[1]) + (c[2] + c[3]);
 }
 
-// Cross-half exchange.  Lanes 0..31 hold partials (p0 of query A, p1 of
-// query B) over heads with (row/4) even, lanes 32..63 the other heads, for
-// key column l%32.  Returns, in lanes 0..31, A's full sum for key l; in
-// lanes 32..63, B's full sum for key l-32.  Each lane adds its own partial
-// and its partner's (lane^32); fp32 addition is commutative, so every path
-// gets the same bits for a (query, key) pair.
-// (The exchange goes through ds_bpermute: at -O3 this compiler folds the two
-// results of the gfx950 permlane32 swap builtin into one.)
-__device__ __forceinline__ float combine_halves(float p0, float p1, int lane) {
-  const bool lo = lane < 32;
-  const float own = lo ? p0 : p1;
-  const float send = lo ? p1 : p0;
-  return own + __shfl_xor(send, 32, 64);
-}
-
-// Single query: the full sum for key l%32 in every lane.
+// Cross-half sum through an LDS permute: the same bits as combine_swap.
+// Kernels whose MFMA/VALU interleave is steered by scheduling groups use
+// this form: the scheduler does not group around the inline asm of the swap.
 __device__ __forceinline__ float combine_single(float p) { return p + __shfl_xor(p, 32, 64); }
+
+// Cross-half sum: lanes l and l^32 hold the two halves (heads with row/4
+// even / odd) of the same key column's head sum; every lane gets p[l] +
+// p[l^32].  One v_permlane32_swap of two copies of p leaves lanes 0..31 of
+// the first copy and lanes 32..63 of the second unchanged and swaps the
+// other halves, so first + second is the pair sum in every lane (fp32
+// addition is commutative: the same bits in both lanes of a pair, and in
+// every path).  Written in inline asm because this compiler folds the two
+// results of the permlane32 swap builtin into one; the s_nop pairs keep two
+// wait states on both sides of the swap.  A VALU swap instead of an LDS
+// permute keeps the exchange off the LDS queue.
+__device__ __forceinline__ float combine_swap(float p) {
+  float a = p, b = p;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
 
 // Dequantisation of fp8 scores: (q_scale * k_scale) * head_sum, same order everywhere.
 __device__ __forceinline__ float apply_scales(float sum, float qscale, float kscale) {

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_scores(const uint8_t* __restrict__ q, c
         const int key = kc + lk;
         float s = -INFINITY;
         if (kc < vis) {  // wave-uniform
-          float tot = combine_single(query_partial<DT>(qs, f[h]));
+          float tot = combine_swap(query_partial<DT>(qs, f[h]));
           if constexpr (DT == kFP8) tot = apply_scales(tot, qscale, ksc[(size_t)b * N + min(key, N - 1)]);
           s = key < vis ? tot : -INFINITY;
         }

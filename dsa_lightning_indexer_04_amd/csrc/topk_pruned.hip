@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
           const int key = sd[min(si, nseed - 1)];
           Frag<DT> f;
           load_frag_lds<DT>(f, ktile[cur], 32 * sb + (lane & 31), lane);
-          float s = combine_single(query_partial_w<DT>(qa, f, my_w, lane));
+          float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
           if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[cur][32 * sb + (lane & 31)]);
           append_rec(rs, make_record(s, (uint32_t)key), lane < 32 && si < nseed && key < vis, my_stage, my_hist,
                      topk, cap, lane);
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       const int tk = key / KT, r = key - tk * KT, slot = tk % kRing;
       Frag<DT> f;
       load_frag_lds<DT>(f, ktile[slot], r, lane);
-      float s = combine_single(query_partial_w<DT>(qa, f, my_w, lane));
+      float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
       if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[slot][r]);
       if (rs.nst > KT) {  // the stage holds KT + 32 records: make room for this batch
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
           for (int v = 0; v < 16; ++v) p = __builtin_fmaf(__builtin_fabsf(dd[v]), cl[v], p);
           p += __builtin_fmaf(m_lin, dd[15], -relu_bits(__builtin_fmaf(m_aux, dd[14], -e_neg * kn)));
-          float U = __builtin_fmaf(kappa, kn, combine_single(p));
+          float U = __builtin_fmaf(kappa, kn, combine_swap(p));
           if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][32 * sb + lk]);
           const int key = kb + lk;
           const uint32_t seedw = sbits_tile[cur][sb];
