@@ -214,20 +214,27 @@ __device__ __forceinline__ float query_partial(const QuerySide<DT>& qs, const Fr
 // head sum is head_partial's, operation for operation: chain g starts at +0
 // and takes relu(p0[4g+e]) * wl[0][4g+e] for e = 0..3, then the same over
 // p1 and wl[1]; only the four chains are interleaved with each other.
-template <int DT>
-__device__ __forceinline__ float pipelined_partial(const QuerySide<DT>& qs, const Frag<DT>& kb, const f32x16& p0,
-                                                   const f32x16& p1, f32x16& n0, f32x16& n1) {
+// Rolling operand prefetch: once both MFMAs of k-step i have been issued,
+// step i of kb is dead and `next(i)` reloads it with step i of the next
+// block's key fragment, so the LDS reads of block j+1 run under block j's
+// MFMAs and no MFMA waits on a fresh LDS read.
+template <int DT, class Next>
+__device__ __forceinline__ float pipelined_partial(const QuerySide<DT>& qs, Frag<DT>& kb, const f32x16& p0,
+                                                   const f32x16& p1, f32x16& n0, f32x16& n1, Next&& next) {
   constexpr int kMfma = 2 * Frag<DT>::kSteps;
   constexpr int kUnits = 32 / kMfma;  // (relu, fma) pairs after each MFMA
+  constexpr int kReads = Frag<DT>::kLaneBytes / 16 / Frag<DT>::kSteps;  // ds_read_b128 per k-step
   float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   n0 = zero16();
   n1 = zero16();
 #pragma unroll
   for (int m = 0; m < kMfma; ++m) {
-    if ((m & 1) == 0)
+    if ((m & 1) == 0) {
       n0 = mma_step<DT>(qs.a[0], kb, m >> 1, n0);
-    else
+    } else {
       n1 = mma_step<DT>(qs.a[1], kb, m >> 1, n1);
+      next(m >> 1);
+    }
 #pragma unroll
     for (int u = m * kUnits; u < (m + 1) * kUnits; ++u) {
       const int e = u >> 2, g = u & 3;
@@ -235,7 +242,8 @@ __device__ __forceinline__ float pipelined_partial(const QuerySide<DT>& qs, cons
       const float wv = e < 4 ? qs.wl[0][4 * g + e] : qs.wl[1][4 * g + e - 4];
       c[g] = __builtin_fmaf(relu_bits(x), wv, c[g]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // this MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // this MFMA
+    if (m & 1) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // the freed step's reload
     __builtin_amdgcn_sched_group_barrier(0x002, 2 * kUnits, 0);  // then its VALU share
   }
   return (c[0] + c[1]) + (c[2] + c[3]);

@@ -6,36 +6,24 @@
 // records" is a unique set.
 //
 // A selection is (prefix, mask): the kept records are those r with
-// (r & mask) >= prefix.  Digits come from the top: bits 63..53 first, then
-// 11/10/11/11/10 more bits; it stops as soon as the digit bin holding the
-// boundary is taken whole (exact), or -- for a mid-scan cut of a candidate
-// buffer -- as soon as the kept count is small enough.  `prefix` is always a
-// valid running threshold: every record below it is beaten by at least
-// `need` kept records.
-//
-// The first digit's histogram (H1, 2048 bins over bits 63..53) is kept up to
-// date by the caller as records are appended, so the first pass costs no
-// buffer read.  Later passes read the buffer 8 records per lane at a time so
-// that many loads are in flight.
+// (r & mask) >= prefix.  Digits come from the top, 8 bits at a time; it
+// stops as soon as the digit bin holding the boundary is taken whole
+// (exact), or -- for a mid-scan cut of a candidate buffer -- as soon as the
+// kept count is small enough.  `prefix` is always a valid running
+// threshold: every record below it is beaten by at least `need` kept
+// records.  Passes read the buffer 8 records per lane at a time so that
+// many loads are in flight.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dsa {
 
-constexpr int kH1Shift = 53;
-constexpr uint32_t kH1Bins = 2048;
-
 struct SelectResult {
   uint64_t prefix;
   uint64_t mask;
   uint32_t kept;  // number of records with (r & mask) >= prefix
 };
-
-__device__ __forceinline__ int digit_shift(int pass) {
-  return pass == 0 ? 53 : pass == 1 ? 42 : pass == 2 ? 32 : pass == 3 ? 21 : pass == 4 ? 10 : 0;
-}
-__device__ __forceinline__ int digit_width(int pass) { return (pass == 2 || pass == 5) ? 10 : 11; }
 
 // Wave-wide exclusive suffix sum of `x` over lanes above this one.
 __device__ __forceinline__ uint32_t wave_suffix_excl(uint32_t x, int lane) {
@@ -98,67 +86,9 @@ __device__ __forceinline__ void hist_pass(const uint64_t* buf, int cnt, uint64_t
   }
 }
 
-// Select the `need` best of the cnt records in buf (1 <= need <= cnt).
-// On entry hist holds H1 of exactly these records; it is clobbered.
-// exact = false stops once kept <= goal.
-static __device__ __noinline__ SelectResult select_records(const uint64_t* buf, int cnt, uint32_t need, uint32_t* hist,
-                                                    bool exact, uint32_t goal, int lane) {
-  uint32_t bin, above, count;
-  find_boundary(hist, kH1Bins, need, lane, bin, above, count);
-  uint64_t prefix = (uint64_t)bin << kH1Shift;
-  uint64_t mask = (uint64_t)(kH1Bins - 1) << kH1Shift;
-  uint32_t remaining = need - above;
-  uint32_t kept = need - remaining + count;
-  for (int pass = 1; pass < 6; ++pass) {
-    if (count == remaining) break;  // boundary bin taken whole: exact
-    if (!exact && kept <= goal) break;
-    const int S = digit_shift(pass);
-    const uint32_t nb = 1u << digit_width(pass);
-    for (uint32_t i = lane; i < nb; i += 64) hist[i] = 0;
-    hist_pass(buf, cnt, prefix, mask, S, nb, hist, lane);
-    find_boundary(hist, nb, remaining, lane, bin, above, count);
-    prefix |= (uint64_t)bin << S;
-    mask |= (uint64_t)(nb - 1) << S;
-    remaining -= above;
-    kept = need - remaining + count;
-  }
-  return {prefix, mask, kept};
-}
-
-// In place: keep records with (r & mask) >= prefix, in their order, and
-// rebuild H1 over the kept ones.  Returns the kept count.
-static __device__ __noinline__ int compact_records(uint64_t* buf, int cnt, SelectResult sel, uint32_t* hist,
-                                                   int lane) {
-  for (uint32_t i = lane; i < kH1Bins; i += 64) hist[i] = 0;
-  int base = 0;
-  for (int i0 = 0; i0 < cnt; i0 += 512) {
-    uint64_t r[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + 64 * j + lane;
-      r[j] = i < cnt ? buf[i] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + 64 * j + lane;
-      const bool keep = i < cnt && (r[j] & sel.mask) >= sel.prefix;
-      const uint64_t bal = __ballot(keep);
-      const uint32_t before =
-          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      if (keep) {
-        buf[base + before] = r[j];
-        atomicAdd(&hist[(uint32_t)(r[j] >> kH1Shift)], 1u);
-      }
-      base += __popcll(bal);
-    }
-  }
-  return base;
-}
-
-// Variant without the incremental first-digit histogram, for paths that
-// select rarely and cannot spare 8 KB of LDS per row: eight passes of 8-bit
-// digits over a 256-bin histogram, each pass reading the buffer.  Same
-// result contract as select_records.
+// Select the `need` best of the cnt records in buf (1 <= need <= cnt): up
+// to eight passes of 8-bit digits over a 256-bin histogram, each pass
+// reading the buffer.  exact = false stops once kept <= goal.
 static __device__ __noinline__ SelectResult select_records_d8(const uint64_t* buf, int cnt, uint32_t need,
                                                               uint32_t* hist, bool exact, uint32_t goal, int lane) {
   uint64_t prefix = 0, mask = 0;
@@ -179,8 +109,8 @@ static __device__ __noinline__ SelectResult select_records_d8(const uint64_t* bu
   return {prefix, mask, kept};
 }
 
-// In place: keep records with (r & mask) >= prefix, in their order (no
-// histogram upkeep).  Returns the kept count.
+// In place: keep records with (r & mask) >= prefix, in their order.
+// Returns the kept count.
 static __device__ __noinline__ int compact_records_d8(uint64_t* buf, int cnt, SelectResult sel, int lane) {
   int base = 0;
   for (int i0 = 0; i0 < cnt; i0 += 512) {

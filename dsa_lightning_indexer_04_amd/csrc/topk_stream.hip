@@ -14,10 +14,12 @@
 //               per wave held in registers as MFMA A fragments (64 heads x
 //               128 dims) plus its head weights; two waves per SIMD, so one
 //               wave's MFMAs overlap the other's fp32 epilogue;
-//   key tiles (16 KiB: 64 bf16 or 128 fp8 keys) are double-buffered in LDS:
-//   the next tile is fetched into registers while the current one is scored
-//   and stored at the tile's end, in an XOR-swizzled chunk order so the
-//   32-lane column reads are bank-conflict free; all 8 waves read each tile.
+//   key tiles (32 KiB: 128 bf16 or 256 fp8 keys) rotate through three LDS
+//   slots: the tile after next streams from global memory straight into
+//   LDS while the current one is scored, in a padded key-major layout so
+//   the column reads are bank-conflict free; all 8 waves read each tile,
+//   and each wave's key fragment for the next 32 keys is read while the
+//   current 32 are multiplied.
 //   After the head sum every lane holds the score of key l%32, so the
 //   threshold test, ballot and append are one wave op on lanes 0..31.
 //   Workgroups are issued longest-prefix first (causal imbalance).
@@ -27,6 +29,8 @@
 #include "stream_common.h"
 
 namespace dsa {
+
+constexpr int kSlots = 3;  // LDS key-tile slots
 
 template <int DT>
 struct BlockAcc {
@@ -41,25 +45,29 @@ struct Cands {
   float thr_f;
 };
 
-// Append the records of one scored 32-key block (lanes 0..31; `live` masks
-// keys that are not visible or not real).  The stage has room: the caller
-// flushes it and cuts the buffer at tile boundaries.
-__device__ __forceinline__ void append_block(Cands& c, float s, int key, bool live, uint64_t* stage, uint32_t* hist,
-                                             int lane) {
-  if (__ballot(live && s >= c.thr_f)) {  // cheap float pre-test; rare once thr has risen
-    const uint64_t rec = make_record(s, (uint32_t)key);
-    const bool take = live && rec >= c.thr;
-    const uint64_t bal = __ballot(take);
-    if (take) {
-      stage[c.nst + __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)] = rec;
-      atomicAdd(&hist[(uint32_t)(rec >> kH1Shift)], 1u);
-    }
-    c.nst += __popcll(bal);
-  }
+// Append the records of two scored 32-key blocks at once: lane l holds the
+// score of key `key` (the earlier block in lanes 0..31, the later one in
+// 32..63; `live` masks keys that are not visible).  A key is kept if its
+// score reaches thr_f, the float floor of the threshold record: that keeps
+// every record >= thr (and at most a few equal-score records below it,
+// which the exact selections drop).  Branch-free, so the scheduler can
+// overlap it with the next block's MFMAs: every lane stores its record,
+// the kept ones to the next stage slots and the others to their own slot of
+// the stage's scratch tail (stage[dummy + lane]).  The stage has room: the
+// caller flushes it and cuts the buffer at tile boundaries.
+__device__ __forceinline__ void append_pair(Cands& c, float s, int key, bool live, uint64_t* stage, int dummy,
+                                            int lane) {
+  const bool take = live && s >= c.thr_f;
+  const uint64_t bal = __ballot(take);
+  const int before =
+      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+  stage[take ? c.nst + before : dummy + lane] = make_record(s, (uint32_t)key);
+  c.nst += __popcll(bal);
 }
 
 // Flush the stage to the buffer; if `room` more records could overflow the
-// buffer, cut it back (radix select) and raise the threshold.
+// buffer, cut it back (radix select) to between topk and topk + (cap -
+// topk) / 8 records and raise the threshold to the cut's boundary.
 __device__ __forceinline__ void flush_and_cut(Cands& c, uint64_t* buf, const uint64_t* stage, uint32_t* hist,
                                               int topk, int cap, int room, int lane) {
   if (c.nst) {
@@ -67,11 +75,9 @@ __device__ __forceinline__ void flush_and_cut(Cands& c, uint64_t* buf, const uin
     c.nst = 0;
   }
   if (c.cnt > cap - room) {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
-    const SelectResult sel =
-        select_records(buf, c.cnt, (uint32_t)topk, hist, false, (uint32_t)(topk + (cap - topk) / 2), lane);
-    c.cnt = compact_records(buf, c.cnt, sel, hist, lane);
-    c.thr = sel.prefix;
+    const Cut cut = cut_candidates_d8(buf, c.cnt, stage, 0, hist, topk, topk + (cap - topk) / 8, lane);
+    c.cnt = cut.cnt;
+    c.thr = cut.thr;
     c.thr_f = record_floor(c.thr);
   }
 }
@@ -81,13 +87,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
     int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  using Tile = DirectTile<DT>;
   constexpr int RB = Frag<DT>::kRowBytes;
-  constexpr int KT = kTileBytes / RB;  // keys per tile
-  constexpr int NSB = KT / 32;         // 32-key blocks per tile (even)
-  __shared__ u32x4 ktile[2][kTileChunks];
-  __shared__ float kscale_tile[2][KT];
-  __shared__ uint32_t hist[kWaves][kH1Bins];
-  __shared__ uint64_t stage[kWaves][KT];
+  constexpr int KT = Tile::KT;   // keys per tile
+  constexpr int NSB = KT / 32;   // 32-key blocks per tile (even)
+  __shared__ u32x4 ktile[kSlots][kDirectSlots];
+  __shared__ float kscale_tile[kSlots][KT];
+  __shared__ uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits)
+  __shared__ uint64_t stage[kWaves][KT + 64];  // KT records + 64 scratch slots
+  __shared__ uint32_t toff[kWaves][Tile::PER_WAVE * 64];  // tile-load source offsets
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = gridDim.x - 1 - blockIdx.x;  // longest prefixes first
@@ -108,63 +116,85 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   uint32_t* my_hist = hist[wave];
   uint64_t* my_stage = stage[wave];
-  for (uint32_t i = lane; i < kH1Bins; i += 64) my_hist[i] = 0;
   uint64_t* buf = cand + row * (size_t)cap;
   Cands cs{0, 0, 0, -INFINITY};
   const uint8_t* kbase = k + (size_t)b * N * RB;
   const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
 
-  TileFetch<DT> tf;
+  // Key tiles rotate through kSlots LDS slots: while tile ti is scored, tile
+  // ti+1 already sits in the next slot (so the last block of tile ti can
+  // prefetch the first fragment of tile ti+1) and tile ti+2 streams from
+  // global memory straight into the slot tile ti-1 used.
+  Tile tl;
+  tl.init(toff[wave], wave, lane);
   const int ntiles = (wg_vis + KT - 1) / KT;
-  if (ntiles > 0) {
-    tf.fetch(kbase, kscb, 0, N, tid);
-    tf.commit(ktile[0], kscale_tile[0], tid);
+  for (int ti = 0; ti < min(ntiles, 2); ++ti) {
+    tl.load(ktile[ti], kbase, ti * KT, N, lane);
+    if constexpr (DT == kFP8) tl.load_scales(kscale_tile[ti], kscb, ti * KT, N, lane);
   }
   wait_vmem_all();
   __syncthreads();
 
   // Software pipeline over 32-key blocks j = 0, 1, ...: step j issues block
-  // j's MFMAs (key fragment from the LDS tile) interleaved with the head sum
-  // of block j-1 (from registers), then appends block j-1.  Every step runs
-  // the same straight-line code; keys past the row's visible prefix and the
-  // empty block -1 are masked at the append.  acc[j & 1] holds block j,
-  // kscl[j & 1] its fp8 key scales.
+  // j's MFMAs (key fragment f, loaded during step j-1) interleaved with the
+  // head sum of block j-1 (from registers) and the reload of f with block
+  // j+1.  Blocks are appended in pairs: an odd step keeps block j-1's score,
+  // an even step appends blocks j-2 and j-1 (64 consecutive keys, one per
+  // lane).  Every step runs the same straight-line code; keys past the row's
+  // visible prefix and the blocks before 0 are masked at the append.
+  // acc[j & 1] holds block j, kscl[j & 1] its fp8 key scales.
   BlockAcc<DT> acc[2];
   acc[0].s0 = acc[0].s1 = acc[1].s0 = acc[1].s1 = zero16();
   float kscl[2] = {1.0f, 1.0f};
+  float s_prev = 0.0f;
   const int lk = lane & 31;
+  Frag<DT> f;
+  Tile::frag(f, ktile[0], lk, lane);
+  int cur = 0;  // slot of tile ti
   for (int ti = 0; ti < ntiles; ++ti) {
-    const int cur = ti & 1;
+    const int nxt = cur == kSlots - 1 ? 0 : cur + 1;       // slot of tile ti+1
+    const int spare = nxt == kSlots - 1 ? 0 : nxt + 1;     // slot of tile ti-1, refilled with ti+2
     flush_and_cut(cs, buf, my_stage, my_hist, topk, cap, KT, lane);
-    if (ti + 1 < ntiles) tf.fetch(kbase, kscb, (ti + 1) * KT, N, tid);
+    if (ti + 2 < ntiles) {
+      tl.load(ktile[spare], kbase, (ti + 2) * KT, N, lane);
+      if constexpr (DT == kFP8) tl.load_scales(kscale_tile[spare], kscb, (ti + 2) * KT, N, lane);
+    }
 #pragma unroll
     for (int sub = 0; sub < NSB; ++sub) {
       const int j = ti * NSB + sub;
       BlockAcc<DT>& an = acc[sub & 1];
       const BlockAcc<DT>& ap = acc[(sub & 1) ^ 1];
-      Frag<DT> f;
-      load_frag_lds<DT>(f, ktile[cur], 32 * sub + lk, lane);
-      float s = combine_single(pipelined_partial<DT>(qs, f, ap.s0, ap.s1, an.s0, an.s1));
+      // the next block: the same tile's next 32 keys, else the next tile's
+      // first (the last tile's last block reloads keys it never scores)
+      const u32x4* ntile = sub + 1 < NSB ? ktile[cur] : ktile[ti + 1 < ntiles ? nxt : cur];
+      const int nkey = sub + 1 < NSB ? 32 * (sub + 1) + lk : lk;
+      float s = combine_single(pipelined_partial<DT>(qs, f, ap.s0, ap.s1, an.s0, an.s1,
+                                                     [&](int i) { Tile::frag_step(f, ntile, nkey, i, lane); }));
       if constexpr (DT == kFP8) {
         s = apply_scales(s, qscale, kscl[(sub & 1) ^ 1]);
         kscl[sub & 1] = kscale_tile[cur][32 * sub + lk];
       }
-      const int key = 32 * (j - 1) + lk;
-      append_block(cs, s, key, lane < 32 && j > 0 && key < vis, my_stage, my_hist, lane);
+      if (sub & 1) {
+        s_prev = s;
+      } else {
+        const int key = 32 * (j - 2) + lane;
+        append_pair(cs, lane < 32 ? s_prev : s, key, j >= 2 && key < vis, my_stage, KT, lane);
+      }
     }
-    if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid);
+    wait_vmem_all();  // this wave's loads of tile ti+2 have landed
     __syncthreads();
+    cur = nxt;
   }
   if (!valid) return;
-  if (ntiles > 0) {  // drain: the last block, j = ntiles * NSB - 1, is in acc[1]
-    flush_and_cut(cs, buf, my_stage, my_hist, topk, cap, 32, lane);
+  if (ntiles > 0) {  // drain: the last block, j = ntiles * NSB - 1 (odd), is in acc[1]
+    flush_and_cut(cs, buf, my_stage, my_hist, topk, cap, 64, lane);
     float s = combine_single(head_partial(acc[1].s0, acc[1].s1, qs.wl));
     if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscl[1]);
-    const int key = 32 * (ntiles * NSB - 1) + lk;
-    append_block(cs, s, key, lane < 32 && key < vis, my_stage, my_hist, lane);
+    const int key = 32 * (ntiles * NSB - 2) + lane;
+    append_pair(cs, lane < 32 ? s_prev : s, key, key < vis, my_stage, KT, lane);
   }
-  emit_topk(buf, cs.cnt, my_stage, cs.nst, my_hist, topk, out_idx + row * (size_t)topk,
-            out_score ? out_score + row * (size_t)topk : nullptr, lane);
+  emit_topk_d8(buf, cs.cnt, my_stage, cs.nst, my_hist, topk, out_idx + row * (size_t)topk,
+               out_score ? out_score + row * (size_t)topk : nullptr, lane);
 }
 
 hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
