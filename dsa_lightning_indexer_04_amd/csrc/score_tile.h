@@ -270,6 +270,12 @@ __device__ __forceinline__ float combine_swap(float p) {
   return a + b;
 }
 
+// The lane exchange of combine_swap on two values: afterwards a holds
+// (a[0..31], b[0..31]) and b holds (a[32..63], b[32..63]).
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
 // Dequantisation of fp8 scores: (q_scale * k_scale) * head_sum, same order everywhere.
 __device__ __forceinline__ float apply_scales(float sum, float qscale, float kscale) {
   return sum * (qscale * kscale);

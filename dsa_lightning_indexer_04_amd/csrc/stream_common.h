@@ -9,53 +9,6 @@
 namespace dsa {
 
 constexpr int kWaves = 8;           // query rows per workgroup, one per wave
-constexpr int kTileBytes = 16384;   // one LDS key tile (64 bf16 or 128 fp8 keys)
-
-// LDS key tile layout: chunk-major with one chunk of padding per chunk row.
-// 16-byte chunk c of tile key r lives at chunk index c * (KT + 1) + r, so
-//  - the 32 (or 16) lanes that read chunk c of consecutive keys read one
-//    contiguous run (conflict-free), and a lane's successive chunks are a
-//    constant stride apart (immediate ds_read offsets from one base address);
-//  - the 16 (bf16) / 8 (fp8) threads that store the chunks of one key hit
-//    different banks, the row pitch being (KT + 1) * 16 bytes.
-constexpr int kTileChunks = 1040;  // max over dtypes of (chunks per key) * (KT + 1)
-
-template <int DT>
-__device__ __forceinline__ int tile_chunk(int key, int c) {
-  constexpr int KT = kTileBytes / Frag<DT>::kRowBytes;
-  return c * (KT + 1) + key;
-}
-
-// Fragment of key `key` (tile-relative) from an LDS tile.
-template <int DT>
-__device__ __forceinline__ void load_frag_lds(Frag<DT>& f, const u32x4* tile, int key, int lane) {
-  constexpr int CPL = Frag<DT>::kLaneBytes / 16;  // chunks per lane
-  const int c0 = (lane >> 5) * CPL;
-  if constexpr (DT == kBF16) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f.v[i] = tile[tile_chunk<DT>(key, c0 + i)];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      u32x4 lo = tile[tile_chunk<DT>(key, c0 + 2 * i)], hi = tile[tile_chunk<DT>(key, c0 + 2 * i + 1)];
-      f.v[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-  }
-}
-
-// k-step i of a key fragment from an LDS tile (the slice load_frag_lds puts
-// in f.v[i]).
-template <int DT>
-__device__ __forceinline__ void load_frag_step_lds(Frag<DT>& f, const u32x4* tile, int key, int i, int lane) {
-  constexpr int CPL = Frag<DT>::kLaneBytes / 16;
-  const int c0 = (lane >> 5) * CPL;
-  if constexpr (DT == kBF16) {
-    f.v[i] = tile[tile_chunk<DT>(key, c0 + i)];
-  } else {
-    u32x4 lo = tile[tile_chunk<DT>(key, c0 + 2 * i)], hi = tile[tile_chunk<DT>(key, c0 + 2 * i + 1)];
-    f.v[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  }
-}
 
 // Candidate bookkeeping of one row (one wave): records are appended to a
 // small LDS stage during a tile and flushed to the row's global buffer at the
@@ -136,6 +89,7 @@ struct DirectTile {
   static constexpr int NI = SLOTS / 64;                // load instructions per tile
   static constexpr int PER_WAVE = (NI + kWaves - 1) / kWaves;
   static_assert(SLOTS % 64 == 0, "tile slots fill whole load instructions");
+  static_assert(kWaves * (PER_WAVE - 1) <= NI, "only the last load of a wave may be past the tile");
   const uint32_t* off;  // this wave's [PER_WAVE][64] source offsets (LDS), from the tile's first row
   int wave;             // wave-uniform
 
@@ -152,33 +106,66 @@ struct DirectTile {
     }
   }
   // Issue this wave's loads of tile rows ts..ts+KT-1 into `slot` (keys at or
-  // past N read key N-1, never scored: visibility masks them).
+  // past N read key N-1, never scored: visibility masks them).  All offsets
+  // are read first (one LDS wait); every wave issues the first PER_WAVE - 1
+  // instructions (8 (PER_WAVE - 1) <= NI), only the last one is guarded.
   __device__ __forceinline__ void load(u32x4* slot, const uint8_t* kbase, int ts, int N, int lane) const {
+    uint32_t o[PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) o[j] = off[64 * j + lane];
     if (ts + KT <= N) {
       const uint8_t* base = kbase + (size_t)ts * RB;
 #pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int n = wave + kWaves * j;
-        if (n < NI) __builtin_amdgcn_global_load_lds(base + off[64 * j + lane], slot + 64 * n, 16, 0, 0);
-      }
+      for (int j = 0; j < PER_WAVE; ++j)
+        if (j < PER_WAVE - 1 || wave + kWaves * j < NI)
+          __builtin_amdgcn_global_load_lds(base + o[j], slot + 64 * (wave + kWaves * j), 16, 0, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int n = wave + kWaves * j;
-        if (n < NI) {
-          const uint32_t o = off[64 * j + lane];
-          const int key = min(ts + (int)(o / RB), N - 1);
-          __builtin_amdgcn_global_load_lds(kbase + (size_t)key * RB + o % RB, slot + 64 * n, 16, 0, 0);
+      for (int j = 0; j < PER_WAVE; ++j)
+        if (j < PER_WAVE - 1 || wave + kWaves * j < NI) {
+          const int key = min(ts + (int)(o[j] / RB), N - 1);
+          __builtin_amdgcn_global_load_lds(kbase + (size_t)key * RB + o[j] % RB, slot + 64 * (wave + kWaves * j),
+                                           16, 0, 0);
         }
-      }
     }
   }
-  // fp8 key scales of the tile's rows (4 bytes per lane, waves 0..KT/64-1).
-  __device__ __forceinline__ void load_scales(float* kst, const float* kscb, int ts, int N, int lane) const {
-    if (wave < KT / 64) {
-      const int key = min(ts + 64 * wave + lane, N - 1);
-      __builtin_amdgcn_global_load_lds(kscb + key, kst + 64 * wave, 4, 0, 0);
+  // The same for a gathered tile: tile row r is key idx[min(ts + r, nidx - 1)].
+  __device__ __forceinline__ void load_gather(u32x4* slot, const uint8_t* kbase, const int32_t* idx, int ts, int nidx,
+                                              int lane) const {
+    uint32_t o[PER_WAVE];
+    int key[PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) o[j] = off[64 * j + lane];
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) key[j] = idx[min(ts + (int)(o[j] / RB), nidx - 1)];
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j)
+      if (j < PER_WAVE - 1 || wave + kWaves * j < NI)
+        __builtin_amdgcn_global_load_lds(kbase + (size_t)key[j] * RB + o[j] % RB, slot + 64 * (wave + kWaves * j), 16,
+                                         0, 0);
+  }
+  // One 4-byte word per tile row (fp8 key scale, key norm): dst[r] =
+  // src[min(ts + r, N - 1)], loaded by waves w0 .. w0 + KT/64 - 1.
+  __device__ __forceinline__ void load_words(float* dst, const float* src, int ts, int N, int w0, int lane) const {
+    const int wr = wave - w0;
+    if (wr >= 0 && wr < KT / 64) {
+      const int key = min(ts + 64 * wr + lane, N - 1);
+      __builtin_amdgcn_global_load_lds(src + key, dst + 64 * wr, 4, 0, 0);
     }
+  }
+  __device__ __forceinline__ void load_words_gather(float* dst, const float* src, const int32_t* idx, int ts,
+                                                    int nidx, int w0, int lane) const {
+    const int wr = wave - w0;
+    if (wr >= 0 && wr < KT / 64) {
+      const int key = idx[min(ts + 64 * wr + lane, nidx - 1)];
+      __builtin_amdgcn_global_load_lds(src + key, dst + 64 * wr, 4, 0, 0);
+    }
+  }
+  // 64 words of a per-key bitmap from the tile's first word on (the tile
+  // uses the first KT / 32; indexes clamp to the last word), by the last wave.
+  __device__ __forceinline__ void load_bits(uint32_t* dst, const uint32_t* bits, int ts, int words, int lane) const {
+    if (wave == kWaves - 1)
+      __builtin_amdgcn_global_load_lds(bits + min(ts / 32 + lane, words - 1), dst, 4, 0, 0);
   }
   // Fragment of tile key `key` (lane layout of load_frag).
   __device__ __forceinline__ static void frag(Frag<DT>& f, const u32x4* slot, int key, int lane) {
@@ -198,56 +185,5 @@ struct DirectTile {
   }
 };
 constexpr int kDirectSlots = 2304;  // max over dtypes of DirectTile::SLOTS
-
-// Next key tile: each thread fetches two 16-byte chunks into registers at the
-// start of a tile and stores them (swizzled) into the other LDS buffer at its
-// end, so the fetch latency hides behind the current tile's MFMAs.  Keys at
-// or past N read key N-1 (never scored: visibility masks them).
-template <int DT>
-struct TileFetch {
-  static constexpr int CPR = Frag<DT>::kRowBytes / 16;
-  static constexpr int CHUNKS = kTileBytes / 16;
-  static constexpr int PER_THREAD = CHUNKS / (kWaves * 64);
-  static constexpr int KT = kTileBytes / Frag<DT>::kRowBytes;
-  u32x4 v[PER_THREAD];
-  float ks;   // fp8 key scale of tile row tid (tid < KT)
-  float kn;   // key norm of tile row tid (pruned path, tid < KT)
-  uint32_t sbw;  // seed-bitmap word tid (pruned path, tid < KT / 32)
-
-  // Tile rows ts..ts+KT-1 of the key sequence; with `gidx`, tile row r is key
-  // gidx[min(ts + r, nidx - 1)] (a gathered tile), else key min(ts + r, N - 1).
-  // `knorm` / `sbits` (pruned path) also stage each row's |k| and the seed
-  // bitmap words of a contiguous tile.
-  __device__ __forceinline__ void fetch(const uint8_t* kbase, const float* kscb, int ts, int N, int tid,
-                                        const int32_t* gidx = nullptr, int nidx = 0, const float* knorm = nullptr,
-                                        const uint32_t* sbits = nullptr) {
-#pragma unroll
-    for (int j = 0; j < PER_THREAD; ++j) {
-      const int c = tid + j * kWaves * 64;
-      const int key = c / CPR, ch = c % CPR;
-      const int gk = gidx ? gidx[min(ts + key, nidx - 1)] : min(ts + key, N - 1);
-      v[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)gk * Frag<DT>::kRowBytes + ch * 16);
-    }
-    if (tid < KT) {
-      const int gk = gidx ? gidx[min(ts + tid, nidx - 1)] : min(ts + tid, N - 1);
-      if constexpr (DT == kFP8) ks = kscb[gk];
-      if (knorm) kn = knorm[gk];
-    }
-    if (sbits && tid < KT / 32) sbw = sbits[min(ts / 32 + tid, (N - 1) / 32)];
-  }
-  __device__ __forceinline__ void commit(u32x4* tile, float* kst, int tid, float* knt = nullptr,
-                                         uint32_t* sbt = nullptr) const {
-#pragma unroll
-    for (int j = 0; j < PER_THREAD; ++j) {
-      const int c = tid + j * kWaves * 64;
-      tile[tile_chunk<DT>(c / CPR, c % CPR)] = v[j];
-    }
-    if (tid < KT) {
-      if constexpr (DT == kFP8) kst[tid] = ks;
-      if (knt) knt[tid] = kn;
-    }
-    if (sbt && tid < KT / 32) sbt[tid] = sbw;
-  }
-};
 
 }  // namespace dsa

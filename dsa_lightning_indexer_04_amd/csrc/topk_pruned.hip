@@ -7,13 +7,14 @@
 //      seed record is the threshold tau (K distinct visible keys reach it, so
 //      it cannot exceed the true K-th score);
 //   2. screen: every other visible key gets the certified upper bound U from
-//      16 plan rows (14 retained heads, the folded negative-head row, the
-//      linear row; see prune_prep.hip) -- one 16x16 MFMA block per 16 keys --
-//      and survives iff its record (U, key) is not below the row's running
-//      threshold; a 64-lane ballot packs the survivors into a bitmask;
+//      32 plan rows (up to 30 retained heads, the folded negative-head row,
+//      the linear row; see prune_prep.hip) -- one 32x32 MFMA block per 32
+//      keys -- and survives iff U reaches the row's running threshold; a
+//      64-lane ballot packs the survivors of a block into a bitmask;
 //   3. compact + refine: survivors are queued per row and rescored with all
-//      heads in batches of 32 (keys gathered by index, same score routine),
-//      and only records not below the threshold are written as candidates;
+//      heads in batches of 32 (key rows gathered by index, same score
+//      routine), and only records not below the threshold are kept as
+//      candidates;
 //   4. select: the row's candidates (seed Top-K and refined survivors) are cut
 //      to the exact Top-K by score, then key index.
 // The running threshold starts at tau and only rises when the candidate
@@ -33,8 +34,8 @@ constexpr int kLinRowK = 31;
 constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
 constexpr int kCutSlack = 1024;  // records kept beyond topk before the threshold is raised
-constexpr int kRing = 6;         // LDS key tiles: the screen's, the next one, and four awaiting refinement
-constexpr int kRefineEvery = 4;  // tiles between refine rounds
+constexpr int kSlots = 3;        // LDS key-tile slots
+constexpr int kStage = 96;       // candidate stage records per row
 
 struct PrunePlan {
   const uint8_t* rows;       // [R][32][128] dtype: bound rows
@@ -85,16 +86,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
     int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
     PrunePlan pp) {
+  using Tile = DirectTile<DT>;
   constexpr int RB = Frag<DT>::kRowBytes;
-  constexpr int KT = kTileBytes / RB;
-  constexpr int NSB = KT / 32;
-  __shared__ u32x4 ktile[kRing][kTileChunks];
-  __shared__ float kscale_tile[kRing][KT];
-  __shared__ uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits)
-  __shared__ uint64_t stage[kWaves][KT + 32];
-  __shared__ int32_t squeue[kWaves][kRefineEvery * KT];  // survivor list (see below)
-  __shared__ float knorm_tile[kRing][KT];
-  __shared__ uint32_t sbits_tile[kRing][KT / 32];
+  constexpr int KT = Tile::KT;     // keys per tile (128 bf16, 256 fp8)
+  constexpr int NSB = KT / 32;     // 32-key blocks per tile
+  constexpr int QCAP = KT + 96;    // survivor queue per row (see the refine schedule)
+  __shared__ u32x4 ktile[kSlots][kDirectSlots];
+  __shared__ float kscale_tile[kSlots][KT];
+  __shared__ float knorm_tile[kSlots][KT];
+  __shared__ uint32_t sbits_tile[kSlots][64];
+  __shared__ uint32_t hist[kWaves][256];      // radix-select bins (8-bit digits)
+  __shared__ uint64_t stage[kWaves][kStage];  // candidate records awaiting a flush
+  __shared__ int32_t squeue[kWaves][QCAP + 64];  // survivor keys awaiting refinement (+ scratch)
+  __shared__ uint32_t toff[kWaves][Tile::PER_WAVE * 64];
+  __shared__ __align__(16) float wrow[kWaves][kHeads];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = gridDim.x - 1 - blockIdx.x;
@@ -110,7 +115,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // query rows in registers; head weights in LDS (read at each full epilogue)
-  __shared__ __align__(16) float wrow[kWaves][kHeads];
   Frag<DT> qa[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], q + (row * kHeads + 32 * blk + (lane & 31)) * RB, lane);
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // screen side: the 32 plan rows as one 32x32 MFMA A operand; lane l holds
   // rows 8*(v/4) + 4*(l/32) + v%4 of the result (v = 0..15), with their
   // coefficients in cl[v].  Rows 30 (aux) and 31 (linear) land in lanes
-  // 32..63 at v = 14, 15; the other lanes get zero multipliers for them.
+  // 32..63 at v = 14, 15, whose cl is zero; they enter the bound separately.
   Frag<DT> sa;
   load_frag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 31)) * RB, lane);
   const float* co = pp.coef + row * kPlanRowsK;
@@ -131,9 +135,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     cl[v] = r < kRetainedK ? co[r] : 0.0f;
   }
-  const bool hi_half = lane >= 32;
-  const float m_aux = hi_half ? co[kAuxRowK] : 0.0f, m_lin = hi_half ? co[kLinRowK] : 0.0f;
-  const float kappa = pp.misc[row * 4 + 0], e_neg = hi_half ? pp.misc[row * 4 + 1] : 0.0f;
+  const float m_aux = co[kAuxRowK], m_lin = co[kLinRowK];
+  const float kappa = pp.misc[row * 4 + 0], e_neg = pp.misc[row * 4 + 1];
   const bool recover = pp.flag[row] != 0;
 
   uint32_t* my_hist = hist[wave];
@@ -146,41 +149,54 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int nseed = pp.seed_count[b];
   const int32_t* sd = pp.seeds + (size_t)b * pp.seed_stride;
   const uint32_t* sbits = pp.seed_bits + (size_t)b * pp.bits_stride;
-  TileFetch<DT> tf;
+  const int lk = lane & 31;
+  Tile tl;
+  tl.init(toff[wave], wave, lane);
+
+  // Exact scores of up to 32 keys (lane l % 32: key keys_l, fragment f) go
+  // to the candidate buffer if their records reach the threshold.
+  auto score_and_keep = [&](const Frag<DT>& f, int key, float ks, bool live) {
+    float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
+    if constexpr (DT == kFP8) s = apply_scales(s, qscale, ks);
+    if (rs.nst > kStage - 32) {
+      rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+      rs.nst = 0;
+    }
+    append_rec(rs, make_record(s, (uint32_t)key), live, my_stage, my_hist, topk, cap, lane);
+  };
 
   // ---------------------------------------------------------------- 1. seeds
   {
     const int ntiles = (nseed + KT - 1) / KT;
-    if (ntiles > 0) {
-      tf.fetch(kbase, kscb, 0, N, tid, sd, nseed);
-      tf.commit(ktile[0], kscale_tile[0], tid);
+    for (int ti = 0; ti < min(ntiles, 2); ++ti) {
+      tl.load_gather(ktile[ti], kbase, sd, ti * KT, nseed, lane);
+      if constexpr (DT == kFP8) tl.load_words_gather(kscale_tile[ti], kscb, sd, ti * KT, nseed, 0, lane);
     }
     wait_vmem_all();
     __syncthreads();
+    int cur = 0;
     for (int ti = 0; ti < ntiles; ++ti) {
-      const int cur = ti & 1;
-      const int ts = ti * KT;
-      if (rs.nst) {
-        rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
-        rs.nst = 0;
+      const int nxt = cur == kSlots - 1 ? 0 : cur + 1;
+      const int spare = nxt == kSlots - 1 ? 0 : nxt + 1;
+      if (ti + 2 < ntiles) {
+        tl.load_gather(ktile[spare], kbase, sd, (ti + 2) * KT, nseed, lane);
+        if constexpr (DT == kFP8) tl.load_words_gather(kscale_tile[spare], kscb, sd, (ti + 2) * KT, nseed, 0, lane);
       }
-      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, sd, nseed);
-#pragma unroll
+      const int ts = ti * KT;
       for (int sb = 0; sb < NSB; ++sb) {
         const int s0 = ts + 32 * sb;
         if (s0 < nseed && sd[s0] < vis) {  // seeds ascend: wave-uniform test
-          const int si = s0 + (lane & 31);
+          const int si = s0 + lk;
           const int key = sd[min(si, nseed - 1)];
           Frag<DT> f;
-          load_frag_lds<DT>(f, ktile[cur], 32 * sb + (lane & 31), lane);
-          float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
-          if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[cur][32 * sb + (lane & 31)]);
-          append_rec(rs, make_record(s, (uint32_t)key), lane < 32 && si < nseed && key < vis, my_stage, my_hist,
-                     topk, cap, lane);
+          Tile::frag(f, ktile[cur], 32 * sb + lk, lane);
+          score_and_keep(f, key, (DT == kFP8) ? kscale_tile[cur][32 * sb + lk] : 1.0f,
+                         lane < 32 && si < nseed && key < vis);
         }
       }
-      if (ti + 1 < ntiles) tf.commit(ktile[cur ^ 1], kscale_tile[cur ^ 1], tid);
+      wait_vmem_all();
       __syncthreads();
+      cur = nxt;
     }
   }
   // tau: the exact K-th seed record (records below it can never be selected)
@@ -198,47 +214,41 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---------------------------------------------------------------- 2-3. screen + refine
-  // Key tiles stream through a ring of kRing LDS slots (tile ti in slot
-  // ti % kRing).  The screen appends surviving keys to the wave's list
-  // my_q[0..nq) (one LDS store per survivor); every kRefineEvery tiles all
-  // waves rescore their lists together, 32 keys per MFMA batch, with the key
-  // fragments read from the ring (the survivors' tiles are still resident:
-  // a slot is refilled only kRing tiles later).  Refining in the same tiles
-  // keeps the eight waves, which meet at every tile, in step.
-  int nq = 0, screened = 0, survived = 0;
-  auto refine_round = [&]() {
-    for (int p0 = 0; p0 < nq; p0 += 32) {
-      const int n = min(32, nq - p0);
-      const int key = my_q[p0 + ((lane & 31) < n ? (lane & 31) : 0)];
-      const int tk = key / KT, r = key - tk * KT, slot = tk % kRing;
-      Frag<DT> f;
-      load_frag_lds<DT>(f, ktile[slot], r, lane);
-      float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
-      if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscale_tile[slot][r]);
-      if (rs.nst > KT) {  // the stage holds KT + 32 records: make room for this batch
-        rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
-        rs.nst = 0;
-      }
-      append_rec(rs, make_record(s, (uint32_t)key), lane < n, my_stage, my_hist, topk, cap, lane);
-    }
-    nq = 0;
+  // Survivors are pushed to the row's queue my_q[qh, nq).  Refine schedule,
+  // per tile: at its start, if 32 survivors are queued, pop them and issue
+  // the loads of their key rows (global memory; the rows were streamed
+  // moments ago, so they come from cache); score them at the tile's end,
+  // after the screen of the tile has covered the load latency.  A row whose
+  // queue still holds more than 96 keys at the tile's end refines further
+  // batches on the spot (rows with very many survivors, e.g. recovered
+  // rows), so the next tile's KT survivors always fit.
+  int qh = 0, nq = 0, screened = 0, survived = 0;
+  float thr_f = record_floor(rs.thr);
+  auto batch_keys = [&](int n) { return my_q[qh + (lk < n ? lk : 0)]; };
+  auto refine_now = [&](int n) {  // pop n <= 32 keys and rescore them synchronously
+    const int key = batch_keys(n);
+    Frag<DT> f;
+    load_frag<DT>(f, kbase + (size_t)key * RB, lane);
+    const float ks = (DT == kFP8) ? kscb[key] : 1.0f;
+    qh += n;
+    score_and_keep(f, key, ks, lane < n);
   };
   {
     const int ntiles = (wg_vis + KT - 1) / KT;
-    if (ntiles > 0) {
-      tf.fetch(kbase, kscb, 0, N, tid, nullptr, 0, knb, sbits);
-      tf.commit(ktile[0], kscale_tile[0], tid, knorm_tile[0], sbits_tile[0]);
+    const int words = pp.bits_stride;
+    for (int ti = 0; ti < min(ntiles, 2); ++ti) {
+      tl.load(ktile[ti], kbase, ti * KT, N, lane);
+      if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, 0, lane);
+      tl.load_words(knorm_tile[ti], knb, ti * KT, N, 4, lane);
+      tl.load_bits(sbits_tile[ti], sbits, ti * KT, words, lane);
     }
     wait_vmem_all();
     __syncthreads();
-    const int lk = lane & 31;
+    int cur = 0;
     for (int ti = 0; ti < ntiles; ++ti) {
-      const int cur = ti % kRing;
+      const int nxt = cur == kSlots - 1 ? 0 : cur + 1;
+      const int spare = nxt == kSlots - 1 ? 0 : nxt + 1;
       const int ts = ti * KT;
-      // The loop is bound by the latency of the next tile's fetch: issue it
-      // first, so that refine rounds and cuts run in its shadow.
-      if (ti + 1 < ntiles) tf.fetch(kbase, kscb, ts + KT, N, tid, nullptr, 0, knb, sbits);
-      if (ti > 0 && ti % kRefineEvery == 0) refine_round();
       if (rs.nst) {
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
         rs.nst = 0;
@@ -250,49 +260,112 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         const Cut c = cut_candidates_d8(rs.buf, rs.cnt, my_stage, 0, my_hist, topk, topk, lane);
         rs.cnt = c.cnt;
         rs.thr = c.thr;
+        thr_f = record_floor(rs.thr);
       }
+      if (ti + 2 < ntiles) {
+        const int tn = (ti + 2) * KT;
+        tl.load(ktile[spare], kbase, tn, N, lane);
+        if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, tn, N, 0, lane);
+        tl.load_words(knorm_tile[spare], knb, tn, N, 4, lane);
+        tl.load_bits(sbits_tile[spare], sbits, tn, words, lane);
+      }
+      // refine batch, part 1: pop and issue the key-row loads
+      const bool pend = nq - qh >= 32;
+      Frag<DT> rf;
+      int rkey = 0;
+      float rks = 1.0f;
+      if (pend) {
+        rkey = batch_keys(32);
+        load_frag<DT>(rf, kbase + (size_t)rkey * RB, lane);
+        if constexpr (DT == kFP8) rks = kscb[rkey];
+        qh += 32;
+      }
+      // screen, two 32-key blocks (64 keys, one per lane after the exchange)
+      // at a time: the 32x32 MFMA block of each (32 plan rows x 32 keys),
+      // each lane's 16 retained-row terms in two chains, then one lane swap
+      // pairs the two halves of every key's sum -- lane l ends up with key
+      // kb + l -- and two more bring the aux and linear rows' dots (rows 30,
+      // 31, held by lanes 32..63) to the same layout.
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        const int kb = ts + 32 * sb;
+      for (int pr = 0; pr < NSB / 2; ++pr) {
+        const int kb = ts + 64 * pr;
         if (kb < vis) {  // wave-uniform
-          // -- bound of 32 keys: one 32x32 block (32 plan rows x 32 keys);
-          //    each lane sums its 16 rows, the cross-half exchange the rest
           Frag<DT> kf;
-          load_frag_lds<DT>(kf, ktile[cur], 32 * sb + lk, lane);
-          const f32x16 dd = mma_block<DT>(sa, kf, zero16());
-          const float kn = knorm_tile[cur][32 * sb + lk];
-          float p = 0.0f;
+          Tile::frag(kf, ktile[cur], 64 * pr + lk, lane);
+          const f32x16 dA = mma_block<DT>(sa, kf, zero16());
+          Tile::frag(kf, ktile[cur], 64 * pr + 32 + lk, lane);
+          const f32x16 dB = mma_block<DT>(sa, kf, zero16());
+          float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) p = __builtin_fmaf(__builtin_fabsf(dd[v]), cl[v], p);
-          p += __builtin_fmaf(m_lin, dd[15], -relu_bits(__builtin_fmaf(m_aux, dd[14], -e_neg * kn)));
-          float U = __builtin_fmaf(kappa, kn, combine_swap(p));
-          if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][32 * sb + lk]);
-          const int key = kb + lk;
-          const uint32_t seedw = sbits_tile[cur][sb];
-          const bool ck = (lane < 32) & (key < vis) & !((seedw >> lk) & 1u);
-          const bool sv = ck & (recover | (make_record(U, (uint32_t)key) >= rs.thr));
+          for (int v = 0; v < 8; ++v) {
+            a0 = __builtin_fmaf(__builtin_fabsf(dA[v]), cl[v], a0);
+            a1 = __builtin_fmaf(__builtin_fabsf(dA[v + 8]), cl[v + 8], a1);
+            b0 = __builtin_fmaf(__builtin_fabsf(dB[v]), cl[v], b0);
+            b1 = __builtin_fmaf(__builtin_fabsf(dB[v + 8]), cl[v + 8], b1);
+          }
+          float sA = a0 + a1, sB = b0 + b1;
+          swap_halves(sA, sB);
+          float xA = dA[14], xB = dB[14], yA = dA[15], yB = dB[15];
+          swap_halves(xA, xB);  // xB: row-30 (aux) dot of key kb + lane
+          swap_halves(yA, yB);  // yB: row-31 (linear) dot of key kb + lane
+          const float kn = knorm_tile[cur][64 * pr + lane];
+          float U = __builtin_fmaf(m_lin, yB, sA + sB);
+          U -= relu_bits(__builtin_fmaf(m_aux, xB, -e_neg * kn));
+          U = __builtin_fmaf(kappa, kn, U);
+          if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][64 * pr + lane]);
+          const int key = kb + lane;
+          const uint32_t seedw = sbits_tile[cur][2 * pr + (lane >> 5)];
+          const bool ck = (key < vis) & !((seedw >> lk) & 1u);
+          // U >= the threshold's float floor keeps every key whose record
+          // (U, key) reaches the threshold (and at most a few equal-bound
+          // keys below it, which the refine drops)
+          const bool sv = ck & (recover | (U >= thr_f));
           if (pp.st_ub && ck) pp.st_ub[row * (size_t)N + key] = U;
           screened += __popcll(__ballot(ck));
-          const uint32_t mask = (uint32_t)__ballot(sv);  // bit i: key kb + i survives
-          survived += __popc(mask);
-          if (mask) {  // append the survivors to the list (key order)
-            if (sv) my_q[nq + __popc(mask & ((1u << lk) - 1u))] = key;
-            nq += __popc(mask);
-          }
+          const uint64_t mask = __ballot(sv);  // bit l: key kb + l survives
+          const int before =
+              (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          my_q[sv ? nq + before : QCAP + lane] = key;  // branch-free: the others write scratch slots
+          nq += __popcll(mask);
+          survived += __popcll(mask);
         }
       }
-      if (ti + 1 < ntiles)
-        tf.commit(ktile[(ti + 1) % kRing], kscale_tile[(ti + 1) % kRing], tid, knorm_tile[(ti + 1) % kRing],
-                  sbits_tile[(ti + 1) % kRing]);
+      // refine batch, part 2: score the popped keys
+      if (pend) score_and_keep(rf, rkey, rks, lane < 32);
+      // compact the queue to its front; refine on the spot while it is long
+      if (qh > 0) {
+        const int left = nq - qh;
+        for (int i = lane; i < left; i += 64) {
+          const int v = my_q[qh + i];
+          __builtin_amdgcn_wave_barrier();
+          my_q[i] = v;
+        }
+        nq = left;
+        qh = 0;
+      }
+      while (nq > QCAP - KT) {
+        refine_now(32);
+        const int left = nq - qh;
+        for (int i = lane; i < left; i += 64) {
+          const int v = my_q[qh + i];
+          __builtin_amdgcn_wave_barrier();
+          my_q[i] = v;
+        }
+        nq = left;
+        qh = 0;
+      }
+      thr_f = record_floor(rs.thr);
+      wait_vmem_all();
       __syncthreads();
+      cur = nxt;
     }
-    refine_round();  // the last tiles' survivors (their slots are untouched)
+    while (nq > qh) refine_now(min(32, nq - qh));  // the last survivors
   }
 
   // ---------------------------------------------------------------- 4. select
   if (!valid) return;
   emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
-            out_score ? out_score + row * (size_t)topk : nullptr, lane);
+               out_score ? out_score + row * (size_t)topk : nullptr, lane);
   if (lane == 0) {
     if (pp.st_tau) pp.st_tau[row] = tau;
     if (pp.st_screened) pp.st_screened[row] = screened;
