@@ -128,12 +128,28 @@ constexpr int kLinRow = 31;     // linear row E
 constexpr int kPlanRows = 32;
 constexpr int kSweeps = 20;     // coordinate-descent sweeps of the projection
 constexpr int kSamples = 128;   // sample keys for the activation statistics
-constexpr int kQPad = kDim + 1; // padded LDS row (conflict-free column reads)
+constexpr int kPlanWaves = 4;   // query rows per planner workgroup (one per wave)
 
 __device__ __forceinline__ double wave_sum_d(double x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
   return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+// Orders LDS traffic between the lanes of one wave (the planner's waves
+// share no LDS, so no workgroup barrier is needed).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+// gamma_n = n u / (1 - n u), u = 2^-24: relative error bound of n fp32 roundings.
+__device__ __forceinline__ float gamma_f(int n) {
+  const float u = 5.9604645e-08f;
+  return n * u / (1.0f - n * u);
 }
 
 // Round fp64 v to a nearby value of the dtype (bf16: via fp32, then RNE;
@@ -169,53 +185,72 @@ __device__ __forceinline__ double round_to_dtype(double v, uint32_t* code) {
   }
 }
 
-// One wave per query row.  Writes the 32 bound rows (dtype), the per-row
-// coefficients (c_0..c_29, aux-row multiplier, linear-row multiplier), the
-// |k| coefficient kappa and the aux rounding bound e_neg, and the recovery
-// flag (non-finite plan, forced, or invalid seeds for the sequence).
+// Scatter of a 32x32 MFMA result block into a [64][33] staging array: lane l,
+// register v holds row 32*blk + 8*(v/4) + 4*(l/32) + v%4, column l%32.
+__device__ __forceinline__ void stage_block(float (*red)[33], const f32x16& x, int blk, int lane) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = x[v];
+}
+
+// One wave per query row, kPlanWaves rows per workgroup.  Writes the 32
+// bound rows (dtype), the per-row coefficients (c_0..c_29, aux-row
+// multiplier, linear-row multiplier), the |k| coefficient kappa and the aux
+// rounding bound e_neg, and the recovery flag (non-finite plan, forced, or
+// invalid seeds for the sequence).
+//
+// Arithmetic: the projection, the residuals and the folded rows are
+// computed in fp32; every quantity that enters the bound carries an explicit
+// upper bound of its rounding error (gamma_n of the dot products involved),
+// so the bound stays certified.
 template <int DT>
-__global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-                                             const float* __restrict__ w, const int32_t* __restrict__ pos, int Q,
-                                             int N, int nret, const int32_t* __restrict__ seeds,
-                                             const int32_t* __restrict__ seed_count, int seed_stride,
-                                             const int32_t* __restrict__ batch_flag,
-                                             const uint8_t* __restrict__ force_recover,
-                                             uint8_t* __restrict__ plan_rows, float* __restrict__ plan_coef,
-                                             float* __restrict__ plan_misc, int32_t* __restrict__ plan_flag) {
+__global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
+    const int32_t* __restrict__ pos, int Q, int N, int nret, size_t nrows, const int32_t* __restrict__ seeds,
+    const int32_t* __restrict__ seed_count, int seed_stride, const int32_t* __restrict__ batch_flag,
+    const uint8_t* __restrict__ force_recover, uint8_t* __restrict__ plan_rows, float* __restrict__ plan_coef,
+    float* __restrict__ plan_misc, int32_t* __restrict__ plan_flag) {
   constexpr int RB = Frag<DT>::kRowBytes;
-  __shared__ float qs[kHeads][kQPad];
-  __shared__ float red[kHeads][33];   // per-head staging of MFMA results
-  __shared__ float G[kRetained][kRetained];
-  __shared__ double cch[kRetained];  // c_i = e_i (folded retained coefficients)
-  __shared__ int ridx[kRetained];
-  __shared__ double vec[2][kDim];  // E, q_neg (fp64)
-  const int lane = threadIdx.x;
-  const size_t row = blockIdx.x;
+  __shared__ float red_all[kPlanWaves][kHeads][33];  // MFMA staging; later the projection C[j][a]
+  __shared__ __align__(16) float G_all[kPlanWaves][kRetained][32];
+  __shared__ float inv_all[kPlanWaves][32];
+  __shared__ float cch_all[kPlanWaves][32];
+  __shared__ float w_all[kPlanWaves][kHeads];
+  __shared__ int ridx_all[kPlanWaves][32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * kPlanWaves + wv;
+  if (row >= nrows) return;  // whole wave
+  float(*red)[33] = red_all[wv];
+  float(*G)[32] = G_all[wv];
+  float* inv = inv_all[wv];
+  float* cch = cch_all[wv];
+  float* ws = w_all[wv];
+  int* ridx = ridx_all[wv];
+
   const int b = (int)(row / (size_t)Q);
   const uint8_t* qrow = q + row * kHeads * RB;
   const int vis = min(max(pos[row] + 1, 0), N);
+  const float wj = w[row * kHeads + lane];
+  ws[lane] = wj;
 
-  // 1. query rows into LDS (fp32 values: exact for bf16 and e4m3 codes)
-  for (int j = 0; j < kHeads; ++j)
-    for (int d = lane; d < kDim; d += 64) qs[j][d] = elem<DT>(qrow + (size_t)j * RB, d);
-  const double wj = w[row * kHeads + lane];
-  __syncthreads();
-  double qn2 = 0.0;
-  for (int d = 0; d < kDim; ++d) qn2 = fma((double)qs[lane][d], (double)qs[lane][d], qn2);
-  const double qnorm = sqrt(qn2);
+  // 1. query fragments; head norms |q_j| from the diagonal of Q Q^T (MFMA;
+  //    products of dtype values are exact in fp32, the sum rounds by at
+  //    most gamma_128 relative, covered by the margin)
+  Frag<DT> qa[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], qrow + (size_t)(32 * blk + (lane & 31)) * RB, lane);
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) stage_block(red, mma_block<DT>(qa[blk], qa[blk], zero16()), blk, lane);
+  wave_sync();
+  const float qnorm = sqrtf(fmaxf(red[lane][lane & 31], 0.0f)) * (1.0f + 1e-5f);
+  wave_sync();
 
   // 2. activation statistics of each head over 128 sample keys (seeds, or
   //    evenly spaced visible keys): X = Q K_s^T by MFMA, 32 samples at a
   //    time (dtype code units for fp8: the scales are positive, so signs and
-  //    the head ranking are those of the real values).  Lane l holds sample
-  //    l % 32 for heads 32*blk + 8*(v/4) + 4*(l/32) + v%4; the per-head sums
-  //    over the 32 sample columns go through LDS.
+  //    the head ranking are those of the real values)
   const int nseed = seed_count[b];
   const int32_t* sb = seeds + (size_t)b * seed_stride;
   const int nsamp = min(kSamples, nseed > 0 ? nseed : vis);
-  Frag<DT> qa[2];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], qrow + (size_t)(32 * blk + (lane & 31)) * RB, lane);
   float pa[2][16], pn[2][16];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
@@ -246,34 +281,34 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = pass ? pn[blk][v] : pa[blk][v];
-    __syncthreads();
+    wave_sync();
     float sum = 0.0f;
     for (int c = 0; c < 32; ++c) sum += red[lane][c];
     if (pass)
       npos = (int)sum;
     else
       act = sum;
-    __syncthreads();
+    wave_sync();
   }
 
   // 3. retained set: the (at most nret) positive-weight heads with the
   //    largest w_j * activation
-  const float key_j = wj > 0.0 ? (float)wj * act : -1.0f;
+  const float key_j = wj > 0.0f ? wj * act : -1.0f;
   int rank = 0;
   for (int i = 0; i < kHeads; ++i) {
     const float ki = __shfl(key_j, i, 64);
     rank += (ki > key_j) || (ki == key_j && i < lane);
   }
-  const int npos_heads = __popcll(__ballot(wj > 0.0));
+  const int npos_heads = __popcll(__ballot(wj > 0.0f));
   nret = min(nret, npos_heads);
-  const bool retained = wj > 0.0 && rank < nret;
+  const bool retained = wj > 0.0f && rank < nret;
   if (retained) ridx[rank] = lane;
-  __syncthreads();
+  wave_sync();
 
   // 4. dots of every head with every retained row, G_full = Q Q_R^T, by one
   //    MFMA pass (fp32: these only steer the projection, whose residual is
-  //    measured exactly below).  G = rows ridx of G_full; head j's
-  //    right-hand side b_j = row j of G_full.
+  //    bounded rigorously below).  G = rows ridx of G_full, zero-padded to
+  //    30 x 32; head j's right-hand side b_j = row j of G_full.
   {
     Frag<DT> fr;
     const int ri = (lane & 31) < nret ? ridx[lane & 31] : -1;
@@ -284,139 +319,179 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
       for (int i = 0; i < Frag<DT>::kSteps; ++i) fr.v[i] = {};
     }
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const f32x16 x = mma_block<DT>(qa[blk], fr, zero16());
-#pragma unroll
-      for (int v = 0; v < 16; ++v) red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = x[v];
-    }
+    for (int blk = 0; blk < 2; ++blk) stage_block(red, mma_block<DT>(qa[blk], fr, zero16()), blk, lane);
   }
-  __syncthreads();
-  for (int e = lane; e < nret * nret; e += 64) {
-    const int a = e / nret, c = e % nret;
-    G[a][c] = red[ridx[a]][c];
+  wave_sync();
+  for (int e = lane; e < kRetained * 32; e += 64) {
+    const int a = e >> 5, c = e & 31;
+    G[a][c] = (a < nret && c < nret) ? red[ridx[a]][c] : 0.0f;
   }
-  __syncthreads();
-
+  if (lane < 32) inv[lane] = 0.0f;
+  wave_sync();
+  if (lane < nret) inv[lane] = G[lane][lane] > 0.0f ? 1.0f / G[lane][lane] : 0.0f;
   // 5. each omitted positive head (lane) projects onto the retained rows
   //    with nonnegative coefficients: coordinate descent on
   //    min |q_j - C Q_R|^2, C >= 0, from C = 0, a fixed number of sweeps.
-  //    Any C >= 0 gives a valid bound (convergence only tightens it); the
-  //    residual is then measured in fp64 from the C actually used.
-  const bool in_P = !retained && wj > 0.0;
-  float C[kRetained];
-  float bq[kRetained];
-  double rnorm = 0.0;
+  //    Any C >= 0 gives a valid bound (convergence only tightens it).
+  const bool in_P = !retained && wj > 0.0f;
+  float C[kRetained], bq[kRetained];
 #pragma unroll
   for (int a = 0; a < kRetained; ++a) {
     C[a] = 0.0f;
-    bq[a] = 0.0f;
+    bq[a] = (in_P && a < nret) ? red[lane][a] : 0.0f;
   }
-  if (in_P && nret > 0) {
-#pragma unroll
-    for (int a = 0; a < kRetained; ++a)
-      if (a < nret) bq[a] = red[lane][a];
+  wave_sync();
+  if (__ballot(in_P) != 0 && nret > 0) {
     for (int sw = 0; sw < kSweeps; ++sw) {
-      // re-read G from LDS each sweep (keeps its 900 entries out of registers)
+      // re-read G from LDS each sweep (keeps its 960 entries out of registers)
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < kRetained; ++i) {
-        if (i < nret && G[i][i] > 0.0f) {
-          float g = -bq[i];
+        if (i < nret) {
+          const float4* gi = reinterpret_cast<const float4*>(G[i]);
+          float g[4] = {-bq[i], 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int m = 0; m < kRetained; ++m)
-            if (m < nret) g = fmaf(C[m], G[i][m], g);  // G is symmetric: row i
-          C[i] = fmaxf(0.0f, C[i] - g / G[i][i]);
+          for (int m4 = 0; m4 < 8; ++m4) {
+            const float4 x = gi[m4];
+            if (4 * m4 + 0 < kRetained) g[0] = __builtin_fmaf(C[4 * m4 + 0], x.x, g[0]);
+            if (4 * m4 + 1 < kRetained) g[1] = __builtin_fmaf(C[4 * m4 + 1], x.y, g[1]);
+            if (4 * m4 + 2 < kRetained) g[2] = __builtin_fmaf(C[4 * m4 + 2], x.z, g[2]);
+            if (4 * m4 + 3 < kRetained) g[3] = __builtin_fmaf(C[4 * m4 + 3], x.w, g[3]);
+          }
+          C[i] = fmaxf(0.0f, C[i] - ((g[0] + g[1]) + (g[2] + g[3])) * inv[i]);
         }
       }
     }
   }
-  if (in_P) {
-    double r2 = 0.0, rmag = 0.0;
-    for (int d = 0; d < kDim; ++d) {
-      double r = qs[lane][d];
-      double m = fabs(r);
+  // the projection as an LDS matrix C[j][a] (zero rows outside P)
 #pragma unroll
-      for (int a = 0; a < kRetained; ++a) {
-        if (a < nret) {
-          r = fma(-(double)C[a], (double)qs[ridx[a]][d], r);
-          m += fabs((double)C[a] * qs[ridx[a]][d]);
-        }
-      }
-      r2 = fma(r, r, r2);
-      rmag = fmax(rmag, m);
-    }
-    // fp64 rounding of the residual: at most ~(nret+2) ulps of the term sizes
-    rnorm = sqrt(r2) + 32.0 * (nret + 2) * 1.1102230246251565e-16 * rmag * sqrt((double)kDim);
-  }
+  for (int a = 0; a < kRetained; ++a) red[lane][a] = in_P ? C[a] : 0.0f;
+  wave_sync();
 
-  // 6. folded coefficients (C >= 0, so b_i = 0): a_i = w_i + sum_P w_j C_ji,
-  //    c_i = e_i = a_i / 2 (wave-uniform, kept in LDS); rho = sum_P w_j |r_j|
-  const double rho = wave_sum_d(in_P ? wj * rnorm : 0.0);
+  // 6. folded coefficients (lanes = retained rows): a_i = w_i + sum_P w_j
+  //    C_ji, all terms >= 0, so the fp32 sum is low by at most gamma_65
+  //    relative; c_i = e_i = a_i / 2 rounded up (a larger c_i keeps the
+  //    bound valid: sum 2 c_i ReLU(d_i) >= sum a_i ReLU(d_i))
+  if (lane < 32) {
+    float ai = 0.0f;
+    if (lane < nret) {
+      ai = ws[ridx[lane]];
+      for (int j = 0; j < kHeads; ++j) ai = __builtin_fmaf(fmaxf(ws[j], 0.0f), red[j][lane], ai);
+      ai = 0.5f * ai * (1.0f + 2e-5f);
+    }
+    cch[lane] = ai;
+  }
+  wave_sync();
+
+  // 7. lanes = dims d0 = lane, d1 = lane + 64: the retained rows' values,
+  //    then per omitted head the residual r_j = q_j - sum_a C_ja q_a.  Its
+  //    fp32 evaluation (an fma chain from q_j) is off by at most gamma_31
+  //    (|q_j| + sum_a C_ja |q_a|) per component, so
+  //    |r_j| <= |r_computed| + gamma_31 |m_j| (m_j: that sum).
+  const int d0 = lane, d1 = lane + 64;
+  float qr0[kRetained], qr1[kRetained];
 #pragma unroll
   for (int a = 0; a < kRetained; ++a) {
-    if (a < nret) {
-      const double ap = wave_sum_d(in_P ? wj * (double)C[a] : 0.0);
-      const double wa = __shfl(wj, ridx[a], 64);
-      if (lane == 0) cch[a] = 0.5 * (wa + ap);
-    } else if (lane == 0) {
-      cch[a] = 0.0;
-    }
+    const bool ok = a < nret;
+    const uint8_t* ra = qrow + (size_t)(ok ? ridx[a] : 0) * RB;
+    qr0[a] = ok ? elem<DT>(ra, d0) : 0.0f;
+    qr1[a] = ok ? elem<DT>(ra, d1) : 0.0f;
   }
-  __syncthreads();
+  float rho = 0.0f;
+  uint64_t pmask = __ballot(in_P);
+  while (pmask) {
+    const int j = __builtin_ctzll(pmask);
+    pmask &= pmask - 1;
+    const float* cj = red[j];
+    const float qj0 = elem<DT>(qrow + (size_t)j * RB, d0), qj1 = elem<DT>(qrow + (size_t)j * RB, d1);
+    float r0 = qj0, r1 = qj1, m0 = fabsf(qj0), m1 = fabsf(qj1);
+#pragma unroll
+    for (int a = 0; a < kRetained; ++a) {
+      const float c = cj[a];
+      r0 = __builtin_fmaf(-c, qr0[a], r0);
+      r1 = __builtin_fmaf(-c, qr1[a], r1);
+      m0 = __builtin_fmaf(c, fabsf(qr0[a]), m0);
+      m1 = __builtin_fmaf(c, fabsf(qr1[a]), m1);
+    }
+    const float sr = wave_sum_f(__builtin_fmaf(r0, r0, r1 * r1));
+    const float sm = wave_sum_f(__builtin_fmaf(m0, m0, m1 * m1));
+    const float rn = (sqrtf(sr) + gamma_f(32) * sqrtf(sm)) * (1.0f + 2e-5f);
+    rho = __builtin_fmaf(__shfl(wj, j, 64), rn, rho);
+  }
+  rho *= 1.0f + 1e-5f;  // nonnegative terms: sum low by at most gamma_34
 
-  // 7. folded negative row: negative heads active on >= half the samples
+  // 8. folded negative row: negative heads active on >= half the samples
   //    (all negative heads if none is)
-  const bool negom = !retained && wj < 0.0;
+  const bool negom = !retained && wj < 0.0f;
   const bool act_half = negom && 2 * npos >= nsamp && nsamp > 0;
   const bool use_half = __ballot(act_half) != 0;
   const bool in_N = use_half ? act_half : negom;
 
-  // 8. E and q_neg in fp64 (lanes over dims), rounded to the dtype
-  for (int d = lane; d < kDim; d += 64) {
-    double e = 0.0;
+  // 9. E = sum_a c_a q_a and q_neg = sum_N' |w_j| q_j in fp32 (lanes =
+  //    dims) with their component error bounds gamma_n * (sum of |terms|)
+  float E0 = 0.0f, E1 = 0.0f, mE0 = 0.0f, mE1 = 0.0f;
 #pragma unroll
-    for (int a = 0; a < kRetained; ++a)
-      if (a < nret) e = fma(cch[a], (double)qs[ridx[a]][d], e);
-    vec[0][d] = e;
-    double n = 0.0;
-    for (int j = 0; j < kHeads; ++j) {
-      const double wjj = __shfl(wj, j, 64);
-      const bool inj = __shfl((int)in_N, j, 64) != 0;
-      if (inj) n = fma(fabs(wjj), (double)qs[j][d], n);
-    }
-    vec[1][d] = n;
+  for (int a = 0; a < kRetained; ++a) {
+    const float c = cch[a];
+    E0 = __builtin_fmaf(c, qr0[a], E0);
+    E1 = __builtin_fmaf(c, qr1[a], E1);
+    mE0 = __builtin_fmaf(c, fabsf(qr0[a]), mE0);
+    mE1 = __builtin_fmaf(c, fabsf(qr1[a]), mE1);
   }
-  __syncthreads();
+  float N0 = 0.0f, N1 = 0.0f, mN0 = 0.0f, mN1 = 0.0f;
+  uint64_t nmask = __ballot(in_N);
+  while (nmask) {
+    const int j = __builtin_ctzll(nmask);
+    nmask &= nmask - 1;
+    const float aw = fabsf(ws[j]);
+    const float qj0 = elem<DT>(qrow + (size_t)j * RB, d0), qj1 = elem<DT>(qrow + (size_t)j * RB, d1);
+    N0 = __builtin_fmaf(aw, qj0, N0);
+    N1 = __builtin_fmaf(aw, qj1, N1);
+    mN0 = __builtin_fmaf(aw, fabsf(qj0), mN0);
+    mN1 = __builtin_fmaf(aw, fabsf(qj1), mN1);
+  }
   // row multipliers: 1 for bf16; for fp8 a power of two that brings the
   // row's largest magnitude within the e4m3 range
   double mult[2] = {1.0, 1.0};
   if constexpr (DT == kFP8) {
-    for (int v = 0; v < 2; ++v) {
-      double amax = 0.0;
-      for (int d = lane; d < kDim; d += 64) amax = fmax(amax, fabs(vec[v][d]));
+    float am[2] = {fmaxf(fabsf(E0), fabsf(E1)), fmaxf(fabsf(N0), fabsf(N1))};
 #pragma unroll
-      for (int dd = 32; dd >= 1; dd >>= 1) amax = fmax(amax, __shfl_xor(amax, dd, 64));
-      mult[v] = amax > 0 ? ldexp(1.0, (int)ceil(log2(amax / 448.0))) : 1.0;
+    for (int v = 0; v < 2; ++v) {
+#pragma unroll
+      for (int dd = 32; dd >= 1; dd >>= 1) am[v] = fmaxf(am[v], __shfl_xor(am[v], dd, 64));
+      mult[v] = am[v] > 0.0f ? ldexp(1.0, (int)ceil(log2((double)am[v] / 448.0))) : 1.0;
     }
   }
-  double err2[2] = {0.0, 0.0}, nrm2[2] = {0.0, 0.0};
+  // store the rounded rows; |E - E_stored| <= |E_fp32 - E_stored| + gamma_30 |mE|
+  // (likewise q_neg with gamma_64), differences and norms in fp64
   uint8_t* prow = plan_rows + row * kPlanRows * RB;
+  double err2[2] = {0.0, 0.0}, nrm2[2] = {0.0, 0.0}, mag2[2] = {0.0, 0.0};
+#pragma unroll
   for (int v = 0; v < 2; ++v) {
     uint8_t* dst = prow + (size_t)(v == 0 ? kLinRow : kAuxRow) * RB;
-    for (int d = lane; d < kDim; d += 64) {
+    const float x0 = v == 0 ? E0 : N0, x1 = v == 0 ? E1 : N1;
+    const float g0 = v == 0 ? mE0 : mN0, g1 = v == 0 ? mE1 : mN1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = h ? d1 : d0;
+      const double x = h ? x1 : x0;
       uint32_t code;
-      const double rv = round_to_dtype<DT>(vec[v][d] / mult[v], &code) * mult[v];
+      const double rv = round_to_dtype<DT>(x / mult[v], &code) * mult[v];
       if constexpr (DT == kBF16)
         reinterpret_cast<uint16_t*>(dst)[d] = (uint16_t)code;
       else
         dst[d] = (uint8_t)code;
-      err2[v] = fma(vec[v][d] - rv, vec[v][d] - rv, err2[v]);
+      err2[v] = fma(x - rv, x - rv, err2[v]);
       nrm2[v] = fma(rv, rv, nrm2[v]);
+      const double g = h ? g1 : g0;
+      mag2[v] = fma(g, g, mag2[v]);
     }
     err2[v] = wave_sum_d(err2[v]);
     nrm2[v] = wave_sum_d(nrm2[v]);
+    mag2[v] = wave_sum_d(mag2[v]);
   }
-  const double e_lin = sqrt(err2[0]) * (1.0 + 1e-12), e_neg = sqrt(err2[1]) * (1.0 + 1e-12);
+  const double e_lin = (sqrt(err2[0]) + (double)gamma_f(32) * sqrt(mag2[0]) * (1.0 + 1e-6)) * (1.0 + 1e-12);
+  const double e_neg = (sqrt(err2[1]) + (double)gamma_f(66) * sqrt(mag2[1]) * (1.0 + 1e-6)) * (1.0 + 1e-12);
   const double n_lin = sqrt(nrm2[0]), n_neg = sqrt(nrm2[1]);
 
   // retained rows: the query's own codes
@@ -427,29 +502,28 @@ __global__ __launch_bounds__(64) void k_plan(const uint8_t* __restrict__ q, cons
       reinterpret_cast<uint32_t*>(dst)[x] = a < nret ? reinterpret_cast<const uint32_t*>(src)[x] : 0u;
   }
 
-  // 9. guard: the GPU's fp32 score differs from the exact one by at most
+  // 10. guard: the GPU's fp32 score differs from the exact one by at most
   //    (g_128 + 2 g_64) W1 |k| (128-term dots, 64-term head sum, final
   //    combine), and the fp32 bound from its exact value by at most
   //    (g_128 + g_24) Wb |k| + g_24 (e_neg + rho + e_lin) |k|, where
-  //    g_n = n u / (1 - n u), u = 2^-24 (the screen adds each lane's 16
-  //    rows in one chain, then the other half's sum and the |k| term: at
-  //    most 20 roundings per term, within g_24).  Doubled for margin.
+  //    g_n = n u / (1 - n u), u = 2^-24 (the screen adds each lane's rows
+  //    in two chains of eight, then the chain sum, the other half's sum and
+  //    the aux, linear and |k| terms: at most 14 roundings per term, within
+  //    g_24).  Doubled for margin.
   const double u = 5.9604644775390625e-08;
   auto gam = [u](double n) { return n * u / (1.0 - n * u); };
-  const double W1 = wave_sum_d(fabs(wj) * qnorm);
+  const double W1 = wave_sum_d(fabs((double)wj) * (double)qnorm);
   double Wb = n_lin + n_neg;
-#pragma unroll
-  for (int a = 0; a < kRetained; ++a)
-    if (a < nret) Wb += fabs(cch[a]) * __shfl(qnorm, ridx[a], 64);
+  for (int a = 0; a < nret; ++a) Wb += (double)cch[a] * (double)__shfl(qnorm, ridx[a], 64);
   const double guard =
       2.0 * ((gam(128) + 2.0 * gam(64) + gam(4)) * W1 + (gam(128) + gam(24)) * Wb + gam(24) * (e_neg + rho + e_lin));
-  const double kappa = (rho + e_lin + guard) * (1.0 + 1e-9);
+  const double kappa = ((double)rho + e_lin + guard) * (1.0 + 1e-9);
 
   bool finite = isfinite(kappa) && isfinite(e_neg) && isfinite(mult[0]) && isfinite(mult[1]);
   for (int a = 0; a < kRetained; ++a) finite = finite && isfinite(cch[a]);
   if (lane == 0) {
     float* co = plan_coef + row * kPlanRows;
-    for (int a = 0; a < kRetained; ++a) co[a] = __double2float_ru(cch[a]);
+    for (int a = 0; a < kRetained; ++a) co[a] = cch[a];
     co[kAuxRow] = (float)mult[1];
     co[kLinRow] = (float)mult[0];
     float* mi = plan_misc + row * 4;
@@ -490,13 +564,16 @@ hipError_t launch_plan(const Problem& p, int nret, const int32_t* seeds, const i
                        const int32_t* batch_flag, const uint8_t* force_recover, uint8_t* plan_rows, float* plan_coef,
                        float* plan_misc, int32_t* plan_flag, hipStream_t st) {
   const int prof_slot = prof_open("k_plan", st);
-  const dim3 grid((unsigned)((size_t)p.B * p.Q));
+  const size_t nrows = (size_t)p.B * p.Q;
+  const dim3 grid((unsigned)((nrows + kPlanWaves - 1) / kPlanWaves));
   if (p.dtype == kBF16)
-    hipLaunchKernelGGL(k_plan<kBF16>, grid, dim3(64), 0, st, p.q, p.k, p.w, p.pos, p.Q, p.N, nret, seeds,
-                       seed_count, seed_stride, batch_flag, force_recover, plan_rows, plan_coef, plan_misc, plan_flag);
+    hipLaunchKernelGGL(k_plan<kBF16>, grid, dim3(kPlanWaves * 64), 0, st, p.q, p.k, p.w, p.pos, p.Q, p.N, nret, nrows,
+                       seeds, seed_count, seed_stride, batch_flag, force_recover, plan_rows, plan_coef, plan_misc,
+                       plan_flag);
   else
-    hipLaunchKernelGGL(k_plan<kFP8>, grid, dim3(64), 0, st, p.q, p.k, p.w, p.pos, p.Q, p.N, nret, seeds, seed_count,
-                       seed_stride, batch_flag, force_recover, plan_rows, plan_coef, plan_misc, plan_flag);
+    hipLaunchKernelGGL(k_plan<kFP8>, grid, dim3(kPlanWaves * 64), 0, st, p.q, p.k, p.w, p.pos, p.Q, p.N, nret, nrows,
+                       seeds, seed_count, seed_stride, batch_flag, force_recover, plan_rows, plan_coef, plan_misc,
+                       plan_flag);
   prof_close(prof_slot, st);
   return hipGetLastError();
 }
