@@ -33,9 +33,13 @@ constexpr int kPlanRowsK = 32;
 constexpr int kLinRowK = 31;
 constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
-constexpr int kCutSlack = 1024;  // records kept beyond topk before the threshold is raised
 constexpr int kSlots = 3;        // LDS key-tile slots
 constexpr int kStage = 96;       // candidate stage records per row
+constexpr int kCutGoal = 512;    // a forced cut keeps at most topk + kCutGoal records (a quarter of the spare room at most)
+
+// Records a forced cut may keep: topk + min(kCutGoal, (cap - topk) / 4), so
+// it frees at least three quarters of the room beyond topk.
+__device__ __forceinline__ int cut_goal(int topk, int cap) { return topk + min(kCutGoal, (cap - topk) / 4); }
 
 struct PrunePlan {
   const uint8_t* rows;       // [R][32][128] dtype: bound rows
@@ -55,32 +59,115 @@ struct PrunePlan {
   float* st_ub;              // [R][N] debug bounds or null
 };
 
-// Append state of one row (all wave-uniform except `rec`/`live`).
+// Candidate state of one row (wave-uniform).  Besides the buffer (cnt
+// records, nst more in the LDS stage) and the threshold thr, the row keeps a
+// threshold histogram: 256 LDS bins over the score code c (the high half of
+// a record), bin min(255, (c - base) >> shift), counting every record in the
+// buffer and the stage; base never exceeds the threshold's code, so every
+// kept record lands in a bin.
 struct RowState {
   uint64_t* buf;
   int cnt, nst;
   uint64_t thr;
+  uint32_t base;
+  int shift;
+  bool grown;  // records kept since the last threshold raise
 };
 
+__device__ __forceinline__ uint32_t thr_bin(uint32_t code, uint32_t base, int shift) {
+  return min(255u, (code - base) >> shift);
+}
+
+struct Rebuilt {
+  int cnt;
+  uint64_t thr;
+  uint32_t base;
+  int shift;
+};
+
+// Flush the stage, keep only the records >= thr; if more than `goal` remain,
+// cut them by radix select to between topk and goal (the threshold becomes
+// the cut's boundary); then rebuild the histogram over the kept records from
+// base = the threshold's code, with a bin width that spans their codes.
+static __device__ __noinline__ Rebuilt rebuild_candidates(uint64_t* buf, int cnt, const uint64_t* stage, int nst,
+                                                          uint32_t* hist, uint64_t thr, int topk, int goal,
+                                                          int lane) {
+  cnt = flush_stage(buf, cnt, stage, nst, lane);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  cnt = compact_records_d8(buf, cnt, SelectResult{thr, ~0ull, 0u}, lane);
+  if (cnt > goal) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+    const SelectResult sel = select_records_d8(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)goal, lane);
+    cnt = compact_records_d8(buf, cnt, sel, lane);
+    thr = sel.prefix;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  const uint32_t base = (uint32_t)(thr >> 32);
+  uint32_t mx = base;
+  for (int i = lane; i < cnt; i += 64) mx = max(mx, (uint32_t)(buf[i] >> 32));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  const uint32_t span = mx - base;
+  const int shift = span ? max(0, 24 - (int)__builtin_clz(span)) : 0;  // span >> shift < 256
+  for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+  for (int i = lane; i < cnt; i += 64) atomicAdd(&hist[thr_bin((uint32_t)(buf[i] >> 32), base, shift)], 1u);
+  return {cnt, thr, base, shift};
+}
+
+__device__ __forceinline__ void apply_rebuild(RowState& rs, const Rebuilt& r) {
+  rs.cnt = r.cnt;
+  rs.nst = 0;
+  rs.thr = r.thr;
+  rs.base = r.base;
+  rs.shift = r.shift;
+  rs.grown = true;
+}
+
+// Keep the records of up to 64 lanes that reach the threshold (stage + one
+// histogram count each); a full buffer is compacted first.
 __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live, uint64_t* stage, uint32_t* hist,
                                            int topk, int cap, int lane) {
   uint64_t bal = __ballot(live && rec >= rs.thr);
   if (bal) {
     if (rs.cnt + rs.nst + __popcll(bal) > cap) {
-      const Cut c = cut_candidates_d8(rs.buf, rs.cnt, stage, rs.nst, hist, topk, topk, lane);
-      rs.cnt = c.cnt;
-      rs.thr = c.thr;
-      rs.nst = 0;
+      apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, stage, rs.nst, hist, rs.thr, topk, cut_goal(topk, cap), lane));
       bal = __ballot(live && rec >= rs.thr);
     }
-    if (live && rec >= rs.thr)
+    if (live && rec >= rs.thr) {
       stage[rs.nst + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
           rec;
+      atomicAdd(&hist[thr_bin((uint32_t)(rec >> 32), rs.base, rs.shift)], 1u);
+    }
     rs.nst += __popcll(bal);
+    rs.grown = true;
   }
 }
 
-template <int DT>
+// Raise the threshold to the lower edge of the highest bin b whose bins >= b
+// hold at least topk records: at least topk kept records reach that code, so
+// it is at most the K-th best record seen (and within one bin of it).
+__device__ __forceinline__ void raise_threshold(RowState& rs, const uint32_t* hist, int topk, int lane) {
+  const u32x4 h = reinterpret_cast<const u32x4*>(hist)[lane];  // bins 4 lane .. 4 lane + 3
+  const uint32_t local = h.x + h.y + h.z + h.w;
+  const uint32_t above = wave_suffix_excl(local, lane);  // records in the bins above lane's
+  const uint64_t bal = __ballot(above < (uint32_t)topk && (uint32_t)topk <= above + local);
+  rs.grown = false;
+  if (!bal) return;  // fewer than topk records counted
+  const int src = __builtin_ctzll(bal);
+  uint32_t b = 4u * lane;
+  if (above + h.w >= (uint32_t)topk)
+    b += 3;
+  else if (above + h.w + h.z >= (uint32_t)topk)
+    b += 2;
+  else if (above + h.w + h.z + h.y >= (uint32_t)topk)
+    b += 1;
+  b = (uint32_t)__shfl((int)b, src, 64);
+  const uint32_t code = rs.base + (b << rs.shift);
+  if (code > (uint32_t)(rs.thr >> 32)) rs.thr = (uint64_t)code << 32;
+}
+
+// kBounds: also write every screened key's bound U to pp.st_ub (diagnostics).
+template <int DT, bool kBounds>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_topk_pruned(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
@@ -142,7 +229,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   uint32_t* my_hist = hist[wave];
   uint64_t* my_stage = stage[wave];
   int32_t* my_q = squeue[wave];
-  RowState rs{cand + row * (size_t)cap, 0, 0, 0};
+  RowState rs{cand + row * (size_t)cap, 0, 0, 0, 0u, 24, false};
   const uint8_t* kbase = k + (size_t)b * N * RB;
   const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
   const float* knb = pp.knorm + (size_t)b * N;
@@ -212,6 +299,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     rs.thr = min_record(rs.buf, rs.cnt, lane);
     tau = record_score(rs.thr);
   }
+  apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, my_stage, 0, my_hist, rs.thr, topk, cap, lane));
+  rs.grown = false;
 
   // ---------------------------------------------------------------- 2-3. screen + refine
   // Survivors are pushed to the row's queue my_q[qh, nq).  Refine schedule,
@@ -254,12 +343,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         rs.nst = 0;
       }
       // Keep the survivor threshold near the K-th best exact record seen so
-      // far: cut back to exactly topk records whenever kCutSlack more have
-      // been kept.
-      if (rs.cnt >= topk + kCutSlack) {
-        const Cut c = cut_candidates_d8(rs.buf, rs.cnt, my_stage, 0, my_hist, topk, topk, lane);
-        rs.cnt = c.cnt;
-        rs.thr = c.thr;
+      // far (to within one histogram bin), at no buffer traffic.
+      if (rs.grown) {
+        raise_threshold(rs, my_hist, topk, lane);
         thr_f = record_floor(rs.thr);
       }
       if (ti + 2 < ntiles) {
@@ -286,49 +372,56 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       // pairs the two halves of every key's sum -- lane l ends up with key
       // kb + l -- and two more bring the aux and linear rows' dots (rows 30,
       // 31, held by lanes 32..63) to the same layout.
-#pragma unroll
-      for (int pr = 0; pr < NSB / 2; ++pr) {
+      auto screen_pair = [&](int pr) {
         const int kb = ts + 64 * pr;
-        if (kb < vis) {  // wave-uniform
-          Frag<DT> kf;
-          Tile::frag(kf, ktile[cur], 64 * pr + lk, lane);
-          const f32x16 dA = mma_block<DT>(sa, kf, zero16());
-          Tile::frag(kf, ktile[cur], 64 * pr + 32 + lk, lane);
-          const f32x16 dB = mma_block<DT>(sa, kf, zero16());
-          float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
+        Frag<DT> kf;
+        Tile::frag(kf, ktile[cur], 64 * pr + lk, lane);
+        const f32x16 dA = mma_block<DT>(sa, kf, zero16());
+        Tile::frag(kf, ktile[cur], 64 * pr + 32 + lk, lane);
+        const f32x16 dB = mma_block<DT>(sa, kf, zero16());
+        float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            a0 = __builtin_fmaf(__builtin_fabsf(dA[v]), cl[v], a0);
-            a1 = __builtin_fmaf(__builtin_fabsf(dA[v + 8]), cl[v + 8], a1);
-            b0 = __builtin_fmaf(__builtin_fabsf(dB[v]), cl[v], b0);
-            b1 = __builtin_fmaf(__builtin_fabsf(dB[v + 8]), cl[v + 8], b1);
-          }
-          float sA = a0 + a1, sB = b0 + b1;
-          swap_halves(sA, sB);
-          float xA = dA[14], xB = dB[14], yA = dA[15], yB = dB[15];
-          swap_halves(xA, xB);  // xB: row-30 (aux) dot of key kb + lane
-          swap_halves(yA, yB);  // yB: row-31 (linear) dot of key kb + lane
-          const float kn = knorm_tile[cur][64 * pr + lane];
-          float U = __builtin_fmaf(m_lin, yB, sA + sB);
-          U -= relu_bits(__builtin_fmaf(m_aux, xB, -e_neg * kn));
-          U = __builtin_fmaf(kappa, kn, U);
-          if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][64 * pr + lane]);
-          const int key = kb + lane;
-          const uint32_t seedw = sbits_tile[cur][2 * pr + (lane >> 5)];
-          const bool ck = (key < vis) & !((seedw >> lk) & 1u);
-          // U >= the threshold's float floor keeps every key whose record
-          // (U, key) reaches the threshold (and at most a few equal-bound
-          // keys below it, which the refine drops)
-          const bool sv = ck & (recover | (U >= thr_f));
-          if (pp.st_ub && ck) pp.st_ub[row * (size_t)N + key] = U;
-          screened += __popcll(__ballot(ck));
-          const uint64_t mask = __ballot(sv);  // bit l: key kb + l survives
-          const int before =
-              (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-          my_q[sv ? nq + before : QCAP + lane] = key;  // branch-free: the others write scratch slots
-          nq += __popcll(mask);
-          survived += __popcll(mask);
+        for (int v = 0; v < 8; ++v) {
+          a0 = __builtin_fmaf(__builtin_fabsf(dA[v]), cl[v], a0);
+          a1 = __builtin_fmaf(__builtin_fabsf(dA[v + 8]), cl[v + 8], a1);
+          b0 = __builtin_fmaf(__builtin_fabsf(dB[v]), cl[v], b0);
+          b1 = __builtin_fmaf(__builtin_fabsf(dB[v + 8]), cl[v + 8], b1);
         }
+        float sA = a0 + a1, sB = b0 + b1;
+        swap_halves(sA, sB);
+        float xA = dA[14], xB = dB[14], yA = dA[15], yB = dB[15];
+        swap_halves(xA, xB);  // xB: row-30 (aux) dot of key kb + lane
+        swap_halves(yA, yB);  // yB: row-31 (linear) dot of key kb + lane
+        const float kn = knorm_tile[cur][64 * pr + lane];
+        float U = __builtin_fmaf(m_lin, yB, sA + sB);
+        U -= relu_bits(__builtin_fmaf(m_aux, xB, -e_neg * kn));
+        U = __builtin_fmaf(kappa, kn, U);
+        if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][64 * pr + lane]);
+        const int key = kb + lane;
+        const uint32_t seedw = sbits_tile[cur][2 * pr + (lane >> 5)];
+        const bool ck = (key < vis) & !((seedw >> lk) & 1u);
+        // U >= the threshold's float floor keeps every key whose record
+        // (U, key) reaches the threshold (and at most a few equal-bound keys
+        // below it, which the refine drops)
+        const bool sv = ck & (recover | (U >= thr_f));
+        if constexpr (kBounds) {
+          if (ck) pp.st_ub[row * (size_t)N + key] = U;
+        }
+        screened += __popcll(__ballot(ck));
+        const uint64_t mask = __ballot(sv);  // bit l: key kb + l survives
+        const int before =
+            (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        my_q[sv ? nq + before : QCAP + lane] = key;  // branch-free: the others write scratch slots
+        nq += __popcll(mask);
+        survived += __popcll(mask);
+      };
+      if (ts + KT <= vis) {  // a whole visible tile: one straight run of pairs
+#pragma unroll
+        for (int pr = 0; pr < NSB / 2; ++pr) screen_pair(pr);
+      } else {
+#pragma unroll
+        for (int pr = 0; pr < NSB / 2; ++pr)
+          if (ts + 64 * pr < vis) screen_pair(pr);  // wave-uniform
       }
       // refine batch, part 2: score the popped keys
       if (pend) score_and_keep(rf, rkey, rks, lane < 32);
@@ -374,6 +467,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+#define DSA_PRUNED_KERNEL(DT_, B_)                                                                             \
+  template __global__ void k_topk_pruned<DT_, B_>(const uint8_t* __restrict__, const uint8_t* __restrict__,   \
+                                                  const float* __restrict__, const float* __restrict__,       \
+                                                  const float* __restrict__, const int32_t* __restrict__, int, \
+                                                  int, int, int, uint64_t* __restrict__, int32_t* __restrict__, \
+                                                  float* __restrict__, PrunePlan);
+DSA_PRUNED_KERNEL(kBF16, false)
+DSA_PRUNED_KERNEL(kBF16, true)
+DSA_PRUNED_KERNEL(kFP8, false)
+DSA_PRUNED_KERNEL(kFP8, true)
+#undef DSA_PRUNED_KERNEL
+
 __global__ void k_fill_nan(float* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = __builtin_nanf("");
@@ -390,12 +495,12 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
                pb.st_ub};
   dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
   const int prof_slot = prof_open("k_topk_pruned", st);
-  if (p.dtype == kBF16)
-    hipLaunchKernelGGL(k_topk_pruned<kBF16>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
-                       p.pos, p.Q, p.N, topk, cap, cand, out_idx, out_score, pp);
-  else
-    hipLaunchKernelGGL(k_topk_pruned<kFP8>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
-                       p.pos, p.Q, p.N, topk, cap, cand, out_idx, out_score, pp);
+  using Kern = void (*)(const uint8_t*, const uint8_t*, const float*, const float*, const float*, const int32_t*, int,
+                        int, int, int, uint64_t*, int32_t*, float*, PrunePlan);
+  const Kern kern = p.dtype == kBF16 ? (pb.st_ub ? k_topk_pruned<kBF16, true> : k_topk_pruned<kBF16, false>)
+                                     : (pb.st_ub ? k_topk_pruned<kFP8, true> : k_topk_pruned<kFP8, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos, p.Q, p.N, topk,
+                     cap, cand, out_idx, out_score, pp);
   prof_close(prof_slot, st);
   return hipGetLastError();
 }
