@@ -35,6 +35,7 @@ constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
 constexpr int kSlots = 3;        // LDS key-tile slots
 constexpr int kStage = 96;       // candidate stage records per row
+constexpr int kRaiseEvery = 32;  // kept records between threshold raises
 constexpr int kCutGoal = 512;    // a forced cut keeps at most topk + kCutGoal records (a quarter of the spare room at most)
 
 // Records a forced cut may keep: topk + min(kCutGoal, (cap - topk) / 4), so
@@ -71,7 +72,7 @@ struct RowState {
   uint64_t thr;
   uint32_t base;
   int shift;
-  bool grown;  // records kept since the last threshold raise
+  int added;  // records kept since the last threshold raise
 };
 
 __device__ __forceinline__ uint32_t thr_bin(uint32_t code, uint32_t base, int shift) {
@@ -120,7 +121,7 @@ __device__ __forceinline__ void apply_rebuild(RowState& rs, const Rebuilt& r) {
   rs.thr = r.thr;
   rs.base = r.base;
   rs.shift = r.shift;
-  rs.grown = true;
+  rs.added = kRaiseEvery;
 }
 
 // Keep the records of up to 64 lanes that reach the threshold (stage + one
@@ -139,29 +140,45 @@ __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live
       atomicAdd(&hist[thr_bin((uint32_t)(rec >> 32), rs.base, rs.shift)], 1u);
     }
     rs.nst += __popcll(bal);
-    rs.grown = true;
+    rs.added += __popcll(bal);
   }
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr DPP steps inside each row
+// of 16 lanes, then the row totals read out and added to the later rows.
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x, int lane) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int rw = lane >> 4;
+  return (uint32_t)(v + (rw >= 1 ? r0 : 0) + (rw >= 2 ? r1 : 0) + (rw >= 3 ? r2 : 0));
 }
 
 // Raise the threshold to the lower edge of the highest bin b whose bins >= b
 // hold at least topk records: at least topk kept records reach that code, so
-// it is at most the K-th best record seen (and within one bin of it).
+// it is at most the K-th best record seen (and within one bin of it).  Lane l
+// reads bins 252 - 4l .. 255 - 4l (the top bins in lane 0), so the records
+// above a lane's bins are a prefix sum over the lanes before it.
 __device__ __forceinline__ void raise_threshold(RowState& rs, const uint32_t* hist, int topk, int lane) {
-  const u32x4 h = reinterpret_cast<const u32x4*>(hist)[lane];  // bins 4 lane .. 4 lane + 3
+  const u32x4 h = reinterpret_cast<const u32x4*>(hist)[63 - lane];  // h.w: bin 255 - 4 lane
   const uint32_t local = h.x + h.y + h.z + h.w;
-  const uint32_t above = wave_suffix_excl(local, lane);  // records in the bins above lane's
+  const uint32_t above = wave_prefix_incl(local, lane) - local;
   const uint64_t bal = __ballot(above < (uint32_t)topk && (uint32_t)topk <= above + local);
-  rs.grown = false;
+  rs.added = 0;
   if (!bal) return;  // fewer than topk records counted
   const int src = __builtin_ctzll(bal);
-  uint32_t b = 4u * lane;
+  uint32_t b = 4u * (63 - lane);
   if (above + h.w >= (uint32_t)topk)
     b += 3;
   else if (above + h.w + h.z >= (uint32_t)topk)
     b += 2;
   else if (above + h.w + h.z + h.y >= (uint32_t)topk)
     b += 1;
-  b = (uint32_t)__shfl((int)b, src, 64);
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
   const uint32_t code = rs.base + (b << rs.shift);
   if (code > (uint32_t)(rs.thr >> 32)) rs.thr = (uint64_t)code << 32;
 }
@@ -209,27 +226,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const float* my_w = wrow[wave];
   const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
 
-  // screen side: the 32 plan rows as one 32x32 MFMA A operand; lane l holds
-  // rows 8*(v/4) + 4*(l/32) + v%4 of the result (v = 0..15), with their
-  // coefficients in cl[v].  Rows 30 (aux) and 31 (linear) land in lanes
-  // 32..63 at v = 14, 15, whose cl is zero; they enter the bound separately.
-  Frag<DT> sa;
-  load_frag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 31)) * RB, lane);
-  const float* co = pp.coef + row * kPlanRowsK;
-  float cl[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    cl[v] = r < kRetainedK ? co[r] : 0.0f;
-  }
-  const float m_aux = co[kAuxRowK], m_lin = co[kLinRowK];
-  const float kappa = pp.misc[row * 4 + 0], e_neg = pp.misc[row * 4 + 1];
-  const bool recover = pp.flag[row] != 0;
-
   uint32_t* my_hist = hist[wave];
   uint64_t* my_stage = stage[wave];
   int32_t* my_q = squeue[wave];
-  RowState rs{cand + row * (size_t)cap, 0, 0, 0, 0u, 24, false};
+  RowState rs{cand + row * (size_t)cap, 0, 0, 0, 0u, 24, 0};
   const uint8_t* kbase = k + (size_t)b * N * RB;
   const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
   const float* knb = pp.knorm + (size_t)b * N;
@@ -253,6 +253,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   };
 
   // ---------------------------------------------------------------- 1. seeds
+  bool hist_set = false;
   {
     const int ntiles = (nseed + KT - 1) / KT;
     for (int ti = 0; ti < min(ntiles, 2); ++ti) {
@@ -281,6 +282,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
                          lane < 32 && si < nseed && key < vis);
         }
       }
+      // once the row holds a cut's worth of records, set up the threshold
+      // histogram; from then on the threshold rises with the seeds
+      if (!hist_set && rs.cnt + rs.nst >= cut_goal(topk, cap)) {
+        apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, rs.thr, topk,
+                                             cut_goal(topk, cap), lane));
+        hist_set = true;
+      }
+      if (hist_set && rs.added >= kRaiseEvery) raise_threshold(rs, my_hist, topk, lane);
       wait_vmem_all();
       __syncthreads();
       cur = nxt;
@@ -300,7 +309,25 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     tau = record_score(rs.thr);
   }
   apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, my_stage, 0, my_hist, rs.thr, topk, cap, lane));
-  rs.grown = false;
+  rs.added = 0;
+
+  // screen side: the 32 plan rows as one 32x32 MFMA A operand; lane l holds
+  // rows 8*(v/4) + 4*(l/32) + v%4 of the result (v = 0..15), with their
+  // coefficients in cl[v].  Rows 30 (aux) and 31 (linear) land in lanes
+  // 32..63 at v = 14, 15, whose cl is zero; they enter the bound separately.
+  Frag<DT> sa;
+  load_frag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 31)) * RB, lane);
+  const float* co = pp.coef + row * kPlanRowsK;
+  float cl[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    cl[v] = r < kRetainedK ? co[r] : 0.0f;
+  }
+  const float m_aux = co[kAuxRowK], m_lin = co[kLinRowK];
+  const float kappa = pp.misc[row * 4 + 0], e_neg = pp.misc[row * 4 + 1];
+  const bool recover = pp.flag[row] != 0;
+
 
   // ---------------------------------------------------------------- 2-3. screen + refine
   // Survivors are pushed to the row's queue my_q[qh, nq).  Refine schedule,
@@ -344,7 +371,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       }
       // Keep the survivor threshold near the K-th best exact record seen so
       // far (to within one histogram bin), at no buffer traffic.
-      if (rs.grown) {
+      if (rs.added >= kRaiseEvery) {
         raise_threshold(rs, my_hist, topk, lane);
         thr_f = record_floor(rs.thr);
       }
