@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int KT = Tile::KT;     // keys per tile (128 bf16, 256 fp8)
   constexpr int NSB = KT / 32;     // 32-key blocks per tile
   constexpr int QCAP = KT + 96;    // survivor queue per row (see the refine schedule)
+  constexpr int kPend = (DT == kFP8) ? 2 : 1;  // refine batches in flight per tile (register budget)
   __shared__ u32x4 ktile[kSlots][kDirectSlots];
   __shared__ float kscale_tile[kSlots][KT];
   __shared__ float knorm_tile[kSlots][KT];
@@ -331,10 +332,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   // ---------------------------------------------------------------- 2-3. screen + refine
   // Survivors are pushed to the row's queue my_q[qh, nq).  Refine schedule,
-  // per tile: at its start, if 32 survivors are queued, pop them and issue
-  // the loads of their key rows (global memory; the rows were streamed
-  // moments ago, so they come from cache); score them at the tile's end,
-  // after the screen of the tile has covered the load latency.  A row whose
+  // per tile: at its start, pop up to kPend full batches of 32 queued
+  // survivors and issue the loads of their key rows (global memory; the rows
+  // were streamed moments ago, so they come from cache); score them at the
+  // tile's end, after the screen of the tile has covered the load latency.  A row whose
   // queue still holds more than 96 keys at the tile's end refines further
   // batches on the spot (rows with very many survivors, e.g. recovered
   // rows), so the next tile's KT survivors always fit.
@@ -382,16 +383,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         tl.load_words(knorm_tile[spare], knb, tn, N, 4, lane);
         tl.load_bits(sbits_tile[spare], sbits, tn, words, lane);
       }
-      // refine batch, part 1: pop and issue the key-row loads
-      const bool pend = nq - qh >= 32;
-      Frag<DT> rf;
-      int rkey = 0;
-      float rks = 1.0f;
-      if (pend) {
-        rkey = batch_keys(32);
-        load_frag<DT>(rf, kbase + (size_t)rkey * RB, lane);
-        if constexpr (DT == kFP8) rks = kscb[rkey];
-        qh += 32;
+      // refine batches, part 1: pop up to kPend full batches and issue the
+      // loads of their key rows
+      const int npend = min(kPend, (nq - qh) >> 5);
+      Frag<DT> rf[kPend];
+      int rkey[kPend];
+      float rks[kPend];
+#pragma unroll
+      for (int i = 0; i < kPend; ++i) {
+        rkey[i] = 0;
+        rks[i] = 1.0f;
+        if (i < npend) {
+          rkey[i] = batch_keys(32);
+          load_frag<DT>(rf[i], kbase + (size_t)rkey[i] * RB, lane);
+          if constexpr (DT == kFP8) rks[i] = kscb[rkey[i]];
+          qh += 32;
+        }
       }
       // screen, two 32-key blocks (64 keys, one per lane after the exchange)
       // at a time: the 32x32 MFMA block of each (32 plan rows x 32 keys),
@@ -450,8 +457,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         for (int pr = 0; pr < NSB / 2; ++pr)
           if (ts + 64 * pr < vis) screen_pair(pr);  // wave-uniform
       }
-      // refine batch, part 2: score the popped keys
-      if (pend) score_and_keep(rf, rkey, rks, lane < 32);
+      // refine batches, part 2: score the popped keys
+#pragma unroll
+      for (int i = 0; i < kPend; ++i)
+        if (i < npend) score_and_keep(rf[i], rkey[i], rks[i], lane < 32);
       // compact the queue to its front; refine on the spot while it is long
       if (qh > 0) {
         const int left = nq - qh;
