@@ -8,7 +8,6 @@
 
 namespace dsa {
 
-constexpr int kWaves = 8;           // query rows per workgroup, one per wave
 
 // Candidate bookkeeping of one row (one wave): records are appended to a
 // small LDS stage during a tile and flushed to the row's global buffer at the
@@ -69,7 +68,8 @@ static __device__ __noinline__ void emit_topk_d8(uint64_t* buf, int cnt, const u
 }
 
 // Key tile loaded straight from global memory into LDS (global_load_lds, 16
-// bytes per lane, no staging registers): the KT keys of one 32 KiB tile,
+// bytes per lane, no staging registers): the KT keys of one tile of
+// kTileBytes key bytes, shared by the kWaves waves of a workgroup,
 // key-major with one pad chunk per key, 16-byte chunk c of tile key r at
 // slot r * (CPR + 1) + c.  With that pitch the 16 lanes served together by
 // a 16-byte LDS read (16 consecutive keys, one chunk) hit 16 different bank
@@ -80,16 +80,17 @@ static __device__ __noinline__ void emit_topk_d8(uint64_t* buf, int cnt, const u
 // issued by wave n % kWaves; the per-lane byte offsets are fixed, so a load
 // costs no vector ALU work.  Completion: each wave waits for its own loads
 // (vmcnt), then a workgroup barrier publishes the tile.
-template <int DT>
+template <int DT, int kTileBytes, int kWaves>
 struct DirectTile {
   static constexpr int RB = Frag<DT>::kRowBytes;
   static constexpr int CPR = RB / 16;                  // chunks per key
-  static constexpr int KT = 32768 / RB;                // keys per tile: 128 bf16, 256 fp8
-  static constexpr int SLOTS = KT * (CPR + 1);         // 2176 / 2304: whole instructions
+  static constexpr int KT = kTileBytes / RB;           // keys per tile
+  static constexpr int SLOTS = KT * (CPR + 1);         // LDS chunks, whole load instructions
   static constexpr int NI = SLOTS / 64;                // load instructions per tile
   static constexpr int PER_WAVE = (NI + kWaves - 1) / kWaves;
   static_assert(SLOTS % 64 == 0, "tile slots fill whole load instructions");
   static_assert(kWaves * (PER_WAVE - 1) <= NI, "only the last load of a wave may be past the tile");
+  static_assert(KT / 64 <= kWaves / 2, "per-row words are loaded by one half of the waves each");
   const uint32_t* off;  // this wave's [PER_WAVE][64] source offsets (LDS), from the tile's first row
   int wave;             // wave-uniform
 
@@ -145,7 +146,8 @@ struct DirectTile {
                                          0, 0);
   }
   // One 4-byte word per tile row (fp8 key scale, key norm): dst[r] =
-  // src[min(ts + r, N - 1)], loaded by waves w0 .. w0 + KT/64 - 1.
+  // src[min(ts + r, N - 1)], loaded by waves w0 .. w0 + KT/64 - 1 (w0 = 0
+  // or kWaves / 2).
   __device__ __forceinline__ void load_words(float* dst, const float* src, int ts, int N, int w0, int lane) const {
     const int wr = wave - w0;
     if (wr >= 0 && wr < KT / 64) {
@@ -184,6 +186,8 @@ struct DirectTile {
     }
   }
 };
-constexpr int kDirectSlots = 2304;  // max over dtypes of DirectTile::SLOTS
+// LDS chunks of a tile of `tile_bytes` key bytes, the larger over the dtypes
+// (fp8: 9 chunks per 128-byte key).
+constexpr int direct_slots(int tile_bytes) { return tile_bytes / 128 * 9; }
 
 }  // namespace dsa

@@ -33,6 +33,8 @@ constexpr int kPlanRowsK = 32;
 constexpr int kLinRowK = 31;
 constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
+constexpr int kWaves = 8;        // query rows per workgroup, one per wave
+constexpr int kTileBytes = 32768;  // key bytes of one LDS tile: 128 bf16 or 256 fp8 keys
 constexpr int kSlots = 3;        // LDS key-tile slots
 constexpr int kStage = 96;       // candidate stage records per row
 constexpr int kRaiseEvery = 32;  // kept records between threshold raises
@@ -190,13 +192,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
     int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
     PrunePlan pp) {
-  using Tile = DirectTile<DT>;
+  using Tile = DirectTile<DT, kTileBytes, kWaves>;
   constexpr int RB = Frag<DT>::kRowBytes;
   constexpr int KT = Tile::KT;     // keys per tile (128 bf16, 256 fp8)
   constexpr int NSB = KT / 32;     // 32-key blocks per tile
   constexpr int QCAP = KT + 96;    // survivor queue per row (see the refine schedule)
   constexpr int kPend = (DT == kFP8) ? 2 : 1;  // refine batches in flight per tile (register budget)
-  __shared__ u32x4 ktile[kSlots][kDirectSlots];
+  __shared__ u32x4 ktile[kSlots][direct_slots(kTileBytes)];
   __shared__ float kscale_tile[kSlots][KT];
   __shared__ float knorm_tile[kSlots][KT];
   __shared__ uint32_t sbits_tile[kSlots][64];
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     for (int ti = 0; ti < min(ntiles, 2); ++ti) {
       tl.load(ktile[ti], kbase, ti * KT, N, lane);
       if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, 0, lane);
-      tl.load_words(knorm_tile[ti], knb, ti * KT, N, 4, lane);
+      tl.load_words(knorm_tile[ti], knb, ti * KT, N, kWaves / 2, lane);
       tl.load_bits(sbits_tile[ti], sbits, ti * KT, words, lane);
     }
     wait_vmem_all();
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         const int tn = (ti + 2) * KT;
         tl.load(ktile[spare], kbase, tn, N, lane);
         if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, tn, N, 0, lane);
-        tl.load_words(knorm_tile[spare], knb, tn, N, 4, lane);
+        tl.load_words(knorm_tile[spare], knb, tn, N, kWaves / 2, lane);
         tl.load_bits(sbits_tile[spare], sbits, tn, words, lane);
       }
       // refine batches, part 1: pop up to kPend full batches and issue the

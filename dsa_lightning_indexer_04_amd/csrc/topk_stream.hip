@@ -10,11 +10,12 @@
 // end the buffer's best min(topk, visible) records are the exact Top-K.
 //
 // Organisation (gfx950):
-//   workgroup = 8 waves = 8 consecutive query rows of one sequence, one row
+//   workgroup = 4 waves = 4 consecutive query rows of one sequence, one row
 //               per wave held in registers as MFMA A fragments (64 heads x
-//               128 dims) plus its head weights; two waves per SIMD, so one
-//               wave's MFMAs overlap the other's fp32 epilogue;
-//   key tiles (32 KiB: 128 bf16 or 256 fp8 keys) rotate through three LDS
+//               128 dims) plus its head weights; two workgroups per CU, two
+//               waves per SIMD, so one wave's MFMAs overlap the other's fp32
+//               epilogue and one workgroup's tile barrier the other's work;
+//   key tiles (16 KiB: 64 bf16 or 128 fp8 keys) rotate through three LDS
 //   slots: the tile after next streams from global memory straight into
 //   LDS while the current one is scored, in a padded key-major layout so
 //   the column reads are bank-conflict free; all 8 waves read each tile,
@@ -30,7 +31,9 @@
 
 namespace dsa {
 
-constexpr int kSlots = 3;  // LDS key-tile slots
+constexpr int kWaves = 4;           // query rows per workgroup, one per wave (two workgroups per CU)
+constexpr int kTileBytes = 16384;   // key bytes of one LDS tile: 64 bf16 or 128 fp8 keys
+constexpr int kSlots = 3;           // LDS key-tile slots
 
 template <int DT>
 struct BlockAcc {
@@ -87,11 +90,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
     int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
-  using Tile = DirectTile<DT>;
+  using Tile = DirectTile<DT, kTileBytes, kWaves>;
   constexpr int RB = Frag<DT>::kRowBytes;
   constexpr int KT = Tile::KT;   // keys per tile
   constexpr int NSB = KT / 32;   // 32-key blocks per tile (even)
-  __shared__ u32x4 ktile[kSlots][kDirectSlots];
+  __shared__ u32x4 ktile[kSlots][direct_slots(kTileBytes)];
   __shared__ float kscale_tile[kSlots][KT];
   __shared__ uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits)
   __shared__ uint64_t stage[kWaves][KT + 64];  // KT records + 64 scratch slots
