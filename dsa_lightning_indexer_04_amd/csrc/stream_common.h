@@ -67,6 +67,116 @@ static __device__ __noinline__ void emit_topk_d8(uint64_t* buf, int cnt, const u
   }
 }
 
+constexpr int kRaiseEvery = 32;  // kept records between threshold raises
+constexpr int kCutGoal = 512;    // a forced cut keeps at most topk + kCutGoal records (a quarter of the spare room at most)
+
+// Records a forced cut may keep: topk + min(kCutGoal, (cap - topk) / 4), so
+// it frees at least three quarters of the room beyond topk.
+__device__ __forceinline__ int cut_goal(int topk, int cap) { return topk + min(kCutGoal, (cap - topk) / 4); }
+
+// Candidate state of one row (wave-uniform).  Besides the buffer (cnt
+// records, nst more in the LDS stage) and the threshold thr, the row keeps a
+// threshold histogram: 256 LDS bins over the score code c (the high half of
+// a record), bin min(255, (c - base) >> shift), counting every record in the
+// buffer and the stage; base never exceeds the threshold's code, so every
+// kept record lands in a bin.
+struct RowState {
+  uint64_t* buf;
+  int cnt, nst;
+  uint64_t thr;
+  uint32_t base;
+  int shift;
+  int added;  // records kept since the last threshold raise
+};
+
+__device__ __forceinline__ uint32_t thr_bin(uint32_t code, uint32_t base, int shift) {
+  return min(255u, (code - base) >> shift);
+}
+
+struct Rebuilt {
+  int cnt;
+  uint64_t thr;
+  uint32_t base;
+  int shift;
+};
+
+// Flush the stage, keep only the records >= thr; if more than `goal` remain,
+// cut them by radix select to between topk and goal (the threshold becomes
+// the cut's boundary); then rebuild the histogram over the kept records from
+// base = the threshold's code, with a bin width that spans their codes.
+static __device__ __noinline__ Rebuilt rebuild_candidates(uint64_t* buf, int cnt, const uint64_t* stage, int nst,
+                                                          uint32_t* hist, uint64_t thr, int topk, int goal,
+                                                          int lane) {
+  cnt = flush_stage(buf, cnt, stage, nst, lane);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  cnt = compact_records_d8(buf, cnt, SelectResult{thr, ~0ull, 0u}, lane);
+  if (cnt > goal) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+    const SelectResult sel = select_records_d8(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)goal, lane);
+    cnt = compact_records_d8(buf, cnt, sel, lane);
+    thr = sel.prefix;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  const uint32_t base = (uint32_t)(thr >> 32);
+  uint32_t mx = base;
+  for (int i = lane; i < cnt; i += 64) mx = max(mx, (uint32_t)(buf[i] >> 32));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  const uint32_t span = mx - base;
+  const int shift = span ? max(0, 24 - (int)__builtin_clz(span)) : 0;  // span >> shift < 256
+  for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+  for (int i = lane; i < cnt; i += 64) atomicAdd(&hist[thr_bin((uint32_t)(buf[i] >> 32), base, shift)], 1u);
+  return {cnt, thr, base, shift};
+}
+
+__device__ __forceinline__ void apply_rebuild(RowState& rs, const Rebuilt& r) {
+  rs.cnt = r.cnt;
+  rs.nst = 0;
+  rs.thr = r.thr;
+  rs.base = r.base;
+  rs.shift = r.shift;
+  rs.added = kRaiseEvery;
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr DPP steps inside each row
+// of 16 lanes, then the row totals read out and added to the later rows.
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x, int lane) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int rw = lane >> 4;
+  return (uint32_t)(v + (rw >= 1 ? r0 : 0) + (rw >= 2 ? r1 : 0) + (rw >= 3 ? r2 : 0));
+}
+
+// Raise the threshold to the lower edge of the highest bin b whose bins >= b
+// hold at least topk records: at least topk kept records reach that code, so
+// it is at most the K-th best record seen (and within one bin of it).  Lane l
+// reads bins 252 - 4l .. 255 - 4l (the top bins in lane 0), so the records
+// above a lane's bins are a prefix sum over the lanes before it.
+__device__ __forceinline__ void raise_threshold(RowState& rs, const uint32_t* hist, int topk, int lane) {
+  const u32x4 h = reinterpret_cast<const u32x4*>(hist)[63 - lane];  // h.w: bin 255 - 4 lane
+  const uint32_t local = h.x + h.y + h.z + h.w;
+  const uint32_t above = wave_prefix_incl(local, lane) - local;
+  const uint64_t bal = __ballot(above < (uint32_t)topk && (uint32_t)topk <= above + local);
+  rs.added = 0;
+  if (!bal) return;  // fewer than topk records counted
+  const int src = __builtin_ctzll(bal);
+  uint32_t b = 4u * (63 - lane);
+  if (above + h.w >= (uint32_t)topk)
+    b += 3;
+  else if (above + h.w + h.z >= (uint32_t)topk)
+    b += 2;
+  else if (above + h.w + h.z + h.y >= (uint32_t)topk)
+    b += 1;
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+  const uint32_t code = rs.base + (b << rs.shift);
+  if (code > (uint32_t)(rs.thr >> 32)) rs.thr = (uint64_t)code << 32;
+}
+
 // Key tile loaded straight from global memory into LDS (global_load_lds, 16
 // bytes per lane, no staging registers): the KT keys of one tile of
 // kTileBytes key bytes, shared by the kWaves waves of a workgroup,
