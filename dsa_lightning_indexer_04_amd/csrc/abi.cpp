@@ -202,6 +202,11 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
   uint8_t* scount = take(B * 4);
   uint8_t* bits = take(B * words * 4);
   uint8_t* bflag = take(B * 4);
+  uint8_t* skeys = take(B * (uint64_t)pc.num_seeds * 128 * elem_bytes(in->dtype));
+  uint8_t* sksc = take(B * (uint64_t)pc.num_seeds * 4);
+  uint8_t* spos = take(R * 4);
+  uint8_t* stidx = take(R * (uint64_t)topk * 4);
+  uint8_t* stsc = take(R * (uint64_t)topk * 4);
   if (base && pb) {
     if (cand) *cand = reinterpret_cast<uint64_t*>(c);
     pb->plan_rows = rows;
@@ -215,6 +220,11 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
     pb->seed_bits = reinterpret_cast<uint32_t*>(bits);
     pb->bits_stride = (int)words;
     pb->batch_flag = reinterpret_cast<int32_t*>(bflag);
+    pb->seed_keys = skeys;
+    pb->seed_kscale = reinterpret_cast<float*>(sksc);
+    pb->seed_pos = reinterpret_cast<int32_t*>(spos);
+    pb->seed_top_idx = reinterpret_cast<int32_t*>(stidx);
+    pb->seed_top_score = reinterpret_cast<float*>(stsc);
   }
   return off;
 }
@@ -295,6 +305,21 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
                                              pb.batch_flag, st))))
     return rc;
   if ((rc = hip_status(dsa::launch_key_norms(p, pb.knorm, st)))) return rc;
+  // the seeds' exact Top-K per row: the streaming Top-K over the packed seed
+  // keys (the same score routine, so the same scores)
+  if ((rc = hip_status(dsa::launch_seed_pack(p, pb.seeds, pb.seed_count, pb.seed_stride, pb.seed_keys,
+                                             pb.seed_kscale, pb.seed_pos, st))))
+    return rc;
+  {
+    dsa::Problem sp = p;
+    sp.N = pb.seed_stride;
+    sp.k = pb.seed_keys;
+    sp.k_scale = in->dtype == DSA_BF16 ? nullptr : pb.seed_kscale;
+    sp.pos = pb.seed_pos;
+    if ((rc = hip_status(dsa::launch_topk_stream(sp, topk, dsa::stream_capacity(topk), cand, pb.seed_top_idx,
+                                                 pb.seed_top_score, st))))
+      return rc;
+  }
   if ((rc = hip_status(dsa::launch_plan(p, pc.num_retained, pb.seeds, pb.seed_count, pb.seed_stride, pb.batch_flag,
                                         pc.force_recover, pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag,
                                         st))))

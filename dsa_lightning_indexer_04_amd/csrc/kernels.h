@@ -48,6 +48,11 @@ struct PrunedBuffers {
   uint32_t* seed_bits; // [B][bits_stride]
   int bits_stride;
   int32_t* batch_flag; // [B]
+  uint8_t* seed_keys;     // [B][seed_stride] key rows (dtype): the seeds packed
+  float* seed_kscale;     // [B][seed_stride] their fp8 key scales
+  int32_t* seed_pos;      // [B*Q]: (number of the row's visible seeds) - 1
+  int32_t* seed_top_idx;  // [B*Q][topk]: the row's exact seed Top-K (seed numbers, -1 padded)
+  float* seed_top_score;  // [B*Q][topk]: their scores
   float* st_tau;
   int32_t* st_screened;
   int32_t* st_surv;
@@ -58,6 +63,10 @@ struct PrunedBuffers {
 hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, int32_t* seeds, int32_t* seed_count,
                             uint32_t* bits, int32_t* batch_flag, hipStream_t st);
 hipError_t launch_key_norms(const Problem& p, float* knorm, hipStream_t st);
+// Packs the seed keys (and fp8 scales) of every sequence and counts each
+// row's visible seeds, so the streaming Top-K can score the seeds.
+hipError_t launch_seed_pack(const Problem& p, const int32_t* seeds, const int32_t* seed_count, int seed_stride,
+                            uint8_t* seed_keys, float* seed_kscale, int32_t* seed_pos, hipStream_t st);
 hipError_t launch_plan(const Problem& p, int nret, const int32_t* seeds, const int32_t* seed_count, int seed_stride,
                        const int32_t* batch_flag, const uint8_t* force_recover, uint8_t* plan_rows, float* plan_coef,
                        float* plan_misc, int32_t* plan_flag, hipStream_t st);

@@ -120,6 +120,50 @@ __global__ __launch_bounds__(256) void k_key_norms(const uint8_t* __restrict__ k
   knorm[s] = __double2float_ru(sqrt(acc) * (1.0 + 1e-15));
 }
 
+// ---------------------------------------------------------------- seed pack
+
+// Seed rows packed per sequence: row i of sequence b is key seeds[b][i] for
+// i < seed_count[b], else the last seed (key 0 if there is none); these pad
+// rows are never visible.  One 16-byte chunk per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void k_seed_gather(const uint8_t* __restrict__ k, const float* __restrict__ ksc,
+                                                     int N, const int32_t* __restrict__ seeds,
+                                                     const int32_t* __restrict__ seed_count, int S,
+                                                     uint8_t* __restrict__ seed_keys, float* __restrict__ seed_kscale) {
+  constexpr int RB = Frag<DT>::kRowBytes, CPR = RB / 16;
+  const int b = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk index within the sequence
+  if (c >= (int64_t)S * CPR) return;
+  const int i = (int)(c / CPR), ch = (int)(c % CPR);
+  const int cnt = seed_count[b];
+  const int key = cnt > 0 ? seeds[(size_t)b * S + min(i, cnt - 1)] : 0;
+  const u32x4* src = reinterpret_cast<const u32x4*>(k + ((size_t)b * N + key) * RB) + ch;
+  reinterpret_cast<u32x4*>(seed_keys + ((size_t)b * S + i) * RB)[ch] = *src;
+  if (DT == kFP8 && ch == 0) seed_kscale[(size_t)b * S + i] = ksc[(size_t)b * N + key];
+}
+
+// seed_pos[row] = (number of the row's sequence's seeds at or below the
+// row's position) - 1, by binary search over the ascending seeds.
+__global__ __launch_bounds__(256) void k_seed_positions(const int32_t* __restrict__ pos, int Q, size_t rows,
+                                                        const int32_t* __restrict__ seeds,
+                                                        const int32_t* __restrict__ seed_count, int S,
+                                                        int32_t* __restrict__ seed_pos) {
+  const size_t row = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  const int b = (int)(row / (size_t)Q);
+  const int32_t* sb = seeds + (size_t)b * S;
+  const int p = pos[row];
+  int lo = 0, hi = seed_count[b];  // first seed > p lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (sb[mid] <= p)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  seed_pos[row] = lo - 1;
+}
+
 // ---------------------------------------------------------------- planner
 
 constexpr int kRetained = 30;   // retained heads: plan rows 0..29
@@ -556,6 +600,24 @@ hipError_t launch_key_norms(const Problem& p, float* knorm, hipStream_t st) {
     hipLaunchKernelGGL(k_key_norms<kBF16>, grid, dim3(256), 0, st, p.k, n, knorm);
   else
     hipLaunchKernelGGL(k_key_norms<kFP8>, grid, dim3(256), 0, st, p.k, n, knorm);
+  prof_close(prof_slot, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_seed_pack(const Problem& p, const int32_t* seeds, const int32_t* seed_count, int seed_stride,
+                            uint8_t* seed_keys, float* seed_kscale, int32_t* seed_pos, hipStream_t st) {
+  const int prof_slot = prof_open("k_seed_pack", st);
+  const int cpr = (p.dtype == kBF16 ? Frag<kBF16>::kRowBytes : Frag<kFP8>::kRowBytes) / 16;
+  const dim3 grid((unsigned)(((int64_t)seed_stride * cpr + 255) / 256), p.B);
+  if (p.dtype == kBF16)
+    hipLaunchKernelGGL(k_seed_gather<kBF16>, grid, dim3(256), 0, st, p.k, p.k_scale, p.N, seeds, seed_count,
+                       seed_stride, seed_keys, seed_kscale);
+  else
+    hipLaunchKernelGGL(k_seed_gather<kFP8>, grid, dim3(256), 0, st, p.k, p.k_scale, p.N, seeds, seed_count,
+                       seed_stride, seed_keys, seed_kscale);
+  const size_t rows = (size_t)p.B * p.Q;
+  hipLaunchKernelGGL(k_seed_positions, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p.pos, p.Q, rows, seeds,
+                     seed_count, seed_stride, seed_pos);
   prof_close(prof_slot, st);
   return hipGetLastError();
 }

@@ -240,21 +240,6 @@ struct DirectTile {
         }
     }
   }
-  // The same for a gathered tile: tile row r is key idx[min(ts + r, nidx - 1)].
-  __device__ __forceinline__ void load_gather(u32x4* slot, const uint8_t* kbase, const int32_t* idx, int ts, int nidx,
-                                              int lane) const {
-    uint32_t o[PER_WAVE];
-    int key[PER_WAVE];
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) o[j] = off[64 * j + lane];
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) key[j] = idx[min(ts + (int)(o[j] / RB), nidx - 1)];
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j)
-      if (j < PER_WAVE - 1 || wave + kWaves * j < NI)
-        __builtin_amdgcn_global_load_lds(kbase + (size_t)key[j] * RB + o[j] % RB, slot + 64 * (wave + kWaves * j), 16,
-                                         0, 0);
-  }
   // One 4-byte word per tile row (fp8 key scale, key norm): dst[r] =
   // src[min(ts + r, N - 1)], loaded by waves w0 .. w0 + KT/64 - 1 (w0 = 0
   // or kWaves / 2).
@@ -262,14 +247,6 @@ struct DirectTile {
     const int wr = wave - w0;
     if (wr >= 0 && wr < KT / 64) {
       const int key = min(ts + 64 * wr + lane, N - 1);
-      __builtin_amdgcn_global_load_lds(src + key, dst + 64 * wr, 4, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void load_words_gather(float* dst, const float* src, const int32_t* idx, int ts,
-                                                    int nidx, int w0, int lane) const {
-    const int wr = wave - w0;
-    if (wr >= 0 && wr < KT / 64) {
-      const int key = idx[min(ts + 64 * wr + lane, nidx - 1)];
       __builtin_amdgcn_global_load_lds(src + key, dst + 64 * wr, 4, 0, 0);
     }
   }

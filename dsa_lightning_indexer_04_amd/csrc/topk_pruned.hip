@@ -49,6 +49,8 @@ struct PrunePlan {
   int seed_stride;
   const uint32_t* seed_bits; // [B][bits_stride]
   int bits_stride;
+  const int32_t* seed_top_idx;   // [R][topk]: the row's exact seed Top-K (seed numbers, -1 padded)
+  const float* seed_top_score;   // [R][topk]: their scores
   float* st_tau;
   int32_t* st_screened;
   int32_t* st_surv;
@@ -148,58 +150,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   };
 
   // ---------------------------------------------------------------- 1. seeds
-  bool hist_set = false;
+  // The row's exact seed Top-K, scored beforehand by the streaming Top-K over
+  // the packed seed keys (the same score routine, so the same bits), become
+  // its first candidate records; tau is the K-th best of them.
   {
-    const int ntiles = (nseed + KT - 1) / KT;
-    for (int ti = 0; ti < min(ntiles, 2); ++ti) {
-      tl.load_gather(ktile[ti], kbase, sd, ti * KT, nseed, lane);
-      if constexpr (DT == kFP8) tl.load_words_gather(kscale_tile[ti], kscb, sd, ti * KT, nseed, 0, lane);
+    const int32_t* si = pp.seed_top_idx + row * (size_t)topk;
+    const float* ss = pp.seed_top_score + row * (size_t)topk;
+    int nk = 0;
+    for (int i0 = 0; i0 < topk; i0 += 64) {
+      const int i = i0 + lane;
+      const int32_t idx = i < topk ? si[i] : -1;
+      const bool ok = valid && idx >= 0;  // rows past Q keep no records
+      const uint64_t bal = __ballot(ok);
+      if (ok)
+        rs.buf[nk + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+            make_record(ss[i], (uint32_t)sd[idx]);
+      nk += __popcll(bal);
     }
-    wait_vmem_all();
-    __syncthreads();
-    int cur = 0;
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const int nxt = cur == kSlots - 1 ? 0 : cur + 1;
-      const int spare = nxt == kSlots - 1 ? 0 : nxt + 1;
-      if (ti + 2 < ntiles) {
-        tl.load_gather(ktile[spare], kbase, sd, (ti + 2) * KT, nseed, lane);
-        if constexpr (DT == kFP8) tl.load_words_gather(kscale_tile[spare], kscb, sd, (ti + 2) * KT, nseed, 0, lane);
-      }
-      const int ts = ti * KT;
-      for (int sb = 0; sb < NSB; ++sb) {
-        const int s0 = ts + 32 * sb;
-        if (s0 < nseed && sd[s0] < vis) {  // seeds ascend: wave-uniform test
-          const int si = s0 + lk;
-          const int key = sd[min(si, nseed - 1)];
-          Frag<DT> f;
-          Tile::frag(f, ktile[cur], 32 * sb + lk, lane);
-          score_and_keep(f, key, (DT == kFP8) ? kscale_tile[cur][32 * sb + lk] : 1.0f,
-                         lane < 32 && si < nseed && key < vis);
-        }
-      }
-      // once the row holds a cut's worth of records, set up the threshold
-      // histogram; from then on the threshold rises with the seeds
-      if (!hist_set && rs.cnt + rs.nst >= cut_goal(topk, cap)) {
-        apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, rs.thr, topk,
-                                             cut_goal(topk, cap), lane));
-        hist_set = true;
-      }
-      if (hist_set && rs.added >= kRaiseEvery) raise_threshold(rs, my_hist, topk, lane);
-      wait_vmem_all();
-      __syncthreads();
-      cur = nxt;
-    }
-  }
-  // tau: the exact K-th seed record (records below it can never be selected)
-  if (rs.nst) {
-    rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
-    rs.nst = 0;
+    rs.cnt = nk;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
   float tau = -INFINITY;
   if (rs.cnt >= topk) {
-    const SelectResult sel = select_records_d8(rs.buf, rs.cnt, (uint32_t)topk, my_hist, true, 0, lane);
-    rs.cnt = compact_records_d8(rs.buf, rs.cnt, sel, lane);
     rs.thr = min_record(rs.buf, rs.cnt, lane);
     tau = record_score(rs.thr);
   }
@@ -420,9 +392,10 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
     const size_t n = (size_t)p.B * p.Q * p.N;
     hipLaunchKernelGGL(k_fill_nan, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pb.st_ub, n);
   }
-  PrunePlan pp{pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag, pb.knorm, pb.seeds, pb.seed_count,
-               pb.seed_stride, pb.seed_bits, pb.bits_stride, pb.st_tau, pb.st_screened, pb.st_surv, pb.st_rec,
-               pb.st_ub};
+  PrunePlan pp{pb.plan_rows,    pb.plan_coef,    pb.plan_misc,      pb.plan_flag,    pb.knorm,
+               pb.seeds,        pb.seed_count,   pb.seed_stride,    pb.seed_bits,    pb.bits_stride,
+               pb.seed_top_idx, pb.seed_top_score, pb.st_tau,       pb.st_screened,  pb.st_surv,
+               pb.st_rec,       pb.st_ub};
   dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
   const int prof_slot = prof_open("k_topk_pruned", st);
   using Kern = void (*)(const uint8_t*, const uint8_t*, const float*, const float*, const float*, const int32_t*, int,
