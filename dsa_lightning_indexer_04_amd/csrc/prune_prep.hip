@@ -39,11 +39,14 @@ namespace dsa {
 
 // ---------------------------------------------------------------- decoding
 
-// Exact value of an OCP e4m3fn code (bias 7, subnormals m * 2^-9).
+// Exact value of an OCP e4m3fn code (bias 7, subnormals m * 2^-9), built
+// as fp32 bits: a normal code (e >= 1) is (1 + m/8) 2^(e-7), i.e. exponent
+// field e + 120 and mantissa m << 20; a subnormal one is the exact product
+// m * 2^-9.  (Codes 0x7F / 0xFF are NaN in e4m3fn and never produced here.)
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
-  return (c & 0x80u) ? -mag : mag;
+  const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((c & 0x80u) << 24));
 }
 __device__ __forceinline__ float bf16_value(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
 
