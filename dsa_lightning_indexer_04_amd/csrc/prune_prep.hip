@@ -108,19 +108,41 @@ __global__ __launch_bounds__(256) void k_seed_prep(const int32_t* __restrict__ p
 
 // ---------------------------------------------------------------- key norms
 
-// |k_s| (code units for fp8), accumulated in fp64 and rounded up to fp32.
+// |k_s| (code units for fp8): each lane squares the values of one 16-byte
+// chunk of a key row (exact in fp64), the lanes of a key add their sums, and
+// the root is rounded up to fp32 after a margin that covers the fp64
+// rounding of the 128-term sum (below 128 * 2^-53 relative).
 template <int DT>
 __global__ __launch_bounds__(256) void k_key_norms(const uint8_t* __restrict__ k, size_t nkeys,
                                                    float* __restrict__ knorm) {
-  const size_t s = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= nkeys) return;
-  const uint8_t* row = k + s * Frag<DT>::kRowBytes;
+  constexpr int RB = Frag<DT>::kRowBytes, CPR = RB / 16;  // lanes per key
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t key = t / CPR;
+  const int ch = (int)(t % CPR);
   double acc = 0.0;
-  for (int d = 0; d < kDim; ++d) {
-    const double v = elem<DT>(row, d);
-    acc = fma(v, v, acc);
+  if (key < nkeys) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(k + key * RB + ch * 16);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const double x = bf16_value((uint16_t)(w4[i] >> (16 * h)));
+          acc = fma(x, x, acc);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const double x = e4m3_value((w4[i] >> (8 * h)) & 0xFFu);
+          acc = fma(x, x, acc);
+        }
+      }
+    }
   }
-  knorm[s] = __double2float_ru(sqrt(acc) * (1.0 + 1e-15));
+#pragma unroll
+  for (int d = CPR / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);  // the key's lanes (aligned group)
+  if (key < nkeys && ch == 0) knorm[key] = __double2float_ru(sqrt(acc * (1.0 + 1e-13)));
 }
 
 // ---------------------------------------------------------------- seed pack
@@ -598,7 +620,8 @@ hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, 
 hipError_t launch_key_norms(const Problem& p, float* knorm, hipStream_t st) {
   const int prof_slot = prof_open("k_key_norms", st);
   const size_t n = (size_t)p.B * p.N;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const int cpr = (p.dtype == kBF16 ? Frag<kBF16>::kRowBytes : Frag<kFP8>::kRowBytes) / 16;
+  const dim3 grid((unsigned)((n * cpr + 255) / 256));
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_key_norms<kBF16>, grid, dim3(256), 0, st, p.k, n, knorm);
   else
