@@ -200,7 +200,6 @@ struct DirectTile {
   static constexpr int PER_WAVE = (NI + kWaves - 1) / kWaves;
   static_assert(SLOTS % 64 == 0, "tile slots fill whole load instructions");
   static_assert(kWaves * (PER_WAVE - 1) <= NI, "only the last load of a wave may be past the tile");
-  static_assert(KT / 64 <= kWaves / 2, "per-row words are loaded by one half of the waves each");
   const uint32_t* off;  // this wave's [PER_WAVE][64] source offsets (LDS), from the tile's first row
   int wave;             // wave-uniform
 
@@ -241,13 +240,15 @@ struct DirectTile {
     }
   }
   // One 4-byte word per tile row (fp8 key scale, key norm): dst[r] =
-  // src[min(ts + r, N - 1)], loaded by waves w0 .. w0 + KT/64 - 1 (w0 = 0
-  // or kWaves / 2).
-  __device__ __forceinline__ void load_words(float* dst, const float* src, int ts, int N, int w0, int lane) const {
-    const int wr = wave - w0;
-    if (wr >= 0 && wr < KT / 64) {
-      const int key = min(ts + 64 * wr + lane, N - 1);
-      __builtin_amdgcn_global_load_lds(src + key, dst + 64 * wr, 4, 0, 0);
+  // src[min(ts + r, N - 1)], 64 rows per instruction, instructions spread
+  // over the waves.
+  __device__ __forceinline__ void load_words(float* dst, const float* src, int ts, int N, int lane) const {
+#pragma unroll
+    for (int wr = 0; wr < KT / 64; wr += kWaves) {
+      if (wr + wave < KT / 64) {
+        const int key = min(ts + 64 * (wr + wave) + lane, N - 1);
+        __builtin_amdgcn_global_load_lds(src + key, dst + 64 * (wr + wave), 4, 0, 0);
+      }
     }
   }
   // 64 words of a per-key bitmap from the tile's first word on (the tile

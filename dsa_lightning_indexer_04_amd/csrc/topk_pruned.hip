@@ -33,9 +33,21 @@ constexpr int kPlanRowsK = 32;
 constexpr int kLinRowK = 31;
 constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
-constexpr int kWaves = 8;        // query rows per workgroup, one per wave
-constexpr int kTileBytes = 32768;  // key bytes of one LDS tile: 128 bf16 or 256 fp8 keys
-constexpr int kSlots = 3;        // LDS key-tile slots
+// Workgroup geometry per dtype: query rows per workgroup (one per wave), key
+// bytes of an LDS tile, tile slots (tiles are loaded kSlots - 1 ahead).  Both
+// dtypes use 8 rows on 32 KiB tiles in 3 slots, one workgroup per CU (4 rows
+// on 24 KiB tiles in 2 slots, two workgroups per CU, measured no faster on
+// fp8 keys: the per-tile work grows with the tile count).
+template <int DT>
+struct PrunedGeom;
+template <>
+struct PrunedGeom<kBF16> {
+  static constexpr int kWaves = 8, kTileBytes = 32768, kSlots = 3;
+};
+template <>
+struct PrunedGeom<kFP8> {
+  static constexpr int kWaves = 8, kTileBytes = 32768, kSlots = 3;
+};
 constexpr int kStage = 96;       // candidate stage records per row
 
 struct PrunePlan {
@@ -80,15 +92,17 @@ __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live
 
 // kBounds: also write every screened key's bound U to pp.st_ub (diagnostics).
 template <int DT, bool kBounds>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_topk_pruned(
+__global__ __launch_bounds__(PrunedGeom<DT>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_topk_pruned(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
     int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
     PrunePlan pp) {
+  constexpr int kWaves = PrunedGeom<DT>::kWaves, kTileBytes = PrunedGeom<DT>::kTileBytes;
+  constexpr int kSlots = PrunedGeom<DT>::kSlots, kAhead = kSlots - 1;  // tiles loaded ahead
   using Tile = DirectTile<DT, kTileBytes, kWaves>;
   constexpr int RB = Frag<DT>::kRowBytes;
   constexpr int KT = Tile::KT;     // keys per tile (128 bf16, 256 fp8)
-  constexpr int NSB = KT / 32;     // 32-key blocks per tile
+  constexpr int NSB = KT / 32;     // 32-key blocks per tile (even)
   constexpr int QCAP = KT + 96;    // survivor queue per row (see the refine schedule)
   constexpr int kPend = (DT == kFP8) ? 2 : 1;  // refine batches in flight per tile (register budget)
   __shared__ u32x4 ktile[kSlots][direct_slots(kTileBytes)];
@@ -219,10 +233,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   {
     const int ntiles = (wg_vis + KT - 1) / KT;
     const int words = pp.bits_stride;
-    for (int ti = 0; ti < min(ntiles, 2); ++ti) {
+    for (int ti = 0; ti < min(ntiles, kAhead); ++ti) {
       tl.load(ktile[ti], kbase, ti * KT, N, lane);
-      if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, 0, lane);
-      tl.load_words(knorm_tile[ti], knb, ti * KT, N, kWaves / 2, lane);
+      if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, lane);
+      tl.load_words(knorm_tile[ti], knb, ti * KT, N, lane);
       tl.load_bits(sbits_tile[ti], sbits, ti * KT, words, lane);
     }
     wait_vmem_all();
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     int cur = 0;
     for (int ti = 0; ti < ntiles; ++ti) {
       const int nxt = cur == kSlots - 1 ? 0 : cur + 1;
-      const int spare = nxt == kSlots - 1 ? 0 : nxt + 1;
+      const int spare = cur + kAhead >= kSlots ? cur + kAhead - kSlots : cur + kAhead;  // tile ti + kAhead
       const int ts = ti * KT;
       if (rs.nst) {
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
@@ -242,11 +256,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         raise_threshold(rs, my_hist, topk, lane);
         thr_f = record_floor(rs.thr);
       }
-      if (ti + 2 < ntiles) {
-        const int tn = (ti + 2) * KT;
+      if (ti + kAhead < ntiles) {
+        const int tn = (ti + kAhead) * KT;
         tl.load(ktile[spare], kbase, tn, N, lane);
-        if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, tn, N, 0, lane);
-        tl.load_words(knorm_tile[spare], knb, tn, N, kWaves / 2, lane);
+        if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, tn, N, lane);
+        tl.load_words(knorm_tile[spare], knb, tn, N, lane);
         tl.load_bits(sbits_tile[spare], sbits, tn, words, lane);
       }
       // refine batches, part 1: pop up to kPend full batches and issue the
@@ -396,13 +410,14 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
                pb.seeds,        pb.seed_count,   pb.seed_stride,    pb.seed_bits,    pb.bits_stride,
                pb.seed_top_idx, pb.seed_top_score, pb.st_tau,       pb.st_screened,  pb.st_surv,
                pb.st_rec,       pb.st_ub};
-  dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
+  const int waves = p.dtype == kBF16 ? PrunedGeom<kBF16>::kWaves : PrunedGeom<kFP8>::kWaves;
+  dim3 grid((p.Q + waves - 1) / waves, p.B);
   const int prof_slot = prof_open("k_topk_pruned", st);
   using Kern = void (*)(const uint8_t*, const uint8_t*, const float*, const float*, const float*, const int32_t*, int,
                         int, int, int, uint64_t*, int32_t*, float*, PrunePlan);
   const Kern kern = p.dtype == kBF16 ? (pb.st_ub ? k_topk_pruned<kBF16, true> : k_topk_pruned<kBF16, false>)
                                      : (pb.st_ub ? k_topk_pruned<kFP8, true> : k_topk_pruned<kFP8, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos, p.Q, p.N, topk,
+  hipLaunchKernelGGL(kern, grid, dim3(waves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos, p.Q, p.N, topk,
                      cap, cand, out_idx, out_score, pp);
   prof_close(prof_slot, st);
   return hipGetLastError();

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int ntiles = (wg_vis + KT - 1) / KT;
   for (int ti = 0; ti < min(ntiles, 2); ++ti) {
     tl.load(ktile[ti], kbase, ti * KT, N, lane);
-    if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, 0, lane);
+    if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, lane);
   }
   wait_vmem_all();
   __syncthreads();
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     flush_and_cut(cs, buf, my_stage, my_hist, topk, cap, KT, lane);
     if (ti + 2 < ntiles) {
       tl.load(ktile[spare], kbase, (ti + 2) * KT, N, lane);
-      if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, (ti + 2) * KT, N, 0, lane);
+      if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, (ti + 2) * KT, N, lane);
     }
 #pragma unroll
     for (int sub = 0; sub < NSB; ++sub) {
