@@ -12,5 +12,7 @@ Modules:
     prune    -- the DoSA certificate pieces: seed threshold and the score
                 upper bound built from retained heads, projected positive
                 heads with a residual term, and a folded negative-head penalty.
+    project  -- the indexer projections (Q^I, K^I, W^I) and the per-token
+                e4m3fn quantisation of their fp32 results.
 """
-from . import counts, indexer, prune  # noqa: F401
+from . import counts, indexer, project, prune  # noqa: F401
