@@ -38,8 +38,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("chunked_prefill_128k", "k_topk_stream"): ("3bad31e85441afec", 6151394, 1766511),
-    ("chunked_prefill_128k", "k_topk_pruned"): ("3bad31e85441afec", 4092890, 737031),
+    ("chunked_prefill_128k", "k_topk_stream"): ("f34f99b8e474ab38", 6195342, 1766313),
+    ("chunked_prefill_128k", "k_topk_pruned"): ("1fac2fb6bcbfa0be", 4486728, 742244),
+    ("projection_prefill_128k", "k_proj_out"): ("76da2995e52193f3", 1073178, 553001),
 }
 PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
 SCREEN_FLOPS = 2 * 128 * 32  # 32-row bound (30 retained heads, aux row, linear row) of one pair
@@ -60,7 +61,7 @@ def parse():
     ap.add_argument(
         "--also",
         default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,prefill_32k:topk,"
-        "decode_64x128k:topk",
+        "decode_64x128k:topk,projection_prefill_128k:project",
         help="comma list of extra workload[:path] runs (or 'none')",
     )
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,23 +71,32 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest():
-    """Digest of the HIP kernel sources (the key of MEASURED_KIB)."""
-    import glob
+# Source files whose code a kernel is built from (its own file and the headers
+# it includes).  A stored counter reading is valid while their digest holds.
+KERNEL_SOURCES = {
+    "k_topk_stream": ["topk_stream.hip", "stream_common.h", "score_tile.h", "select.h", "kernels.h"],
+    "k_topk_pruned": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h", "kernels.h"],
+    "k_scores": ["scores.hip", "score_tile.h", "kernels.h"],
+    "k_proj_out": ["project.hip", "kernels.h"],
+}
+
+
+def source_digest(kernel):
+    """Digest of the HIP sources of one kernel (the key of MEASURED_KIB)."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dsa_lightning_indexer_04_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for f in sorted(KERNEL_SOURCES[kernel]):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, kernel):
     m = MEASURED_KIB.get((workload, kernel))
-    if m is None or m[0] != source_digest():
+    if m is None or kernel not in KERNEL_SOURCES or m[0] != source_digest(kernel):
         return None
     return (m[1] * FETCH_SCALE + m[2] * WRITE_SCALE) * 1024
 
@@ -199,6 +209,82 @@ def run_workload(name, path, steps, warmup):
     return res
 
 
+# Indexer projection workloads: tokens projected per step (DeepSeek-V3.2 sizes).
+PROJ_WORKLOADS = {"projection_prefill_128k": 131072, "projection_chunk_8k": 8192}
+
+
+def run_projection(name, steps, warmup):
+    """The projection prologue: C^Q W_IQ, X [W_IK W_IW] (rocBLAS, bf16 -> fp32)
+    and the per-token fp8 output pass, on T synthetic tokens."""
+    import torch
+
+    import dsa_lightning_indexer_04_amd as dsa
+    from dsa_lightning_indexer_04_amd import _lib, inputs
+
+    T = PROJ_WORKLOADS[name]
+    L, D = inputs.PROJ_Q_LATENT, inputs.PROJ_HIDDEN
+    t0 = time.time()
+    d = inputs.make_projection_inputs(T, D, L, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
+    args = (d["c_q"], d["x"], d["w_iq"], d["w_ik"], d["w_iw"])
+    ws = torch.empty(_lib.project_workspace_bytes(_lib.make_proj_struct(*args)), dtype=torch.uint8, device="cuda")
+
+    def call():
+        return dsa.project(*args, out="fp8", workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    _lib.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernels = _lib.profile_end()
+    ms = wall * 1e3 / steps
+    flops = 2 * T * (L * 64 * 128 + D * 128 + D * 64)
+    # tokens one launch of each kernel covers (the query GEMM and the output
+    # pass run per token block, the key/weight GEMM once over all tokens)
+    per_launch = {n: T * steps / c for n, (c, _) in kernels.items()}
+    blk = per_launch.get("k_proj_out", T)
+    gq = kernels.get("gemm_q_proj", (0, float("nan")))[1]
+    gkw = kernels.get("gemm_kw_proj", (0, float("nan")))[1]
+    po = kernels.get("k_proj_out", (0, float("nan")))[1]
+    kw_tokens = per_launch.get("gemm_kw_proj", T)
+    out_bytes = blk * ((64 * 128 + 128 + 64) * 4 + 64 * 128 + 128 + 64 * 4 + 8)  # fp32 staging in; codes, w, scales out
+    res = {
+        "workload": name,
+        "path": "project",
+        "dtype": "bf16",
+        "tokens": T,
+        "ms_per_step": ms,
+        "tokens_per_s": T / (wall / steps),
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "kernels_ms": {n: round(v, 4) for n, (c, v) in kernels.items()},
+        "roofline_gemm_q": {"bound": "mfma", "achieved": 2 * blk * L * 64 * 128 / (gq * 1e-3) / 1e12,
+                            "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s", "kernel": "rocBLAS gemm (C^Q W_IQ)"},
+        # 192 FLOP per byte of X: below the bf16 ridge (2500 TFLOP/s / 8 TB/s), so HBM-bound
+        "roofline_gemm_kw": {"bound": "hbm", "achieved": kw_tokens * (D * 2 + 192 * 4) / (gkw * 1e-3) / 1e9,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "kernel": "rocBLAS gemm (X [W_IK W_IW])",
+                             "tflops": 2 * kw_tokens * D * 192 / (gkw * 1e-3) / 1e12},
+        "roofline_out": {"bound": "hbm", "achieved": out_bytes / (po * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "kernel": "k_proj_out", "bytes_per_launch": out_bytes,
+                         "traffic": measured_traffic(name, "k_proj_out")},
+    }
+    for key in ("roofline_gemm_q", "roofline_gemm_kw", "roofline_out"):
+        res[key]["frac"] = res[key]["achieved"] / res[key]["peak"]
+    log(f"[bench] {name}: {ms:.3f} ms/step, {res['tflops']:.0f} TFLOP/s overall; gemm_q {gq:.3f} ms "
+        f"({100 * res['roofline_gemm_q']['frac']:.1f}% bf16), gemm_kw {gkw:.3f} ms "
+        f"({100 * res['roofline_gemm_kw']['frac']:.1f}% HBM), k_proj_out {po:.3f} ms "
+        f"({100 * res['roofline_out']['frac']:.1f}% HBM); {blk:.0f} tokens per query-GEMM block")
+    del d, args, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, rows_wanted):
     """Time the float64 oracle (scores + sort Top-K) on a bounded row sample."""
     from dsa_lightning_indexer_04_amd import inputs
@@ -279,9 +365,12 @@ def main():
             if not item:
                 continue
             name, _, pth = item.partition(":")
+            if name in PROJ_WORKLOADS:
+                extra[item] = run_projection(name, max(3, args.steps // 2), max(1, args.warmup // 2))
+                continue
             extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
     for wname in {args.workload} | {k.partition(":")[0] for k in extra}:
-        runs = [r for r in [main_res, *extra.values()] if r["workload"] == wname]
+        runs = [r for r in [main_res, *extra.values()] if r["workload"] == wname and r["path"] != "project"]
         t = {r["path"]: r["ms_per_step"] for r in runs}
         if "pruned" in t and "unpruned" in t:
             for r in runs:

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
 
-DSA_BF16, DSA_FP8_E4M3 = 0, 1
+DSA_BF16, DSA_FP8_E4M3, DSA_F32 = 0, 1, 2
 DSA_OP_SCORES, DSA_OP_TOPK, DSA_OP_TOPK_PRUNED = 0, 1, 2
 ERR = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 
@@ -56,11 +56,28 @@ class PruneStats(ctypes.Structure):
     ]
 
 
+class ProjInputs(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("q_latent", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("c_q", ctypes.c_void_p),
+        ("x", ctypes.c_void_p),
+        ("w_iq", ctypes.c_void_p),
+        ("w_ik", ctypes.c_void_p),
+        ("w_iw", ctypes.c_void_p),
+    ]
+
+
 EXPORTED = [
     "dsa_indexer_scores",
     "dsa_indexer_topk",
     "dsa_indexer_topk_pruned",
     "dsa_indexer_workspace_bytes",
+    "dsa_indexer_project",
+    "dsa_indexer_project_workspace_bytes",
     "dsa_indexer_error_string",
     "dsa_indexer_last_error",
     "dsa_indexer_profile_begin",
@@ -100,6 +117,10 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_topk_pruned.restype = ctypes.c_int
     lib.dsa_indexer_workspace_bytes.argtypes = [ctypes.c_int, ctypes.POINTER(Inputs), I32, ctypes.POINTER(PruneOpts)]
     lib.dsa_indexer_workspace_bytes.restype = SZ
+    lib.dsa_indexer_project.argtypes = [ctypes.POINTER(ProjInputs), I32, P, P, P, P, P, P, SZ, P]
+    lib.dsa_indexer_project.restype = ctypes.c_int
+    lib.dsa_indexer_project_workspace_bytes.argtypes = [ctypes.POINTER(ProjInputs)]
+    lib.dsa_indexer_project_workspace_bytes.restype = SZ
     lib.dsa_indexer_error_string.argtypes = [ctypes.c_int]
     lib.dsa_indexer_error_string.restype = ctypes.c_char_p
     lib.dsa_indexer_last_error.argtypes = []
@@ -265,6 +286,60 @@ def topk_pruned(
         )
     )
     return idx, sc, st
+
+
+def make_proj_struct(c_q, x, w_iq, w_ik, w_iw) -> ProjInputs:
+    """C struct of the projection inputs: bf16 device tensors c_q [T, q_latent],
+    x [T, hidden] and out-feature-major weights w_iq [64*128, q_latent],
+    w_ik [128, hidden], w_iw [64, hidden]."""
+    for name, t in (("c_q", c_q), ("x", x), ("w_iq", w_iq), ("w_ik", w_ik), ("w_iw", w_iw)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    T, L = c_q.shape
+    if x.shape[0] != T:
+        raise ValueError("c_q and x must have the same number of tokens")
+    D = x.shape[1]
+    if tuple(w_iq.shape) != (64 * 128, L) or tuple(w_ik.shape) != (128, D) or tuple(w_iw.shape) != (64, D):
+        raise ValueError("weights must be w_iq [8192, q_latent], w_ik [128, hidden], w_iw [64, hidden]")
+    return ProjInputs(T, D, L, 64, 128, _ptr(c_q), _ptr(x), _ptr(w_iq), _ptr(w_ik), _ptr(w_iw))
+
+
+_PROJ_OUT = {"fp8": (DSA_FP8_E4M3, torch.float8_e4m3fn), "bf16": (DSA_BF16, torch.bfloat16), "f32": (DSA_F32, torch.float32)}
+
+
+def project(c_q, x, w_iq, w_ik, w_iw, out: str = "fp8", workspace=None) -> dict:
+    """Indexer projections Q^I = C^Q W_IQ, K^I = X W_IK, W^I = X W_IW and the
+    output conversion.  Returns {"q" [T,64,128], "k" [T,128], "w" [T,64] fp32,
+    "q_scale" [T], "k_scale" [T] (fp8 only, else None)}: for one sequence,
+    the q, k, w and scales the scoring calls take."""
+    lib = load()
+    if out not in _PROJ_OUT:
+        raise ValueError(f"out must be one of {sorted(_PROJ_OUT)}")
+    code, dt = _PROJ_OUT[out]
+    inp = make_proj_struct(c_q, x, w_iq, w_ik, w_iw)
+    need = lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp))
+    if need == 0:
+        raise IndexerError(1, lib.dsa_indexer_last_error().decode())
+    ws = workspace if workspace is not None else _workspace(need, c_q.device)
+    T, dev = c_q.shape[0], c_q.device
+    q = torch.empty((T, 64, 128), dtype=dt, device=dev)
+    k = torch.empty((T, 128), dtype=dt, device=dev)
+    w = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    qs = torch.empty((T,), dtype=torch.float32, device=dev) if out == "fp8" else None
+    ks = torch.empty((T,), dtype=torch.float32, device=dev) if out == "fp8" else None
+    _check(lib.dsa_indexer_project(ctypes.byref(inp), code, _ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(w), _ptr(ws),
+                                   ws.numel(), _stream()))
+    return {"q": q, "k": k, "w": w, "q_scale": qs, "k_scale": ks}
+
+
+def project_workspace_bytes(inp: ProjInputs) -> int:
+    lib = load()
+    n = lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp))
+    if n == 0:
+        raise IndexerError(1, lib.dsa_indexer_last_error().decode())
+    return n
 
 
 def profile_begin():

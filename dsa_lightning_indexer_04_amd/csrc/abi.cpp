@@ -229,6 +229,34 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
   return off;
 }
 
+
+// ---------------------------------------------------------------- projections
+
+int check_proj_inputs(const dsa_proj_inputs* in) {
+  if (!in) return fail(DSA_ERR_INVALID_ARG, "projection inputs struct is NULL");
+  if (in->num_tokens < 1 || in->num_tokens > (1 << 22))
+    return fail(DSA_ERR_INVALID_ARG, "num_tokens must be in 1..4194304");
+  if (in->heads != 64) return fail(DSA_ERR_UNSUPPORTED, "heads must be 64");
+  if (in->head_dim != 128) return fail(DSA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (in->hidden < 8 || in->hidden > 65536 || in->hidden % 8 || in->q_latent < 8 || in->q_latent > 65536 ||
+      in->q_latent % 8)
+    return fail(DSA_ERR_INVALID_ARG, "hidden and q_latent must be multiples of 8 in 8..65536");
+  const void* ptrs[] = {in->c_q, in->x, in->w_iq, in->w_ik, in->w_iw};
+  for (const void* p : ptrs) {
+    if (!p) return fail(DSA_ERR_INVALID_ARG, "c_q, x, w_iq, w_ik, w_iw are required");
+    if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "input pointers must be 16-byte aligned");
+  }
+  return DSA_OK;
+}
+
+int check_proj_no_alias(const dsa_proj_inputs* in, Range out) {
+  const uint64_t T = in->num_tokens, D = in->hidden, L = in->q_latent;
+  const Range r[] = {span(in->c_q, T * L * 2), span(in->x, T * D * 2), span(in->w_iq, 8192 * L * 2),
+                     span(in->w_ik, 128 * D * 2), span(in->w_iw, 64 * D * 2)};
+  for (const Range& x : r)
+    if (overlaps(x, out)) return fail(DSA_ERR_INVALID_ARG, "an output aliases an input");
+  return DSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -326,6 +354,63 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
     return rc;
   return hip_status(
       dsa::launch_topk_pruned(p, topk, dsa::stream_capacity(topk), cand, out_idx, out_score, pb, st));
+}
+
+size_t dsa_indexer_project_workspace_bytes(const dsa_proj_inputs* in) {
+  g_last_error.clear();
+  if (check_proj_inputs(in)) return 0;
+  return dsa::proj_workspace_bytes(in->num_tokens, in->hidden);
+}
+
+int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_out, float* q_scale, void* k_out,
+                        float* k_scale, float* w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_proj_inputs(in);
+  if (rc) return rc;
+  int mode;
+  if (out_dtype == DSA_FP8_E4M3)
+    mode = 0;
+  else if (out_dtype == DSA_BF16)
+    mode = 1;
+  else if (out_dtype == DSA_F32)
+    mode = 2;
+  else
+    return fail(DSA_ERR_UNSUPPORTED, "out_dtype must be DSA_FP8_E4M3, DSA_BF16 or DSA_F32");
+  if (!q_out || !k_out || !w_out) return fail(DSA_ERR_INVALID_ARG, "q_out, k_out and w_out are required");
+  if (mode == 0 && (!q_scale || !k_scale)) return fail(DSA_ERR_INVALID_ARG, "fp8 outputs need q_scale and k_scale");
+  if (mode != 0 && (q_scale || k_scale)) return fail(DSA_ERR_INVALID_ARG, "only fp8 outputs take scales");
+  const void* outs_p[] = {q_out, k_out, w_out, q_scale, k_scale};
+  for (const void* p : outs_p)
+    if (p && !aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  const uint64_t T = in->num_tokens;
+  const uint64_t eb = mode == 0 ? 1 : mode == 1 ? 2 : 4;
+  const size_t need = dsa::proj_workspace_bytes(in->num_tokens, in->hidden);
+  if (workspace_bytes < need || !workspace)
+    return fail(DSA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const Range outs[] = {span(q_out, T * 8192 * eb), span(k_out, T * 128 * eb), span(w_out, T * 64 * 4),
+                        span(q_scale, q_scale ? T * 4 : 0), span(k_scale, k_scale ? T * 4 : 0),
+                        span(workspace, need)};
+  for (int i = 0; i < 6; ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    if ((rc = check_proj_no_alias(in, outs[i]))) return rc;
+    for (int j = 0; j < i; ++j)
+      if (outs[j].lo != outs[j].hi && overlaps(outs[i], outs[j]))
+        return fail(DSA_ERR_INVALID_ARG, "outputs and workspace must not overlap");
+  }
+  const dsa::ProjProblem p{in->num_tokens,
+                           in->hidden,
+                           in->q_latent,
+                           static_cast<const uint16_t*>(in->c_q),
+                           static_cast<const uint16_t*>(in->x),
+                           static_cast<const uint16_t*>(in->w_iq),
+                           static_cast<const uint16_t*>(in->w_ik),
+                           static_cast<const uint16_t*>(in->w_iw)};
+  std::string err;
+  if (dsa::run_projection(p, mode, static_cast<uint8_t*>(q_out), q_scale, static_cast<uint8_t*>(k_out), k_scale,
+                          w_out, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream), &err))
+    return fail(DSA_ERR_HIP, err);
+  return DSA_OK;
 }
 
 const char* dsa_indexer_error_string(int code) {

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace dsa {
 
 // Optional per-kernel event timing (see dsa_indexer_profile.h): a launcher
@@ -72,6 +74,27 @@ hipError_t launch_plan(const Problem& p, int nret, const int32_t* seeds, const i
                        float* plan_misc, int32_t* plan_flag, hipStream_t st);
 hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx, float* out_score,
                               const PrunedBuffers& pb, hipStream_t st);
+
+// ---------------------------------------------------------------- projections
+
+// bf16 operands of the indexer projections (weights out-feature major).
+struct ProjProblem {
+  int T, hidden, q_latent;
+  const uint16_t* c_q;   // [T][q_latent]
+  const uint16_t* x;     // [T][hidden]
+  const uint16_t* w_iq;  // [8192][q_latent]
+  const uint16_t* w_ik;  // [128][hidden]
+  const uint16_t* w_iw;  // [64][hidden]
+};
+// Device scratch handed to rocBLAS from the workspace.
+constexpr size_t kProjBlasScratch = size_t(32) << 20;
+// Tokens per GEMM block (the fp32 staging rows held at once).
+int proj_block_tokens(int T);
+size_t proj_workspace_bytes(int T, int hidden);
+// The GEMMs and the output pass; out 0 = fp8 + scales, 1 = bf16, 2 = fp32.
+// Returns 0, or 1 with *err set.
+int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale, uint8_t* k_out, float* k_scale,
+                   float* w_out, uint8_t* ws, hipStream_t st, std::string* err);
 
 // Candidate capacity (records per row) used by the streaming Top-K.
 inline int stream_capacity(int topk) { return 4 * topk + 128; }

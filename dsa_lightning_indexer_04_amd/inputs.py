@@ -204,6 +204,43 @@ def evenly_spaced_seeds(num_seeds: int, common_prefix_end: int) -> np.ndarray:
     return ((np.arange(s, dtype=np.int64) * p1) // s).astype(np.int32)
 
 
+# DeepSeek-V3.2 sizes of the indexer projections (hidden d, query latent d_qc).
+PROJ_HIDDEN = 7168
+PROJ_Q_LATENT = 1536
+
+
+def make_projection_inputs(T: int, hidden: int = PROJ_HIDDEN, q_latent: int = PROJ_Q_LATENT, seed: int = 0,
+                           device="cpu") -> dict:
+    """Seeded bf16 operands of the indexer projections.
+
+    c_q [T, q_latent] and x [T, hidden] have i.i.d. N(0,1) entries (the
+    normalised query latent and hidden state); the out-feature-major weights
+    w_iq [64*128, q_latent], w_ik [128, hidden], w_iw [64, hidden] have
+    i.i.d. N(0, 1/fan_in) entries, so every projection output has unit
+    variance.  Drawn with torch's generator on ``device`` (draws on the GPU
+    and on the CPU differ); T can be large on a GPU.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape, std):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        step = max(1, (1 << 26) // shape[1])  # bound the fp32 temporary
+        for r in range(0, shape[0], step):
+            n = min(step, shape[0] - r)
+            x = torch.randn((n, shape[1]), generator=g, device=device, dtype=torch.float32)
+            out[r:r + n] = (x * std).to(torch.bfloat16)
+        return out
+
+    return {
+        "c_q": draw((T, q_latent), 1.0),
+        "x": draw((T, hidden), 1.0),
+        "w_iq": draw((HEADS * HEAD_DIM, q_latent), 1.0 / math.sqrt(q_latent)),
+        "w_ik": draw((HEAD_DIM, hidden), 1.0 / math.sqrt(hidden)),
+        "w_iw": draw((HEADS, hidden), 1.0 / math.sqrt(hidden)),
+    }
+
+
 def to_bits(x: torch.Tensor) -> np.ndarray:
     """Raw bit patterns of a bf16 (uint16) or fp8 (uint8) tensor as numpy."""
     if x.dtype == torch.bfloat16:

@@ -24,8 +24,10 @@
  * Conventions shared by all entry points
  *  - Every array pointer is DEVICE memory owned by the caller, row-major and
  *    contiguous, innermost dimension last, 16-byte aligned.  The library
- *    never allocates, frees or synchronises; work is enqueued on `stream`
- *    (a hipStream_t; NULL is the default stream) and returns at once.
+ *    never allocates, frees or synchronises (one exception: the first
+ *    dsa_indexer_project call on a thread creates a rocBLAS handle); work is
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream) and
+ *    returns at once.
  *  - Scores are fp32 computed with fp32 accumulation; every path uses the
  *    same instruction sequence for a (t, s) pair, so a score is bit-identical
  *    whichever entry point or tile produced it.
@@ -153,6 +155,67 @@ enum { DSA_OP_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_TOPK_PRUNED = 2 };
  * Returns 0 and sets the last error if the arguments are invalid.          */
 size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t topk,
                                    const dsa_prune_opts* opts);
+
+/* ------------------------------------------------------------ projections
+ *
+ * The indexer projections that produce the inputs above (DeepSeek DSA FLOPs
+ * notes, section "Indexer projections"): with T tokens,
+ *     Q^I = C^Q W_IQ   (T,d_qc) x (d_qc, H d)  -> (T, H, d)
+ *     K^I = X   W_IK   (T,d)    x (d, d)       -> (T, d)      (d = 128 here)
+ *     W^I = X   W_IW   (T,d)    x (d, H)       -> (T, H)
+ * followed by the output conversion of q and k.  All inputs are bf16 bits
+ * (uint16), device, row-major:
+ *   c_q   [T, q_latent]        the MLA query latent C^Q of each token
+ *   x     [T, hidden]          the hidden state X of each token
+ *   w_iq  [heads*head_dim, q_latent]  W_IQ stored out-feature major: row o
+ *                              holds column o of W_IQ (output o = head o/128,
+ *                              dimension o%128)
+ *   w_ik  [head_dim, hidden]   W_IK, same layout
+ *   w_iw  [heads, hidden]      W_IW, same layout
+ * heads must be 64 and head_dim 128; hidden and q_latent are multiples of 8
+ * in 8..65536 (DeepSeek-V3.2: hidden 7168, q_latent 1536); num_tokens is
+ * 1..4194304.                                                            */
+typedef struct dsa_proj_inputs {
+  int32_t num_tokens, hidden, q_latent, heads, head_dim;
+  const void* c_q;
+  const void* x;
+  const void* w_iq;
+  const void* w_ik;
+  const void* w_iw;
+} dsa_proj_inputs;
+
+enum { DSA_F32 = 2 }; /* projection outputs only: the raw fp32 projections */
+
+/* Projections with fp32 accumulation of exact bf16 products, then per token:
+ *   out_dtype DSA_FP8_E4M3: q_out [T,64,128] and k_out [T,128] e4m3fn codes
+ *     (uint8); q_scale [T] / k_scale [T] fp32.  One scale per token for its
+ *     8192 query values (shared by its heads) and one for its 128 key values:
+ *     scale = amax / 448 and code = e4m3fn round-to-nearest-even of
+ *     x * (448 / amax), saturated to +-448, each fp32 step IEEE-rounded to
+ *     nearest even; a row of zeros gets scale 1.  (The pages say the indexer
+ *     runs in FP8 and fix no scaling rule; this per-token rule is the one the
+ *     fp8 inputs of dsa_indexer_inputs take.)
+ *   out_dtype DSA_BF16: q_out, k_out bf16 bits, rounded to nearest even;
+ *     q_scale and k_scale must be NULL.
+ *   out_dtype DSA_F32: q_out, k_out fp32 (the projections themselves);
+ *     q_scale and k_scale must be NULL.
+ *   w_out [T,64] fp32, the head weights W^I, in every mode.
+ * For one sequence the outputs are the q, k, w, q_scale, k_scale of
+ * dsa_indexer_inputs (batch 1: each token is both a query row and a key).
+ * workspace: at least dsa_indexer_project_workspace_bytes(in) bytes,
+ * 256-byte aligned; it holds the fp32 projections of a block of tokens and
+ * the GEMM scratch.  The three products run as two rocBLAS GEMMs per token
+ * block (X is read once for W_IK and W_IW together) on `stream`; the first
+ * call on a thread and device creates that thread's rocBLAS handle, whose
+ * state rocBLAS allocates then; after that the call allocates nothing.
+ * Results are bit-reproducible for a given shape: rocBLAS atomics are off.
+ * Errors as for the other entry points; a rocBLAS failure is DSA_ERR_HIP.   */
+int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_out, float* q_scale, void* k_out,
+                        float* k_scale, float* w_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of dsa_indexer_project (0 and the last error set if the
+ * inputs are invalid).                                                      */
+size_t dsa_indexer_project_workspace_bytes(const dsa_proj_inputs* in);
 
 /* Static name of an error code, and the calling thread's last error detail. */
 const char* dsa_indexer_error_string(int code);

@@ -96,3 +96,61 @@ def test_topk_argument_errors(lib):
     # an output aliasing an input
     assert lib.dsa_indexer_topk(ctypes.byref(inp), 16, ctypes.c_void_p(FAKE * 3), None, None, need, None) == 1
     assert lib.dsa_indexer_error_string(3) == b"workspace too small"
+
+
+def _proj(_lib, **kw):
+    d = dict(num_tokens=16, hidden=7168, q_latent=1536, heads=64, head_dim=128, c_q=FAKE, x=FAKE * 2,
+             w_iq=FAKE * 3, w_ik=FAKE * 4, w_iw=FAKE * 5)
+    d.update(kw)
+    return _lib.ProjInputs(**d)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(heads=32), 2),
+        (dict(head_dim=64), 2),
+        (dict(num_tokens=0), 1),
+        (dict(hidden=7170), 1),
+        (dict(q_latent=0), 1),
+        (dict(x=None), 1),
+        (dict(w_iq=FAKE + 2), 1),
+    ],
+)
+def test_projection_inputs_are_rejected(lib, kw, code):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _proj(_lib, **kw)
+    o = ctypes.c_void_p
+    rc = lib.dsa_indexer_project(ctypes.byref(inp), 0, o(FAKE * 8), None, o(FAKE * 9), None, o(FAKE * 10),
+                                 o(FAKE * 64), 1 << 40, None)
+    assert rc == code
+    assert lib.dsa_indexer_last_error()
+    assert lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp)) == 0
+
+
+def test_projection_argument_errors(lib):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _proj(_lib)
+    o = ctypes.c_void_p
+    need = lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp))
+    # the fp32 staging block of 16 tokens, the concatenated key/weight matrix and the GEMM scratch
+    assert need >= 16 * (8192 + 192) * 4 + 192 * 7168 * 2 + (32 << 20)
+    # outputs clear of every input span (w_iq alone spans 24 MiB from FAKE * 3)
+    qo, ko, wo, ws = o(FAKE * 64), o(FAKE * 65), o(FAKE * 66), o(FAKE * 128)
+    qs, ks = o(FAKE * 67), o(FAKE * 68)
+    call = lib.dsa_indexer_project
+    assert call(ctypes.byref(inp), 5, qo, None, ko, None, wo, ws, need, None) == 2  # unknown out dtype
+    assert call(ctypes.byref(inp), 1, qo, None, ko, None, wo, ws, need, None) == 1  # fp8 without scales
+    assert call(ctypes.byref(inp), 0, qo, qs, ko, ks, wo, ws, need, None) == 1  # bf16 with scales
+    assert call(ctypes.byref(inp), 2, None, None, ko, None, wo, ws, need, None) == 1  # missing q_out
+    assert call(ctypes.byref(inp), 2, qo, None, ko, None, wo, ws, need - 1, None) == 3  # workspace too small
+    assert call(ctypes.byref(inp), 2, qo, None, ko, None, wo, o(FAKE * 128 + 16), need, None) == 1  # misaligned
+    assert b"256-byte" in lib.dsa_indexer_last_error()
+    assert call(ctypes.byref(inp), 2, o(FAKE * 2), None, ko, None, wo, ws, need, None) == 1  # q_out aliases x
+    assert b"aliases an input" in lib.dsa_indexer_last_error()
+    assert call(ctypes.byref(inp), 2, qo, None, qo, None, wo, ws, need, None) == 1  # outputs overlap
+    assert b"must not overlap" in lib.dsa_indexer_last_error()
+    assert call(ctypes.byref(inp), 1, qo, qs, ko, ks, wo, o(FAKE * 67), need, None) == 1  # workspace over a scale
+    assert b"must not overlap" in lib.dsa_indexer_last_error()
