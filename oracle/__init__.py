@@ -14,5 +14,6 @@ Modules:
                 heads with a residual term, and a folded negative-head penalty.
     project  -- the indexer projections (Q^I, K^I, W^I) and the per-token
                 e4m3fn quantisation of their fp32 results.
+    sparse_mla -- the core attention over the selected keys (MLA, MQA mode).
 """
-from . import counts, indexer, project, prune  # noqa: F401
+from . import counts, indexer, project, prune, sparse_mla  # noqa: F401
