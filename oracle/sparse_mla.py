@@ -20,9 +20,10 @@ Readings (the notes leave these open):
 * the softmax is taken of sm_scale * (S^A + S^R) for a caller-given
   sm_scale > 0 (the notes' formula is sm_scale = 1; the benchmark uses
   1/sqrt(d_c + d_r), the usual scaled-dot-product factor for that length);
-* the selected set is the index list as given: entries < 0 are padding and
-  are skipped; a row with no selected position outputs Z = 0 and
-  log-sum-exp -inf;
+* the selected set is the index list as given: entries outside 0..N-1
+  (the Top-K's -1 padding) are skipped, the others are used as they stand
+  (a repeated entry counts twice); a row with no selected position outputs
+  Z = 0 and log-sum-exp -inf;
 * besides Z the call reports lse = log(sum_i exp(sm_scale * s_i)), natural log.
 """
 from __future__ import annotations
@@ -40,7 +41,7 @@ def sparse_mla_row(q_row: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale:
     kv = np.asarray(kv, dtype=np.float64)
     idx = np.asarray(idx)
     h = q_row.shape[0]
-    sel = idx[idx >= 0]
+    sel = idx[(idx >= 0) & (idx < kv.shape[0])]
     if sel.size == 0:
         return np.zeros((h, d_c)), np.full(h, -np.inf)
     rows = kv[sel]  # (m, d_c + d_r)
@@ -61,7 +62,8 @@ def value_abs_bound_row(q_row: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_s
     error of Z when each weight P carries a small relative error."""
     q_row = np.asarray(q_row, dtype=np.float64)
     kv = np.asarray(kv, dtype=np.float64)
-    sel = np.asarray(idx)[np.asarray(idx) >= 0]
+    idx = np.asarray(idx)
+    sel = idx[(idx >= 0) & (idx < kv.shape[0])]
     h = q_row.shape[0]
     if sel.size == 0:
         return np.zeros((h, d_c))

@@ -99,10 +99,14 @@ def test_padding_order_and_convexity():
     assert np.all(np.abs(z) <= b + 1e-12)
 
 
-def test_empty_selection():
+def test_empty_selection_and_out_of_range_entries():
     q, kv = _rand()
-    z, lse = sparse_mla.sparse_mla_row(q, kv, np.array([-1, -1]), 1.0)
+    z, lse = sparse_mla.sparse_mla_row(q, kv, np.array([-1, -1, 50, 99]), 1.0)  # kv has 50 rows
     assert np.all(z == 0) and np.all(np.isneginf(lse))
+    z1, l1 = sparse_mla.sparse_mla_row(q, kv, np.array([7, 50, 3]), 0.3)
+    z2, l2 = sparse_mla.sparse_mla_row(q, kv, np.array([7, 3]), 0.3)
+    np.testing.assert_array_equal(z1, z2)
+    np.testing.assert_array_equal(l1, l2)
 
 
 def test_flops_per_pair_printed():
