@@ -61,7 +61,7 @@ def parse():
     ap.add_argument(
         "--also",
         default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,prefill_32k:topk,"
-        "decode_64x128k:topk,projection_prefill_128k:project",
+        "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla",
         help="comma list of extra workload[:path] runs (or 'none')",
     )
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -78,6 +78,7 @@ KERNEL_SOURCES = {
     "k_topk_pruned": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h", "kernels.h"],
     "k_scores": ["scores.hip", "score_tile.h", "kernels.h"],
     "k_proj_out": ["project.hip", "kernels.h"],
+    "k_sparse_mla": ["sparse_mla.hip", "kernels.h"],
 }
 
 
@@ -285,6 +286,75 @@ def run_projection(name, steps, warmup):
     return res
 
 
+# Sparse MLA workloads: the indexer block whose Top-K the attention consumes.
+MLA_WORKLOADS = {"sparse_mla_128k": "chunked_prefill_128k"}
+MLA_PAIR_FLOPS = 2 * 128 * (2 * 512 + 64)  # 2h(2 d_c + d_r) per selected pair
+
+
+def run_sparse_mla(name, steps, warmup):
+    """Core attention over the indexer's Top-K: the block's selections come
+    from one dsa_indexer_topk call (untimed); q [Q,128,576] and the latent
+    cache [N,576] are synthetic bf16."""
+    import math
+
+    import torch
+
+    import dsa_lightning_indexer_04_amd as dsa
+    from dsa_lightning_indexer_04_amd import _lib, inputs
+
+    wl = inputs.WORKLOADS[MLA_WORKLOADS[name]]
+    d = inputs.make_workload(wl)
+    dev = torch.device("cuda:0")
+    q8, k8, w, pos = (d[n].to(dev) for n in ("q", "k", "w", "pos"))
+    idx, _ = dsa.topk(q8, k8, w, pos, wl.topk, return_scores=False)
+    del q8, k8, w, d
+    t0 = time.time()
+    md = inputs.make_mla_inputs(wl.batch, wl.num_q, wl.num_k, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
+    q, kv = md["q"], md["kv"]
+    sm_scale = 1.0 / math.sqrt(576)
+    ws = torch.empty(_lib.sparse_mla_workspace_bytes(_lib.make_mla_struct(q, kv, idx)), dtype=torch.uint8, device=dev)
+    pairs = int((idx >= 0).sum().item())
+
+    def call():
+        return dsa.sparse_mla(q, kv, idx, sm_scale, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    _lib.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernels = _lib.profile_end()
+    ms = wall * 1e3 / steps
+    km = kernels.get("k_sparse_mla", (0, float("nan")))[1]
+    flops = pairs * MLA_PAIR_FLOPS
+    res = {
+        "workload": name,
+        "path": "sparse_mla",
+        "dtype": "bf16",
+        "indexer_block": MLA_WORKLOADS[name],
+        "selected_pairs": pairs,
+        "ms_per_step": ms,
+        "pairs_per_s": pairs / (wall / steps),
+        "kernels_ms": {n: round(v, 4) for n, (c, v) in kernels.items()},
+        "roofline": {"bound": "mfma", "achieved": flops / (km * 1e-3) / 1e12, "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "kernel": "k_sparse_mla", "flops_per_launch": flops,
+                     "traffic": measured_traffic(name, "k_sparse_mla")},
+    }
+    res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
+    log(f"[bench] {name}: {ms:.3f} ms/step, {res['pairs_per_s']:.3e} selected pairs/s; k_sparse_mla {km:.3f} ms at "
+        f"{res['roofline']['achieved']:.0f} TFLOP/s ({100 * res['roofline']['frac']:.1f}% of bf16 peak)")
+    del q, kv, idx, ws, md
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, rows_wanted):
     """Time the float64 oracle (scores + sort Top-K) on a bounded row sample."""
     from dsa_lightning_indexer_04_amd import inputs
@@ -368,9 +438,13 @@ def main():
             if name in PROJ_WORKLOADS:
                 extra[item] = run_projection(name, max(3, args.steps // 2), max(1, args.warmup // 2))
                 continue
+            if name in MLA_WORKLOADS:
+                extra[item] = run_sparse_mla(name, max(3, args.steps // 2), max(1, args.warmup // 2))
+                continue
             extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
     for wname in {args.workload} | {k.partition(":")[0] for k in extra}:
-        runs = [r for r in [main_res, *extra.values()] if r["workload"] == wname and r["path"] != "project"]
+        runs = [r for r in [main_res, *extra.values()]
+                if r["workload"] == wname and r["path"] not in ("project", "sparse_mla")]
         t = {r["path"]: r["ms_per_step"] for r in runs}
         if "pruned" in t and "unpruned" in t:
             for r in runs:

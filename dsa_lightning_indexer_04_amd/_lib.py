@@ -71,6 +71,21 @@ class ProjInputs(ctypes.Structure):
     ]
 
 
+class MlaInputs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q", ctypes.c_int32),
+        ("num_k", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("latent_dim", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("kv", ctypes.c_void_p),
+        ("indices", ctypes.c_void_p),
+    ]
+
+
 EXPORTED = [
     "dsa_indexer_scores",
     "dsa_indexer_topk",
@@ -78,6 +93,8 @@ EXPORTED = [
     "dsa_indexer_workspace_bytes",
     "dsa_indexer_project",
     "dsa_indexer_project_workspace_bytes",
+    "dsa_sparse_mla",
+    "dsa_sparse_mla_workspace_bytes",
     "dsa_indexer_error_string",
     "dsa_indexer_last_error",
     "dsa_indexer_profile_begin",
@@ -121,6 +138,10 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_project.restype = ctypes.c_int
     lib.dsa_indexer_project_workspace_bytes.argtypes = [ctypes.POINTER(ProjInputs)]
     lib.dsa_indexer_project_workspace_bytes.restype = SZ
+    lib.dsa_sparse_mla.argtypes = [ctypes.POINTER(MlaInputs), ctypes.c_float, P, P, P, SZ, P]
+    lib.dsa_sparse_mla.restype = ctypes.c_int
+    lib.dsa_sparse_mla_workspace_bytes.argtypes = [ctypes.POINTER(MlaInputs)]
+    lib.dsa_sparse_mla_workspace_bytes.restype = SZ
     lib.dsa_indexer_error_string.argtypes = [ctypes.c_int]
     lib.dsa_indexer_error_string.restype = ctypes.c_char_p
     lib.dsa_indexer_last_error.argtypes = []
@@ -337,6 +358,47 @@ def project(c_q, x, w_iq, w_ik, w_iw, out: str = "fp8", workspace=None) -> dict:
 def project_workspace_bytes(inp: ProjInputs) -> int:
     lib = load()
     n = lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp))
+    if n == 0:
+        raise IndexerError(1, lib.dsa_indexer_last_error().decode())
+    return n
+
+
+def make_mla_struct(q, kv, indices) -> MlaInputs:
+    """C struct of the sparse MLA inputs: q [B,Q,128,576] bf16, kv [B,N,576]
+    bf16, indices [B,Q,topk] int32 (device tensors)."""
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise TypeError("q and kv must be bfloat16")
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    for name, t in (("q", q), ("kv", kv), ("indices", indices)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Q, H, D = q.shape
+    if kv.shape[0] != B or kv.shape[2] != D or tuple(indices.shape[:2]) != (B, Q):
+        raise ValueError("shapes must be q [B,Q,H,576], kv [B,N,576], indices [B,Q,topk]")
+    return MlaInputs(B, Q, kv.shape[1], H, 512, D - 512, indices.shape[2], _ptr(q), _ptr(kv), _ptr(indices))
+
+
+def sparse_mla(q, kv, indices, sm_scale: float, return_lse: bool = True, workspace=None):
+    """MLA core attention (MQA mode) over the selected positions: returns
+    (out [B,Q,128,512] bf16, lse [B,Q,128] fp32 or None)."""
+    lib = load()
+    inp = make_mla_struct(q, kv, indices)
+    need = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp))
+    if need == 0:
+        raise IndexerError(1, lib.dsa_indexer_last_error().decode())
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    B, Q = q.shape[:2]
+    out = torch.empty((B, Q, 128, 512), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Q, 128), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.dsa_sparse_mla(ctypes.byref(inp), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                              _stream()))
+    return out, lse
+
+
+def sparse_mla_workspace_bytes(inp: MlaInputs) -> int:
+    lib = load()
+    n = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp))
     if n == 0:
         raise IndexerError(1, lib.dsa_indexer_last_error().decode())
     return n

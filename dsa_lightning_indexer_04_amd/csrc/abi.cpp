@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -257,6 +258,33 @@ int check_proj_no_alias(const dsa_proj_inputs* in, Range out) {
     if (overlaps(x, out)) return fail(DSA_ERR_INVALID_ARG, "an output aliases an input");
   return DSA_OK;
 }
+
+// ---------------------------------------------------------------- sparse MLA
+
+int check_mla_inputs(const dsa_mla_inputs* in) {
+  if (!in) return fail(DSA_ERR_INVALID_ARG, "attention inputs struct is NULL");
+  if (in->batch < 1 || in->num_q < 1 || in->num_k < 1)
+    return fail(DSA_ERR_INVALID_ARG, "batch, num_q and num_k must be >= 1");
+  if (in->heads != 128) return fail(DSA_ERR_UNSUPPORTED, "heads must be 128");
+  if (in->latent_dim != 512 || in->rope_dim != 64)
+    return fail(DSA_ERR_UNSUPPORTED, "latent_dim must be 512 and rope_dim 64");
+  if (in->topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1");
+  if (in->topk > 2048) return fail(DSA_ERR_UNSUPPORTED, "topk must be <= 2048");
+  const void* ptrs[] = {in->q, in->kv, in->indices};
+  for (const void* p : ptrs) {
+    if (!p) return fail(DSA_ERR_INVALID_ARG, "q, kv and indices are required");
+    if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "input pointers must be 16-byte aligned");
+  }
+  const uint64_t rows = (uint64_t)in->batch * in->num_q;
+  if (rows > (1ull << 31) || (uint64_t)in->batch * in->num_k > (1ull << 40))
+    return fail(DSA_ERR_INVALID_ARG, "problem too large");
+  return DSA_OK;
+}
+
+size_t mla_workspace(const dsa_mla_inputs* in) {
+  const uint64_t rows = (uint64_t)in->batch * in->num_q;
+  return round_up(rows * 128 * 4, 256) + round_up(rows * 4, 256);
+}
 }  // namespace
 
 extern "C" {
@@ -411,6 +439,45 @@ int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_ou
                           w_out, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream), &err))
     return fail(DSA_ERR_HIP, err);
   return DSA_OK;
+}
+
+size_t dsa_sparse_mla_workspace_bytes(const dsa_mla_inputs* in) {
+  g_last_error.clear();
+  if (check_mla_inputs(in)) return 0;
+  return mla_workspace(in);
+}
+
+int dsa_sparse_mla(const dsa_mla_inputs* in, float sm_scale, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int rc = check_mla_inputs(in);
+  if (rc) return rc;
+  if (!(sm_scale >= 0.0f) || !(sm_scale < INFINITY)) return fail(DSA_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  if (!out) return fail(DSA_ERR_INVALID_ARG, "out is required");
+  if (!aligned16(out) || (lse && !aligned16(lse))) return fail(DSA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  const size_t need = mla_workspace(in);
+  if (workspace_bytes < need || !workspace)
+    return fail(DSA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const uint64_t rows = (uint64_t)in->batch * in->num_q, B = in->batch, N = in->num_k;
+  const Range inputs[] = {span(in->q, rows * 128 * 576 * 2), span(in->kv, B * N * 576 * 2),
+                          span(in->indices, rows * (uint64_t)in->topk * 4)};
+  const Range outs[] = {span(out, rows * 128 * 512 * 2), span(lse, lse ? rows * 128 * 4 : 0), span(workspace, need)};
+  for (int i = 0; i < 3; ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (const Range& x : inputs)
+      if (overlaps(x, outs[i])) return fail(DSA_ERR_INVALID_ARG, "an output aliases an input");
+    for (int j = 0; j < i; ++j)
+      if (outs[j].lo != outs[j].hi && overlaps(outs[i], outs[j]))
+        return fail(DSA_ERR_INVALID_ARG, "outputs and workspace must not overlap");
+  }
+  const dsa::MlaProblem p{in->batch, in->num_q, in->num_k, in->topk, static_cast<const uint16_t*>(in->q),
+                          static_cast<const uint16_t*>(in->kv), in->indices};
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* row_max = reinterpret_cast<float*>(ws);
+  int32_t* retry = reinterpret_cast<int32_t*>(ws + round_up(rows * 128 * 4, 256));
+  return hip_status(dsa::launch_sparse_mla(p, sm_scale, static_cast<uint16_t*>(out), lse, row_max, retry,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 const char* dsa_indexer_error_string(int code) {

@@ -96,6 +96,21 @@ size_t proj_workspace_bytes(int T, int hidden);
 int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale, uint8_t* k_out, float* k_scale,
                    float* w_out, uint8_t* ws, hipStream_t st, std::string* err);
 
+// ---------------------------------------------------------------- sparse MLA
+
+// Core attention over selected positions: q [B*Q][128][576], kv [B][N][576]
+// (bf16, [latent 512 | RoPE 64]), indices [B*Q][topk] (topk <= 2048).
+struct MlaProblem {
+  int B, Q, N, topk;
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* indices;
+};
+// out [B*Q][128][512] bf16, lse [B*Q][128] fp32 (may be null); row_max
+// [B*Q][128] fp32 and retry [B*Q] int32 are scratch (the second pass).
+hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
+                             int32_t* retry, hipStream_t st);
+
 // Candidate capacity (records per row) used by the streaming Top-K.
 inline int stream_capacity(int topk) { return 4 * topk + 128; }
 

@@ -1,0 +1,331 @@
+// sparse_mla.hip -- MLA core attention (MQA mode) over the indexer's selected
+// positions.
+//
+// DeepSeek DSA FLOPs notes, section "Core Sparse Attention FLOPs": for query
+// row t and its selected positions S_t, every one of the h = 128 heads scores
+// the shared cache rows [C^KV | K^R] (512 + 64 values) with its query
+// [Q^A | Q^R], a softmax over the selected positions gives P, and the output
+// is Z = P C^KV_S (h x 512).  The softmax is taken of sm_scale * score.
+//
+// One workgroup per query row, 4 waves, 32 heads per wave.  Per tile of 32
+// selected positions:
+//   * the 32 cache rows are gathered straight from HBM into LDS (one 16-byte
+//     chunk per lane, key-major, one pad chunk per row so column reads are
+//     conflict-free), double-buffered: the next tile's rows load while this
+//     tile is computed;
+//   * S^T = K Q^T as a 32 keys x 32 heads MFMA block (36 k-steps of
+//     32x32x16 bf16; the wave's 32 x 576 query block stays in registers), so
+//     a lane owns one head: the softmax statistics are lane-local plus one
+//     cross-half exchange;
+//   * O^T += V^T P^T over the 16 blocks of 32 latent dims: P^T is taken from
+//     the S^T accumulators as they lie (the contraction runs over the keys in
+//     a permuted order, and V^T is stored in LDS in that same order), V^T is
+//     built from the key-major tile once per tile by all waves.
+// Softmax reference: each head subtracts a fixed reference (its first
+// selected tile's maximum) instead of a running maximum, so the accumulators
+// are never rescaled (a rescale, like any loop restart, makes the register
+// allocator spill the query block).  The softmax does not depend on the
+// constant subtracted; weights stay below 2^32 as long as no later score
+// exceeds the reference by more than 32 (log2 units).  A row where one does
+// is flagged together with its heads' true maxima, and a second launch of the
+// kernel recomputes just the flagged rows with those maxima as references
+// (no weight above 1).  Scores of ordinary range never flag a row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kHeads = 128;
+constexpr int kDc = 512;           // latent dims
+constexpr int kDr = 64;            // RoPE dims
+constexpr int kRow = kDc + kDr;    // values per cache row / query head
+constexpr int kChunks = kRow / 8;  // 16-byte chunks per row (72)
+constexpr int kSlots = kChunks + 1;  // LDS slots per key row (one pad)
+constexpr int kTile = 32;          // selected positions per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+// one direct-load instruction fills 1 KiB (64 lanes x 16 B): the buffer is
+// padded to whole instructions so the last one's lanes past the tile land in it
+constexpr int kKtBytes = (kTile * kSlots * 16 + 1023) / 1024 * 1024;  // 37888
+constexpr int kVtStride = 80;                  // bytes per V^T row: 32 keys + 16 B pad
+constexpr int kVtBytes = kDc * kVtStride;      // 40960
+constexpr int kKSteps = kRow / 16;             // 36
+constexpr int kMaxTopk = 2048;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRestartMargin = 32.0f;
+constexpr int kAhead = 4;  // LDS operand reads in flight per MFMA chain
+
+// Column of key r (0..31) in a V^T row: k-step g = r/16 covers columns
+// 16g..16g+15, and its half h (lanes 32h..32h+31 of the MFMA operand) takes
+// keys {16g+4h+0..3, 16g+8+4h+0..3} -- the keys the S^T accumulator of a lane
+// in that half holds -- as 8 consecutive columns.
+__device__ __forceinline__ int vt_col(int r) {
+  return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+
+constexpr int kOBlocks = kDc / 32;      // 32-dim output blocks per head group
+constexpr int kORegBlocks = kOBlocks - 2;  // kept in registers; the last two live in LDS
+constexpr int kOLdsBlocks = kOBlocks - kORegBlocks;
+
+template <int kBufs>
+struct Smem {
+  uint8_t kt[kBufs][kKtBytes];
+  uint8_t vt[kVtBytes];
+  f32x16 olast[kOLdsBlocks][kWaves][64];  // each lane's accumulators of the last output blocks
+  int32_t idx[kMaxTopk];
+  int32_t last[kWaves];
+  int32_t vote[kWaves];  // a wave saw a score above its reference + margin
+};
+
+// kRetry = false: first pass over every row; true: recompute the rows the
+// first pass flagged, with the recorded maxima as references.
+template <bool kRetry>
+__global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ kv,
+                                                            const int32_t* __restrict__ indices, int Q, int N,
+                                                            int topk, float scale_log2, uint16_t* __restrict__ out,
+                                                            float* __restrict__ lse, float* __restrict__ row_max,
+                                                            int32_t* __restrict__ retry) {
+  if (kRetry && retry[blockIdx.x] == 0) return;  // uniform over the workgroup
+  __shared__ Smem<2> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const size_t row = blockIdx.x;  // b * Q + t
+  const size_t b = row / (size_t)Q;
+  const uint16_t* kvb = kv + b * (size_t)N * kRow;
+
+  // ---- selected positions of the row: LDS copy (-1 past topk or out of range)
+  const int32_t* irow = indices + row * (size_t)topk;
+  int last = -1;
+  for (int i = tid; i < kMaxTopk; i += kThreads) {
+    int v = -1;
+    if (i < topk) {
+      v = irow[i];
+      if (v < 0 || v >= N) v = -1;
+    }
+    sm.idx[i] = v;
+    if (v >= 0) last = i;
+  }
+  // the last valid entry bounds the tiles to visit
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (lane == 0) {
+    sm.last[wave] = last;
+    sm.vote[wave] = 0;
+  }
+
+  // ---- this wave's 32 heads of the query row as MFMA B operands (Q^T):
+  // lane l holds head l%32, dims 16kk + 8(l/32) .. +7 for k-step kk
+  const uint16_t* qh = q + (row * kHeads + wave * 32 + l32) * kRow + 8 * half;
+  u32x4 qf[kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *reinterpret_cast<const u32x4*>(qh + 16 * kk);
+  __syncthreads();
+  const int lastv = max(max(sm.last[0], sm.last[1]), max(sm.last[2], sm.last[3]));
+  const int ntiles = (lastv + kTile) / kTile;  // 0 when nothing is selected
+
+  // ---- gather of one tile into kt[buf]: slot s of the tile (key s/73, chunk
+  // s%73) is lane (s % 64) of load instruction s/64; pad slots re-read chunk 0
+  auto issue_tile = [&](int tile, int buf) {
+    constexpr int kInstr = (kTile * kSlots + 63) / 64;  // 37
+    for (int j = wave; j < kInstr; j += kWaves) {
+      const int s = j * 64 + lane;
+      int key = s / kSlots, c = s - key * kSlots;
+      if (s >= kTile * kSlots) key = kTile - 1, c = 0;  // past the tile: a harmless re-read
+      if (c == kChunks) c = 0;
+      int pos = sm.idx[tile * kTile + key];
+      if (pos < 0) pos = 0;  // invalid entries load row 0; their scores are masked
+      const uint16_t* src = kvb + (size_t)pos * kRow + 8 * c;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint32_t*>(&sm.kt[buf][j * 1024]), 16, 0, 0);
+    }
+  };
+
+  // O^T accumulators: blocks 0..13 in registers, blocks 14, 15 in LDS (the
+  // accumulator registers hold 14 output blocks, the score block and one
+  // LDS block while it is updated)
+  f32x16 o[kORegBlocks];
+#pragma unroll
+  for (int i = 0; i < kORegBlocks; ++i) o[i] = f32x16{0};
+#pragma unroll
+  for (int i = 0; i < kOLdsBlocks; ++i) sm.olast[i][wave][lane] = f32x16{0};
+  const int head = wave * 32 + l32;
+  float m_ref = kRetry ? row_max[row * kHeads + head] : -INFINITY;
+  float m_seen = -INFINITY, l_run = 0.0f;
+  bool over = false;  // a score exceeded the reference by more than the margin
+
+  if (ntiles > 0) issue_tile(0, 0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
+    __syncthreads();
+    const int buf = tile & 1;
+    // V^T[d][vt_col(r)] for d < 512: pairs of keys (2p, 2p+1) -> one dword per dim.
+    // The per-lane bases are made opaque here so that the addresses below
+    // are formed from them with immediate offsets instead of being hoisted
+    // out of the tile loop (which would hold ~40 registers across it).
+    {
+      const int p = lane & 15, c0 = wave * 4 + (lane >> 4);
+      uint32_t rd = (uint32_t)(((2 * p) * kSlots + c0) * 16 + buf * kKtBytes);
+      uint32_t wr = (uint32_t)(8 * c0 * kVtStride + 2 * vt_col(2 * p));
+      asm volatile("" : "+v"(rd), "+v"(wr));
+      const uint8_t* kt0 = reinterpret_cast<const uint8_t*>(sm.kt) + rd;
+      uint8_t* vt0 = sm.vt + wr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // chunk c = c0 + 16 i: dims 8c .. 8c+7 of keys 2p, 2p+1
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16);
+        const u32x4 bq = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16 + kSlots * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // dims 8c+2j (low halves) and 8c+2j+1 (high halves)
+          const uint32_t lo = __builtin_amdgcn_perm(bq[j], a[j], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(bq[j], a[j], 0x07060302u);
+          *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j) * kVtStride) = lo;
+          *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j + 1) * kVtStride) = hi;
+        }
+      }
+    }
+    if (tile + 1 < ntiles) issue_tile(tile + 1, buf ^ 1);
+    __syncthreads();
+
+    // ---- S^T = K Q^T (32 keys x 32 heads); operands read 4 k-steps ahead
+    f32x16 s = f32x16{0};
+    const uint8_t* ka = &sm.kt[buf][(l32 * kSlots + half) * 16];
+    {
+      u32x4 ar[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(ka + i * 32);
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[kk % kAhead]),
+                                                    __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
+        if (kk + kAhead < kKSteps) ar[kk % kAhead] = *reinterpret_cast<const u32x4*>(ka + (kk + kAhead) * 32);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+      }
+    }
+    // ---- online softmax per head (lane l%32), base 2
+    // lane holds keys 8(v/4) + 4*half + v%4 of the tile; bit r of `valid`
+    // says whether the tile's key r is a selected position
+    const uint32_t valid = (uint32_t)__builtin_amdgcn_ballot_w64(sm.idx[tile * kTile + l32] >= 0);
+    const uint32_t mine = valid >> (4 * half);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = (mine >> (8 * (v >> 2) + (v & 3))) & 1u;
+      s[v] = ok ? s[v] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (!kRetry) {
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == -INFINITY) m_ref = mx;  // first selected tile (nothing accumulated yet)
+      over |= mx > m_ref + kRestartMargin;
+    }
+    // weights; a head with nothing selected yet keeps m_ref = -inf and weights 0
+    const float msub = m_ref == -INFINITY ? 0.0f : m_ref;
+    u32x4 pb[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j] - msub);
+        const float p1 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j + 1] - msub);
+        l_run += p0 + p1;
+        const __bf16 h0 = static_cast<__bf16>(p0), h1 = static_cast<__bf16>(p1);
+        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      }
+      pb[g] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    // ---- O^T += V^T P^T: 16 blocks of 32 latent dims, 2 k-steps of 16 keys;
+    // operands read 4 steps ahead
+    const uint8_t* va = &sm.vt[l32 * kVtStride + 16 * half];
+    {
+      constexpr int kSteps = 2 * kORegBlocks;
+      auto vaddr = [&](int st) { return va + (st >> 1) * 32 * kVtStride + 32 * (st & 1); };
+      u32x4 ar[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(vaddr(i));
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[st % kAhead]),
+                                                             __builtin_bit_cast(bf16x8, pb[st & 1]), o[st >> 1], 0, 0,
+                                                             0);
+        if (st + kAhead < kSteps) ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(st + kAhead));
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      // the last blocks through LDS, one at a time
+#pragma unroll
+      for (int i = 0; i < kOLdsBlocks; ++i) {
+        f32x16 ol = sm.olast[i][wave][lane];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vaddr(2 * (kORegBlocks + i) + g));
+          ol = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb[g]),
+                                                       ol, 0, 0, 0);
+        }
+        sm.olast[i][wave][lane] = ol;
+      }
+    }
+  }
+
+  // ---- normalise and write: lane holds head l%32 and, per block, dims
+  // 32 blk + 8(v/4) + 4 half + v%4
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (!kRetry) {
+    // flag the row if any head saw a score too far above its reference, and
+    // record every head's maximum for the second pass
+    const bool w_over = __builtin_amdgcn_ballot_w64(over) != 0;
+    if (lane == 0) sm.vote[wave] = w_over;
+    __syncthreads();
+    if (tid == 0) retry[row] = sm.vote[0] | sm.vote[1] | sm.vote[2] | sm.vote[3];
+    if (half == 0) row_max[row * kHeads + head] = m_seen;
+  }
+  uint16_t* orow = out + (row * kHeads + head) * kDc;
+  auto store_block = [&](int blk, const f32x16& acc) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const __bf16 h0 = static_cast<__bf16>(acc[4 * g + 2 * j] * inv);
+        const __bf16 h1 = static_cast<__bf16>(acc[4 * g + 2 * j + 1] * inv);
+        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      }
+      *reinterpret_cast<uint2*>(orow + 32 * blk + 8 * g + 4 * half) = make_uint2(w[0], w[1]);
+    }
+  };
+#pragma unroll
+  for (int blk = 0; blk < kORegBlocks; ++blk) store_block(blk, o[blk]);
+#pragma unroll
+  for (int i = 0; i < kOLdsBlocks; ++i) store_block(kORegBlocks + i, sm.olast[i][wave][lane]);
+  if (lse && half == 0)
+    lse[row * kHeads + head] = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
+                             int32_t* retry, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)p.B * p.Q)), block(kThreads);
+  int slot = prof_open("k_sparse_mla", st);
+  hipLaunchKernelGGL(k_sparse_mla<false>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk,
+                     sm_scale * kLog2e, out, lse, row_max, retry);
+  prof_close(slot, st);
+  slot = prof_open("k_sparse_mla_retry", st);
+  hipLaunchKernelGGL(k_sparse_mla<true>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk,
+                     sm_scale * kLog2e, out, lse, row_max, retry);
+  prof_close(slot, st);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

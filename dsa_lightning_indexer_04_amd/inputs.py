@@ -241,6 +241,47 @@ def make_projection_inputs(T: int, hidden: int = PROJ_HIDDEN, q_latent: int = PR
     }
 
 
+# Sizes of the sparse MLA core attention (DeepSeek-V3.2: 128 heads, latent 512, RoPE 64).
+MLA_HEADS = 128
+MLA_LATENT = 512
+MLA_ROPE = 64
+
+
+def make_mla_inputs(B: int, Q: int, N: int, seed: int = 0, device="cpu") -> dict:
+    """Seeded bf16 operands of the sparse MLA attention: q [B,Q,128,576]
+    ([Q^A | Q^R] per head) and kv [B,N,576] ([C^KV | K^R] per position), all
+    entries i.i.d. N(0,1) (normalised latents; with sm_scale = 1/sqrt(576) a
+    score is N(0,1)).  Drawn with torch's generator on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    d = MLA_LATENT + MLA_ROPE
+
+    def draw(shape):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = out.view(-1, d)
+        step = 1 << 16
+        for r in range(0, flat.shape[0], step):
+            n = min(step, flat.shape[0] - r)
+            flat[r:r + n] = torch.randn((n, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        return out
+
+    return {"q": draw((B, Q, MLA_HEADS, d)), "kv": draw((B, N, d))}
+
+
+def random_selection(B: int, Q: int, N: int, topk: int, pos: np.ndarray, seed: int = 0) -> np.ndarray:
+    """[B,Q,topk] int32: for each row, min(topk, visible) distinct random
+    positions in 0..pos (in random order), then -1 padding."""
+    rng = np.random.default_rng(seed)
+    out = np.full((B, Q, topk), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(Q):
+            vis = int(min(max(pos[b, t] + 1, 0), N))
+            m = min(topk, vis)
+            if m:
+                out[b, t, :m] = rng.choice(vis, size=m, replace=False)
+    return out
+
+
 def to_bits(x: torch.Tensor) -> np.ndarray:
     """Raw bit patterns of a bf16 (uint16) or fp8 (uint8) tensor as numpy."""
     if x.dtype == torch.bfloat16:

@@ -217,6 +217,50 @@ int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_ou
  * inputs are invalid).                                                      */
 size_t dsa_indexer_project_workspace_bytes(const dsa_proj_inputs* in);
 
+/* ---------------------------------------------------------- sparse MLA
+ *
+ * The core attention that consumes the selected indices (DeepSeek DSA FLOPs
+ * notes, section "Core Sparse Attention FLOPs"): MLA in MQA mode, every head
+ * reading the same latent cache row [C^KV | K^R] of each selected position.
+ * For query row t with selected positions S_t (the Top-K output):
+ *     s[h,i] = q[t,h,:] . kv[S_t[i],:]      (content score S^A plus RoPE score S^R)
+ *     P[h,:] = softmax_i(sm_scale * s[h,:])
+ *     Z[t,h,:] = sum_i P[h,i] * kv[S_t[i], 0:latent_dim]
+ *     lse[t,h] = log(sum_i exp(sm_scale * s[h,i]))   (natural log)
+ * Inputs (device):
+ *   q        [B,Q,heads,latent_dim+rope_dim] bf16 bits: [Q^A | Q^R] per head
+ *   kv       [B,N,latent_dim+rope_dim]       bf16 bits: [C^KV | K^R] per position
+ *   indices  [B,Q,topk] int32: positions into the row's sequence; entries
+ *            outside 0..N-1 (the Top-K's -1 padding) are skipped, others are
+ *            used as given (a repeated entry counts twice)
+ * heads must be 128, latent_dim 512, rope_dim 64 (DeepSeek-V3.2); topk is
+ * 1..2048.                                                                  */
+typedef struct dsa_mla_inputs {
+  int32_t batch, num_q, num_k, heads, latent_dim, rope_dim, topk;
+  const void* q;
+  const void* kv;
+  const int32_t* indices;
+} dsa_mla_inputs;
+
+/* Sparse MLA attention over the selected positions.
+ *   sm_scale   finite, >= 0 (the pages' formula has 1; scaled-dot-product
+ *              attention over 576-value rows takes 1/sqrt(576))
+ *   out        [B,Q,heads,latent_dim] bf16 out (Z, rounded to nearest even);
+ *              zeros for a row with no selected position
+ *   lse        [B,Q,heads] fp32 out, or NULL; -inf for a row with nothing
+ *              selected
+ *   workspace  dsa_sparse_mla_workspace_bytes(in) bytes, 256-byte aligned:
+ *              per-row softmax maxima for the rare rows whose scores span
+ *              more than 2^32 in weight, which a second launch recomputes
+ * Scores accumulate in fp32 (exact bf16 products), the weights enter the
+ * weighted sum as bf16, the sums accumulate in fp32.                       */
+int dsa_sparse_mla(const dsa_mla_inputs* in, float sm_scale, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of dsa_sparse_mla (0 and the last error set if the inputs
+ * are invalid).                                                             */
+size_t dsa_sparse_mla_workspace_bytes(const dsa_mla_inputs* in);
+
 /* Static name of an error code, and the calling thread's last error detail. */
 const char* dsa_indexer_error_string(int code);
 const char* dsa_indexer_last_error(void);

@@ -154,3 +154,52 @@ def test_projection_argument_errors(lib):
     assert b"must not overlap" in lib.dsa_indexer_last_error()
     assert call(ctypes.byref(inp), 1, qo, qs, ko, ks, wo, o(FAKE * 67), need, None) == 1  # workspace over a scale
     assert b"must not overlap" in lib.dsa_indexer_last_error()
+
+
+def _mla(_lib, **kw):
+    d = dict(batch=1, num_q=8, num_k=4096, heads=128, latent_dim=512, rope_dim=64, topk=2048, q=FAKE * 256,
+             kv=FAKE * 512, indices=FAKE * 600)
+    d.update(kw)
+    return _lib.MlaInputs(**d)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(heads=64), 2),
+        (dict(latent_dim=256), 2),
+        (dict(rope_dim=0), 2),
+        (dict(topk=4096), 2),
+        (dict(topk=0), 1),
+        (dict(num_k=0), 1),
+        (dict(kv=None), 1),
+        (dict(indices=FAKE * 600 + 4), 1),
+    ],
+)
+def test_sparse_mla_inputs_are_rejected(lib, kw, code):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _mla(_lib, **kw)
+    o = ctypes.c_void_p
+    rc = lib.dsa_sparse_mla(ctypes.byref(inp), 0.04, o(FAKE * 700), None, o(FAKE * 800), 1 << 30, None)
+    assert rc == code
+    assert lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp)) == 0
+
+
+def test_sparse_mla_argument_errors(lib):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _mla(_lib)
+    o = ctypes.c_void_p
+    need = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp))
+    assert need >= 8 * 128 * 4 + 8 * 4
+    out, ws = o(FAKE * 700), o(FAKE * 800)
+    call = lib.dsa_sparse_mla
+    assert call(ctypes.byref(inp), -1.0, out, None, ws, need, None) == 1
+    assert call(ctypes.byref(inp), float("inf"), out, None, ws, need, None) == 1
+    assert call(ctypes.byref(inp), 0.04, None, None, ws, need, None) == 1
+    assert call(ctypes.byref(inp), 0.04, out, None, ws, need - 1, None) == 3
+    assert call(ctypes.byref(inp), 0.04, o(FAKE * 512), None, ws, need, None) == 1  # out aliases kv
+    assert b"aliases an input" in lib.dsa_indexer_last_error()
+    assert call(ctypes.byref(inp), 0.04, out, None, out, need, None) == 1  # workspace over out
+    assert b"must not overlap" in lib.dsa_indexer_last_error()
