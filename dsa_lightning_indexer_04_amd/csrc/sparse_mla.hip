@@ -135,7 +135,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
   // s%73) is lane (s % 64) of load instruction s/64; pad slots re-read chunk 0
   auto issue_tile = [&](int tile, int buf) {
     constexpr int kInstr = (kTile * kSlots + 63) / 64;  // 37
-    for (int j = wave; j < kInstr; j += kWaves) {
+#pragma unroll
+    for (int i = 0; i < (kInstr + kWaves - 1) / kWaves; ++i) {
+      const int j = wave + kWaves * i;
+      if (j >= kInstr) break;  // uniform per wave
       const int s = j * 64 + lane;
       int key = s / kSlots, c = s - key * kSlots;
       if (s >= kTile * kSlots) key = kTile - 1, c = 0;  // past the tile: a harmless re-read
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
     __syncthreads();
     const int buf = tile & 1;
+    if (tile + 1 < ntiles) issue_tile(tile + 1, buf ^ 1);
     // V^T[d][vt_col(r)] for d < 512: pairs of keys (2p, 2p+1) -> one dword per dim.
     // The per-lane bases are made opaque here so that the addresses below
     // are formed from them with immediate offsets instead of being hoisted
@@ -191,23 +195,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
         }
       }
     }
-    if (tile + 1 < ntiles) issue_tile(tile + 1, buf ^ 1);
     __syncthreads();
 
-    // ---- S^T = K Q^T (32 keys x 32 heads); operands read 4 k-steps ahead
+    // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps ahead
     f32x16 s = f32x16{0};
     const uint8_t* ka = &sm.kt[buf][(l32 * kSlots + half) * 16];
     {
       u32x4 ar[kAhead];
+      // fenced steps keep the reads kAhead MFMAs ahead (left free, the
+      // scheduler moves each read next to its MFMA and waits on it)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(ka + i * 32);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[kk % kAhead]),
                                                     __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
         if (kk + kAhead < kKSteps) ar[kk % kAhead] = *reinterpret_cast<const u32x4*>(ka + (kk + kAhead) * 32);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then one LDS read
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // ---- online softmax per head (lane l%32), base 2
@@ -244,23 +250,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
       }
       pb[g] = u32x4{w[0], w[1], w[2], w[3]};
     }
-    // ---- O^T += V^T P^T: 16 blocks of 32 latent dims, 2 k-steps of 16 keys;
-    // operands read 4 steps ahead
+    // ---- O^T += V^T P^T: 16 blocks of 32 latent dims, 2 k-steps of 16 keys
+    // (k-step outer, so consecutive MFMAs update different blocks); operands
+    // read kAhead steps ahead
     const uint8_t* va = &sm.vt[l32 * kVtStride + 16 * half];
     {
       constexpr int kSteps = 2 * kORegBlocks;
-      auto vaddr = [&](int st) { return va + (st >> 1) * 32 * kVtStride + 32 * (st & 1); };
+      // step st: k-step g = st / kORegBlocks, block st % kORegBlocks
+      auto vaddr = [&](int blk, int g) { return va + blk * 32 * kVtStride + 32 * g; };
       u32x4 ar[kAhead];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(vaddr(i));
+      for (int i = 0; i < kAhead; ++i)
+        ar[i] = *reinterpret_cast<const u32x4*>(vaddr(i % kORegBlocks, i / kORegBlocks));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
-        o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[st % kAhead]),
-                                                             __builtin_bit_cast(bf16x8, pb[st & 1]), o[st >> 1], 0, 0,
-                                                             0);
-        if (st + kAhead < kSteps) ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(st + kAhead));
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        const int blk = st % kORegBlocks, g = st / kORegBlocks;
+        o[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[st % kAhead]),
+                                                         __builtin_bit_cast(bf16x8, pb[g]), o[blk], 0, 0, 0);
+        const int nx = st + kAhead;
+        if (nx < kSteps)
+          ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(nx % kORegBlocks, nx / kORegBlocks));
+        __builtin_amdgcn_sched_barrier(0);
       }
       // the last blocks through LDS, one at a time
 #pragma unroll
@@ -268,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
         f32x16 ol = sm.olast[i][wave][lane];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vaddr(2 * (kORegBlocks + i) + g));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vaddr(kORegBlocks + i, g));
           ol = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb[g]),
                                                        ol, 0, 0, 0);
         }
