@@ -71,15 +71,12 @@ __device__ __forceinline__ int vt_col(int r) {
   return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
 }
 
-constexpr int kOBlocks = kDc / 32;      // 32-dim output blocks per head group
-constexpr int kORegBlocks = kOBlocks - 2;  // kept in registers; the last two live in LDS
-constexpr int kOLdsBlocks = kOBlocks - kORegBlocks;
+constexpr int kOBlocks = kDc / 32;  // 32-dim output blocks per head group
 
 template <int kBufs>
 struct Smem {
   uint8_t kt[kBufs][kKtBytes];
   uint8_t vt[kVtBytes];
-  f32x16 olast[kOLdsBlocks][kWaves][64];  // each lane's accumulators of the last output blocks
   int32_t idx[kMaxTopk];
   int32_t last[kWaves];
   int32_t vote[kWaves];  // a wave saw a score above its reference + margin
@@ -150,14 +147,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     }
   };
 
-  // O^T accumulators: blocks 0..13 in registers, blocks 14, 15 in LDS (the
-  // accumulator registers hold 14 output blocks, the score block and one
-  // LDS block while it is updated)
-  f32x16 o[kORegBlocks];
+  // O^T accumulators: 16 blocks of 32 latent dims x 32 heads (256 registers)
+  f32x16 o[kOBlocks];
 #pragma unroll
-  for (int i = 0; i < kORegBlocks; ++i) o[i] = f32x16{0};
-#pragma unroll
-  for (int i = 0; i < kOLdsBlocks; ++i) sm.olast[i][wave][lane] = f32x16{0};
+  for (int i = 0; i < kOBlocks; ++i) o[i] = f32x16{0};
   const int head = wave * 32 + l32;
   float m_ref = kRetry ? row_max[row * kHeads + head] : -INFINITY;
   float m_seen = -INFINITY, l_run = 0.0f;
@@ -255,36 +248,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     // read kAhead steps ahead
     const uint8_t* va = &sm.vt[l32 * kVtStride + 16 * half];
     {
-      constexpr int kSteps = 2 * kORegBlocks;
-      // step st: k-step g = st / kORegBlocks, block st % kORegBlocks
+      constexpr int kSteps = 2 * kOBlocks;
+      // step st: k-step g = st / kOBlocks, block st % kOBlocks
       auto vaddr = [&](int blk, int g) { return va + blk * 32 * kVtStride + 32 * g; };
       u32x4 ar[kAhead];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kAhead; ++i)
-        ar[i] = *reinterpret_cast<const u32x4*>(vaddr(i % kORegBlocks, i / kORegBlocks));
+        ar[i] = *reinterpret_cast<const u32x4*>(vaddr(i % kOBlocks, i / kOBlocks));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
-        const int blk = st % kORegBlocks, g = st / kORegBlocks;
+        const int blk = st % kOBlocks, g = st / kOBlocks;
         o[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[st % kAhead]),
                                                          __builtin_bit_cast(bf16x8, pb[g]), o[blk], 0, 0, 0);
         const int nx = st + kAhead;
         if (nx < kSteps)
-          ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(nx % kORegBlocks, nx / kORegBlocks));
+          ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(nx % kOBlocks, nx / kOBlocks));
         __builtin_amdgcn_sched_barrier(0);
-      }
-      // the last blocks through LDS, one at a time
-#pragma unroll
-      for (int i = 0; i < kOLdsBlocks; ++i) {
-        f32x16 ol = sm.olast[i][wave][lane];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vaddr(kORegBlocks + i, g));
-          ol = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb[g]),
-                                                       ol, 0, 0, 0);
-        }
-        sm.olast[i][wave][lane] = ol;
       }
     }
   }
@@ -317,9 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     }
   };
 #pragma unroll
-  for (int blk = 0; blk < kORegBlocks; ++blk) store_block(blk, o[blk]);
-#pragma unroll
-  for (int i = 0; i < kOLdsBlocks; ++i) store_block(kORegBlocks + i, sm.olast[i][wave][lane]);
+  for (int blk = 0; blk < kOBlocks; ++blk) store_block(blk, o[blk]);
   if (lse && half == 0)
     lse[row * kHeads + head] = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
