@@ -51,9 +51,11 @@ constexpr int kSlots = kChunks + 1;  // LDS slots per key row (one pad)
 constexpr int kTile = 32;          // selected positions per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-// one direct-load instruction fills 1 KiB (64 lanes x 16 B): the buffer is
-// padded to whole instructions so the last one's lanes past the tile land in it
-constexpr int kKtBytes = (kTile * kSlots * 16 + 1023) / 1024 * 1024;  // 37888
+// one direct-load instruction fills 1 KiB (64 lanes x 16 B); each wave
+// issues the same number of them per tile, so the buffer holds
+// kWaves * ceil(37 / kWaves) KiB and the slots past the tile land in it
+constexpr int kLoadsPerWave = (kTile * kSlots * 16 / 1024 + 1 + kWaves - 1) / kWaves;  // 10
+constexpr int kKtBytes = kWaves * kLoadsPerWave * 1024;                                // 40960
 constexpr int kVtStride = 80;                  // bytes per V^T row: 32 keys + 16 B pad
 constexpr int kVtBytes = kDc * kVtStride;      // 40960
 constexpr int kKSteps = kRow / 16;             // 36
@@ -129,22 +131,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
   const int ntiles = (lastv + kTile) / kTile;  // 0 when nothing is selected
 
   // ---- gather of one tile into kt[buf]: slot s of the tile (key s/73, chunk
-  // s%73) is lane (s % 64) of load instruction s/64; pad slots re-read chunk 0
+  // s%73) is lane s%64 of load instruction s/64; wave w issues instructions
+  // w, w+4, ... (kLoadsPerWave of them), each filling 1 KiB of LDS.  Pad
+  // slots (chunk 72) and slots past the tile re-read a chunk of the tile;
+  // invalid entries read row 0 (their scores are masked).  A cursor walks
+  // this lane's slots: consecutive instructions of a wave are 256 slots apart
+  // (3 rows of 73 plus 37), so no division per load.
+  struct Cursor {
+    int key, c;
+  };
+  auto cursor0 = [&]() {
+    const int s0 = wave * 64 + lane;
+    return Cursor{s0 / kSlots, s0 - (s0 / kSlots) * kSlots};
+  };
+  auto issue_one = [&](int tile, int buf, int i, Cursor& cur) {
+    const int j = wave + kWaves * i;
+    const bool past = cur.key >= kTile;
+    const int key = past ? kTile - 1 : cur.key;
+    const int c = (past || cur.c == kChunks) ? 0 : cur.c;
+    const int pos = max(sm.idx[tile * kTile + key], 0);
+    const uint16_t* src = kvb + (size_t)pos * kRow + 8 * c;
+    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint32_t*>(&sm.kt[buf][j * 1024]), 16, 0, 0);
+    cur.c += kWaves * 64 - 3 * kSlots;
+    cur.key += 3;
+    if (cur.c >= kSlots) cur.c -= kSlots, cur.key += 1;
+  };
   auto issue_tile = [&](int tile, int buf) {
-    constexpr int kInstr = (kTile * kSlots + 63) / 64;  // 37
+    Cursor cur = cursor0();
 #pragma unroll
-    for (int i = 0; i < (kInstr + kWaves - 1) / kWaves; ++i) {
-      const int j = wave + kWaves * i;
-      if (j >= kInstr) break;  // uniform per wave
-      const int s = j * 64 + lane;
-      int key = s / kSlots, c = s - key * kSlots;
-      if (s >= kTile * kSlots) key = kTile - 1, c = 0;  // past the tile: a harmless re-read
-      if (c == kChunks) c = 0;
-      int pos = sm.idx[tile * kTile + key];
-      if (pos < 0) pos = 0;  // invalid entries load row 0; their scores are masked
-      const uint16_t* src = kvb + (size_t)pos * kRow + 8 * c;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<uint32_t*>(&sm.kt[buf][j * 1024]), 16, 0, 0);
-    }
+    for (int i = 0; i < kLoadsPerWave; ++i) issue_one(tile, buf, i, cur);
   };
 
   // O^T accumulators: 16 blocks of 32 latent dims x 32 heads (256 registers)
@@ -161,7 +176,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
     __syncthreads();
     const int buf = tile & 1;
-    if (tile + 1 < ntiles) issue_tile(tile + 1, buf ^ 1);
+    // the next tile's rows load into the other buffer during this whole tile
+    // (interleaved with the score MFMAs below); that buffer's last readers
+    // finished before the barrier above.  The last tile re-reads itself into
+    // the idle buffer.
+    const int nt = tile + 1 < ntiles ? tile + 1 : tile;
+    Cursor cur = cursor0();
+
+    // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps ahead
+    f32x16 s = f32x16{0};
+    const uint8_t* ka = &sm.kt[buf][(l32 * kSlots + half) * 16];
+    {
+      u32x4 ar[kAhead];
+      // fenced steps keep the reads kAhead MFMAs ahead (left free, the
+      // scheduler moves each read next to its MFMA and waits on it)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(ka + i * 32);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[kk % kAhead]),
+                                                    __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
+        if (kk + kAhead < kKSteps) ar[kk % kAhead] = *reinterpret_cast<const u32x4*>(ka + (kk + kAhead) * 32);
+        // one gather instruction of the next tile every third MFMA
+        if (kk % 3 == 1 && kk / 3 < kLoadsPerWave) issue_one(nt, buf ^ 1, kk / 3, cur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // ---- online softmax per head (lane l%32), base 2
+    // lane holds keys 8(v/4) + 4*half + v%4 of the tile; bit r of `valid`
+    // says whether the tile's key r is a selected position
+    const uint32_t valid = (uint32_t)__builtin_amdgcn_ballot_w64(sm.idx[tile * kTile + l32] >= 0);
+    const uint32_t mine = valid >> (4 * half);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = (mine >> (8 * (v >> 2) + (v & 3))) & 1u;
+      s[v] = ok ? s[v] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (!kRetry) {
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == -INFINITY) m_ref = mx;  // first selected tile (nothing accumulated yet)
+      over |= mx > m_ref + kRestartMargin;
+    }
+    // ---- V^T of this tile (the previous tile's value MFMAs are done)
     // V^T[d][vt_col(r)] for d < 512: pairs of keys (2p, 2p+1) -> one dword per dim.
     // The per-lane bases are made opaque here so that the addresses below
     // are formed from them with immediate offsets instead of being hoisted
@@ -188,45 +249,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
         }
       }
     }
-    __syncthreads();
+    // V^T complete for all waves.  A plain barrier after this wave's LDS
+    // writes: a __syncthreads() fence would also wait for the next tile's
+    // loads, which nothing before the next tile reads.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps ahead
-    f32x16 s = f32x16{0};
-    const uint8_t* ka = &sm.kt[buf][(l32 * kSlots + half) * 16];
-    {
-      u32x4 ar[kAhead];
-      // fenced steps keep the reads kAhead MFMAs ahead (left free, the
-      // scheduler moves each read next to its MFMA and waits on it)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(ka + i * 32);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[kk % kAhead]),
-                                                    __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
-        if (kk + kAhead < kKSteps) ar[kk % kAhead] = *reinterpret_cast<const u32x4*>(ka + (kk + kAhead) * 32);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // ---- online softmax per head (lane l%32), base 2
-    // lane holds keys 8(v/4) + 4*half + v%4 of the tile; bit r of `valid`
-    // says whether the tile's key r is a selected position
-    const uint32_t valid = (uint32_t)__builtin_amdgcn_ballot_w64(sm.idx[tile * kTile + l32] >= 0);
-    const uint32_t mine = valid >> (4 * half);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool ok = (mine >> (8 * (v >> 2) + (v & 3))) & 1u;
-      s[v] = ok ? s[v] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[v]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (!kRetry) {
-      m_seen = fmaxf(m_seen, mx);
-      if (m_ref == -INFINITY) m_ref = mx;  // first selected tile (nothing accumulated yet)
-      over |= mx > m_ref + kRestartMargin;
-    }
     // weights; a head with nothing selected yet keeps m_ref = -inf and weights 0
     const float msub = m_ref == -INFINITY ? 0.0f : m_ref;
     u32x4 pb[2];
@@ -269,6 +299,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
       }
     }
   }
+
+  // the last tile's redundant loads into the idle buffer must land before
+  // the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- normalise and write: lane holds head l%32 and, per block, dims
   // 32 blk + 8(v/4) + 4 half + v%4
