@@ -63,7 +63,7 @@ constexpr int kMaxTopk = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRestartMargin = 32.0f;
-constexpr int kAhead = 4;  // LDS operand reads in flight per MFMA chain
+constexpr int kAhead = 6;  // LDS operand reads in flight per MFMA chain
 
 // Column of key r (0..31) in a V^T row: k-step g = r/16 covers columns
 // 16g..16g+15, and its half h (lanes 32h..32h+31 of the MFMA operand) takes
@@ -183,13 +183,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     const int nt = tile + 1 < ntiles ? tile + 1 : tile;
     Cursor cur = cursor0();
 
-    // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps ahead
+    // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps
+    // ahead.  The fenced steps also carry this tile's V^T build (its LDS
+    // reads at step 6i, the permutes and writes 4 steps later) and the next
+    // tile's gather (one load every third step): the MFMAs run while these
+    // issue.
     f32x16 s = f32x16{0};
     const uint8_t* ka = &sm.kt[buf][(l32 * kSlots + half) * 16];
     {
+      // V^T[d][vt_col(r)] for d < 512 from pairs of keys (2p, 2p+1), chunk c
+      // = c0 + 16 i (dims 8c .. 8c+7) for task i.  The per-lane bases are made
+      // opaque so the addresses are formed with immediate offsets instead of
+      // being hoisted out of the tile loop (~40 registers across it).
+      const int p = lane & 15, c0 = wave * 4 + (lane >> 4);
+      uint32_t rd = (uint32_t)(((2 * p) * kSlots + c0) * 16 + buf * kKtBytes);
+      uint32_t wr = (uint32_t)(8 * c0 * kVtStride + 2 * vt_col(2 * p));
+      asm volatile("" : "+v"(rd), "+v"(wr));
+      const uint8_t* kt0 = reinterpret_cast<const uint8_t*>(sm.kt) + rd;
+      uint8_t* vt0 = sm.vt + wr;
+      u32x4 va0, vb0;  // the task in flight: chunk of key 2p, chunk of key 2p+1
+
       u32x4 ar[kAhead];
-      // fenced steps keep the reads kAhead MFMAs ahead (left free, the
-      // scheduler moves each read next to its MFMA and waits on it)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) ar[i] = *reinterpret_cast<const u32x4*>(ka + i * 32);
@@ -199,11 +213,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[kk % kAhead]),
                                                     __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
         if (kk + kAhead < kKSteps) ar[kk % kAhead] = *reinterpret_cast<const u32x4*>(ka + (kk + kAhead) * 32);
-        // one gather instruction of the next tile every third MFMA
         if (kk % 3 == 1 && kk / 3 < kLoadsPerWave) issue_one(nt, buf ^ 1, kk / 3, cur);
+        if (kk % 6 == 0 && kk / 6 < 4) {
+          const int i = kk / 6;
+          va0 = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16);
+          vb0 = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16 + kSlots * 16);
+        }
+        if (kk % 6 == 4 && kk / 6 < 4) {
+          const int i = kk / 6;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // dims 8c+2j (low halves) and 8c+2j+1 (high halves) of keys 2p, 2p+1
+            const uint32_t lo = __builtin_amdgcn_perm(vb0[j], va0[j], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(vb0[j], va0[j], 0x07060302u);
+            *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j) * kVtStride) = lo;
+            *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j + 1) * kVtStride) = hi;
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // V^T complete for all waves.  A plain barrier after this wave's LDS
+    // writes: a __syncthreads() fence would also wait for the next tile's
+    // loads, which nothing before the next tile reads.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
     // ---- online softmax per head (lane l%32), base 2
     // lane holds keys 8(v/4) + 4*half + v%4 of the tile; bit r of `valid`
     // says whether the tile's key r is a selected position
@@ -222,66 +259,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
       if (m_ref == -INFINITY) m_ref = mx;  // first selected tile (nothing accumulated yet)
       over |= mx > m_ref + kRestartMargin;
     }
-    // ---- V^T of this tile (the previous tile's value MFMAs are done)
-    // V^T[d][vt_col(r)] for d < 512: pairs of keys (2p, 2p+1) -> one dword per dim.
-    // The per-lane bases are made opaque here so that the addresses below
-    // are formed from them with immediate offsets instead of being hoisted
-    // out of the tile loop (which would hold ~40 registers across it).
-    {
-      const int p = lane & 15, c0 = wave * 4 + (lane >> 4);
-      uint32_t rd = (uint32_t)(((2 * p) * kSlots + c0) * 16 + buf * kKtBytes);
-      uint32_t wr = (uint32_t)(8 * c0 * kVtStride + 2 * vt_col(2 * p));
-      asm volatile("" : "+v"(rd), "+v"(wr));
-      const uint8_t* kt0 = reinterpret_cast<const uint8_t*>(sm.kt) + rd;
-      uint8_t* vt0 = sm.vt + wr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // chunk c = c0 + 16 i: dims 8c .. 8c+7 of keys 2p, 2p+1
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16);
-        const u32x4 bq = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16 + kSlots * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // dims 8c+2j (low halves) and 8c+2j+1 (high halves)
-          const uint32_t lo = __builtin_amdgcn_perm(bq[j], a[j], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(bq[j], a[j], 0x07060302u);
-          *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j) * kVtStride) = lo;
-          *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j + 1) * kVtStride) = hi;
-        }
-      }
-    }
-    // V^T complete for all waves.  A plain barrier after this wave's LDS
-    // writes: a __syncthreads() fence would also wait for the next tile's
-    // loads, which nothing before the next tile reads.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
     // weights; a head with nothing selected yet keeps m_ref = -inf and weights 0
     const float msub = m_ref == -INFINITY ? 0.0f : m_ref;
+    auto weights = [&](int g, int j, uint32_t& w) {
+      const float p0 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j] - msub);
+      const float p1 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j + 1] - msub);
+      l_run += p0 + p1;
+      const __bf16 h0 = static_cast<__bf16>(p0), h1 = static_cast<__bf16>(p1);
+      w = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    };
     u32x4 pb[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    {
       uint32_t w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j] - msub);
-        const float p1 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j + 1] - msub);
-        l_run += p0 + p1;
-        const __bf16 h0 = static_cast<__bf16>(p0), h1 = static_cast<__bf16>(p1);
-        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-      }
-      pb[g] = u32x4{w[0], w[1], w[2], w[3]};
+      for (int j = 0; j < 4; ++j) weights(0, j, w[j]);
+      pb[0] = u32x4{w[0], w[1], w[2], w[3]};
     }
     // ---- O^T += V^T P^T: 16 blocks of 32 latent dims, 2 k-steps of 16 keys
     // (k-step outer, so consecutive MFMAs update different blocks); operands
-    // read kAhead steps ahead
+    // read kAhead steps ahead; the second k-step's weights are formed during
+    // the first k-step's MFMAs
     const uint8_t* va = &sm.vt[l32 * kVtStride + 16 * half];
     {
       constexpr int kSteps = 2 * kOBlocks;
       // step st: k-step g = st / kOBlocks, block st % kOBlocks
       auto vaddr = [&](int blk, int g) { return va + blk * 32 * kVtStride + 32 * g; };
       u32x4 ar[kAhead];
+      uint32_t w1[4];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kAhead; ++i)
@@ -290,11 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         const int blk = st % kOBlocks, g = st / kOBlocks;
+        if (st == kOBlocks) pb[1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
         o[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[st % kAhead]),
                                                          __builtin_bit_cast(bf16x8, pb[g]), o[blk], 0, 0, 0);
         const int nx = st + kAhead;
         if (nx < kSteps)
           ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(nx % kOBlocks, nx / kOBlocks));
+        if (st < 4) weights(1, st, w1[st]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
