@@ -245,13 +245,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     // lane holds keys 8(v/4) + 4*half + v%4 of the tile; bit r of `valid`
     // says whether the tile's key r is a selected position
     const uint32_t valid = (uint32_t)__builtin_amdgcn_ballot_w64(sm.idx[tile * kTile + l32] >= 0);
-    const uint32_t mine = valid >> (4 * half);
+    float sv[16];
     float mx = -INFINITY;
+    if (valid == 0xFFFFFFFFu) {  // uniform: every key of the tile selected (all but a row's last tile)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool ok = (mine >> (8 * (v >> 2) + (v & 3))) & 1u;
-      s[v] = ok ? s[v] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[v]);
+      for (int v = 0; v < 16; ++v) {
+        sv[v] = s[v] * scale_log2;
+        mx = fmaxf(mx, sv[v]);
+      }
+    } else {
+      const uint32_t mine = valid >> (4 * half);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool ok = (mine >> (8 * (v >> 2) + (v & 3))) & 1u;
+        sv[v] = ok ? s[v] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[v]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (!kRetry) {
@@ -262,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     // weights; a head with nothing selected yet keeps m_ref = -inf and weights 0
     const float msub = m_ref == -INFINITY ? 0.0f : m_ref;
     auto weights = [&](int g, int j, uint32_t& w) {
-      const float p0 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j] - msub);
-      const float p1 = __builtin_amdgcn_exp2f(s[8 * g + 2 * j + 1] - msub);
+      const float p0 = __builtin_amdgcn_exp2f(sv[8 * g + 2 * j] - msub);
+      const float p1 = __builtin_amdgcn_exp2f(sv[8 * g + 2 * j + 1] - msub);
       l_run += p0 + p1;
       const __bf16 h0 = static_cast<__bf16>(p0), h1 = static_cast<__bf16>(p1);
       w = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
