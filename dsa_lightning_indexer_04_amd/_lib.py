@@ -83,6 +83,10 @@ class MlaInputs(ctypes.Structure):
         ("q", ctypes.c_void_p),
         ("kv", ctypes.c_void_p),
         ("indices", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
     ]
 
 
@@ -363,27 +367,39 @@ def project_workspace_bytes(inp: ProjInputs) -> int:
     return n
 
 
-def make_mla_struct(q, kv, indices) -> MlaInputs:
-    """C struct of the sparse MLA inputs: q [B,Q,128,576] bf16, kv [B,N,576]
-    bf16, indices [B,Q,topk] int32 (device tensors)."""
+def make_mla_struct(q, kv, indices, page_table=None, num_k=None) -> MlaInputs:
+    """C struct of the sparse MLA inputs: q [B,Q,128,576] bf16, indices
+    [B,Q,topk] int32 and either kv [B,N,576] bf16, or (paged) a page pool kv
+    [num_pages,page_size,576] with page_table [B,pages_per_seq] int32 and the
+    sequence length num_k (device tensors)."""
     if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
         raise TypeError("q and kv must be bfloat16")
-    if indices.dtype != torch.int32:
-        raise TypeError("indices must be int32")
-    for name, t in (("q", q), ("kv", kv), ("indices", indices)):
-        if not t.is_contiguous():
+    if indices.dtype != torch.int32 or (page_table is not None and page_table.dtype != torch.int32):
+        raise TypeError("indices and page_table must be int32")
+    for name, t in (("q", q), ("kv", kv), ("indices", indices), ("page_table", page_table)):
+        if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     B, Q, H, D = q.shape
-    if kv.shape[0] != B or kv.shape[2] != D or tuple(indices.shape[:2]) != (B, Q):
-        raise ValueError("shapes must be q [B,Q,H,576], kv [B,N,576], indices [B,Q,topk]")
-    return MlaInputs(B, Q, kv.shape[1], H, 512, D - 512, indices.shape[2], _ptr(q), _ptr(kv), _ptr(indices))
+    if kv.shape[-1] != D or tuple(indices.shape[:2]) != (B, Q):
+        raise ValueError("shapes must be q [B,Q,H,576], kv [..,576], indices [B,Q,topk]")
+    if page_table is None:
+        if kv.shape[0] != B:
+            raise ValueError("a flat kv is [B,N,576]")
+        return MlaInputs(B, Q, kv.shape[1], H, 512, D - 512, indices.shape[2], _ptr(q), _ptr(kv), _ptr(indices),
+                         None, 0, 0, 0)
+    if num_k is None or page_table.shape[0] != B:
+        raise ValueError("a paged kv needs num_k and page_table [B,pages_per_seq]")
+    return MlaInputs(B, Q, num_k, H, 512, D - 512, indices.shape[2], _ptr(q), _ptr(kv), _ptr(indices),
+                     _ptr(page_table), kv.shape[1], page_table.shape[1], kv.shape[0])
 
 
-def sparse_mla(q, kv, indices, sm_scale: float, return_lse: bool = True, workspace=None):
+def sparse_mla(q, kv, indices, sm_scale: float, return_lse: bool = True, workspace=None, *, page_table=None,
+               num_k=None):
     """MLA core attention (MQA mode) over the selected positions: returns
-    (out [B,Q,128,512] bf16, lse [B,Q,128] fp32 or None)."""
+    (out [B,Q,128,512] bf16, lse [B,Q,128] fp32 or None).  With page_table,
+    kv is a page pool [num_pages,page_size,576] and num_k the sequence length."""
     lib = load()
-    inp = make_mla_struct(q, kv, indices)
+    inp = make_mla_struct(q, kv, indices, page_table, num_k)
     need = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp))
     if need == 0:
         raise IndexerError(1, lib.dsa_indexer_last_error().decode())

@@ -275,6 +275,15 @@ int check_mla_inputs(const dsa_mla_inputs* in) {
     if (!p) return fail(DSA_ERR_INVALID_ARG, "q, kv and indices are required");
     if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "input pointers must be 16-byte aligned");
   }
+  if (in->page_table) {
+    if (!aligned16(in->page_table)) return fail(DSA_ERR_INVALID_ARG, "page_table must be 16-byte aligned");
+    if (in->page_size < 1 || in->num_pages < 1 || in->pages_per_seq < 1)
+      return fail(DSA_ERR_INVALID_ARG, "page_size, pages_per_seq and num_pages must be >= 1");
+    if ((uint64_t)in->pages_per_seq * in->page_size < (uint64_t)in->num_k)
+      return fail(DSA_ERR_INVALID_ARG, "pages_per_seq * page_size must cover num_k");
+    if ((uint64_t)in->num_pages * in->page_size > (1ull << 31))
+      return fail(DSA_ERR_INVALID_ARG, "num_pages * page_size must be <= 2^31");
+  }
   const uint64_t rows = (uint64_t)in->batch * in->num_q;
   if (rows > (1ull << 31) || (uint64_t)in->batch * in->num_k > (1ull << 40))
     return fail(DSA_ERR_INVALID_ARG, "problem too large");
@@ -460,8 +469,10 @@ int dsa_sparse_mla(const dsa_mla_inputs* in, float sm_scale, void* out, float* l
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const uint64_t rows = (uint64_t)in->batch * in->num_q, B = in->batch, N = in->num_k;
-  const Range inputs[] = {span(in->q, rows * 128 * 576 * 2), span(in->kv, B * N * 576 * 2),
-                          span(in->indices, rows * (uint64_t)in->topk * 4)};
+  const uint64_t kv_rows = in->page_table ? (uint64_t)in->num_pages * in->page_size : B * N;
+  const Range inputs[] = {span(in->q, rows * 128 * 576 * 2), span(in->kv, kv_rows * 576 * 2),
+                          span(in->indices, rows * (uint64_t)in->topk * 4),
+                          span(in->page_table, in->page_table ? B * (uint64_t)in->pages_per_seq * 4 : 0)};
   const Range outs[] = {span(out, rows * 128 * 512 * 2), span(lse, lse ? rows * 128 * 4 : 0), span(workspace, need)};
   for (int i = 0; i < 3; ++i) {
     if (outs[i].lo == outs[i].hi) continue;
@@ -471,8 +482,17 @@ int dsa_sparse_mla(const dsa_mla_inputs* in, float sm_scale, void* out, float* l
       if (outs[j].lo != outs[j].hi && overlaps(outs[i], outs[j]))
         return fail(DSA_ERR_INVALID_ARG, "outputs and workspace must not overlap");
   }
-  const dsa::MlaProblem p{in->batch, in->num_q, in->num_k, in->topk, static_cast<const uint16_t*>(in->q),
-                          static_cast<const uint16_t*>(in->kv), in->indices};
+  const dsa::MlaProblem p{in->batch,
+                          in->num_q,
+                          in->num_k,
+                          in->topk,
+                          static_cast<const uint16_t*>(in->q),
+                          static_cast<const uint16_t*>(in->kv),
+                          in->indices,
+                          in->page_table,
+                          in->page_table ? in->page_size : 1,
+                          in->page_table ? in->pages_per_seq : 1,
+                          in->page_table ? in->num_pages : 1};
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* row_max = reinterpret_cast<float*>(ws);
   int32_t* retry = reinterpret_cast<int32_t*>(ws + round_up(rows * 128 * 4, 256));

@@ -103,8 +103,10 @@ int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale
 struct MlaProblem {
   int B, Q, N, topk;
   const uint16_t* q;
-  const uint16_t* kv;
+  const uint16_t* kv;  // [B][N][576], or a page pool [num_pages][page_size][576]
   const int32_t* indices;
+  const int32_t* page_table;  // [B][pages_per_seq], or null for the flat layout
+  int page_size, pages_per_seq, num_pages;
 };
 // out [B*Q][128][512] bf16, lse [B*Q][128] fp32 (may be null); row_max
 // [B*Q][128] fp32 and retry [B*Q] int32 are scratch (the second pass).

@@ -90,7 +90,9 @@ template <bool kRetry>
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ kv,
                                                             const int32_t* __restrict__ indices, int Q, int N,
-                                                            int topk, float scale_log2, uint16_t* __restrict__ out,
+                                                            int topk, const int32_t* __restrict__ page_table,
+                                                            int page_size, int pages_per_seq, int num_pages,
+                                                            float scale_log2, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, float* __restrict__ row_max,
                                                             int32_t* __restrict__ retry) {
   if (kRetry && retry[blockIdx.x] == 0) return;  // uniform over the workgroup
@@ -98,9 +100,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const size_t row = blockIdx.x;  // b * Q + t
   const size_t b = row / (size_t)Q;
-  const uint16_t* kvb = kv + b * (size_t)N * kRow;
+  // flat layout: the sequence's rows; paged: the pool, rows addressed through the table
+  const uint16_t* kvb = page_table ? kv : kv + b * (size_t)N * kRow;
+  const int32_t* ptab = page_table ? page_table + b * (size_t)pages_per_seq : nullptr;
 
-  // ---- selected positions of the row: LDS copy (-1 past topk or out of range)
+  // ---- selected positions of the row: LDS copy of their cache rows (-1 past
+  // topk or out of range)
   const int32_t* irow = indices + row * (size_t)topk;
   int last = -1;
   for (int i = tid; i < kMaxTopk; i += kThreads) {
@@ -108,6 +113,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     if (i < topk) {
       v = irow[i];
       if (v < 0 || v >= N) v = -1;
+      if (v >= 0 && ptab) {
+        const int pg = min(max(ptab[v / page_size], 0), num_pages - 1);
+        v = pg * page_size + v % page_size;
+      }
     }
     sm.idx[i] = v;
     if (v >= 0) last = i;
@@ -358,12 +367,12 @@ hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out,
                              int32_t* retry, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.B * p.Q)), block(kThreads);
   int slot = prof_open("k_sparse_mla", st);
-  hipLaunchKernelGGL(k_sparse_mla<false>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk,
-                     sm_scale * kLog2e, out, lse, row_max, retry);
+  hipLaunchKernelGGL(k_sparse_mla<false>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk, p.page_table,
+                     p.page_size, p.pages_per_seq, p.num_pages, sm_scale * kLog2e, out, lse, row_max, retry);
   prof_close(slot, st);
   slot = prof_open("k_sparse_mla_retry", st);
-  hipLaunchKernelGGL(k_sparse_mla<true>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk,
-                     sm_scale * kLog2e, out, lse, row_max, retry);
+  hipLaunchKernelGGL(k_sparse_mla<true>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk, p.page_table,
+                     p.page_size, p.pages_per_seq, p.num_pages, sm_scale * kLog2e, out, lse, row_max, retry);
   prof_close(slot, st);
   return hipGetLastError();
 }

@@ -233,6 +233,14 @@ size_t dsa_indexer_project_workspace_bytes(const dsa_proj_inputs* in);
  *   indices  [B,Q,topk] int32: positions into the row's sequence; entries
  *            outside 0..N-1 (the Top-K's -1 padding) are skipped, others are
  *            used as given (a repeated entry counts twice)
+ * Paged cache (page_table non-NULL): kv is instead a pool
+ *   kv          [num_pages, page_size, latent_dim+rope_dim] bf16, and
+ *   page_table  [B, pages_per_seq] int32: the pool page holding positions
+ *               j*page_size .. (j+1)*page_size-1 of sequence b
+ * (pages_per_seq >= ceil(N / page_size), num_pages * page_size <= 2^31);
+ * page ids outside 0..num_pages-1 are clamped into it, so a bad table reads
+ * wrong rows but never outside the pool.  With page_table NULL the three
+ * paging fields are ignored and kv is [B,N,latent_dim+rope_dim].
  * heads must be 128, latent_dim 512, rope_dim 64 (DeepSeek-V3.2); topk is
  * 1..2048.                                                                  */
 typedef struct dsa_mla_inputs {
@@ -240,6 +248,8 @@ typedef struct dsa_mla_inputs {
   const void* q;
   const void* kv;
   const int32_t* indices;
+  const int32_t* page_table;
+  int32_t page_size, pages_per_seq, num_pages;
 } dsa_mla_inputs;
 
 /* Sparse MLA attention over the selected positions.

@@ -158,7 +158,7 @@ def test_projection_argument_errors(lib):
 
 def _mla(_lib, **kw):
     d = dict(batch=1, num_q=8, num_k=4096, heads=128, latent_dim=512, rope_dim=64, topk=2048, q=FAKE * 256,
-             kv=FAKE * 512, indices=FAKE * 600)
+             kv=FAKE * 512, indices=FAKE * 600, page_table=None, page_size=0, pages_per_seq=0, num_pages=0)
     d.update(kw)
     return _lib.MlaInputs(**d)
 
@@ -174,6 +174,10 @@ def _mla(_lib, **kw):
         (dict(num_k=0), 1),
         (dict(kv=None), 1),
         (dict(indices=FAKE * 600 + 4), 1),
+        (dict(page_table=FAKE * 650, page_size=64, pages_per_seq=63, num_pages=100), 1),  # 63*64 < 4096
+        (dict(page_table=FAKE * 650, page_size=0, pages_per_seq=64, num_pages=100), 1),
+        (dict(page_table=FAKE * 650 + 8, page_size=64, pages_per_seq=64, num_pages=100), 1),
+        (dict(page_table=FAKE * 650, page_size=1 << 16, pages_per_seq=1, num_pages=1 << 16), 1),  # pool > 2^31 rows
     ],
 )
 def test_sparse_mla_inputs_are_rejected(lib, kw, code):

@@ -124,6 +124,35 @@ def test_consumes_the_topk_output():
     _check_rows(d["q"], d["kv"], idx_np, out, lse, 1.0 / math.sqrt(576), [(0, t) for t in (0, 1, 17, 31, 32, 39)])
 
 
+def test_paged_cache_matches_flat_bit_for_bit():
+    """The same cache stored as shuffled pages of a pool behind a page table
+    gives bit-identical outputs (the gather resolves each position to the
+    same row), including positions in a partial last page."""
+    need_gpu()
+    B, Q, N, k, P = 2, 6, 1000, 256, 64
+    d = inputs.make_mla_inputs(B, Q, N, seed=6)
+    pos = np.array([[999, 998, 500, 63, 64, 0], [999, 640, 639, 1, 200, 999]])
+    idx = inputs.random_selection(B, Q, N, k, pos, seed=6)
+    pps = (N + P - 1) // P  # 16 pages per sequence, the last one partial
+    num_pages = B * pps + 5
+    rng = np.random.default_rng(6)
+    phys = rng.permutation(num_pages)[: B * pps].reshape(B, pps).astype(np.int32)
+    pool = torch.zeros((num_pages, P, 576), dtype=torch.bfloat16)
+    for b in range(B):
+        for j in range(pps):
+            n = min(P, N - j * P)
+            pool[phys[b, j], :n] = d["kv"][b, j * P:j * P + n]
+    q = d["q"].cuda()
+    idx_t = torch.from_numpy(idx).cuda()
+    flat, lflat = dsa.sparse_mla(q, d["kv"].cuda(), idx_t, 1.0 / math.sqrt(576))
+    paged, lpaged = dsa.sparse_mla(q, pool.cuda(), idx_t, 1.0 / math.sqrt(576), page_table=torch.from_numpy(phys).cuda(),
+                                   num_k=N)
+    torch.cuda.synchronize()
+    assert torch.equal(flat.view(torch.int16), paged.view(torch.int16))
+    assert torch.equal(lflat.view(torch.int32), lpaged.view(torch.int32))
+    _check_rows(d["q"], d["kv"], idx, paged, lpaged, 1.0 / math.sqrt(576), [(0, 0), (0, 3), (1, 1), (1, 3)])
+
+
 def test_fullsize_block_sampled_rows():
     """The 128K chunked-prefill block as the benchmark runs it: 8192 rows,
     each with the 2048 positions the indexer selects among 131072 keys;
