@@ -62,7 +62,8 @@ def parse():
     ap.add_argument(
         "--also",
         default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,prefill_32k:topk,"
-        "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla",
+        "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla,"
+        "sparse_mla_decode_64x128k:sparse_mla",
         help="comma list of extra workload[:path] runs (or 'none')",
     )
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -288,7 +289,7 @@ def run_projection(name, steps, warmup):
 
 
 # Sparse MLA workloads: the indexer block whose Top-K the attention consumes.
-MLA_WORKLOADS = {"sparse_mla_128k": "chunked_prefill_128k"}
+MLA_WORKLOADS = {"sparse_mla_128k": "chunked_prefill_128k", "sparse_mla_decode_64x128k": "decode_64x128k"}
 MLA_PAIR_FLOPS = 2 * 128 * (2 * 512 + 64)  # 2h(2 d_c + d_r) per selected pair
 
 

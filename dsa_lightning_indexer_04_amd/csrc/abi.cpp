@@ -290,10 +290,31 @@ int check_mla_inputs(const dsa_mla_inputs* in) {
   return DSA_OK;
 }
 
-size_t mla_workspace(const dsa_mla_inputs* in) {
+// Workspace of the sparse MLA call: per work unit (a row, or a row's tile
+// range when rows are few) the head maxima and a retry flag, and for split
+// rows the partial outputs and (reference, weight sum) pairs.
+struct MlaLayout {
+  int nsplit;
+  size_t row_max, retry, part_o, part_ml, total;
+};
+MlaLayout mla_layout(const dsa_mla_inputs* in) {
   const uint64_t rows = (uint64_t)in->batch * in->num_q;
-  return round_up(rows * 128 * 4, 256) + round_up(rows * 4, 256);
+  MlaLayout L{};
+  L.nsplit = dsa::mla_splits((int)rows);
+  const uint64_t units = rows * L.nsplit;
+  size_t off = 0;
+  L.row_max = off;
+  off += round_up(units * 128 * 4, 256);
+  L.retry = off;
+  off += round_up(units * 4, 256);
+  L.part_o = off;
+  if (L.nsplit > 1) off += round_up(units * 128 * 512 * 4, 256);
+  L.part_ml = off;
+  if (L.nsplit > 1) off += round_up(units * 128 * 2 * 4, 256);
+  L.total = off;
+  return L;
 }
+size_t mla_workspace(const dsa_mla_inputs* in) { return mla_layout(in).total; }
 }  // namespace
 
 extern "C" {
@@ -494,10 +515,11 @@ int dsa_sparse_mla(const dsa_mla_inputs* in, float sm_scale, void* out, float* l
                           in->page_table ? in->pages_per_seq : 1,
                           in->page_table ? in->num_pages : 1};
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* row_max = reinterpret_cast<float*>(ws);
-  int32_t* retry = reinterpret_cast<int32_t*>(ws + round_up(rows * 128 * 4, 256));
-  return hip_status(dsa::launch_sparse_mla(p, sm_scale, static_cast<uint16_t*>(out), lse, row_max, retry,
-                                           static_cast<hipStream_t>(stream)));
+  const MlaLayout L = mla_layout(in);
+  return hip_status(dsa::launch_sparse_mla(
+      p, sm_scale, static_cast<uint16_t*>(out), lse, reinterpret_cast<float*>(ws + L.row_max),
+      reinterpret_cast<int32_t*>(ws + L.retry), L.nsplit, L.nsplit > 1 ? reinterpret_cast<float*>(ws + L.part_o) : nullptr,
+      L.nsplit > 1 ? reinterpret_cast<float*>(ws + L.part_ml) : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 const char* dsa_indexer_error_string(int code) {

@@ -108,10 +108,13 @@ struct MlaProblem {
   const int32_t* page_table;  // [B][pages_per_seq], or null for the flat layout
   int page_size, pages_per_seq, num_pages;
 };
-// out [B*Q][128][512] bf16, lse [B*Q][128] fp32 (may be null); row_max
-// [B*Q][128] fp32 and retry [B*Q] int32 are scratch (the second pass).
+// Work units per row: 1, or (few rows) a split of each row's tiles.
+int mla_splits(int rows);
+// out [B*Q][128][512] bf16, lse [B*Q][128] fp32 (may be null); scratch:
+// row_max [units][128] fp32 and retry [units] int32 (the second pass), and
+// for nsplit > 1 part_o [units][128][512] and part_ml [units][128][2] fp32.
 hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
-                             int32_t* retry, hipStream_t st);
+                             int32_t* retry, int nsplit, float* part_o, float* part_ml, hipStream_t st);
 
 // Candidate capacity (records per row) used by the streaming Top-K.
 inline int stream_capacity(int topk) { return 4 * topk + 128; }

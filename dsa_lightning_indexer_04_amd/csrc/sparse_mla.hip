@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include "kernels.h"
 
 namespace dsa {
@@ -63,6 +65,7 @@ constexpr int kMaxTopk = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRestartMargin = 32.0f;
+constexpr int kMaxSplits = 8;
 constexpr int kAhead = 6;  // LDS operand reads in flight per MFMA chain
 
 // Column of key r (0..31) in a V^T row: k-step g = r/16 covers columns
@@ -86,7 +89,10 @@ struct Smem {
 
 // kRetry = false: first pass over every row; true: recompute the rows the
 // first pass flagged, with the recorded maxima as references.
-template <bool kRetry>
+// kSplit: each workgroup takes one of nsplit consecutive ranges of a row's
+// tiles (few rows, e.g. decode) and writes fp32 partial results (unnormalised
+// output, reference maximum, weight sum) that k_mla_merge combines.
+template <bool kRetry, bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ kv,
                                                             const int32_t* __restrict__ indices, int Q, int N,
@@ -94,11 +100,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
                                                             int page_size, int pages_per_seq, int num_pages,
                                                             float scale_log2, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, float* __restrict__ row_max,
-                                                            int32_t* __restrict__ retry) {
-  if (kRetry && retry[blockIdx.x] == 0) return;  // uniform over the workgroup
+                                                            int32_t* __restrict__ retry, int nsplit,
+                                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
+  // one work unit: a row, or (kSplit) a row's tile range
+  const size_t unit = blockIdx.x;
+  if (kRetry && retry[unit] == 0) return;  // uniform over the workgroup
   __shared__ Smem<2> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const size_t row = blockIdx.x;  // b * Q + t
+  const size_t row = kSplit ? unit / nsplit : unit;  // b * Q + t
+  const int split = kSplit ? (int)(unit % nsplit) : 0;
   const size_t b = row / (size_t)Q;
   // flat layout: the sequence's rows; paged: the pool, rows addressed through the table
   const uint16_t* kvb = page_table ? kv : kv + b * (size_t)N * kRow;
@@ -176,20 +186,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
 #pragma unroll
   for (int i = 0; i < kOBlocks; ++i) o[i] = f32x16{0};
   const int head = wave * 32 + l32;
-  float m_ref = kRetry ? row_max[row * kHeads + head] : -INFINITY;
+  float m_ref = kRetry ? row_max[unit * kHeads + head] : -INFINITY;
   float m_seen = -INFINITY, l_run = 0.0f;
   bool over = false;  // a score exceeded the reference by more than the margin
 
-  if (ntiles > 0) issue_tile(0, 0);
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // this unit's tiles
+  int t0 = 0, t1 = ntiles;
+  if (kSplit) {
+    const int per = (ntiles + nsplit - 1) / nsplit;
+    t0 = min(ntiles, split * per);
+    t1 = min(ntiles, t0 + per);
+  }
+  if (t0 < t1) issue_tile(t0, 0);
+  for (int tile = t0; tile < t1; ++tile) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
     __syncthreads();
-    const int buf = tile & 1;
+    const int buf = (tile - t0) & 1;
     // the next tile's rows load into the other buffer during this whole tile
     // (interleaved with the score MFMAs below); that buffer's last readers
     // finished before the barrier above.  The last tile re-reads itself into
     // the idle buffer.
-    const int nt = tile + 1 < ntiles ? tile + 1 : tile;
+    const int nt = tile + 1 < t1 ? tile + 1 : tile;
     Cursor cur = cursor0();
 
     // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps
@@ -338,8 +355,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     const bool w_over = __builtin_amdgcn_ballot_w64(over) != 0;
     if (lane == 0) sm.vote[wave] = w_over;
     __syncthreads();
-    if (tid == 0) retry[row] = sm.vote[0] | sm.vote[1] | sm.vote[2] | sm.vote[3];
-    if (half == 0) row_max[row * kHeads + head] = m_seen;
+    if (tid == 0) retry[unit] = sm.vote[0] | sm.vote[1] | sm.vote[2] | sm.vote[3];
+    if (half == 0) row_max[unit * kHeads + head] = m_seen;
+  }
+  if (kSplit) {
+    // partial results: the unnormalised output, the reference and the weight sum
+    float* prow = part_o + (unit * kHeads + head) * kDc;
+#pragma unroll
+    for (int blk = 0; blk < kOBlocks; ++blk) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(prow + 32 * blk + 8 * g + 4 * half) =
+            make_float4(o[blk][4 * g], o[blk][4 * g + 1], o[blk][4 * g + 2], o[blk][4 * g + 3]);
+    }
+    if (half == 0) *reinterpret_cast<float2*>(part_ml + (unit * kHeads + head) * 2) = make_float2(m_ref, l_tot);
+    return;
   }
   uint16_t* orow = out + (row * kHeads + head) * kDc;
   auto store_block = [&](int blk, const f32x16& acc) {
@@ -361,19 +391,83 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     lse[row * kHeads + head] = l_tot > 0.0f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// Combines a row's nsplit partial results: with M the largest reference of
+// the splits that saw a selected position, weights 2^(m_s - M), the output is
+// sum_s w_s O_s / sum_s w_s l_s and the log-sum-exp (M + log2 sum_s w_s l_s) ln 2.
+// Each workgroup takes two heads of one row; a thread takes 4 latent dims.
+__global__ __launch_bounds__(256) void k_mla_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                   int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const size_t row = blockIdx.x / (kHeads / 2);
+  const int head = (int)(blockIdx.x % (kHeads / 2)) * 2 + (threadIdx.x >> 7);
+  const int d = (threadIdx.x & 127) * 4;
+  float2 ml[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    ml[sp] = sp < nsplit ? *reinterpret_cast<const float2*>(part_ml + ((row * nsplit + sp) * kHeads + head) * 2)
+                         : make_float2(-INFINITY, 0.0f);
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (ml[sp].y > 0.0f) mmax = fmaxf(mmax, ml[sp].x);
+  float wsum = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    if (sp >= nsplit) break;
+    const float w = ml[sp].y > 0.0f ? __builtin_amdgcn_exp2f(ml[sp].x - mmax) : 0.0f;
+    wsum += w * ml[sp].y;
+    const float4 v = *reinterpret_cast<const float4*>(part_o + ((row * nsplit + sp) * kHeads + head) * kDc + d);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const __bf16 h0 = static_cast<__bf16>(acc.x * inv), h1 = static_cast<__bf16>(acc.y * inv);
+  const __bf16 h2 = static_cast<__bf16>(acc.z * inv), h3 = static_cast<__bf16>(acc.w * inv);
+  *reinterpret_cast<uint2*>(out + (row * kHeads + head) * kDc + d) =
+      make_uint2((uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
+                 (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16));
+  if (lse && (threadIdx.x & 127) == 0)
+    lse[row * kHeads + head] = wsum > 0.0f ? (mmax + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 }  // namespace
 
+int mla_splits(int rows) {
+  int s = 1;
+  if (rows < 256) s = min(kMaxSplits, (512 + rows - 1) / rows);
+  if (const char* e = std::getenv("DSA_SPARSE_MLA_SPLIT")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= kMaxSplits) s = v;
+  }
+  return s;
+}
+
 hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
-                             int32_t* retry, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.B * p.Q)), block(kThreads);
-  int slot = prof_open("k_sparse_mla", st);
-  hipLaunchKernelGGL(k_sparse_mla<false>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk, p.page_table,
-                     p.page_size, p.pages_per_seq, p.num_pages, sm_scale * kLog2e, out, lse, row_max, retry);
-  prof_close(slot, st);
-  slot = prof_open("k_sparse_mla_retry", st);
-  hipLaunchKernelGGL(k_sparse_mla<true>, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk, p.page_table,
-                     p.page_size, p.pages_per_seq, p.num_pages, sm_scale * kLog2e, out, lse, row_max, retry);
-  prof_close(slot, st);
+                             int32_t* retry, int nsplit, float* part_o, float* part_ml, hipStream_t st) {
+  const size_t rows = (size_t)p.B * p.Q;
+  const dim3 grid((unsigned)(rows * nsplit)), block(kThreads);
+  const float sl = sm_scale * kLog2e;
+  auto run = [&](auto first, auto again) {
+    int slot = prof_open("k_sparse_mla", st);
+    hipLaunchKernelGGL(first, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk, p.page_table, p.page_size,
+                       p.pages_per_seq, p.num_pages, sl, out, lse, row_max, retry, nsplit, part_o, part_ml);
+    prof_close(slot, st);
+    slot = prof_open("k_sparse_mla_retry", st);
+    hipLaunchKernelGGL(again, grid, block, 0, st, p.q, p.kv, p.indices, p.Q, p.N, p.topk, p.page_table, p.page_size,
+                       p.pages_per_seq, p.num_pages, sl, out, lse, row_max, retry, nsplit, part_o, part_ml);
+    prof_close(slot, st);
+  };
+  if (nsplit > 1) {
+    run(k_sparse_mla<false, true>, k_sparse_mla<true, true>);
+    const int slot = prof_open("k_mla_merge", st);
+    hipLaunchKernelGGL(k_mla_merge, dim3((unsigned)(rows * (kHeads / 2))), dim3(256), 0, st, part_o, part_ml, nsplit,
+                       out, lse);
+    prof_close(slot, st);
+  } else {
+    run(k_sparse_mla<false, false>, k_sparse_mla<true, false>);
+  }
   return hipGetLastError();
 }
 

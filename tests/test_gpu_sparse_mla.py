@@ -60,8 +60,16 @@ def _run(d, idx_np, sm_scale):
     return out, lse
 
 
-def test_small_rows_with_padding():
+# few rows split each row's tiles over several workgroups and merge the
+# partial results; "1" pins the unsplit kernel
+SPLITS = ["1", "3", None]
+
+
+@pytest.mark.parametrize("split", SPLITS)
+def test_small_rows_with_padding(split, monkeypatch):
     need_gpu()
+    if split:
+        monkeypatch.setenv("DSA_SPARSE_MLA_SPLIT", split)
     B, Q, N, k = 2, 6, 300, 64
     d = inputs.make_mla_inputs(B, Q, N, seed=1)
     pos = np.array([[299, 40, 10, 0, -1, 63], [299, 299, 150, 31, 32, 100]])
@@ -74,9 +82,12 @@ def test_small_rows_with_padding():
     _check_rows(d["q"], d["kv"], idx, out, lse, 1.0 / math.sqrt(576), [(b, t) for b in range(B) for t in range(Q)])
 
 
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("sm_scale", [1.0 / math.sqrt(576), 0.0, 0.2])
-def test_full_topk_rows(sm_scale):
+def test_full_topk_rows(sm_scale, split, monkeypatch):
     need_gpu()
+    if split:
+        monkeypatch.setenv("DSA_SPARSE_MLA_SPLIT", split)
     B, Q, N, k = 1, 5, 5000, 2048
     d = inputs.make_mla_inputs(B, Q, N, seed=2)
     pos = np.array([[4999, 4999, 2047, 2048, 3000]])
@@ -86,12 +97,15 @@ def test_full_topk_rows(sm_scale):
     _check_rows(d["q"], d["kv"], idx, out, lse, sm_scale, [(0, t) for t in range(Q)])
 
 
-def test_second_pass_rows():
+@pytest.mark.parametrize("split", SPLITS)
+def test_second_pass_rows(split, monkeypatch):
     """Rows whose later scores exceed the first tile's maximum by far more
     than 32 (log2 units) are recomputed by the second launch: the first 32
     selected positions get tiny latent rows, the rest full ones, and a large
     sm_scale stretches the score range."""
     need_gpu()
+    if split:
+        monkeypatch.setenv("DSA_SPARSE_MLA_SPLIT", split)
     B, Q, N, k = 1, 4, 600, 256
     d = inputs.make_mla_inputs(B, Q, N, seed=3)
     d["kv"][0, :100] = (d["kv"][0, :100].float() * 0.01).to(torch.bfloat16)
@@ -151,6 +165,26 @@ def test_paged_cache_matches_flat_bit_for_bit():
     assert torch.equal(flat.view(torch.int16), paged.view(torch.int16))
     assert torch.equal(lflat.view(torch.int32), lpaged.view(torch.int32))
     _check_rows(d["q"], d["kv"], idx, paged, lpaged, 1.0 / math.sqrt(576), [(0, 0), (0, 3), (1, 1), (1, 3)])
+
+
+def test_decode_rows_split_and_merged():
+    """Decode shape: one query row per sequence, 8 sequences, top-2048 of
+    6000 keys each; the automatic split (8 ranges of a row's 64 tiles) and the
+    unsplit kernel both match the oracle."""
+    need_gpu()
+    B, Q, N, k = 8, 1, 6000, 2048
+    d = inputs.make_mla_inputs(B, Q, N, seed=8)
+    pos = np.full((B, Q), N - 1)
+    pos[3, 0] = 1000  # fewer visible keys than k: a shorter selection
+    idx = inputs.random_selection(B, Q, N, k, pos, seed=8)
+    res = {}
+    for split in ("auto", "1"):
+        with pytest.MonkeyPatch.context() as mp:
+            if split == "1":
+                mp.setenv("DSA_SPARSE_MLA_SPLIT", "1")
+            res[split] = _run(d, idx, 1.0 / math.sqrt(576))
+    for out, lse in res.values():
+        _check_rows(d["q"], d["kv"], idx, out, lse, 1.0 / math.sqrt(576), [(b, 0) for b in range(B)])
 
 
 def test_fullsize_block_sampled_rows():
