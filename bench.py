@@ -73,14 +73,16 @@ def parse():
     return ap.parse_args()
 
 
-# Source files whose code a kernel is built from (its own file and the headers
-# it includes).  A stored counter reading is valid while their digest holds.
+# Source files whose code a kernel is built from (its own file and the device
+# headers it includes; kernels.h holds only host-side declarations, and no
+# kernel takes one of its structs).  A stored counter reading is valid while
+# their digest holds.
 KERNEL_SOURCES = {
-    "k_topk_stream": ["topk_stream.hip", "stream_common.h", "score_tile.h", "select.h", "kernels.h"],
-    "k_topk_pruned": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h", "kernels.h"],
-    "k_scores": ["scores.hip", "score_tile.h", "kernels.h"],
-    "k_proj_out": ["project.hip", "kernels.h"],
-    "k_sparse_mla": ["sparse_mla.hip", "kernels.h"],
+    "k_topk_stream": ["topk_stream.hip", "stream_common.h", "score_tile.h", "select.h"],
+    "k_topk_pruned": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h"],
+    "k_scores": ["scores.hip", "score_tile.h"],
+    "k_proj_out": ["project.hip"],
+    "k_sparse_mla": ["sparse_mla.hip"],
 }
 
 
