@@ -38,10 +38,10 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("chunked_prefill_128k", "k_topk_stream"): ("f34f99b8e474ab38", 6195342, 1766313),
-    ("chunked_prefill_128k", "k_topk_pruned"): ("1fac2fb6bcbfa0be", 4486728, 742244),
-    ("projection_prefill_128k", "k_proj_out"): ("76da2995e52193f3", 1073178, 553001),
-    ("sparse_mla_128k", "k_sparse_mla"): ("f4c2711096650f76", 6976084, 1116816),
+    ("chunked_prefill_128k", "k_topk_stream"): ("741939aaaf6f03ae", 6107207, 1766224),
+    ("chunked_prefill_128k", "k_topk_pruned"): ("2e255c9d155fe53e", 4490491, 741755),
+    ("projection_prefill_128k", "k_proj_out"): ("2927dc9503ec6217", 1073178, 553001),
+    ("sparse_mla_128k", "k_sparse_mla"): ("3eab888c59823221", 7005983, 1118301),
 }
 PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
 SCREEN_FLOPS = 2 * 128 * 32  # 32-row bound (30 retained heads, aux row, linear row) of one pair
