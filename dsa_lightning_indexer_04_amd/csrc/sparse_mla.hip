@@ -19,8 +19,11 @@
 //     cross-half exchange;
 //   * O^T += V^T P^T over the 16 blocks of 32 latent dims: P^T is taken from
 //     the S^T accumulators as they lie (the contraction runs over the keys in
-//     a permuted order, and V^T is stored in LDS in that same order), V^T is
-//     built from the key-major tile once per tile by all waves.
+//     the order a lane's accumulator holds them), and the V^T operand is read
+//     straight from the key-major tile with transposing LDS reads
+//     (ds_read_b64_tr_b16: in each group of 16 lanes, lane 4r+q supplies 4
+//     consecutive values of row r and lane c receives value c of each of the
+//     4 rows -- here 4 keys of one latent dim).
 // Softmax reference: each head subtracts a fixed reference (its first
 // selected tile's maximum) instead of a running maximum, so the accumulators
 // are never rescaled (a rescale, like any loop restart, makes the register
@@ -43,6 +46,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 128;
 constexpr int kDc = 512;           // latent dims
@@ -58,8 +62,6 @@ constexpr int kThreads = kWaves * 64;
 // kWaves * ceil(37 / kWaves) KiB and the slots past the tile land in it
 constexpr int kLoadsPerWave = (kTile * kSlots * 16 / 1024 + 1 + kWaves - 1) / kWaves;  // 10
 constexpr int kKtBytes = kWaves * kLoadsPerWave * 1024;                                // 40960
-constexpr int kVtStride = 80;                  // bytes per V^T row: 32 keys + 16 B pad
-constexpr int kVtBytes = kDc * kVtStride;      // 40960
 constexpr int kKSteps = kRow / 16;             // 36
 constexpr int kMaxTopk = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -68,20 +70,11 @@ constexpr float kRestartMargin = 32.0f;
 constexpr int kMaxSplits = 8;
 constexpr int kAhead = 6;  // LDS operand reads in flight per MFMA chain
 
-// Column of key r (0..31) in a V^T row: k-step g = r/16 covers columns
-// 16g..16g+15, and its half h (lanes 32h..32h+31 of the MFMA operand) takes
-// keys {16g+4h+0..3, 16g+8+4h+0..3} -- the keys the S^T accumulator of a lane
-// in that half holds -- as 8 consecutive columns.
-__device__ __forceinline__ int vt_col(int r) {
-  return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
-}
-
 constexpr int kOBlocks = kDc / 32;  // 32-dim output blocks per head group
 
 template <int kBufs>
 struct Smem {
   uint8_t kt[kBufs][kKtBytes];
-  uint8_t vt[kVtBytes];
   int32_t idx[kMaxTopk];
   int32_t last[kWaves];
   int32_t vote[kWaves];  // a wave saw a score above its reference + margin
@@ -210,25 +203,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
     Cursor cur = cursor0();
 
     // ---- S^T = K Q^T (32 keys x 32 heads); operands read kAhead k-steps
-    // ahead.  The fenced steps also carry this tile's V^T build (its LDS
-    // reads at step 6i, the permutes and writes 4 steps later) and the next
-    // tile's gather (one load every third step): the MFMAs run while these
-    // issue.
+    // ahead.  The fenced steps also carry the next tile's gather (one load
+    // every third step): the MFMAs run while these issue.
     f32x16 s = f32x16{0};
     const uint8_t* ka = &sm.kt[buf][(l32 * kSlots + half) * 16];
     {
-      // V^T[d][vt_col(r)] for d < 512 from pairs of keys (2p, 2p+1), chunk c
-      // = c0 + 16 i (dims 8c .. 8c+7) for task i.  The per-lane bases are made
-      // opaque so the addresses are formed with immediate offsets instead of
-      // being hoisted out of the tile loop (~40 registers across it).
-      const int p = lane & 15, c0 = wave * 4 + (lane >> 4);
-      uint32_t rd = (uint32_t)(((2 * p) * kSlots + c0) * 16 + buf * kKtBytes);
-      uint32_t wr = (uint32_t)(8 * c0 * kVtStride + 2 * vt_col(2 * p));
-      asm volatile("" : "+v"(rd), "+v"(wr));
-      const uint8_t* kt0 = reinterpret_cast<const uint8_t*>(sm.kt) + rd;
-      uint8_t* vt0 = sm.vt + wr;
-      u32x4 va0, vb0;  // the task in flight: chunk of key 2p, chunk of key 2p+1
-
       u32x4 ar[kAhead];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -240,33 +219,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
                                                     __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
         if (kk + kAhead < kKSteps) ar[kk % kAhead] = *reinterpret_cast<const u32x4*>(ka + (kk + kAhead) * 32);
         if (kk % 3 == 1 && kk / 3 < kLoadsPerWave) issue_one(nt, buf ^ 1, kk / 3, cur);
-        if (kk % 6 == 0 && kk / 6 < 4) {
-          const int i = kk / 6;
-          va0 = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16);
-          vb0 = *reinterpret_cast<const u32x4*>(kt0 + i * 16 * 16 + kSlots * 16);
-        }
-        if (kk % 6 == 4 && kk / 6 < 4) {
-          const int i = kk / 6;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // dims 8c+2j (low halves) and 8c+2j+1 (high halves) of keys 2p, 2p+1
-            const uint32_t lo = __builtin_amdgcn_perm(vb0[j], va0[j], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(vb0[j], va0[j], 0x07060302u);
-            *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j) * kVtStride) = lo;
-            *reinterpret_cast<uint32_t*>(vt0 + (i * 16 * 8 + 2 * j + 1) * kVtStride) = hi;
-          }
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // V^T complete for all waves.  A plain barrier after this wave's LDS
-    // writes: a __syncthreads() fence would also wait for the next tile's
-    // loads, which nothing before the next tile reads.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
     // ---- online softmax per head (lane l%32), base 2
     // lane holds keys 8(v/4) + 4*half + v%4 of the tile; bit r of `valid`
     // says whether the tile's key r is a selected position
@@ -311,20 +266,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
       pb[0] = u32x4{w[0], w[1], w[2], w[3]};
     }
     // ---- O^T += V^T P^T: 16 blocks of 32 latent dims, 2 k-steps of 16 keys
-    // (k-step outer, so consecutive MFMAs update different blocks); operands
-    // read kAhead steps ahead; the second k-step's weights are formed during
-    // the first k-step's MFMAs
-    const uint8_t* va = &sm.vt[l32 * kVtStride + 16 * half];
+    // (k-step outer, so consecutive MFMAs update different blocks).  The
+    // operand of lane l (latent dim 32 blk + l%32, k-half h = l/32) is keys
+    // 16 g + 4h + 0..3 and 16 g + 8 + 4h + 0..3 of that dim: two transposing
+    // reads, in which lane 4r+q of each 16-lane group supplies dims
+    // 16 (group%2) + 4q .. +3 of key 16 g + 4h + r (+8).  Read kAhead steps ahead.
     {
+      const int grp = lane >> 4, r = (lane >> 2) & 3, qd = lane & 3;
+      uint32_t vb = (uint32_t)(buf * kKtBytes + (4 * (grp >> 1) + r) * kSlots * 16 + (16 * (grp & 1) + 4 * qd) * 2);
+      asm volatile("" : "+v"(vb));
+      const uint8_t* vbase = reinterpret_cast<const uint8_t*>(sm.kt) + vb;
+      auto vread = [&](int st) {
+        const int blk = st % kOBlocks, g = st / kOBlocks;
+        const uint8_t* a0 = vbase + 16 * g * kSlots * 16 + 64 * blk;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(a0 + 8 * kSlots * 16));
+        return u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                     (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                     (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                     (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      };
       constexpr int kSteps = 2 * kOBlocks;
-      // step st: k-step g = st / kOBlocks, block st % kOBlocks
-      auto vaddr = [&](int blk, int g) { return va + blk * 32 * kVtStride + 32 * g; };
       u32x4 ar[kAhead];
       uint32_t w1[4];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i)
-        ar[i] = *reinterpret_cast<const u32x4*>(vaddr(i % kOBlocks, i / kOBlocks));
+      for (int i = 0; i < kAhead; ++i) ar[i] = vread(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
@@ -332,9 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_sparse_mla(const uint16_t* __re
         if (st == kOBlocks) pb[1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
         o[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ar[st % kAhead]),
                                                          __builtin_bit_cast(bf16x8, pb[g]), o[blk], 0, 0, 0);
-        const int nx = st + kAhead;
-        if (nx < kSteps)
-          ar[st % kAhead] = *reinterpret_cast<const u32x4*>(vaddr(nx % kOBlocks, nx / kOBlocks));
+        if (st + kAhead < kSteps) ar[st % kAhead] = vread(st + kAhead);
         if (st < 4) weights(1, st, w1[st]);
         __builtin_amdgcn_sched_barrier(0);
       }
