@@ -41,7 +41,7 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("741939aaaf6f03ae", 6107207, 1766224),
     ("chunked_prefill_128k", "k_topk_pruned"): ("2e255c9d155fe53e", 4490491, 741755),
     ("projection_prefill_128k", "k_proj_out"): ("2927dc9503ec6217", 1073178, 553001),
-    ("sparse_mla_128k", "k_sparse_mla"): ("3eab888c59823221", 7005983, 1118301),
+    ("sparse_mla_128k", "k_sparse_mla"): ("9493b6d2a226cf4a", 6478318, 1127364),
 }
 PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
 SCREEN_FLOPS = 2 * 128 * 32  # 32-row bound (30 retained heads, aux row, linear row) of one pair
