@@ -60,3 +60,31 @@ def test_workload_pair_counts():
     assert wl["decode_64x128k"].visible_pairs == 8388608
     assert wl["chunked_prefill_128k"].visible_pairs == 1040191488
     assert wl["context_1m_fp8"].visible_pairs == 17045659648
+
+
+def test_projection_inputs():
+    a = inputs.make_projection_inputs(6, 256, 128, seed=2)
+    b = inputs.make_projection_inputs(6, 256, 128, seed=2)
+    for key in ("c_q", "x", "w_iq", "w_ik", "w_iw"):
+        assert torch.equal(a[key], b[key]) and a[key].dtype == torch.bfloat16
+    assert a["c_q"].shape == (6, 128) and a["x"].shape == (6, 256)
+    assert a["w_iq"].shape == (64 * 128, 128) and a["w_ik"].shape == (128, 256) and a["w_iw"].shape == (64, 256)
+    # N(0, 1/fan_in) weights: the projections have about unit variance
+    q = a["c_q"].float() @ a["w_iq"].float().T
+    assert 0.7 < float(q.std()) < 1.3
+
+
+def test_mla_inputs_and_selection():
+    d = inputs.make_mla_inputs(2, 3, 100, seed=1)
+    assert d["q"].shape == (2, 3, 128, 576) and d["kv"].shape == (2, 100, 576)
+    assert d["q"].dtype == torch.bfloat16 and 0.9 < float(d["kv"].float().std()) < 1.1
+    pos = np.array([[99, 5, -1], [10, 99, 0]])
+    sel = inputs.random_selection(2, 3, 100, 16, pos, seed=1)
+    assert sel.shape == (2, 3, 16) and sel.dtype == np.int32
+    for b in range(2):
+        for t in range(3):
+            vis = max(0, min(pos[b, t] + 1, 100))
+            m = min(16, vis)
+            row = sel[b, t]
+            assert np.all(row[m:] == -1)
+            assert len(set(row[:m].tolist())) == m and np.all((row[:m] >= 0) & (row[:m] < vis))
