@@ -26,6 +26,11 @@ Two value distributions are provided:
 
 fp8 inputs use one fp32 scale per key row and one per query token (shared by
 its 64 heads): scale = amax / 448, codes = RNE(x / scale) saturated to +-448.
+
+Around the indexer: ``make_projection_inputs`` draws the bf16 operands of the
+indexer projections (activations N(0,1), weights N(0, 1/fan_in)), and
+``make_mla_inputs`` / ``random_selection`` draw the sparse MLA attention's
+query block, latent cache and selected positions.
 """
 from __future__ import annotations
 
