@@ -116,7 +116,9 @@ int mla_splits(int rows);
 hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
                              int32_t* retry, int nsplit, float* part_o, float* part_ml, hipStream_t st);
 
-// Candidate capacity (records per row) used by the streaming Top-K.
-inline int stream_capacity(int topk) { return 4 * topk + 128; }
+// Candidate capacity (records per row) used by the streaming Top-K: a cut
+// keeps at most topk + 512 records, so one more tile of up to 128 keys always
+// fits behind it.
+inline int stream_capacity(int topk) { return 4 * topk + 640; }
 
 }  // namespace dsa

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(PrunedGeom<DT>::kWaves * 64) __attribute__((amdgpu_
   __shared__ float kscale_tile[kSlots][KT];
   __shared__ float knorm_tile[kSlots][KT];
   __shared__ uint32_t sbits_tile[kSlots][64];
-  __shared__ uint32_t hist[kWaves][256];      // radix-select bins (8-bit digits)
+  __shared__ __align__(16) uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits), threshold histogram
   __shared__ uint64_t stage[kWaves][kStage];  // candidate records awaiting a flush
   __shared__ int32_t squeue[kWaves][QCAP + 64];  // survivor keys awaiting refinement (+ scratch)
   __shared__ uint32_t toff[kWaves][Tile::PER_WAVE * 64];

@@ -5,9 +5,12 @@
 // "Full-prefix index scoring"); this kernel does that without ever storing
 // the score matrix.  Each row keeps a running threshold and a candidate
 // buffer of records in global memory; a key is appended only if its record
-// is not below the threshold, and when the buffer fills it is cut back to the
-// row's best `topk` by radix select, which also raises the threshold.  At the
-// end the buffer's best min(topk, visible) records are the exact Top-K.
+// is not below the threshold.  Every 32 kept records the threshold rises to
+// within one bin of the K-th best record seen, read off a per-row histogram
+// of the kept score codes; when the buffer fills it is compacted to the
+// records above the threshold and, if still too full, cut by radix select.
+// At the end the buffer's best min(topk, visible) records are the exact
+// Top-K.
 //
 // Organisation (gfx950):
 //   workgroup = 4 waves = 4 consecutive query rows of one sequence, one row
@@ -18,11 +21,11 @@
 //   key tiles (16 KiB: 64 bf16 or 128 fp8 keys) rotate through three LDS
 //   slots: the tile after next streams from global memory straight into
 //   LDS while the current one is scored, in a padded key-major layout so
-//   the column reads are bank-conflict free; all 8 waves read each tile,
-//   and each wave's key fragment for the next 32 keys is read while the
-//   current 32 are multiplied.
-//   After the head sum every lane holds the score of key l%32, so the
-//   threshold test, ballot and append are one wave op on lanes 0..31.
+//   the column reads are bank-conflict free; the workgroup's 4 waves read
+//   each tile, and each wave's key fragment for the next 32 keys is read
+//   while the current 32 are multiplied.
+//   After the head sum and one cross-half exchange every lane holds the
+//   score of key l%32; two blocks are appended together, one key per lane.
 //   Workgroups are issued longest-prefix first (causal imbalance).
 #include <math.h>
 
@@ -40,48 +43,50 @@ struct BlockAcc {
   f32x16 s0, s1;  // heads 0..31 / 32..63 of one query against 32 keys
 };
 
-// Candidate state of one row (one wave): cnt records in the global buffer,
-// nst in the LDS stage, running threshold thr and its float floor thr_f.
-struct Cands {
-  int cnt, nst;
-  uint64_t thr;
-  float thr_f;
-};
-
 // Append the records of two scored 32-key blocks at once: lane l holds the
 // score of key `key` (the earlier block in lanes 0..31, the later one in
 // 32..63; `live` masks keys that are not visible).  A key is kept if its
 // score reaches thr_f, the float floor of the threshold record: that keeps
 // every record >= thr (and at most a few equal-score records below it,
-// which the exact selections drop).  Branch-free, so the scheduler can
-// overlap it with the next block's MFMAs: every lane stores its record,
-// the kept ones to the next stage slots and the others to their own slot of
-// the stage's scratch tail (stage[dummy + lane]).  The stage has room: the
-// caller flushes it and cuts the buffer at tile boundaries.
-__device__ __forceinline__ void append_pair(Cands& c, float s, int key, bool live, uint64_t* stage, int dummy,
-                                            int lane) {
-  const bool take = live && s >= c.thr_f;
+// which the exact selections drop).  The stores are branch-free, so the
+// scheduler can overlap them with the next block's MFMAs: every lane stores
+// its record, the kept ones to the next stage slots and the others to their
+// own slot of the stage's scratch tail (stage[dummy + lane]); each kept
+// record also counts in the row's threshold histogram.  The stage has room:
+// the caller flushes it at tile boundaries.
+__device__ __forceinline__ void append_pair(RowState& rs, float thr_f, float s, int key, bool live, uint64_t* stage,
+                                            uint32_t* hist, int dummy, int lane) {
+  const bool take = live && s >= thr_f;
   const uint64_t bal = __ballot(take);
   const int before =
       (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-  stage[take ? c.nst + before : dummy + lane] = make_record(s, (uint32_t)key);
-  c.nst += __popcll(bal);
+  const uint64_t rec = make_record(s, (uint32_t)key);
+  stage[take ? rs.nst + before : dummy + lane] = rec;
+  if (take) atomicAdd(&hist[thr_bin((uint32_t)(rec >> 32), rs.base, rs.shift)], 1u);
+  const int n = __popcll(bal);
+  rs.nst += n;
+  rs.added += n;
 }
 
-// Flush the stage to the buffer; if `room` more records could overflow the
-// buffer, cut it back (radix select) to between topk and topk + (cap -
-// topk) / 8 records and raise the threshold to the cut's boundary.
-__device__ __forceinline__ void flush_and_cut(Cands& c, uint64_t* buf, const uint64_t* stage, uint32_t* hist,
-                                              int topk, int cap, int room, int lane) {
-  if (c.nst) {
-    c.cnt = flush_stage(buf, c.cnt, stage, c.nst, lane);
-    c.nst = 0;
+// Tile-boundary bookkeeping of a row: flush the stage to the buffer; every
+// kRaiseEvery kept records raise the threshold from the histogram (to within
+// one bin of the K-th best record seen, no buffer traffic); if `room` more
+// records could overflow the buffer, rebuild: keep the records >= thr, cut
+// them by radix select when too many remain, and rebuild the histogram with
+// bins fitted to the kept records.
+__device__ __forceinline__ void tile_bookkeeping(RowState& rs, float& thr_f, uint64_t* stage, uint32_t* hist,
+                                                 int topk, int cap, int room, int lane) {
+  if (rs.nst) {
+    rs.cnt = flush_stage(rs.buf, rs.cnt, stage, rs.nst, lane);
+    rs.nst = 0;
   }
-  if (c.cnt > cap - room) {
-    const Cut cut = cut_candidates_d8(buf, c.cnt, stage, 0, hist, topk, topk + (cap - topk) / 8, lane);
-    c.cnt = cut.cnt;
-    c.thr = cut.thr;
-    c.thr_f = record_floor(c.thr);
+  if (rs.added >= kRaiseEvery) {
+    raise_threshold(rs, hist, topk, lane);
+    thr_f = record_floor(rs.thr);
+  }
+  if (rs.cnt > cap - room) {
+    apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, stage, 0, hist, rs.thr, topk, cut_goal(topk, cap), lane));
+    thr_f = record_floor(rs.thr);
   }
 }
 
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int NSB = KT / 32;   // 32-key blocks per tile (even)
   __shared__ u32x4 ktile[kSlots][direct_slots(kTileBytes)];
   __shared__ float kscale_tile[kSlots][KT];
-  __shared__ uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits)
+  __shared__ __align__(16) uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits), threshold histogram
   __shared__ uint64_t stage[kWaves][KT + 64];  // KT records + 64 scratch slots
   __shared__ uint32_t toff[kWaves][Tile::PER_WAVE * 64];  // tile-load source offsets
 
@@ -119,8 +124,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   uint32_t* my_hist = hist[wave];
   uint64_t* my_stage = stage[wave];
-  uint64_t* buf = cand + row * (size_t)cap;
-  Cands cs{0, 0, 0, -INFINITY};
+  // threshold histogram: coarse bins over the whole code range (code >> 24)
+  // until the first rebuild
+  for (int i = lane; i < 256; i += 64) my_hist[i] = 0u;
+  RowState rs{cand + row * (size_t)cap, 0, 0, 0, 0u, 24, 0};
+  float thr_f = -INFINITY;
   const uint8_t* kbase = k + (size_t)b * N * RB;
   const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
 
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int nxt = cur == kSlots - 1 ? 0 : cur + 1;       // slot of tile ti+1
     const int spare = nxt == kSlots - 1 ? 0 : nxt + 1;     // slot of tile ti-1, refilled with ti+2
-    flush_and_cut(cs, buf, my_stage, my_hist, topk, cap, KT, lane);
+    tile_bookkeeping(rs, thr_f, my_stage, my_hist, topk, cap, KT, lane);
     if (ti + 2 < ntiles) {
       tl.load(ktile[spare], kbase, (ti + 2) * KT, N, lane);
       if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, (ti + 2) * KT, N, lane);
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         s_prev = s;
       } else {
         const int key = 32 * (j - 2) + lane;
-        append_pair(cs, lane < 32 ? s_prev : s, key, j >= 2 && key < vis, my_stage, KT, lane);
+        append_pair(rs, thr_f, lane < 32 ? s_prev : s, key, j >= 2 && key < vis, my_stage, my_hist, KT, lane);
       }
     }
     wait_vmem_all();  // this wave's loads of tile ti+2 have landed
@@ -190,13 +198,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
   if (!valid) return;
   if (ntiles > 0) {  // drain: the last block, j = ntiles * NSB - 1 (odd), is in acc[1]
-    flush_and_cut(cs, buf, my_stage, my_hist, topk, cap, 64, lane);
+    tile_bookkeeping(rs, thr_f, my_stage, my_hist, topk, cap, 64, lane);
     float s = combine_single(head_partial(acc[1].s0, acc[1].s1, qs.wl));
     if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscl[1]);
     const int key = 32 * (ntiles * NSB - 2) + lane;
-    append_pair(cs, lane < 32 ? s_prev : s, key, key < vis, my_stage, KT, lane);
+    append_pair(rs, thr_f, lane < 32 ? s_prev : s, key, key < vis, my_stage, my_hist, KT, lane);
   }
-  emit_topk_d8(buf, cs.cnt, my_stage, cs.nst, my_hist, topk, out_idx + row * (size_t)topk,
+  emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
                out_score ? out_score + row * (size_t)topk : nullptr, lane);
 }
 

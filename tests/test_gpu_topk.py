@@ -114,3 +114,40 @@ def test_topk_paths_agree_on_a_prefill_block():
     a = torch.sort(out["split"][0], -1).values
     b = torch.sort(out["stream"][0], -1).values
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("path", ["split", "stream"])
+@pytest.mark.parametrize("k", [1, 2, 5, 33])
+def test_topk_rising_scores_small_k(path, k):
+    """Scores that rise with the key index: every fp8 key tile beats the
+    running threshold, the worst case for a row's candidate buffer.  All
+    codes are 1.0 and the key scales are 1 + s/1024 (exact in fp32), so
+    key s scores 8192 * (1 + s/1024) and a row at position p selects the
+    keys p - k + 1 .. p (those that exist)."""
+    need_gpu()
+    Q, N = 12, 3000
+    pos = torch.tensor([[0, 1, 4, 127, 128, 129, 700, 1500, 2047, 2500, 2998, 2999]], dtype=torch.int32)
+    d = {
+        "q": torch.full((1, Q, 64, 128), 1.0).to(torch.float8_e4m3fn),
+        "k": torch.full((1, N, 128), 1.0).to(torch.float8_e4m3fn),
+        "w": torch.ones(1, Q, 64),
+        "pos": pos,
+        "q_scale": torch.ones(1, Q),
+        "k_scale": (1.0 + torch.arange(N, dtype=torch.float32) / 1024)[None],
+    }
+    dd = to_device(d)
+    log(f"topk rising scores {path} k={k}")
+    set_path(path)
+    try:
+        args, kw = call_args(dd)
+        idx, sc = dsa.topk(*args, k, **kw)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    finally:
+        set_path(None)
+    for t in range(Q):
+        p = int(pos[0, t])
+        want = np.arange(max(0, p - k + 1), p + 1)
+        n = want.size
+        assert np.array_equal(np.sort(idx[0, t, :n]), want), (t, idx[0, t])
+        assert np.all(idx[0, t, n:] == -1), t
+        np.testing.assert_array_equal(np.sort(sc[0, t, :n]), 8192.0 * (1.0 + want / 1024).astype(np.float32))
