@@ -14,8 +14,10 @@
 //   rows (M) = heads: two 32-row blocks per query (heads 0..31, 32..63)
 //   cols (N) = 32 keys
 //   K        = the 128 feature dims.  Both operands use the same lane->dim
-//              permutation: lane l (half h = l/32) feeds dims 64h..64h+63,
-//              so each lane reads one contiguous run of its row.
+//              permutation: k-step i takes dims 16i..16i+15 (fp8: 64i..
+//              64i+63), lane l (half h = l/32) the lower or upper half of
+//              them, so the two lanes that feed one row in a step read
+//              adjacent 16 (fp8: 32) bytes of it.
 // bf16: v_mfma_f32_32x32x16_bf16, 8 k-steps of 16 (lane: 8 dims per step).
 // fp8 : v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales, 2 k-steps of 64
 //       (lane: 32 dims per step), OCP e4m3 operands.
@@ -48,7 +50,7 @@ template <>
 struct Frag<kBF16> {
   static constexpr int kSteps = 8;        // 8 x (32x32x16)
   static constexpr int kRowBytes = 256;   // 128 bf16
-  static constexpr int kLaneBytes = 128;  // contiguous bytes one lane feeds
+  static constexpr int kLaneBytes = 128;  // bytes one lane feeds over the k-steps
   u32x4 v[8];
 };
 
@@ -62,16 +64,19 @@ struct Frag<kFP8> {
 
 // Load one lane's fragment of a row (query head row or key row) from any
 // address space: `row` points at the start of the row (kRowBytes long).
+// Step i of half h is 16-byte chunk 2i + h (bf16), chunks 4i + 2h and
+// 4i + 2h + 1 (fp8).
 template <int DT>
 __device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* row, int lane) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(row + (lane >> 5) * Frag<DT>::kLaneBytes);
   if constexpr (DT == kBF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row) + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.v[i] = p[i];
+    for (int i = 0; i < 8; ++i) f.v[i] = p[2 * i];
   } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row) + 2 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      u32x4 lo = p[2 * i], hi = p[2 * i + 1];
+      u32x4 lo = p[4 * i], hi = p[4 * i + 1];
       f.v[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   }

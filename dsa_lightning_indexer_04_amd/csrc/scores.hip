@@ -16,6 +16,8 @@
 
 namespace dsa {
 
+constexpr int kDepth = 2;  // key blocks per wave in flight (k_scores)
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_scores(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                                                 const float* __restrict__ w, const float* __restrict__ qsc,
@@ -34,19 +36,21 @@ __global__ __launch_bounds__(256) void k_scores(const uint8_t* __restrict__ q, c
 
   QuerySide<DT> qs;
   load_query<DT>(qs, q + row * kHeads * RB, w + row * kHeads, lane);
-  // Keys stream straight from HBM: block kb + 128 (this wave's next) is
-  // loaded while block kb is scored, so two blocks per wave are in flight.
-  // The prefetch is unconditional (a block past the end reads key N - 1),
-  // which keeps the number of loads in flight fixed for the waits.
+  // Keys stream straight from HBM: a wave scores the 32-key blocks k0 +
+  // 32 wave + 128 m, m = 0, 1, ..., with the next kDepth - 1 of them already
+  // loading into a ring of fragments.  The prefetch is unconditional (a block
+  // past the end reads key N - 1), which keeps the number of loads in flight
+  // fixed for the waits.
   const int lk = lane & 31;
-  Frag<DT> f[2];
+  Frag<DT> f[kDepth];
   int kb = k0 + 32 * wave;
-  load_frag<DT>(f[0], kbase + (size_t)min(kb + lk, N - 1) * RB, lane);
-  for (; kb < k1; kb += 256) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kDepth - 1; ++h) load_frag<DT>(f[h], kbase + (size_t)min(kb + 128 * h + lk, N - 1) * RB, lane);
+  for (; kb < k1; kb += 128 * kDepth) {
+#pragma unroll
+    for (int h = 0; h < kDepth; ++h) {
       const int kc = kb + 128 * h;  // this block
-      load_frag<DT>(f[h ^ 1], kbase + (size_t)min(kc + 128 + lk, N - 1) * RB, lane);
+      load_frag<DT>(f[(h + kDepth - 1) % kDepth], kbase + (size_t)min(kc + 128 * (kDepth - 1) + lk, N - 1) * RB, lane);
       if (kc < k1) {
         const int key = kc + lk;
         float s = -INFINITY;

@@ -262,14 +262,14 @@ struct DirectTile {
 #pragma unroll
     for (int i = 0; i < Frag<DT>::kSteps; ++i) frag_step(f, slot, key, i, lane);
   }
-  // k-step i of that fragment.
+  // k-step i of that fragment (the chunk order of load_frag).
   __device__ __forceinline__ static void frag_step(Frag<DT>& f, const u32x4* slot, int key, int i, int lane) {
-    constexpr int CPL = Frag<DT>::kLaneBytes / 16;
-    const u32x4* row = slot + key * (CPR + 1) + (lane >> 5) * CPL;
     if constexpr (DT == kBF16) {
-      f.v[i] = row[i];
+      const u32x4* row = slot + key * (CPR + 1) + (lane >> 5);
+      f.v[i] = row[2 * i];
     } else {
-      const u32x4 lo = row[2 * i], hi = row[2 * i + 1];
+      const u32x4* row = slot + key * (CPR + 1) + 2 * (lane >> 5);
+      const u32x4 lo = row[4 * i], hi = row[4 * i + 1];
       f.v[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   }

@@ -51,24 +51,24 @@ struct BlockAcc {
 // which the exact selections drop).  The stores are branch-free, so the
 // scheduler can overlap them with the next block's MFMAs: every lane stores
 // its record, the kept ones to the next stage slots and the others to their
-// own slot of the stage's scratch tail (stage[dummy + lane]); each kept
-// record also counts in the row's threshold histogram.  The stage has room:
-// the caller flushes it at tile boundaries.
+// own slot of the stage's scratch tail (stage[dummy + lane]).  The stage has
+// room: the caller flushes it at tile boundaries.
 __device__ __forceinline__ void append_pair(RowState& rs, float thr_f, float s, int key, bool live, uint64_t* stage,
-                                            uint32_t* hist, int dummy, int lane) {
+                                            int dummy, int lane) {
   const bool take = live && s >= thr_f;
   const uint64_t bal = __ballot(take);
   const int before =
       (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
   const uint64_t rec = make_record(s, (uint32_t)key);
   stage[take ? rs.nst + before : dummy + lane] = rec;
-  if (take) atomicAdd(&hist[thr_bin((uint32_t)(rec >> 32), rs.base, rs.shift)], 1u);
   const int n = __popcll(bal);
   rs.nst += n;
   rs.added += n;
 }
 
-// Tile-boundary bookkeeping of a row: flush the stage to the buffer; every
+// Tile-boundary bookkeeping of a row: count the staged records in the
+// threshold histogram (here, where no key-tile load is in flight, rather than
+// at each append) and flush them to the buffer; every
 // kRaiseEvery kept records raise the threshold from the histogram (to within
 // one bin of the K-th best record seen, no buffer traffic); if `room` more
 // records could overflow the buffer, rebuild: keep the records >= thr, cut
@@ -77,6 +77,7 @@ __device__ __forceinline__ void append_pair(RowState& rs, float thr_f, float s, 
 __device__ __forceinline__ void tile_bookkeeping(RowState& rs, float& thr_f, uint64_t* stage, uint32_t* hist,
                                                  int topk, int cap, int room, int lane) {
   if (rs.nst) {
+    for (int i = lane; i < rs.nst; i += 64) atomicAdd(&hist[thr_bin((uint32_t)(stage[i] >> 32), rs.base, rs.shift)], 1u);
     rs.cnt = flush_stage(rs.buf, rs.cnt, stage, rs.nst, lane);
     rs.nst = 0;
   }
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         s_prev = s;
       } else {
         const int key = 32 * (j - 2) + lane;
-        append_pair(rs, thr_f, lane < 32 ? s_prev : s, key, j >= 2 && key < vis, my_stage, my_hist, KT, lane);
+        append_pair(rs, thr_f, lane < 32 ? s_prev : s, key, j >= 2 && key < vis, my_stage, KT, lane);
       }
     }
     wait_vmem_all();  // this wave's loads of tile ti+2 have landed
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     float s = combine_single(head_partial(acc[1].s0, acc[1].s1, qs.wl));
     if constexpr (DT == kFP8) s = apply_scales(s, qscale, kscl[1]);
     const int key = 32 * (ntiles * NSB - 2) + lane;
-    append_pair(rs, thr_f, lane < 32 ? s_prev : s, key, key < vis, my_stage, my_hist, KT, lane);
+    append_pair(rs, thr_f, lane < 32 ? s_prev : s, key, key < vis, my_stage, KT, lane);
   }
   emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
                out_score ? out_score + row * (size_t)topk : nullptr, lane);
