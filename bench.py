@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("chunked_prefill_128k", "k_topk_stream"): ("741939aaaf6f03ae", 6107207, 1766224),
-    ("chunked_prefill_128k", "k_topk_pruned"): ("2e255c9d155fe53e", 4490491, 741755),
+    ("chunked_prefill_128k", "k_topk_stream"): ("b2d6f7e088e5983d", 2284446, 1380304),
+    ("chunked_prefill_128k", "k_topk_pruned"): ("3dc7434b21e69dfc", 4541126, 745897),
     ("projection_prefill_128k", "k_proj_out"): ("2927dc9503ec6217", 1073178, 553001),
     ("sparse_mla_128k", "k_sparse_mla"): ("9493b6d2a226cf4a", 6478318, 1127364),
 }
