@@ -77,9 +77,10 @@ __device__ __forceinline__ int cut_goal(int topk, int cap) { return topk + min(k
 // Candidate state of one row (wave-uniform).  Besides the buffer (cnt
 // records, nst more in the LDS stage) and the threshold thr, the row keeps a
 // threshold histogram: 256 LDS bins over the score code c (the high half of
-// a record), bin min(255, (c - base) >> shift), counting every record in the
-// buffer and the stage; base never exceeds the threshold's code, so every
-// kept record lands in a bin.
+// a record), bin min(255, (c - base) >> shift), counting every kept record
+// (the pruned kernel counts a record when it stages it, the streaming kernel
+// when it flushes it, before any threshold raise reads the bins); base never
+// exceeds the threshold's code, so every kept record lands in a bin.
 struct RowState {
   uint64_t* buf;
   int cnt, nst;
