@@ -44,6 +44,7 @@ CASES = [
     (2, 12, 2500, 100, "fp8", "clustered", 400),
     (1, 9, 900, 200, "bf16", "clustered", 300),  # seeds fewer than... k < seeds < N
     (1, 10, 500, 64, "bf16", "iid", 32),  # fewer seeds than k: no threshold from seeds
+    (1, 8, 12000, 4096, "bf16", "clustered", 6000),  # the largest supported k
 ]
 
 

@@ -44,6 +44,8 @@ CASES = [
     (1, 12, 400, 500, "bf16", "iid"),  # fewer visible keys than k
     (2, 10, 1100, 128, "fp8", "clustered"),
     (2, 7, 1001, 50, "bf16", "iid"),  # odd row length: unaligned score rows on the split path
+    (1, 6, 9000, 4096, "bf16", "clustered"),  # the largest supported k
+    (1, 5, 7000, 4096, "fp8", "iid"),  # the largest supported k, fp8 (128-key tiles)
 ]
 
 
