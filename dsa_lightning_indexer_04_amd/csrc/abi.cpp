@@ -110,7 +110,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t topk_workspace(const dsa_indexer_inputs* in, int32_t topk) {
   const uint64_t rows = (uint64_t)in->batch * in->num_q;
-  if (use_split_rows(in)) return round_up(rows * in->num_k * 4, 256);
+  if (use_split_rows(in)) return round_up(rows * in->num_k * 4, 256) + rows * dsa::kRowHistBins * 4;
   return round_up(rows * (uint64_t)dsa::stream_capacity(topk) * 8, 256);
 }
 
@@ -124,9 +124,12 @@ int run_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float
   const dsa::Problem p = problem_of(in);
   if (use_split_rows(in)) {
     float* rows = static_cast<float*>(workspace);
-    int rc = hip_status(dsa::launch_scores(p, rows, st));
+    const uint64_t nrows = (uint64_t)in->batch * in->num_q;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
+                                                 round_up(nrows * in->num_k * 4, 256));
+    int rc = hip_status(dsa::launch_scores(p, rows, hist, st));
     if (rc) return rc;
-    return hip_status(dsa::launch_select_rows(p, rows, topk, out_idx, out_score, st));
+    return hip_status(dsa::launch_select_rows(p, rows, hist, topk, out_idx, out_score, st));
   }
   return hip_status(dsa::launch_topk_stream(p, topk, dsa::stream_capacity(topk), static_cast<uint64_t*>(workspace),
                                             out_idx, out_score, st));
@@ -325,7 +328,7 @@ int dsa_indexer_scores(const dsa_indexer_inputs* in, float* scores, void* stream
   if (!scores) return fail(DSA_ERR_INVALID_ARG, "scores output is required");
   if (!aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "scores must be 16-byte aligned");
   if ((rc = check_no_alias(in, span(scores, (uint64_t)in->batch * in->num_q * in->num_k * 4)))) return rc;
-  return hip_status(dsa::launch_scores(problem_of(in), scores, static_cast<hipStream_t>(stream)));
+  return hip_status(dsa::launch_scores(problem_of(in), scores, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float* out_score,

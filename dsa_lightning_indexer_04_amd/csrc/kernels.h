@@ -23,12 +23,17 @@ struct Problem {
   const int32_t* pos;
 };
 
-// Full [B,Q,N] score matrix, -inf where not visible.
-hipError_t launch_scores(const Problem& p, float* scores, hipStream_t st);
+// Full [B,Q,N] score matrix, -inf where not visible.  If row_hist is not
+// null it is set to the [B*Q][kRowHistBins] histogram of each row's visible
+// scores over the leading 11 bits of their monotone codes (the first digit
+// of the row select).
+constexpr int kRowHistBins = 2048;
+hipError_t launch_scores(const Problem& p, float* scores, uint32_t* row_hist, hipStream_t st);
 
-// Exact Top-K of every row of a [B*Q, N] score matrix (visibility from pos).
-hipError_t launch_select_rows(const Problem& p, const float* scores, int topk, int32_t* out_idx,
-                              float* out_score, hipStream_t st);
+// Exact Top-K of every row of a [B*Q, N] score matrix (visibility from pos);
+// row_hist (nullable) is launch_scores' histogram of the same rows.
+hipError_t launch_select_rows(const Problem& p, const float* scores, const uint32_t* row_hist, int topk,
+                              int32_t* out_idx, float* out_score, hipStream_t st);
 
 // Streaming Top-K: scores key tiles and keeps per-row candidate records in
 // `cand` ([B*Q][cap] uint64), never storing the score matrix.

@@ -22,7 +22,15 @@ template <int DT>
 __global__ __launch_bounds__(256) void k_scores(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                                                 const float* __restrict__ w, const float* __restrict__ qsc,
                                                 const float* __restrict__ ksc, const int32_t* __restrict__ pos,
-                                                float* __restrict__ out, int Q, int N, int keys_per_wg) {
+                                                float* __restrict__ out, uint32_t* __restrict__ row_hist, int Q,
+                                                int N, int keys_per_wg) {
+  // With row_hist: the workgroup's share of its row's code histogram, in
+  // four LDS copies (lane & 3) so that a wave's adds to one bin spread out.
+  __shared__ uint32_t lhist[4][kRowHistBins];
+  if (row_hist) {  // kernel-uniform
+    for (int i = threadIdx.x; i < 4 * kRowHistBins; i += blockDim.x) (&lhist[0][0])[i] = 0u;
+    __syncthreads();
+  }
   constexpr int RB = Frag<DT>::kRowBytes;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t row = blockIdx.x;  // b * Q + t
@@ -59,22 +67,41 @@ __global__ __launch_bounds__(256) void k_scores(const uint8_t* __restrict__ q, c
           if constexpr (DT == kFP8) tot = apply_scales(tot, qscale, ksc[(size_t)b * N + min(key, N - 1)]);
           s = key < vis ? tot : -INFINITY;
         }
-        if (lane < 32 && key < k1) orow[key] = s;
+        if (lane < 32 && key < k1) {
+          orow[key] = s;
+          if (row_hist && key < vis) atomicAdd(&lhist[lane & 3][mono_code(s) >> 21], 1u);
+        }
       }
+    }
+  }
+  if (row_hist) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kRowHistBins; i += blockDim.x) {
+      const uint32_t c = lhist[0][i] + lhist[1][i] + lhist[2][i] + lhist[3][i];
+      if (c) atomicAdd(&row_hist[row * kRowHistBins + i], c);
     }
   }
 }
 
-hipError_t launch_scores(const Problem& p, float* scores, hipStream_t st) {
+__global__ void k_zero_words(uint32_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_scores(const Problem& p, float* scores, uint32_t* row_hist, hipStream_t st) {
+  if (row_hist) {  // a fill kernel, not a memset: the launch may be captured into a graph
+    const size_t n = (size_t)p.B * p.Q * kRowHistBins;
+    hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, row_hist, n);
+  }
   const int prof_slot = prof_open("k_scores", st);
   const int kpw = 8192;  // keys per workgroup: long streams amortise the query load
   dim3 grid((unsigned)(p.B * p.Q), (p.N + kpw - 1) / kpw);
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_scores<kBF16>, grid, dim3(256), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
-                       scores, p.Q, p.N, kpw);
+                       scores, row_hist, p.Q, p.N, kpw);
   else
     hipLaunchKernelGGL(k_scores<kFP8>, grid, dim3(256), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
-                       scores, p.Q, p.N, kpw);
+                       scores, row_hist, p.Q, p.N, kpw);
   prof_close(prof_slot, st);
   return hipGetLastError();
 }
@@ -137,9 +164,10 @@ __device__ __forceinline__ void for_row_records(const float* srow, int cnt, bool
 // bin fit, they move to LDS and later passes and the output read them there
 // instead of the row.  The order of the selected keys within the output row
 // is unspecified.
-__global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ scores, const int32_t* __restrict__ pos,
-                                                      int N, int topk, int32_t* __restrict__ out_idx,
-                                                      float* __restrict__ out_score) {
+__global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ scores,
+                                                      const uint32_t* __restrict__ row_hist,
+                                                      const int32_t* __restrict__ pos, int N, int topk,
+                                                      int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   // 8 copies of the histogram (lane & 7 picks one): a row's scores share
   // their leading bits, so most records fall into a few bins, and one copy
   // would serialise a wave's 64 atomic adds on the same address.
@@ -163,12 +191,17 @@ __global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ 
       const int S = (pass == 0) ? 53 : (pass == 1) ? 42 : (pass == 2) ? 32 : (pass == 3) ? 21 : (pass == 4) ? 10 : 0;
       const int W = (pass == 2 || pass == 5) ? 10 : 11;
       const uint32_t nb = 1u << W;
-      for (uint32_t i = tid; i < 8 * nb; i += blockDim.x) hist[i / nb][i % nb] = 0;
+      // the first digit's histogram may come with the rows (row_hist): the
+      // same counts, without a pass over the row
+      const bool given = pass == 0 && row_hist != nullptr;
+      for (uint32_t i = tid; i < 8 * nb; i += blockDim.x)
+        hist[i / nb][i % nb] = (given && i < nb) ? row_hist[row * kRowHistBins + i] : 0u;
       __syncthreads();
       auto add = [&](bool ok, uint64_t r) {
         if (ok && (r & mask) == prefix) atomicAdd(&hist[lane & 7][(uint32_t)(r >> S) & (nb - 1)], 1u);
       };
-      if (ncand < 0) {
+      if (given) {
+      } else if (ncand < 0) {
         for_row_records(srow, vis, aligned, tid, (int)blockDim.x, add);
       } else {
         for (int i = tid; i < ncand; i += blockDim.x) add(true, cand[i]);
@@ -254,10 +287,10 @@ __global__ __launch_bounds__(1024) void k_select_rows(const float* __restrict__ 
   }
 }
 
-hipError_t launch_select_rows(const Problem& p, const float* scores, int topk, int32_t* out_idx, float* out_score,
-                              hipStream_t st) {
+hipError_t launch_select_rows(const Problem& p, const float* scores, const uint32_t* row_hist, int topk,
+                              int32_t* out_idx, float* out_score, hipStream_t st) {
   const int prof_slot = prof_open("k_select_rows", st);
-  hipLaunchKernelGGL(k_select_rows, dim3(p.B * p.Q), dim3(1024), 0, st, scores, p.pos, p.N, topk, out_idx,
+  hipLaunchKernelGGL(k_select_rows, dim3(p.B * p.Q), dim3(1024), 0, st, scores, row_hist, p.pos, p.N, topk, out_idx,
                      out_score);
   prof_close(prof_slot, st);
   return hipGetLastError();
