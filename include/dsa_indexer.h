@@ -84,7 +84,10 @@ typedef struct dsa_indexer_inputs {
  * Intended for checking and small shapes: it writes B*Q*N floats.          */
 int dsa_indexer_scores(const dsa_indexer_inputs* in, float* scores, void* stream);
 
-/* Exact Top-K per query row without forming the score matrix in HBM.
+/* Exact Top-K per query row.  Prefill blocks are scored and selected in one
+ * pass that never stores the score matrix; for few rows (decode: one row per
+ * sequence against a long cache) whole score rows go to the workspace and a
+ * per-row select follows, which fills the GPU with key-split workgroups.
  *   topk       1..4096
  *   out_idx    [B,Q,topk] int32 out: the min(topk, visible) selected key
  *              indices first (in no particular order), then -1 padding
