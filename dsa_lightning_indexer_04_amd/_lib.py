@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
 
 DSA_BF16, DSA_FP8_E4M3, DSA_F32 = 0, 1, 2
 DSA_OP_SCORES, DSA_OP_TOPK, DSA_OP_TOPK_PRUNED = 0, 1, 2
+DSA_FLAG_ROUTE_STREAM, DSA_FLAG_ROUTE_SPLIT = 1, 2
+ROUTES = {None: 0, "auto": 0, "stream": DSA_FLAG_ROUTE_STREAM, "split": DSA_FLAG_ROUTE_SPLIT}
 ERR = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 
 
@@ -34,6 +36,7 @@ class Inputs(ctypes.Structure):
         ("q_scale", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p),
         ("positions", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -63,6 +66,7 @@ class ProjInputs(ctypes.Structure):
         ("q_latent", ctypes.c_int32),
         ("heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
         ("c_q", ctypes.c_void_p),
         ("x", ctypes.c_void_p),
         ("w_iq", ctypes.c_void_p),
@@ -80,6 +84,7 @@ class MlaInputs(ctypes.Structure):
         ("latent_dim", ctypes.c_int32),
         ("rope_dim", ctypes.c_int32),
         ("topk", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
         ("q", ctypes.c_void_p),
         ("kv", ctypes.c_void_p),
         ("indices", ctypes.c_void_p),
@@ -175,12 +180,32 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def make_inputs_struct(q, k, w, positions, q_scale=None, k_scale=None, *, heads=None, head_dim=None) -> Inputs:
-    """Build the C inputs struct from device tensors.
+def _check_device(named, device=None):
+    """All tensors on one CUDA device (the current one unless `device` is given)."""
+    dev = device
+    for name, t in named:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA tensor (got device {t.device})")
+        if dev is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
-    q [B,Q,H,d] (bf16 or float8_e4m3fn), k [B,N,d], w [B,Q,H] fp32,
-    positions [B,Q] int32, q_scale [B,Q] / k_scale [B,N] fp32 (fp8 only).
-    """
+
+def _check_shape(name, t, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def check_index_args(q, k, w, positions, q_scale=None, k_scale=None):
+    """Dtype, layout and shape checks of the indexer inputs (no device check):
+    q [B,Q,H,d] bf16 or float8_e4m3fn, k [B,N,d] of q's dtype, w [B,Q,H] fp32,
+    positions [B,Q] int32, and for fp8 q_scale [B,Q] / k_scale [B,N] fp32
+    (absent for bf16).  Returns (B, Q, H, d, N, dtype code)."""
     if q.dtype == torch.bfloat16:
         dt = DSA_BF16
     elif q.dtype == torch.float8_e4m3fn:
@@ -194,8 +219,38 @@ def make_inputs_struct(q, k, w, positions, q_scale=None, k_scale=None, *, heads=
             raise ValueError(f"{name} must be contiguous")
     if w.dtype != torch.float32 or positions.dtype != torch.int32:
         raise TypeError("w must be float32 and positions int32")
+    if q.dim() != 4 or k.dim() != 3:
+        raise ValueError("q must be [B,Q,H,d] and k [B,N,d]")
     B, Q, H, D = q.shape
     N = k.shape[1]
+    _check_shape("k", k, (B, N, D))
+    _check_shape("w", w, (B, Q, H))
+    _check_shape("positions", positions, (B, Q))
+    if dt == DSA_FP8_E4M3:
+        if q_scale is None or k_scale is None:
+            raise ValueError("fp8 inputs need q_scale and k_scale")
+        for name, t in (("q_scale", q_scale), ("k_scale", k_scale)):
+            if t.dtype != torch.float32:
+                raise TypeError(f"{name} must be float32")
+        _check_shape("q_scale", q_scale, (B, Q))
+        _check_shape("k_scale", k_scale, (B, N))
+    elif q_scale is not None or k_scale is not None:
+        raise ValueError("bf16 inputs take no scales")
+    return B, Q, H, D, N, dt
+
+
+def make_inputs_struct(q, k, w, positions, q_scale=None, k_scale=None, *, heads=None, head_dim=None,
+                       flags: int = 0) -> Inputs:
+    """Build the C inputs struct from device tensors, after checking them.
+
+    q [B,Q,H,d] (bf16 or float8_e4m3fn), k [B,N,d], w [B,Q,H] fp32,
+    positions [B,Q] int32, q_scale [B,Q] / k_scale [B,N] fp32 (fp8 only), all
+    on the current CUDA device.  heads / head_dim override the sizes the
+    struct declares (the library rejects any other than 64 / 128).
+    """
+    B, Q, H, D, N, dt = check_index_args(q, k, w, positions, q_scale, k_scale)
+    _check_device((("q", q), ("k", k), ("w", w), ("positions", positions), ("q_scale", q_scale),
+                   ("k_scale", k_scale)))
     return Inputs(
         B,
         Q,
@@ -209,7 +264,30 @@ def make_inputs_struct(q, k, w, positions, q_scale=None, k_scale=None, *, heads=
         _ptr(q_scale),
         _ptr(k_scale),
         _ptr(positions),
+        flags,
     )
+
+
+def check_prune_args(seed_idx, force_recover, B: int, Q: int, num_seeds: int):
+    """The pruned path's optional device arrays: seed_idx int32 with B*num_seeds
+    elements (num_seeds > 0), force_recover uint8 or bool with B*Q elements,
+    both contiguous."""
+    if seed_idx is not None:
+        if seed_idx.dtype != torch.int32:
+            raise TypeError("seed_idx must be int32")
+        if num_seeds <= 0:
+            raise ValueError("seed_idx needs num_seeds > 0")
+        if seed_idx.numel() != B * num_seeds:
+            raise ValueError(f"seed_idx must hold batch * num_seeds = {B * num_seeds} entries, got {seed_idx.numel()}")
+        if not seed_idx.is_contiguous():
+            raise ValueError("seed_idx must be contiguous")
+    if force_recover is not None:
+        if force_recover.dtype not in (torch.uint8, torch.bool):
+            raise TypeError("force_recover must be uint8 or bool")
+        if force_recover.numel() != B * Q:
+            raise ValueError(f"force_recover must hold batch * num_q = {B * Q} entries, got {force_recover.numel()}")
+        if not force_recover.is_contiguous():
+            raise ValueError("force_recover must be contiguous")
 
 
 def _stream():
@@ -240,10 +318,18 @@ def scores(q, k, w, positions, q_scale=None, k_scale=None) -> torch.Tensor:
     return out
 
 
-def topk(q, k, w, positions, topk: int, q_scale=None, k_scale=None, return_scores: bool = True, workspace=None):
-    """Exact per-row Top-K: (idx [B,Q,topk] int32 with -1 padding, scores or None)."""
+def _route_flags(route):
+    if route not in ROUTES:
+        raise ValueError(f"route must be one of {sorted(r for r in ROUTES if r)} or None")
+    return ROUTES[route]
+
+
+def topk(q, k, w, positions, topk: int, q_scale=None, k_scale=None, return_scores: bool = True, workspace=None,
+         route=None):
+    """Exact per-row Top-K: (idx [B,Q,topk] int32 with -1 padding, scores or None).
+    route: None (the library chooses), "stream" or "split" (DSA_FLAG_ROUTE_*)."""
     lib = load()
-    inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
+    inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale, flags=_route_flags(route))
     nbytes = workspace_bytes(DSA_OP_TOPK, inp, topk)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
     B, Q = q.shape[:2]
@@ -278,6 +364,8 @@ def topk_pruned(
     """
     lib = load()
     inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
+    check_prune_args(seed_idx, force_recover, q.shape[0], q.shape[1], num_seeds)
+    _check_device((("seed_idx", seed_idx), ("force_recover", force_recover)), q.device)
     opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover))
     nbytes = workspace_bytes(DSA_OP_TOPK_PRUNED, inp, topk, opts)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
@@ -313,7 +401,7 @@ def topk_pruned(
     return idx, sc, st
 
 
-def make_proj_struct(c_q, x, w_iq, w_ik, w_iw) -> ProjInputs:
+def make_proj_struct(c_q, x, w_iq, w_ik, w_iw, block_tokens: int = 0) -> ProjInputs:
     """C struct of the projection inputs: bf16 device tensors c_q [T, q_latent],
     x [T, hidden] and out-feature-major weights w_iq [64*128, q_latent],
     w_ik [128, hidden], w_iw [64, hidden]."""
@@ -328,22 +416,24 @@ def make_proj_struct(c_q, x, w_iq, w_ik, w_iw) -> ProjInputs:
     D = x.shape[1]
     if tuple(w_iq.shape) != (64 * 128, L) or tuple(w_ik.shape) != (128, D) or tuple(w_iw.shape) != (64, D):
         raise ValueError("weights must be w_iq [8192, q_latent], w_ik [128, hidden], w_iw [64, hidden]")
-    return ProjInputs(T, D, L, 64, 128, _ptr(c_q), _ptr(x), _ptr(w_iq), _ptr(w_ik), _ptr(w_iw))
+    _check_device((("c_q", c_q), ("x", x), ("w_iq", w_iq), ("w_ik", w_ik), ("w_iw", w_iw)))
+    return ProjInputs(T, D, L, 64, 128, block_tokens, _ptr(c_q), _ptr(x), _ptr(w_iq), _ptr(w_ik), _ptr(w_iw))
 
 
 _PROJ_OUT = {"fp8": (DSA_FP8_E4M3, torch.float8_e4m3fn), "bf16": (DSA_BF16, torch.bfloat16), "f32": (DSA_F32, torch.float32)}
 
 
-def project(c_q, x, w_iq, w_ik, w_iw, out: str = "fp8", workspace=None) -> dict:
+def project(c_q, x, w_iq, w_ik, w_iw, out: str = "fp8", workspace=None, block_tokens: int = 0) -> dict:
     """Indexer projections Q^I = C^Q W_IQ, K^I = X W_IK, W^I = X W_IW and the
     output conversion.  Returns {"q" [T,64,128], "k" [T,128], "w" [T,64] fp32,
     "q_scale" [T], "k_scale" [T] (fp8 only, else None)}: for one sequence,
-    the q, k, w and scales the scoring calls take."""
+    the q, k, w and scales the scoring calls take.  block_tokens: tokens per
+    query-GEMM block (0: the library's 65536)."""
     lib = load()
     if out not in _PROJ_OUT:
         raise ValueError(f"out must be one of {sorted(_PROJ_OUT)}")
     code, dt = _PROJ_OUT[out]
-    inp = make_proj_struct(c_q, x, w_iq, w_ik, w_iw)
+    inp = make_proj_struct(c_q, x, w_iq, w_ik, w_iw, block_tokens)
     need = lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp))
     if need == 0:
         raise IndexerError(1, lib.dsa_indexer_last_error().decode())
@@ -367,7 +457,7 @@ def project_workspace_bytes(inp: ProjInputs) -> int:
     return n
 
 
-def make_mla_struct(q, kv, indices, page_table=None, num_k=None) -> MlaInputs:
+def make_mla_struct(q, kv, indices, page_table=None, num_k=None, num_splits: int = 0) -> MlaInputs:
     """C struct of the sparse MLA inputs: q [B,Q,128,576] bf16, indices
     [B,Q,topk] int32 and either kv [B,N,576] bf16, or (paged) a page pool kv
     [num_pages,page_size,576] with page_table [B,pages_per_seq] int32 and the
@@ -379,27 +469,31 @@ def make_mla_struct(q, kv, indices, page_table=None, num_k=None) -> MlaInputs:
     for name, t in (("q", q), ("kv", kv), ("indices", indices), ("page_table", page_table)):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or indices.dim() != 3 or kv.dim() != 3:
+        raise ValueError("shapes must be q [B,Q,H,576], kv [..,..,576], indices [B,Q,topk]")
     B, Q, H, D = q.shape
     if kv.shape[-1] != D or tuple(indices.shape[:2]) != (B, Q):
         raise ValueError("shapes must be q [B,Q,H,576], kv [..,576], indices [B,Q,topk]")
+    _check_device((("q", q), ("kv", kv), ("indices", indices), ("page_table", page_table)))
     if page_table is None:
         if kv.shape[0] != B:
             raise ValueError("a flat kv is [B,N,576]")
-        return MlaInputs(B, Q, kv.shape[1], H, 512, D - 512, indices.shape[2], _ptr(q), _ptr(kv), _ptr(indices),
-                         None, 0, 0, 0)
+        return MlaInputs(B, Q, kv.shape[1], H, 512, D - 512, indices.shape[2], num_splits, _ptr(q), _ptr(kv),
+                         _ptr(indices), None, 0, 0, 0)
     if num_k is None or page_table.shape[0] != B:
         raise ValueError("a paged kv needs num_k and page_table [B,pages_per_seq]")
-    return MlaInputs(B, Q, num_k, H, 512, D - 512, indices.shape[2], _ptr(q), _ptr(kv), _ptr(indices),
+    return MlaInputs(B, Q, num_k, H, 512, D - 512, indices.shape[2], num_splits, _ptr(q), _ptr(kv), _ptr(indices),
                      _ptr(page_table), kv.shape[1], page_table.shape[1], kv.shape[0])
 
 
 def sparse_mla(q, kv, indices, sm_scale: float, return_lse: bool = True, workspace=None, *, page_table=None,
-               num_k=None):
+               num_k=None, num_splits: int = 0):
     """MLA core attention (MQA mode) over the selected positions: returns
     (out [B,Q,128,512] bf16, lse [B,Q,128] fp32 or None).  With page_table,
-    kv is a page pool [num_pages,page_size,576] and num_k the sequence length."""
+    kv is a page pool [num_pages,page_size,576] and num_k the sequence length.
+    num_splits: work units per row (0: the library chooses)."""
     lib = load()
-    inp = make_mla_struct(q, kv, indices, page_table, num_k)
+    inp = make_mla_struct(q, kv, indices, page_table, num_k, num_splits)
     need = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp))
     if need == 0:
         raise IndexerError(1, lib.dsa_indexer_last_error().decode())

@@ -7,7 +7,6 @@
 
 #include <cmath>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -55,6 +54,10 @@ int check_inputs(const dsa_indexer_inputs* in) {
   const uint64_t rows = (uint64_t)in->batch * in->num_q;
   if (rows > (1ull << 31) || (uint64_t)in->batch * in->num_k > (1ull << 40))
     return fail(DSA_ERR_INVALID_ARG, "problem too large");
+  if (in->flags & ~(uint32_t)(DSA_FLAG_ROUTE_STREAM | DSA_FLAG_ROUTE_SPLIT))
+    return fail(DSA_ERR_INVALID_ARG, "unknown flag bits");
+  if ((in->flags & DSA_FLAG_ROUTE_STREAM) && (in->flags & DSA_FLAG_ROUTE_SPLIT))
+    return fail(DSA_ERR_INVALID_ARG, "DSA_FLAG_ROUTE_STREAM and DSA_FLAG_ROUTE_SPLIT are exclusive");
   return DSA_OK;
 }
 
@@ -94,13 +97,11 @@ int check_topk(int32_t topk) {
 
 // Few query-row groups cannot fill the GPU with one workgroup per 8 rows:
 // such calls (decode) score rows split across the key axis into a stored
-// [B*Q, N] row block and select from it.
+// [B*Q, N] row block and select from it.  The caller's flags can pin either
+// route.
 bool use_split_rows(const dsa_indexer_inputs* in) {
-  // DSA_INDEXER_TOPK_PATH=split|stream pins the choice (tests cover both on small shapes)
-  if (const char* f = std::getenv("DSA_INDEXER_TOPK_PATH")) {
-    if (std::strcmp(f, "split") == 0) return true;
-    if (std::strcmp(f, "stream") == 0) return false;
-  }
+  if (in->flags & DSA_FLAG_ROUTE_SPLIT) return true;
+  if (in->flags & DSA_FLAG_ROUTE_STREAM) return false;
   const uint64_t groups = (uint64_t)in->batch * ((in->num_q + 7) / 8);
   const uint64_t row_bytes = (uint64_t)in->batch * in->num_q * in->num_k * 4;
   return groups < 256 && row_bytes <= (8ull << 30);
@@ -245,6 +246,8 @@ int check_proj_inputs(const dsa_proj_inputs* in) {
   if (in->hidden < 8 || in->hidden > 65536 || in->hidden % 8 || in->q_latent < 8 || in->q_latent > 65536 ||
       in->q_latent % 8)
     return fail(DSA_ERR_INVALID_ARG, "hidden and q_latent must be multiples of 8 in 8..65536");
+  if (in->block_tokens != 0 && (in->block_tokens < 64 || in->block_tokens > (1 << 18)))
+    return fail(DSA_ERR_INVALID_ARG, "block_tokens must be 0 or in 64..262144");
   const void* ptrs[] = {in->c_q, in->x, in->w_iq, in->w_ik, in->w_iw};
   for (const void* p : ptrs) {
     if (!p) return fail(DSA_ERR_INVALID_ARG, "c_q, x, w_iq, w_ik, w_iw are required");
@@ -273,6 +276,7 @@ int check_mla_inputs(const dsa_mla_inputs* in) {
     return fail(DSA_ERR_UNSUPPORTED, "latent_dim must be 512 and rope_dim 64");
   if (in->topk < 1) return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1");
   if (in->topk > 2048) return fail(DSA_ERR_UNSUPPORTED, "topk must be <= 2048");
+  if (in->num_splits < 0 || in->num_splits > 8) return fail(DSA_ERR_INVALID_ARG, "num_splits must be in 0..8");
   const void* ptrs[] = {in->q, in->kv, in->indices};
   for (const void* p : ptrs) {
     if (!p) return fail(DSA_ERR_INVALID_ARG, "q, kv and indices are required");
@@ -303,7 +307,7 @@ struct MlaLayout {
 MlaLayout mla_layout(const dsa_mla_inputs* in) {
   const uint64_t rows = (uint64_t)in->batch * in->num_q;
   MlaLayout L{};
-  L.nsplit = dsa::mla_splits((int)rows);
+  L.nsplit = dsa::mla_splits((int)rows, in->num_splits);
   const uint64_t units = rows * L.nsplit;
   size_t off = 0;
   L.row_max = off;
@@ -420,7 +424,7 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
 size_t dsa_indexer_project_workspace_bytes(const dsa_proj_inputs* in) {
   g_last_error.clear();
   if (check_proj_inputs(in)) return 0;
-  return dsa::proj_workspace_bytes(in->num_tokens, in->hidden);
+  return dsa::proj_workspace_bytes(in->num_tokens, in->hidden, in->block_tokens);
 }
 
 int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_out, float* q_scale, void* k_out,
@@ -444,7 +448,7 @@ int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_ou
     if (p && !aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
   const uint64_t T = in->num_tokens;
   const uint64_t eb = mode == 0 ? 1 : mode == 1 ? 2 : 4;
-  const size_t need = dsa::proj_workspace_bytes(in->num_tokens, in->hidden);
+  const size_t need = dsa::proj_workspace_bytes(in->num_tokens, in->hidden, in->block_tokens);
   if (workspace_bytes < need || !workspace)
     return fail(DSA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -462,6 +466,7 @@ int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_ou
   const dsa::ProjProblem p{in->num_tokens,
                            in->hidden,
                            in->q_latent,
+                           in->block_tokens,
                            static_cast<const uint16_t*>(in->c_q),
                            static_cast<const uint16_t*>(in->x),
                            static_cast<const uint16_t*>(in->w_iq),

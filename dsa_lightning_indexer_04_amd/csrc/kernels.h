@@ -84,7 +84,7 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
 
 // bf16 operands of the indexer projections (weights out-feature major).
 struct ProjProblem {
-  int T, hidden, q_latent;
+  int T, hidden, q_latent, block_tokens;
   const uint16_t* c_q;   // [T][q_latent]
   const uint16_t* x;     // [T][hidden]
   const uint16_t* w_iq;  // [8192][q_latent]
@@ -93,9 +93,10 @@ struct ProjProblem {
 };
 // Device scratch handed to rocBLAS from the workspace.
 constexpr size_t kProjBlasScratch = size_t(32) << 20;
-// Tokens per GEMM block (the fp32 staging rows held at once).
-int proj_block_tokens(int T);
-size_t proj_workspace_bytes(int T, int hidden);
+// Tokens per GEMM block (the fp32 staging rows held at once): `requested`
+// if positive, else 65536, capped at T.
+int proj_block_tokens(int T, int requested);
+size_t proj_workspace_bytes(int T, int hidden, int block_tokens);
 // The GEMMs and the output pass; out 0 = fp8 + scales, 1 = bf16, 2 = fp32.
 // Returns 0, or 1 with *err set.
 int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale, uint8_t* k_out, float* k_scale,
@@ -113,8 +114,9 @@ struct MlaProblem {
   const int32_t* page_table;  // [B][pages_per_seq], or null for the flat layout
   int page_size, pages_per_seq, num_pages;
 };
-// Work units per row: 1, or (few rows) a split of each row's tiles.
-int mla_splits(int rows);
+// Work units per row: `requested` (capped at kMaxSplits = 8) if positive,
+// else 1, or (few rows) a split of each row's tiles.
+int mla_splits(int rows, int requested);
 // out [B*Q][128][512] bf16, lse [B*Q][128] fp32 (may be null); scratch:
 // row_max [units][128] fp32 and retry [units] int32 (the second pass), and
 // for nsplit > 1 part_o [units][128][512] and part_ml [units][128][2] fp32.

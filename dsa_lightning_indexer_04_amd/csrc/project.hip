@@ -163,27 +163,23 @@ rocblas_handle blas_handle(std::string* err) {
 
 }  // namespace
 
-int proj_block_tokens(int T) {
-  int blk = 65536;
-  if (const char* e = std::getenv("DSA_INDEXER_PROJ_BLOCK")) {
-    const int v = std::atoi(e);
-    if (v >= 64 && v <= (1 << 18)) blk = v;
-  }
+int proj_block_tokens(int T, int requested) {
+  const int blk = requested > 0 ? requested : 65536;
   return T < blk ? T : blk;
 }
 
 // Workspace: fp32 query staging for one token block, fp32 key/weight
 // projections of all tokens, [W_IK; W_IW], rocBLAS scratch.
-size_t proj_workspace_bytes(int T, int hidden) {
+size_t proj_workspace_bytes(int T, int hidden, int block_tokens) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t blk = (size_t)proj_block_tokens(T);
+  const size_t blk = (size_t)proj_block_tokens(T, block_tokens);
   return up(blk * kQCols * 4) + up((size_t)T * kKWCols * 4) + up((size_t)kKWCols * hidden * 2) + kProjBlasScratch;
 }
 
 int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale, uint8_t* k_out, float* k_scale,
                    float* w_out, uint8_t* ws, hipStream_t st, std::string* err) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const int blk = proj_block_tokens(p.T);
+  const int blk = proj_block_tokens(p.T, p.block_tokens);
   float* dq = reinterpret_cast<float*>(ws);
   float* dkw = reinterpret_cast<float*>(ws + up((size_t)blk * kQCols * 4));
   uint16_t* wcat = reinterpret_cast<uint16_t*>(ws + up((size_t)blk * kQCols * 4) + up((size_t)p.T * kKWCols * 4));

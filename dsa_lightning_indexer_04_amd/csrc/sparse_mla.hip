@@ -401,14 +401,9 @@ __global__ __launch_bounds__(256) void k_mla_merge(const float* __restrict__ par
 
 }  // namespace
 
-int mla_splits(int rows) {
-  int s = 1;
-  if (rows < 256) s = min(kMaxSplits, (512 + rows - 1) / rows);
-  if (const char* e = std::getenv("DSA_SPARSE_MLA_SPLIT")) {
-    const int v = std::atoi(e);
-    if (v >= 1 && v <= kMaxSplits) s = v;
-  }
-  return s;
+int mla_splits(int rows, int requested) {
+  if (requested > 0) return min(requested, kMaxSplits);
+  return rows < 256 ? min(kMaxSplits, (512 + rows - 1) / rows) : 1;
 }
 
 hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,

@@ -77,7 +77,19 @@ typedef struct dsa_indexer_inputs {
   const float* q_scale;
   const float* k_scale;
   const int32_t* positions;
+  uint32_t flags; /* 0, or DSA_FLAG_* bits below; other bits are DSA_ERR_INVALID_ARG */
 } dsa_indexer_inputs;
+
+/* flags: Top-K route of dsa_indexer_topk (at most one of the two; 0 lets the
+ * library choose: the key-split route when the rows are too few to fill the
+ * GPU with one workgroup per 8 rows and their score rows fit in 8 GiB, else
+ * the streaming route).  Both routes return the same index set; the flags
+ * exist so that callers and tests can pin one.  The workspace size depends on
+ * the route, so pass the same flags to dsa_indexer_workspace_bytes. */
+enum {
+  DSA_FLAG_ROUTE_STREAM = 1u << 0, /* fused score + streaming Top-K, no score rows stored */
+  DSA_FLAG_ROUTE_SPLIT = 1u << 1   /* key-split score rows in the workspace, then a per-row select */
+};
 
 /* Full score matrix (the index-score equation for every pair).
  *   scores [B,Q,N] fp32 out; -inf where the key is not visible.
@@ -180,6 +192,8 @@ size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t
  * 1..4194304.                                                            */
 typedef struct dsa_proj_inputs {
   int32_t num_tokens, hidden, q_latent, heads, head_dim;
+  int32_t block_tokens; /* tokens per query-GEMM block (64..262144), or 0 for 65536;
+                           capped at num_tokens; sets the workspace size */
   const void* c_q;
   const void* x;
   const void* w_iq;
@@ -248,6 +262,10 @@ size_t dsa_indexer_project_workspace_bytes(const dsa_proj_inputs* in);
  * 1..2048.                                                                  */
 typedef struct dsa_mla_inputs {
   int32_t batch, num_q, num_k, heads, latent_dim, rope_dim, topk;
+  int32_t num_splits; /* work units per query row, 1..8 (each takes a share of the row's
+                         selected tiles, merged by log-sum-exp), or 0 to choose: 1 when
+                         there are at least 256 rows, else enough to give ~512 units;
+                         sets the workspace size */
   const void* q;
   const void* kv;
   const int32_t* indices;

@@ -86,10 +86,3 @@ def lexsort_topk_of_scores(S_row: np.ndarray, vis: int, k: int) -> np.ndarray:
     s = S_row[:vis].astype(np.float64)
     order = np.lexsort((np.arange(vis), -s))
     return np.sort(order[: min(k, vis)])
-
-
-def set_path(path: str | None):
-    if path is None:
-        os.environ.pop("DSA_INDEXER_TOPK_PATH", None)
-    else:
-        os.environ["DSA_INDEXER_TOPK_PATH"] = path

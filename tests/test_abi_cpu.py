@@ -207,3 +207,163 @@ def test_sparse_mla_argument_errors(lib):
     assert b"aliases an input" in lib.dsa_indexer_last_error()
     assert call(ctypes.byref(inp), 0.04, out, None, out, need, None) == 1  # workspace over out
     assert b"must not overlap" in lib.dsa_indexer_last_error()
+
+
+@pytest.mark.parametrize("flags", [4, 1 << 31, 3])
+def test_bad_flags_are_rejected(lib, flags):
+    """Unknown flag bits, and both Top-K routes at once."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _inputs(_lib, flags=flags)
+    assert lib.dsa_indexer_topk(ctypes.byref(inp), 16, ctypes.c_void_p(FAKE * 8), None, None, 0, None) == 1
+    assert lib.dsa_indexer_workspace_bytes(1, ctypes.byref(inp), 16, None) == 0
+    assert lib.dsa_indexer_last_error()
+
+
+def test_route_flags_set_the_workspace(lib):
+    """The key-split route stores [B*Q, N] fp32 score rows plus a 2048-bin
+    histogram per row; the streaming route (4*topk + 640) 8-byte records per
+    row; with no flag, 4 rows pick the split route."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    split = lib.dsa_indexer_workspace_bytes(1, ctypes.byref(_inputs(_lib, flags=_lib.DSA_FLAG_ROUTE_SPLIT)), 16, None)
+    stream = lib.dsa_indexer_workspace_bytes(1, ctypes.byref(_inputs(_lib, flags=_lib.DSA_FLAG_ROUTE_STREAM)), 16, None)
+    auto = lib.dsa_indexer_workspace_bytes(1, ctypes.byref(_inputs(_lib)), 16, None)
+    assert split == 4 * 64 * 4 + 4 * 2048 * 4
+    assert stream == ((4 * (4 * 16 + 640) * 8 + 255) // 256) * 256
+    assert auto == split
+
+
+@pytest.mark.parametrize("block,ok", [(0, True), (64, True), (100, True), (1 << 18, True), (63, False),
+                                      ((1 << 18) + 1, False), (-5, False)])
+def test_projection_block_tokens(lib, block, ok):
+    """block_tokens sets the fp32 staging block of the query GEMM (and so the
+    workspace); outside 64..262144 (0: default) it is an argument error."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _proj(_lib, num_tokens=5000, block_tokens=block)
+    need = lib.dsa_indexer_project_workspace_bytes(ctypes.byref(inp))
+    if not ok:
+        assert need == 0 and b"block_tokens" in lib.dsa_indexer_last_error()
+        return
+    blk = min(5000, block or 65536)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == up(blk * 8192 * 4) + up(5000 * 192 * 4) + up(192 * 7168 * 2) + (32 << 20)
+
+
+@pytest.mark.parametrize("splits,ok", [(0, True), (1, True), (8, True), (9, False), (-1, False)])
+def test_sparse_mla_num_splits(lib, splits, ok):
+    """num_splits pins the work units per row (and the partial-output
+    workspace); 0 lets the library choose (8 rows: 8 units per row)."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _mla(_lib, num_splits=splits)
+    need = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(inp))
+    if not ok:
+        assert need == 0 and b"num_splits" in lib.dsa_indexer_last_error()
+        return
+    units = 8 * (splits or 8)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = up(units * 128 * 4) + up(units * 4)
+    if units > 8:
+        want += up(units * 128 * 512 * 4) + up(units * 128 * 2 * 4)
+    assert need == want
+
+
+# ---------------------------------------------------------------- Python wrapper checks (no GPU needed)
+
+
+def _cpu_inputs(dtype="bf16", B=2, Q=3, N=40):
+    import torch
+
+    from dsa_lightning_indexer_04_amd import inputs
+
+    d = inputs.make_inputs(B, Q, N, dtype, "iid", seed=0)
+    return d, torch
+
+
+def test_wrapper_rejects_host_tensors():
+    """Tensors must be CUDA tensors: a host pointer handed to a kernel would fault."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    d, _ = _cpu_inputs()
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        _lib.make_inputs_struct(d["q"], d["k"], d["w"], d["pos"])
+
+
+@pytest.mark.parametrize(
+    "change,exc,msg",
+    [
+        (lambda d, t: d.update(k=d["k"][:1]), ValueError, "k must have shape"),
+        (lambda d, t: d.update(k=d["k"][:, :, :64].contiguous()), ValueError, "k must have shape"),
+        (lambda d, t: d.update(w=d["w"][:, :, :32].contiguous()), ValueError, "w must have shape"),
+        (lambda d, t: d.update(pos=d["pos"][:, :2].contiguous()), ValueError, "positions must have shape"),
+        (lambda d, t: d.update(pos=d["pos"].long()), TypeError, "int32"),
+        (lambda d, t: d.update(w=d["w"].double()), TypeError, "float32"),
+        (lambda d, t: d.update(q=d["q"].float()), TypeError, "unsupported q dtype"),
+        (lambda d, t: d.update(k=d["k"].transpose(1, 2)), ValueError, "contiguous"),
+        (lambda d, t: d.update(q_scale=t.ones(2, 3)), ValueError, "bf16 inputs take no scales"),
+    ],
+)
+def test_wrapper_rejects_bad_shapes_and_dtypes(change, exc, msg):
+    from dsa_lightning_indexer_04_amd import _lib
+
+    d, torch = _cpu_inputs()
+    change(d, torch)
+    with pytest.raises(exc, match=msg):
+        _lib.check_index_args(d["q"], d["k"], d["w"], d["pos"], d.get("q_scale"), d.get("k_scale"))
+
+
+def test_wrapper_checks_fp8_scales():
+    from dsa_lightning_indexer_04_amd import _lib
+
+    d, torch = _cpu_inputs("fp8")
+    assert _lib.check_index_args(d["q"], d["k"], d["w"], d["pos"], d["q_scale"], d["k_scale"])[5] == 1
+    with pytest.raises(ValueError, match="need q_scale"):
+        _lib.check_index_args(d["q"], d["k"], d["w"], d["pos"], None, d["k_scale"])
+    with pytest.raises(ValueError, match="k_scale must have shape"):
+        _lib.check_index_args(d["q"], d["k"], d["w"], d["pos"], d["q_scale"], d["k_scale"][:, :10].contiguous())
+    with pytest.raises(TypeError, match="q_scale must be float32"):
+        _lib.check_index_args(d["q"], d["k"], d["w"], d["pos"], d["q_scale"].double(), d["k_scale"])
+
+
+@pytest.mark.parametrize(
+    "seed,force,num_seeds,exc,msg",
+    [
+        ("i64", None, 8, TypeError, "seed_idx must be int32"),
+        ("short", None, 8, ValueError, "batch \\* num_seeds"),
+        ("ok", None, 0, ValueError, "num_seeds > 0"),
+        (None, "f32", 0, TypeError, "force_recover must be uint8"),
+        (None, "short", 0, ValueError, "batch \\* num_q"),
+    ],
+)
+def test_wrapper_checks_prune_arrays(seed, force, num_seeds, exc, msg):
+    """seed_idx: int32 with batch * num_seeds entries (a seed list without its
+    batch axis is too short); force_recover: uint8/bool with batch * num_q."""
+    import torch
+
+    from dsa_lightning_indexer_04_amd import _lib
+
+    B, Q = 2, 3
+    seeds = {"i64": torch.arange(B * 8, dtype=torch.int64), "short": torch.arange(8, dtype=torch.int32),
+             "ok": torch.arange(B * 8, dtype=torch.int32), None: None}[seed]
+    fr = {"f32": torch.zeros(B * Q), "short": torch.zeros(Q, dtype=torch.uint8), None: None}[force]
+    with pytest.raises(exc, match=msg):
+        _lib.check_prune_args(seeds, fr, B, Q, num_seeds)
+    _lib.check_prune_args(torch.arange(B * 8, dtype=torch.int32), torch.zeros(B, Q, dtype=torch.bool), B, Q, 8)
+
+
+def test_wrapper_rejects_host_tensors_in_other_calls():
+    import torch
+
+    from dsa_lightning_indexer_04_amd import _lib
+
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        _lib.make_proj_struct(torch.zeros(4, 64, dtype=bf), torch.zeros(4, 64, dtype=bf), torch.zeros(8192, 64, dtype=bf),
+                              torch.zeros(128, 64, dtype=bf), torch.zeros(64, 64, dtype=bf))
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        _lib.make_mla_struct(torch.zeros(1, 2, 128, 576, dtype=bf), torch.zeros(1, 50, 576, dtype=bf),
+                             torch.zeros(1, 2, 16, dtype=torch.int32))
+    with pytest.raises(ValueError, match="route"):
+        _lib._route_flags("fast")

@@ -34,10 +34,10 @@ def _dec(t: torch.Tensor) -> np.ndarray:
     return indexer.decode_bf16(inputs.to_bits(t.cpu()))
 
 
-def _run(d: dict, modes=("f32", "fp8", "bf16")) -> dict:
+def _run(d: dict, modes=("f32", "fp8", "bf16"), block_tokens: int = 0) -> dict:
     dev = {k: v.cuda() for k, v in d.items()}
     args = (dev["c_q"], dev["x"], dev["w_iq"], dev["w_ik"], dev["w_iw"])
-    out = {m: dsa.project(*args, out=m) for m in modes}
+    out = {m: dsa.project(*args, out=m, block_tokens=block_tokens) for m in modes}
     torch.cuda.synchronize()
     return {m: {k: (None if v is None else v.cpu()) for k, v in r.items()} for m, r in out.items()}
 
@@ -88,13 +88,11 @@ def _check_conversion(res: dict):
         (4396, 7168, 1536, 1024),  # five token blocks, the last one ragged
     ],
 )
-def test_projection_parity(T, hidden, q_latent, block, monkeypatch):
+def test_projection_parity(T, hidden, q_latent, block):
     need_gpu()
     log(f"[project] T={T} hidden={hidden} q_latent={q_latent} block={block}")
-    if block:
-        monkeypatch.setenv("DSA_INDEXER_PROJ_BLOCK", str(block))
     d = inputs.make_projection_inputs(T, hidden, q_latent, seed=T)
-    res = _run(d)
+    res = _run(d, block_tokens=block or 0)
     if T <= 512:
         tokens = np.arange(T)
     else:

@@ -12,7 +12,7 @@ import torch
 
 import dsa_lightning_indexer_04_amd as dsa
 from dsa_lightning_indexer_04_amd import inputs
-from helpers import OracleRows, assert_rows_ok, call_args, log, need_gpu, set_path, to_device
+from helpers import OracleRows, assert_rows_ok, call_args, log, need_gpu, to_device
 from oracle import indexer
 
 pytestmark = pytest.mark.gpu
@@ -20,11 +20,7 @@ pytestmark = pytest.mark.gpu
 
 def _unpruned(dd, k):
     args, kw = call_args(dd)
-    set_path("stream")
-    try:
-        idx, sc = dsa.topk(*args, k, **kw)
-    finally:
-        set_path(None)
+    idx, sc = dsa.topk(*args, k, **kw, route="stream")
     return idx.cpu().numpy(), sc.cpu().numpy()
 
 

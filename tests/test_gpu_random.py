@@ -14,7 +14,7 @@ import pytest
 
 import dsa_lightning_indexer_04_amd as dsa
 from dsa_lightning_indexer_04_amd import inputs
-from helpers import OracleRows, assert_rows_ok, call_args, lexsort_topk_of_scores, log, need_gpu, set_path, to_device
+from helpers import OracleRows, assert_rows_ok, call_args, lexsort_topk_of_scores, log, need_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -38,11 +38,7 @@ def test_random_shapes(case):
     rows = [(b, t) for b in range(B) for t in range(Q)]
     sets = {}
     for path in ("split", "stream"):
-        set_path(path)
-        try:
-            idx, sc = dsa.topk(*args, k, **kw)
-        finally:
-            set_path(None)
+        idx, sc = dsa.topk(*args, k, **kw, route=path)
         idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
         for b, t in rows:
             vis = int(np.clip(pos[b, t] + 1, 0, N))

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("case", range(8))
-def test_random_projection(case, monkeypatch):
+def test_random_projection(case):
     need_gpu()
     rng = np.random.default_rng(3000 + case)
     T = int(rng.integers(1, 2500))
@@ -24,10 +24,8 @@ def test_random_projection(case, monkeypatch):
     q_latent = 8 * int(rng.integers(1, 257))
     block = int(rng.choice([0, 64, 100, 1024]))
     log(f"random projection case {case}: T={T} hidden={hidden} q_latent={q_latent} block={block or 'default'}")
-    if block:
-        monkeypatch.setenv("DSA_INDEXER_PROJ_BLOCK", str(block))
     d = inputs.make_projection_inputs(T, hidden, q_latent, seed=case)
-    res = _run(d)
+    res = _run(d, block_tokens=block)
     tokens = np.arange(T) if T <= 40 else np.unique(np.concatenate([[0, T - 1], rng.choice(T, 38, replace=False)]))
     _check_products(d, res, tokens)
     _check_conversion(res)

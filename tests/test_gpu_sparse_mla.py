@@ -52,24 +52,22 @@ def _check_rows(q_cpu, kv_cpu, idx, out, lse, sm_scale, rows):
         assert np.all(np.abs(lse[b, t] - l_ref) <= ltol), (b, t, float(np.abs(lse[b, t] - l_ref).max()))
 
 
-def _run(d, idx_np, sm_scale):
+def _run(d, idx_np, sm_scale, num_splits=0):
     q, kv = d["q"].cuda(), d["kv"].cuda()
     idx = torch.from_numpy(idx_np).cuda()
-    out, lse = dsa.sparse_mla(q, kv, idx, sm_scale)
+    out, lse = dsa.sparse_mla(q, kv, idx, sm_scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return out, lse
 
 
 # few rows split each row's tiles over several workgroups and merge the
-# partial results; "1" pins the unsplit kernel
-SPLITS = ["1", "3", None]
+# partial results; 1 pins the unsplit kernel, 0 lets the library choose
+SPLITS = [1, 3, 0]
 
 
 @pytest.mark.parametrize("split", SPLITS)
-def test_small_rows_with_padding(split, monkeypatch):
+def test_small_rows_with_padding(split):
     need_gpu()
-    if split:
-        monkeypatch.setenv("DSA_SPARSE_MLA_SPLIT", split)
     B, Q, N, k = 2, 6, 300, 64
     d = inputs.make_mla_inputs(B, Q, N, seed=1)
     pos = np.array([[299, 40, 10, 0, -1, 63], [299, 299, 150, 31, 32, 100]])
@@ -78,34 +76,30 @@ def test_small_rows_with_padding(split, monkeypatch):
     idx[1, 5, 10:20] = -1  # padding in the middle
     idx[1, 5, 3] = 400  # out of range: skipped
     log("[mla] small rows")
-    out, lse = _run(d, idx, 1.0 / math.sqrt(576))
+    out, lse = _run(d, idx, 1.0 / math.sqrt(576), split)
     _check_rows(d["q"], d["kv"], idx, out, lse, 1.0 / math.sqrt(576), [(b, t) for b in range(B) for t in range(Q)])
 
 
 @pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("sm_scale", [1.0 / math.sqrt(576), 0.0, 0.2])
-def test_full_topk_rows(sm_scale, split, monkeypatch):
+def test_full_topk_rows(sm_scale, split):
     need_gpu()
-    if split:
-        monkeypatch.setenv("DSA_SPARSE_MLA_SPLIT", split)
     B, Q, N, k = 1, 5, 5000, 2048
     d = inputs.make_mla_inputs(B, Q, N, seed=2)
     pos = np.array([[4999, 4999, 2047, 2048, 3000]])
     idx = inputs.random_selection(B, Q, N, k, pos, seed=2)
     log(f"[mla] topk 2048, sm_scale {sm_scale}")
-    out, lse = _run(d, idx, sm_scale)
+    out, lse = _run(d, idx, sm_scale, split)
     _check_rows(d["q"], d["kv"], idx, out, lse, sm_scale, [(0, t) for t in range(Q)])
 
 
 @pytest.mark.parametrize("split", SPLITS)
-def test_second_pass_rows(split, monkeypatch):
+def test_second_pass_rows(split):
     """Rows whose later scores exceed the first tile's maximum by far more
     than 32 (log2 units) are recomputed by the second launch: the first 32
     selected positions get tiny latent rows, the rest full ones, and a large
     sm_scale stretches the score range."""
     need_gpu()
-    if split:
-        monkeypatch.setenv("DSA_SPARSE_MLA_SPLIT", split)
     B, Q, N, k = 1, 4, 600, 256
     d = inputs.make_mla_inputs(B, Q, N, seed=3)
     d["kv"][0, :100] = (d["kv"][0, :100].float() * 0.01).to(torch.bfloat16)
@@ -119,7 +113,7 @@ def test_second_pass_rows(split, monkeypatch):
     s = sm_scale * (qf @ kvf[idx[0, 0, :200]].T) / math.log(2)
     assert (s[:, 32:].max(1) - s[:, :32].max(1)).max() > 40  # the retry path is taken
     log("[mla] second pass")
-    out, lse = _run(d, idx, sm_scale)
+    out, lse = _run(d, idx, sm_scale, split)
     _check_rows(d["q"], d["kv"], idx, out, lse, sm_scale, [(0, t) for t in range(Q)])
 
 
@@ -178,11 +172,8 @@ def test_decode_rows_split_and_merged():
     pos[3, 0] = 1000  # fewer visible keys than k: a shorter selection
     idx = inputs.random_selection(B, Q, N, k, pos, seed=8)
     res = {}
-    for split in ("auto", "1"):
-        with pytest.MonkeyPatch.context() as mp:
-            if split == "1":
-                mp.setenv("DSA_SPARSE_MLA_SPLIT", "1")
-            res[split] = _run(d, idx, 1.0 / math.sqrt(576))
+    for split in (0, 1):
+        res[split] = _run(d, idx, 1.0 / math.sqrt(576), split)
     for out, lse in res.values():
         _check_rows(d["q"], d["kv"], idx, out, lse, 1.0 / math.sqrt(576), [(b, 0) for b in range(B)])
 

@@ -12,7 +12,7 @@ import torch
 
 import dsa_lightning_indexer_04_amd as dsa
 from dsa_lightning_indexer_04_amd import inputs
-from helpers import OracleRows, assert_rows_ok, call_args, lexsort_topk_of_scores, log, need_gpu, set_path, to_device
+from helpers import OracleRows, assert_rows_ok, call_args, lexsort_topk_of_scores, log, need_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -59,13 +59,9 @@ def test_topk_small(path, B, Q, N, k, dtype, dist):
     d = inputs.make_inputs(B, Q, N, dtype, dist, seed=Q, positions=pos)
     dd = to_device(d)
     log(f"topk {path} B={B} Q={Q} N={N} k={k} {dtype} {dist}")
-    set_path(path)
-    try:
-        args, kw = call_args(dd)
-        idx, sc = dsa.topk(*args, k, **kw)
-        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
-    finally:
-        set_path(None)
+    args, kw = call_args(dd)
+    idx, sc = dsa.topk(*args, k, **kw, route=path)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     _exact_vs_own_scores(d, dd, idx, sc, k)
     assert_rows_ok(OracleRows(d), idx, sc, [(b, t) for b in range(B) for t in range(Q)], k)
 
@@ -75,12 +71,8 @@ def test_topk_ties_take_smallest_indices(path):
     need_gpu()
     d = inputs.make_inputs(1, 8, 900, "bf16", "iid", seed=1)
     d["w"] = torch.zeros_like(d["w"])
-    set_path(path)
-    try:
-        args, kw = call_args(to_device(d))
-        idx, _ = dsa.topk(*args, 50, **kw)
-    finally:
-        set_path(None)
+    args, kw = call_args(to_device(d))
+    idx, _ = dsa.topk(*args, 50, **kw, route=path)
     idx = idx.cpu().numpy()
     for t in range(8):
         assert np.array_equal(np.sort(idx[0, t]), np.arange(50))
@@ -108,11 +100,7 @@ def test_topk_paths_agree_on_a_prefill_block():
     args, kw = call_args(dd)
     out = {}
     for path in ("split", "stream"):
-        set_path(path)
-        try:
-            out[path] = [x.cpu() for x in dsa.topk(*args, 256, **kw)]
-        finally:
-            set_path(None)
+        out[path] = [x.cpu() for x in dsa.topk(*args, 256, **kw, route=path)]
     a = torch.sort(out["split"][0], -1).values
     b = torch.sort(out["stream"][0], -1).values
     assert torch.equal(a, b)
@@ -139,13 +127,9 @@ def test_topk_rising_scores_small_k(path, k):
     }
     dd = to_device(d)
     log(f"topk rising scores {path} k={k}")
-    set_path(path)
-    try:
-        args, kw = call_args(dd)
-        idx, sc = dsa.topk(*args, k, **kw)
-        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
-    finally:
-        set_path(None)
+    args, kw = call_args(dd)
+    idx, sc = dsa.topk(*args, k, **kw, route=path)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     for t in range(Q):
         p = int(pos[0, t])
         want = np.arange(max(0, p - k + 1), p + 1)
