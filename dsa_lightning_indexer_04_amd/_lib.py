@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
 DSA_BF16, DSA_FP8_E4M3, DSA_F32 = 0, 1, 2
 DSA_OP_SCORES, DSA_OP_TOPK, DSA_OP_TOPK_PRUNED = 0, 1, 2
 DSA_FLAG_ROUTE_STREAM, DSA_FLAG_ROUTE_SPLIT = 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DSA_NOALLOC_SCRATCH_BYTES
 ROUTES = {None: 0, "auto": 0, "stream": DSA_FLAG_ROUTE_STREAM, "split": DSA_FLAG_ROUTE_SPLIT}
 ERR = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 
@@ -99,6 +100,7 @@ EXPORTED = [
     "dsa_indexer_scores",
     "dsa_indexer_topk",
     "dsa_indexer_topk_pruned",
+    "dsa_indexer_topk_noalloc",
     "dsa_indexer_workspace_bytes",
     "dsa_indexer_project",
     "dsa_indexer_project_workspace_bytes",
@@ -129,6 +131,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_scores.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [ctypes.POINTER(Inputs), I32, P, P, P, SZ, P]
     lib.dsa_indexer_topk.restype = ctypes.c_int
+    lib.dsa_indexer_topk_noalloc.argtypes = [ctypes.POINTER(Inputs), I32, P, P, P]
+    lib.dsa_indexer_topk_noalloc.restype = ctypes.c_int
     lib.dsa_indexer_topk_pruned.argtypes = [
         ctypes.POINTER(Inputs),
         I32,
@@ -336,6 +340,20 @@ def topk(q, k, w, positions, topk: int, q_scale=None, k_scale=None, return_score
     idx = torch.empty((B, Q, topk), dtype=torch.int32, device=q.device)
     sc = torch.empty((B, Q, topk), dtype=torch.float32, device=q.device) if return_scores else None
     _check(lib.dsa_indexer_topk(ctypes.byref(inp), topk, _ptr(idx), _ptr(sc), _ptr(ws), ws.numel(), _stream()))
+    return idx, sc
+
+
+def topk_noalloc(q, k, w, positions, topk: int, q_scale=None, k_scale=None, return_scores: bool = True,
+                 route=None):
+    """dsa_indexer_topk_noalloc: the same Top-K with the library's fixed
+    per-GPU scratch instead of a workspace (the outputs are still allocated
+    here; the library call allocates nothing)."""
+    lib = load()
+    inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale, flags=_route_flags(route))
+    B, Q = q.shape[:2]
+    idx = torch.empty((B, Q, topk), dtype=torch.int32, device=q.device)
+    sc = torch.empty((B, Q, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    _check(lib.dsa_indexer_topk_noalloc(ctypes.byref(inp), topk, _ptr(idx), _ptr(sc), _stream()))
     return idx, sc
 
 

@@ -345,6 +345,22 @@ int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_id
   return run_topk(in, topk, out_idx, out_score, workspace, static_cast<hipStream_t>(stream));
 }
 
+int dsa_indexer_topk_noalloc(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float* out_score,
+                             void* stream) {
+  int rc = check_inputs(in);
+  if (rc) return rc;
+  if ((rc = check_topk(topk))) return rc;
+  const size_t need = topk_workspace(in, topk);
+  if (need > dsa::kNoAllocScratchBytes)
+    return fail(DSA_ERR_WORKSPACE, "call needs " + std::to_string(need) + " bytes of scratch; the fixed scratch holds " +
+                                       std::to_string(dsa::kNoAllocScratchBytes));
+  void* ws = nullptr;
+  std::string err;
+  if (dsa::noalloc_scratch(&ws, &err)) return fail(DSA_ERR_HIP, err);
+  if ((rc = check_topk_outputs(in, topk, out_idx, out_score, ws, dsa::kNoAllocScratchBytes, need))) return rc;
+  return run_topk(in, topk, out_idx, out_score, ws, static_cast<hipStream_t>(stream));
+}
+
 size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t topk, const dsa_prune_opts* opts) {
   g_last_error.clear();
   if (check_inputs(in)) return 0;

@@ -123,6 +123,14 @@ int mla_splits(int rows, int requested);
 hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
                              int32_t* retry, int nsplit, float* part_o, float* part_ml, hipStream_t st);
 
+// ---------------------------------------------------------------- fixed scratch
+
+// Bytes of the per-device scratch array behind dsa_indexer_topk_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of that array on the current device (resolved once per
+// device with hipGetSymbolAddress).  Returns 0, or 1 with *err set.
+int noalloc_scratch(void** ptr, std::string* err);
+
 // Candidate capacity (records per row) used by the streaming Top-K: a cut
 // keeps at most topk + 512 records, so one more tile of up to 128 keys always
 // fits behind it.

@@ -112,6 +112,25 @@ int dsa_indexer_scores(const dsa_indexer_inputs* in, float* scores, void* stream
 int dsa_indexer_topk(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx,
                      float* out_score, void* workspace, size_t workspace_bytes, void* stream);
 
+/* dsa_indexer_topk with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that forbid hipMalloc).  The workspace is a fixed device array of
+ * DSA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * library's load until the process ends; its address on the current device
+ * is looked up on the first call on that device (hipGetSymbolAddress).
+ * Same inputs, route flags, outputs and results as dsa_indexer_topk.
+ * Returns DSA_ERR_WORKSPACE, enqueuing nothing, when the call needs more than
+ * DSA_NOALLOC_SCRATCH_BYTES of workspace (dsa_indexer_workspace_bytes with
+ * DSA_OP_TOPK tells: e.g. 64 decode rows over 131072 keys need 32.5 MiB, the
+ * streaming route (4*topk + 640)*8 bytes per row).  Every call on one GPU
+ * uses that GPU's one array: calls that can overlap in time on one GPU
+ * (different streams, or host threads) race and must be serialised by the
+ * caller.  Calls on one stream are ordered and safe.  The stream must belong
+ * to the current device.                                                     */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dsa_indexer_topk_noalloc(const dsa_indexer_inputs* in, int32_t topk, int32_t* out_idx, float* out_score,
+                             void* stream);
+
 /* Options of the pruned path (host struct; pass NULL for defaults).
  *   num_seeds     seeds per sequence (0 -> 12288), clamped to the common
  *                 visible prefix; seeds rescored with all heads fix the

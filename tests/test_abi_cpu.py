@@ -367,3 +367,22 @@ def test_wrapper_rejects_host_tensors_in_other_calls():
                              torch.zeros(1, 2, 16, dtype=torch.int32))
     with pytest.raises(ValueError, match="route"):
         _lib._route_flags("fast")
+
+
+def test_noalloc_rejects_calls_beyond_the_fixed_scratch(lib):
+    """The no-allocation Top-K refuses, before any GPU call, a call whose
+    workspace exceeds the fixed 64 MiB scratch: 8192 streaming rows at top-2048
+    need 8192 * 8832 * 8 bytes."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _inputs(_lib, num_q=8192, num_k=131072, flags=_lib.DSA_FLAG_ROUTE_STREAM)
+    need = lib.dsa_indexer_workspace_bytes(1, ctypes.byref(inp), 2048, None)
+    assert need == 8192 * (4 * 2048 + 640) * 8 > _lib.NOALLOC_SCRATCH_BYTES
+    rc = lib.dsa_indexer_topk_noalloc(ctypes.byref(inp), 2048, ctypes.c_void_p(FAKE * 8), None, None)
+    assert rc == 3 and b"fixed scratch" in lib.dsa_indexer_last_error()
+    # the decode batch fits: 64 rows x 131072 keys of score rows + histograms
+    dec = _inputs(_lib, batch=64, num_q=1, num_k=131072)
+    assert lib.dsa_indexer_workspace_bytes(1, ctypes.byref(dec), 2048, None) <= _lib.NOALLOC_SCRATCH_BYTES
+    # argument errors come first, as for dsa_indexer_topk
+    assert lib.dsa_indexer_topk_noalloc(ctypes.byref(_inputs(_lib, heads=32)), 16, None, None, None) == 2
+    assert lib.dsa_indexer_topk_noalloc(ctypes.byref(_inputs(_lib)), 0, None, None, None) == 1
