@@ -39,7 +39,6 @@ FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("chunked_prefill_128k", "k_topk_stream"): ("d751b8c67fe2d476", 2284446, 1380304),
-    ("chunked_prefill_128k", "k_topk_pruned"): ("9f83a0be827133e2", 4541126, 745897),
     ("projection_prefill_128k", "k_proj_out"): ("61f24b18bb20f769", 1073178, 553001),
     ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
 }
@@ -79,7 +78,8 @@ def parse():
 # their digest holds.
 KERNEL_SOURCES = {
     "k_topk_stream": ["topk_stream.hip", "stream_common.h", "score_tile.h", "select.h"],
-    "k_topk_pruned": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h"],
+    "k_screen": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h"],
+    "k_refine": ["topk_pruned.hip", "stream_common.h", "score_tile.h", "select.h"],
     "k_scores": ["scores.hip", "score_tile.h"],
     "k_proj_out": ["project.hip"],
     "k_sparse_mla": ["sparse_mla.hip"],
@@ -188,37 +188,55 @@ def run_workload(name, path, steps, warmup):
         "pairs_per_s": pairs / (wall / steps),
         "kernels_ms": {n: round(ms, 4) for n, (c, ms) in kernels.items()},
     }
-    dom = max(kernels.items(), key=lambda kv: kv[1][1])
+    # per kernel: launches and device time per step, and the matrix-product
+    # FLOPs its launches execute per step
+    per_step = {n: {"launches": c / steps, "ms": c * ms / steps} for n, (c, ms) in kernels.items()}
     if use_pruned:
-        # the seeds are scored by their own streaming Top-K launch; the pruned
-        # kernel screens the other visible keys and rescores the survivors
-        dom_flops = stats["screened_pairs"] * SCREEN_FLOPS + stats["survivor_pairs"] * PAIR_FLOPS
-        flops = stats["seed_pairs"] * PAIR_FLOPS + dom_flops
+        # seeds: the streaming Top-K over the packed seed keys; the screen
+        # bounds the other visible keys (32 plan rows each); the refine
+        # rescores the survivors with all 64 heads
+        work = {"k_topk_stream": stats["seed_pairs"] * PAIR_FLOPS,
+                "k_screen": stats["screened_pairs"] * SCREEN_FLOPS,
+                "k_refine": stats["survivor_pairs"] * PAIR_FLOPS}
         res["prune"] = stats
     else:
-        flops = dom_flops = pairs * PAIR_FLOPS
-    res["dominant_kernel"] = dom[0]
-    res["dominant_ms"] = dom[1][1]
+        work = {n: pairs * PAIR_FLOPS for n in per_step if n in ("k_topk_stream", "k_scores")}
+    for n, v in per_step.items():
+        v["flops"] = work.get(n, 0)
+        v["tflops"] = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] > 0 else 0.0
+        v["frac"] = v["tflops"] / PEAK_TFLOPS[wl.dtype]
+    res["kernels"] = per_step
+    dom = max(per_step.items(), key=lambda kv: kv[1]["ms"])  # the kernel with the most device time
+    dk, dv = dom
+    flops = sum(work.values())
+    res["dominant_kernel"] = dk
+    res["dominant_ms"] = dv["ms"] / max(dv["launches"], 1e-9)  # mean per launch
+    res["dominant_launches"] = dv["launches"]
     res["executed_flops"] = flops
-    res["dominant_flops"] = dom_flops
-    res["achieved_tflops"] = dom_flops / (dom[1][1] * 1e-3) / 1e12
+    res["dominant_flops"] = dv["flops"] / max(dv["launches"], 1e-9)  # per launch
+    res["achieved_tflops"] = dv["tflops"]
     res["effective_tflops"] = pairs * PAIR_FLOPS / (res["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     if wl.num_q == 1:
         # one query row per sequence (decode): every key row is read once and
-        # serves 64 heads, far below the MFMA ridge point -> HBM-bound
+        # serves 64 heads, far below the MFMA ridge point -> HBM-bound; the
+        # algorithmic bytes are the keys (and fp8 scales), the query rows and
+        # the weights
         key_bytes = wl.batch * wl.num_k * (256 if wl.dtype == "bf16" else 128 + 4)
         q_bytes = wl.batch * 64 * (256 if wl.dtype == "bf16" else 128) + wl.batch * 64 * 4
-        alg = key_bytes + q_bytes + wl.batch * wl.num_k * 4  # + the stored score rows
-        res["roofline"] = {"bound": "hbm", "achieved": alg / (dom[1][1] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "kernel": dom[0], "bytes_per_launch": alg}
+        alg = key_bytes + q_bytes
+        sk = per_step.get("k_scores", dv)
+        ms = sk["ms"] / max(sk["launches"], 1e-9)
+        res["roofline"] = {"bound": "hbm", "achieved": alg / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "kernel": "k_scores", "bytes_per_launch": alg}
     else:
         res["roofline"] = {"bound": "mfma", "achieved": res["achieved_tflops"], "peak": peak, "unit": "TFLOP/s",
-                           "kernel": dom[0], "flops_per_launch": flops}
+                           "kernel": dk, "flops_per_launch": res["dominant_flops"]}
     res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
     log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s; "
-        f"{dom[0]} {dom[1][1]:.3f} ms at {res['achieved_tflops']:.0f} TFLOP/s ({100 * res['achieved_tflops'] / peak:.1f}%"
-        f" of {wl.dtype} peak)" + (f"; filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
+        + ", ".join(f"{n} {v['ms']:.3f} ms" + (f" ({100 * v['frac']:.1f}%)" if v["flops"] else "")
+                    for n, v in sorted(per_step.items(), key=lambda kv: -kv[1]["ms"]))
+        + (f"; filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
     del q, k, w, pos, qs, ks, ws
     torch.cuda.empty_cache()
     return res

@@ -212,6 +212,10 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
   uint8_t* spos = take(R * 4);
   uint8_t* stidx = take(R * (uint64_t)topk * 4);
   uint8_t* stsc = take(R * (uint64_t)topk * 4);
+  const uint64_t mwords = (uint64_t)dsa::prune_mask_words(in->num_k);
+  uint8_t* ctl = take(R * sizeof(dsa::PruneRowCtl));
+  uint8_t* hist = take(R * 256 * 4);
+  uint8_t* mask = take(R * mwords * 8);
   if (base && pb) {
     if (cand) *cand = reinterpret_cast<uint64_t*>(c);
     pb->plan_rows = rows;
@@ -230,6 +234,10 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
     pb->seed_pos = reinterpret_cast<int32_t*>(spos);
     pb->seed_top_idx = reinterpret_cast<int32_t*>(stidx);
     pb->seed_top_score = reinterpret_cast<float*>(stsc);
+    pb->ctl = reinterpret_cast<dsa::PruneRowCtl*>(ctl);
+    pb->hist = reinterpret_cast<uint32_t*>(hist);
+    pb->mask = reinterpret_cast<uint64_t*>(mask);
+    pb->mask_stride = (int)mwords;
   }
   return off;
 }

@@ -40,7 +40,30 @@ hipError_t launch_select_rows(const Problem& p, const float* scores, const uint3
 hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
                               float* out_score, hipStream_t st);
 
+// Streaming Top-K of the rows whose row_flag[b*Q + t] is non-zero only (the
+// pruned path's recovery); other rows' outputs are left as they are.
+hipError_t launch_topk_stream_rows(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
+                                   float* out_score, const int32_t* row_flag, const char* prof_name, hipStream_t st);
+
 // ---------------------------------------------------------------- pruned path
+
+// Per-row state of the pruned path between its launches (device memory).
+struct PruneRowCtl {
+  uint64_t thr;       // running threshold record
+  int32_t cnt;        // records in the row's candidate buffer
+  uint32_t base;      // threshold histogram: code of bin 0
+  int32_t shift;      // threshold histogram: log2 of the bin width
+  int32_t added;      // records kept since the last threshold raise
+  int32_t screened;   // statistics: bounded keys
+  int32_t survived;   // statistics: keys whose bound reached the threshold
+  float tau;          // threshold from the seeds
+  int32_t pad[3];
+};
+
+// Longest key chunk of the screen/refine schedule.
+constexpr int kMaxPruneChunk = 131072;
+// Bitmask words per row: the longest chunk of the schedule for N keys / 64.
+int prune_mask_words(int N);
 
 // Device buffers of the pruned Top-K (workspace carve-up and optional stats).
 struct PrunedBuffers {
@@ -60,6 +83,10 @@ struct PrunedBuffers {
   int32_t* seed_pos;      // [B*Q]: (number of the row's visible seeds) - 1
   int32_t* seed_top_idx;  // [B*Q][topk]: the row's exact seed Top-K (seed numbers, -1 padded)
   float* seed_top_score;  // [B*Q][topk]: their scores
+  PruneRowCtl* ctl;       // [B*Q]
+  uint32_t* hist;         // [B*Q][256]
+  uint64_t* mask;         // [B*Q][mask_stride]
+  int mask_stride;
   float* st_tau;
   int32_t* st_screened;
   int32_t* st_surv;

@@ -9,6 +9,21 @@
 namespace dsa {
 
 
+// Orders one wave's LDS accesses across its lanes (a value one lane stored
+// is then visible to the others): a wavefront-scope fence plus a scheduling
+// barrier.  No workgroup barrier is involved.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Orders a wave's global-memory accesses across its lanes: the candidate
+// buffer of a row is written and read only by the row's wave, so a
+// workgroup-scope fence suffices (the waves of a workgroup share one CU's
+// vector L1, and this waits for the wave's stores); an agent-scope fence
+// would also write back and invalidate the whole L2 of the XCD.
+__device__ __forceinline__ void row_mem_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+
 // Candidate bookkeeping of one row (one wave): records are appended to a
 // small LDS stage during a tile and flushed to the row's global buffer at the
 // start of the next tile, so the tile-end wait for the next key tile never
@@ -30,7 +45,7 @@ struct Cut {
 static __device__ __noinline__ Cut cut_candidates_d8(uint64_t* buf, int cnt, const uint64_t* stage, int nst,
                                                      uint32_t* hist, int topk, int goal, int lane) {
   cnt = flush_stage(buf, cnt, stage, nst, lane);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  row_mem_sync();
   const SelectResult sel = select_records_d8(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)goal, lane);
   return {compact_records_d8(buf, cnt, sel, lane), sel.prefix};
 }
@@ -39,7 +54,7 @@ static __device__ __noinline__ Cut cut_candidates_d8(uint64_t* buf, int cnt, con
 static __device__ __noinline__ void emit_topk_d8(uint64_t* buf, int cnt, const uint64_t* stage, int nst,
                                                  uint32_t* hist, int topk, int32_t* oi, float* os, int lane) {
   cnt = flush_stage(buf, cnt, stage, nst, lane);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  row_mem_sync();
   const int need = min(topk, cnt);
   SelectResult sel = {0, 0, 0};
   if (need > 0) sel = select_records_d8(buf, cnt, (uint32_t)need, hist, true, 0, lane);
@@ -109,15 +124,15 @@ static __device__ __noinline__ Rebuilt rebuild_candidates(uint64_t* buf, int cnt
                                                           uint32_t* hist, uint64_t thr, int topk, int goal,
                                                           int lane) {
   cnt = flush_stage(buf, cnt, stage, nst, lane);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  row_mem_sync();
   cnt = compact_records_d8(buf, cnt, SelectResult{thr, ~0ull, 0u}, lane);
   if (cnt > goal) {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+    row_mem_sync();
     const SelectResult sel = select_records_d8(buf, cnt, (uint32_t)topk, hist, false, (uint32_t)goal, lane);
     cnt = compact_records_d8(buf, cnt, sel, lane);
     thr = sel.prefix;
   }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+  row_mem_sync();
   const uint32_t base = (uint32_t)(thr >> 32);
   uint32_t mx = base;
   for (int i = lane; i < cnt; i += 64) mx = max(mx, (uint32_t)(buf[i] >> 32));

@@ -1,28 +1,42 @@
-// topk_pruned.hip -- exact Top-K with certified (DoSA) pruning, fused.
+// topk_pruned.hip -- exact Top-K with certified (DoSA) pruning, in key chunks.
 //
 // Flow per query row (DoSA reading notes, annotation LBKERZAW, steps 1-3;
 // 机器之心 DoSA article, sections 03-04, Fig. 2-3):
 //   1. seeds: the seed keys are scored with all heads by the same routine as
-//      every other path and go into the row's candidate buffer; the K-th best
-//      seed record is the threshold tau (K distinct visible keys reach it, so
-//      it cannot exceed the true K-th score);
-//   2. screen: every other visible key gets the certified upper bound U from
-//      32 plan rows (up to 30 retained heads, the folded negative-head row,
-//      the linear row; see prune_prep.hip) -- one 32x32 MFMA block per 32
-//      keys -- and survives iff U reaches the row's running threshold; a
-//      64-lane ballot packs the survivors of a block into a bitmask;
-//   3. compact + refine: survivors are queued per row and rescored with all
-//      heads in batches of 32 (key rows gathered by index, same score
-//      routine), and only records not below the threshold are kept as
-//      candidates;
-//   4. select: the row's candidates (seed Top-K and refined survivors) are cut
-//      to the exact Top-K by score, then key index.
-// The running threshold starts at tau and only rises when the candidate
-// buffer is cut (the K-th best exact score found so far), which is valid for
-// the same reason as tau.  The bounds never rank: only exact scores do.
-// Recovery: a row flagged by the planner (non-finite plan, forced, invalid
-// seeds) lets every key survive, i.e. runs the unpruned computation.
+//      every other path (the streaming Top-K over the packed seeds); the
+//      row's exact seed Top-K become its first candidate records and the
+//      K-th of them is the threshold tau (K distinct visible keys reach it,
+//      so it cannot exceed the true K-th score);
+//   2. screen: every other visible key of a key chunk gets the certified
+//      upper bound U from 32 plan rows (up to 30 retained heads, the folded
+//      negative-head row, the linear row; see prune_prep.hip) -- one 32x32
+//      MFMA block per 32 keys -- and survives iff U reaches the row's
+//      running threshold; a 64-lane ballot packs the survivors of 64 keys
+//      into one bitmask word, written to the workspace;
+//   3. compact + refine: the row's bitmask words are expanded into survivor
+//      key lists (popcount prefix sums) and the survivors are rescored with
+//      all heads in batches of 32 (key rows gathered by index, same score
+//      routine); records not below the threshold are kept as candidates,
+//      and the threshold rises to within one histogram bin of the K-th best
+//      exact record seen;
+//   4. select: after the last chunk the row's candidates (seed Top-K and
+//      refined survivors) are cut to the exact Top-K by score, then key index.
+// Keys are taken in chunks of growing length (the first ones short), each
+// chunk screened with the threshold the previous chunks' refinement left,
+// so most keys meet a threshold close to the row's final K-th score.  The
+// bounds never rank: only exact scores do.
+// Work split (gfx950): the screen shares each LDS key tile among 8 rows, two
+// per wave, so one key fragment read feeds two rows' MFMA blocks; the refine
+// runs one wave per row with no barriers, so rows with many survivors delay
+// only themselves.
+// Recovery: rows flagged by the planner (non-finite plan, forced, invalid
+// seeds) are skipped by the screen and refine and recomputed afterwards by
+// the unpruned streaming Top-K.
 #include <math.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
 
 #include "kernels.h"
 #include "stream_common.h"
@@ -33,42 +47,283 @@ constexpr int kPlanRowsK = 32;
 constexpr int kLinRowK = 31;
 constexpr int kAuxRowK = 30;
 constexpr int kRetainedK = 30;
-// Workgroup geometry per dtype: query rows per workgroup (one per wave), key
-// bytes of an LDS tile, tile slots (tiles are loaded kSlots - 1 ahead).  Both
-// dtypes use 8 rows on 32 KiB tiles in 3 slots, one workgroup per CU (4 rows
-// on 24 KiB tiles in 2 slots, two workgroups per CU, measured no faster on
-// fp8 keys: the per-tile work grows with the tile count).
-template <int DT>
-struct PrunedGeom;
-template <>
-struct PrunedGeom<kBF16> {
-  static constexpr int kWaves = 8, kTileBytes = 32768, kSlots = 3;
-};
-template <>
-struct PrunedGeom<kFP8> {
-  static constexpr int kWaves = 8, kTileBytes = 32768, kSlots = 3;
-};
-constexpr int kStage = 96;       // candidate stage records per row
+constexpr int kStage = 96;           // candidate stage records per row (refine)
+constexpr int kScreenWaves = 4;      // screen: waves per workgroup, two rows each
+constexpr int kScreenTile = 16384;   // screen: key bytes of an LDS tile
+constexpr int kScreenSlots = 3;      // screen: tile slots (two tiles loaded ahead)
+constexpr int kRefineWaves = 4;      // refine: rows per workgroup, one per wave
+constexpr int kGroupWords = 32;      // refine: bitmask words expanded at a time
+constexpr int kQueue = 64 * kGroupWords + 64;  // refine: survivor queue per row
 
-struct PrunePlan {
+static_assert(sizeof(PruneRowCtl) == 48, "row control block layout");
+
+struct PruneArgs {
   const uint8_t* rows;       // [R][32][128] dtype: bound rows
   const float* coef;         // [R][32]: c_0..c_29, aux multiplier, linear multiplier
   const float* misc;         // [R][4]: kappa, e_neg
   const int32_t* flag;       // [R]: 1 = recover (no pruning)
   const float* knorm;        // [B][N]: |k|, rounded up
   const int32_t* seeds;      // [B][seed_stride] ascending
-  const int32_t* seed_count; // [B]
   int seed_stride;
   const uint32_t* seed_bits; // [B][bits_stride]
   int bits_stride;
   const int32_t* seed_top_idx;   // [R][topk]: the row's exact seed Top-K (seed numbers, -1 padded)
   const float* seed_top_score;   // [R][topk]: their scores
+  PruneRowCtl* ctl;          // [R]
+  uint32_t* hist;            // [R][256]: threshold histogram between launches
+  uint64_t* mask;            // [R][mask_stride]: survivor bitmask of the current chunk
+  int mask_stride;
   float* st_tau;
   int32_t* st_screened;
   int32_t* st_surv;
   uint8_t* st_rec;
   float* st_ub;              // [R][N] debug bounds or null
 };
+
+// ---------------------------------------------------------------- 1. seeds
+
+// One wave per row: the row's seed Top-K records into its candidate buffer,
+// tau = the K-th of them, the threshold histogram fitted to them; the row's
+// state goes to its control block.
+__global__ __launch_bounds__(kRefineWaves * 64) void k_prune_init(int Q, size_t R, int topk, int cap,
+                                                                  uint64_t* __restrict__ cand, PruneArgs pa) {
+  __shared__ __align__(16) uint32_t hist[kRefineWaves][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * kRefineWaves + wave;
+  if (row >= R) return;  // whole wave; the waves share nothing
+  const int b = (int)(row / (size_t)Q);
+  uint32_t* my_hist = hist[wave];
+  for (int i = lane; i < 256; i += 64) my_hist[i] = 0u;
+  RowState rs{cand + row * (size_t)cap, 0, 0, 0, 0u, 24, 0};
+  const int32_t* si = pa.seed_top_idx + row * (size_t)topk;
+  const float* ss = pa.seed_top_score + row * (size_t)topk;
+  const int32_t* sd = pa.seeds + (size_t)b * pa.seed_stride;
+  int nk = 0;
+  for (int i0 = 0; i0 < topk; i0 += 64) {
+    const int i = i0 + lane;
+    const int32_t idx = i < topk ? si[i] : -1;
+    const bool ok = idx >= 0;
+    const uint64_t bal = __ballot(ok);
+    if (ok)
+      rs.buf[nk + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+          make_record(ss[i], (uint32_t)sd[idx]);
+    nk += __popcll(bal);
+  }
+  rs.cnt = nk;
+  row_mem_sync();
+  float tau = -INFINITY;
+  if (rs.cnt >= topk) {
+    rs.thr = min_record(rs.buf, rs.cnt, lane);
+    tau = record_score(rs.thr);
+  }
+  apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, nullptr, 0, my_hist, rs.thr, topk, cap, lane));
+  row_mem_sync();
+  uint32_t* gh = pa.hist + row * 256;
+  for (int i = lane; i < 256; i += 64) gh[i] = my_hist[i];
+  if (lane == 0) pa.ctl[row] = PruneRowCtl{rs.thr, rs.cnt, rs.base, rs.shift, 0, 0, 0, tau, {0, 0, 0}};
+}
+
+// ---------------------------------------------------------------- 2. screen
+
+// The screen side of one row: its 32 plan rows as one 32x32 MFMA A operand
+// and the bound's coefficients.  Lane l holds rows 8*(v/4) + 4*(l/32) + v%4
+// of a result block (v = 0..15), with their coefficients in cl[v]; rows 30
+// (aux) and 31 (linear) land in lanes 32..63 at v = 14, 15, whose cl is
+// zero: they enter the bound separately.
+template <int DT>
+struct ScreenRow {
+  Frag<DT> a;
+  float cl[16];
+  float m_aux, m_lin, kappa, e_neg, qscale, thr_f;
+  int vis;
+};
+
+template <int DT>
+__device__ __forceinline__ void load_screen_row(ScreenRow<DT>& sr, const PruneArgs& pa, const float* qsc, size_t row,
+                                                int vis, int lane) {
+  constexpr int RB = Frag<DT>::kRowBytes;
+  load_frag<DT>(sr.a, pa.rows + (row * kPlanRowsK + (lane & 31)) * RB, lane);
+  const float* co = pa.coef + row * kPlanRowsK;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    sr.cl[v] = r < kRetainedK ? co[r] : 0.0f;
+  }
+  sr.m_aux = co[kAuxRowK];
+  sr.m_lin = co[kLinRowK];
+  sr.kappa = pa.misc[row * 4 + 0];
+  sr.e_neg = pa.misc[row * 4 + 1];
+  sr.qscale = (DT == kFP8) ? qsc[row] : 1.0f;
+  sr.thr_f = record_floor(pa.ctl[row].thr);
+  sr.vis = vis;
+}
+
+// The bound of the 64 keys of two 32-key blocks (dA: keys kb..kb+31, dB:
+// kb+32..kb+63) for one row; lane l gets key kb + l.  Each lane's 16
+// retained-row terms in two chains per block, then one lane swap pairs the
+// two halves of every key's sum, and two more bring the aux and linear rows'
+// dots (rows 30, 31, held by lanes 32..63) to the same layout.
+template <int DT>
+__device__ __forceinline__ float pair_bound(const ScreenRow<DT>& sr, const f32x16& dA, const f32x16& dB, float kn,
+                                            float ks) {
+  float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    a0 = __builtin_fmaf(__builtin_fabsf(dA[v]), sr.cl[v], a0);
+    a1 = __builtin_fmaf(__builtin_fabsf(dA[v + 8]), sr.cl[v + 8], a1);
+    b0 = __builtin_fmaf(__builtin_fabsf(dB[v]), sr.cl[v], b0);
+    b1 = __builtin_fmaf(__builtin_fabsf(dB[v + 8]), sr.cl[v + 8], b1);
+  }
+  float sA = a0 + a1, sB = b0 + b1;
+  swap_halves(sA, sB);
+  float xA = dA[14], xB = dB[14], yA = dA[15], yB = dB[15];
+  swap_halves(xA, xB);  // xB: row-30 (aux) dot of key kb + lane
+  swap_halves(yA, yB);  // yB: row-31 (linear) dot of key kb + lane
+  float U = __builtin_fmaf(sr.m_lin, yB, sA + sB);
+  U -= relu_bits(__builtin_fmaf(sr.m_aux, xB, -sr.e_neg * kn));
+  U = __builtin_fmaf(sr.kappa, kn, U);
+  if constexpr (DT == kFP8) U = apply_scales(U, sr.qscale, ks);
+  return U;
+}
+
+// Screen of keys [k0, k1): 2 * kScreenWaves rows per workgroup (rows 2w and
+// 2w + 1 of the group in wave w) share each key tile; word (s - k0) / 64 of
+// a row's bitmask holds the survivors among keys s..s+63 (bit l: key s + l).
+// Words past the row's visible prefix are written as zero up to the end of
+// the workgroup's last tile; the refine reads only the words below the
+// row's prefix.  kBounds: also write every screened key's bound U to
+// pa.st_ub (diagnostics).
+template <int DT, bool kBounds>
+__global__ __launch_bounds__(kScreenWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_screen(
+    const float* __restrict__ qsc, const uint8_t* __restrict__ k, const float* __restrict__ ksc,
+    const int32_t* __restrict__ pos, int Q, int N, int k0, int k1, PruneArgs pa) {
+  using Tile = DirectTile<DT, kScreenTile, kScreenWaves>;
+  constexpr int RB = Frag<DT>::kRowBytes;
+  constexpr int KT = Tile::KT;     // keys per tile (64 bf16, 128 fp8)
+  constexpr int NP = KT / 64;      // 64-key pairs (bitmask words) per tile
+  constexpr int kAhead = kScreenSlots - 1;
+  __shared__ u32x4 ktile[kScreenSlots][direct_slots(kScreenTile)];
+  __shared__ float kscale_tile[kScreenSlots][KT];
+  __shared__ float knorm_tile[kScreenSlots][KT];
+  __shared__ uint32_t sbits_tile[kScreenSlots][64];
+  __shared__ uint32_t toff[kScreenWaves][Tile::PER_WAVE * 64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int group = gridDim.x - 1 - blockIdx.x;  // longest prefixes first
+  const int b = blockIdx.y;
+  constexpr int kRows = 2 * kScreenWaves;
+  // a row takes part if it exists and is not flagged for recovery
+  auto row_vis = [&](int t) {
+    if (t >= Q) return 0;
+    const size_t r = (size_t)b * Q + t;
+    return pa.flag[r] ? 0 : min(max(pos[r] + 1, 0), N);
+  };
+  int wg_end = k0;
+  for (int j = 0; j < kRows; ++j) wg_end = max(wg_end, min(k1, row_vis(group * kRows + j)));
+  const int t0 = group * kRows + 2 * wave;
+  const bool valid0 = t0 < Q, valid1 = t0 + 1 < Q;
+  const size_t row0 = (size_t)b * Q + min(t0, Q - 1), row1 = (size_t)b * Q + min(t0 + 1, Q - 1);
+  ScreenRow<DT> r0, r1;
+  load_screen_row<DT>(r0, pa, qsc, row0, row_vis(t0), lane);
+  load_screen_row<DT>(r1, pa, qsc, row1, row_vis(t0 + 1), lane);
+  uint64_t* mrow0 = pa.mask + row0 * (size_t)pa.mask_stride;
+  uint64_t* mrow1 = pa.mask + row1 * (size_t)pa.mask_stride;
+
+  const uint8_t* kbase = k + (size_t)b * N * RB;
+  const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
+  const float* knb = pa.knorm + (size_t)b * N;
+  const uint32_t* sbits = pa.seed_bits + (size_t)b * pa.bits_stride;
+  const int words = pa.bits_stride;
+  const int lk = lane & 31;
+  Tile tl;
+  tl.init(toff[wave], wave, lane);
+  const int ntiles = (wg_end - k0 + KT - 1) / KT;
+  for (int ti = 0; ti < min(ntiles, kAhead); ++ti) {
+    const int ts = k0 + ti * KT;
+    tl.load(ktile[ti], kbase, ts, N, lane);
+    if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ts, N, lane);
+    tl.load_words(knorm_tile[ti], knb, ts, N, lane);
+    tl.load_bits(sbits_tile[ti], sbits, ts, words, lane);
+  }
+  wait_vmem_all();
+  __syncthreads();
+
+  int screened0 = 0, screened1 = 0, survived0 = 0, survived1 = 0;
+  // bitmask words of the previous tile, lane j holding pair j; written at
+  // the start of the next tile so that the stores complete under its work
+  uint64_t pend0 = 0, pend1 = 0;
+  int pend_w = -1;
+  auto flush_words = [&]() {
+    if (pend_w >= 0 && lane < NP) {
+      if (valid0) mrow0[pend_w + lane] = pend0;
+      if (valid1) mrow1[pend_w + lane] = pend1;
+    }
+  };
+  int cur = 0;
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int nxt = cur == kScreenSlots - 1 ? 0 : cur + 1;
+    const int spare = cur + kAhead >= kScreenSlots ? cur + kAhead - kScreenSlots : cur + kAhead;
+    const int ts = k0 + ti * KT;
+    if (ti + kAhead < ntiles) {
+      const int tn = ts + kAhead * KT;
+      tl.load(ktile[spare], kbase, tn, N, lane);
+      if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, tn, N, lane);
+      tl.load_words(knorm_tile[spare], knb, tn, N, lane);
+      tl.load_bits(sbits_tile[spare], sbits, tn, words, lane);
+    }
+    flush_words();
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      Frag<DT> kfA, kfB;
+      Tile::frag(kfA, ktile[cur], 64 * pr + lk, lane);
+      Tile::frag(kfB, ktile[cur], 64 * pr + 32 + lk, lane);
+      const f32x16 dA0 = mma_block<DT>(r0.a, kfA, zero16());
+      const f32x16 dB0 = mma_block<DT>(r0.a, kfB, zero16());
+      const f32x16 dA1 = mma_block<DT>(r1.a, kfA, zero16());
+      const f32x16 dB1 = mma_block<DT>(r1.a, kfB, zero16());
+      const float kn = knorm_tile[cur][64 * pr + lane];
+      const float ks = (DT == kFP8) ? kscale_tile[cur][64 * pr + lane] : 1.0f;
+      const float U0 = pair_bound<DT>(r0, dA0, dB0, kn, ks);
+      const float U1 = pair_bound<DT>(r1, dA1, dB1, kn, ks);
+      const int key = ts + 64 * pr + lane;
+      const uint32_t seedw = sbits_tile[cur][2 * pr + (lane >> 5)];
+      const bool notseed = !((seedw >> lk) & 1u);
+      const bool ck0 = (key < r0.vis) & notseed, ck1 = (key < r1.vis) & notseed;
+      // U >= the threshold's float floor keeps every key whose record
+      // (U, key) reaches the threshold (and at most a few equal-bound keys
+      // below it, which the refine drops)
+      const uint64_t m0 = __ballot(ck0 & (U0 >= r0.thr_f));
+      const uint64_t m1 = __ballot(ck1 & (U1 >= r1.thr_f));
+      if constexpr (kBounds) {
+        if (ck0 && valid0) pa.st_ub[row0 * (size_t)N + key] = U0;
+        if (ck1 && valid1) pa.st_ub[row1 * (size_t)N + key] = U1;
+      }
+      screened0 += __popcll(__ballot(ck0));
+      screened1 += __popcll(__ballot(ck1));
+      survived0 += __popcll(m0);
+      survived1 += __popcll(m1);
+      pend0 = lane == pr ? m0 : pend0;
+      pend1 = lane == pr ? m1 : pend1;
+    }
+    pend_w = (ts - k0) / 64;
+    wait_vmem_all();  // this wave's loads of tile ti + kAhead and its bitmask stores have landed
+    __syncthreads();
+    cur = nxt;
+  }
+  flush_words();
+  if (lane == 0) {
+    if (valid0) {
+      pa.ctl[row0].screened += screened0;
+      pa.ctl[row0].survived += survived0;
+    }
+    if (valid1) {
+      pa.ctl[row1].screened += screened1;
+      pa.ctl[row1].survived += survived1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 3-4. refine, select
 
 // Keep the records of up to 64 lanes that reach the threshold (stage + one
 // histogram count each); a full buffer is compacted first.
@@ -90,337 +345,243 @@ __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live
   }
 }
 
-// kBounds: also write every screened key's bound U to pp.st_ub (diagnostics).
-template <int DT, bool kBounds>
-__global__ __launch_bounds__(PrunedGeom<DT>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_topk_pruned(
+// One wave per row, kRefineWaves rows per workgroup, no workgroup barrier:
+// the survivors of keys [k0, k1) listed in the row's bitmask are rescored
+// with all heads, 32 at a time, the next batch's key rows loading while the
+// current batch is scored; records that reach the threshold become
+// candidates, and every 32 kept records raise the threshold.  `final`: after
+// the last chunk, select the row's exact Top-K and write the statistics;
+// otherwise save the row's state for the next chunk.
+template <int DT>
+__global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_refine(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
-    int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
-    PrunePlan pp) {
-  constexpr int kWaves = PrunedGeom<DT>::kWaves, kTileBytes = PrunedGeom<DT>::kTileBytes;
-  constexpr int kSlots = PrunedGeom<DT>::kSlots, kAhead = kSlots - 1;  // tiles loaded ahead
-  using Tile = DirectTile<DT, kTileBytes, kWaves>;
+    size_t R, int k0, int k1, int final_chunk, int topk, int cap, uint64_t* __restrict__ cand,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score, PruneArgs pa) {
   constexpr int RB = Frag<DT>::kRowBytes;
-  constexpr int KT = Tile::KT;     // keys per tile (128 bf16, 256 fp8)
-  constexpr int NSB = KT / 32;     // 32-key blocks per tile (even)
-  constexpr int QCAP = KT + 96;    // survivor queue per row (see the refine schedule)
-  constexpr int kPend = (DT == kFP8) ? 2 : 1;  // refine batches in flight per tile (register budget)
-  __shared__ u32x4 ktile[kSlots][direct_slots(kTileBytes)];
-  __shared__ float kscale_tile[kSlots][KT];
-  __shared__ float knorm_tile[kSlots][KT];
-  __shared__ uint32_t sbits_tile[kSlots][64];
-  __shared__ __align__(16) uint32_t hist[kWaves][256];  // radix-select bins (8-bit digits), threshold histogram
-  __shared__ uint64_t stage[kWaves][kStage];  // candidate records awaiting a flush
-  __shared__ int32_t squeue[kWaves][QCAP + 64];  // survivor keys awaiting refinement (+ scratch)
-  __shared__ uint32_t toff[kWaves][Tile::PER_WAVE * 64];
-  __shared__ __align__(16) float wrow[kWaves][kHeads];
+  __shared__ __align__(16) uint32_t hist[kRefineWaves][256];
+  __shared__ uint64_t stage[kRefineWaves][kStage];
+  __shared__ int32_t queue[kRefineWaves][kQueue];
+  __shared__ __align__(16) float wrow[kRefineWaves][kHeads];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int group = gridDim.x - 1 - blockIdx.x;
-  const int b = blockIdx.y;
-  const int t = group * kWaves + wave;
-  const bool valid = t < Q;
-  const size_t row = (size_t)b * Q + min(t, Q - 1);
-  const int vis = valid ? min(max(pos[row] + 1, 0), N) : 0;
-  int wg_vis = 0;
-  for (int j = 0; j < kWaves; ++j) {
-    const int tj = group * kWaves + j;
-    if (tj < Q) wg_vis = max(wg_vis, min(max(pos[(size_t)b * Q + tj] + 1, 0), N));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * kRefineWaves + wave;
+  if (row >= R) return;  // whole wave; the waves share nothing
+  const int b = (int)(row / (size_t)Q);
+  const bool recover = pa.flag[row] != 0;
+  PruneRowCtl c = pa.ctl[row];
+  if (recover) {  // the streaming Top-K recomputes the row afterwards
+    if (final_chunk && lane == 0) {
+      if (pa.st_tau) pa.st_tau[row] = c.tau;
+      if (pa.st_screened) pa.st_screened[row] = 0;
+      if (pa.st_surv) pa.st_surv[row] = 0;
+      if (pa.st_rec) pa.st_rec[row] = 1;
+    }
+    return;
   }
-
-  // query rows in registers; head weights in LDS (read at each full epilogue)
-  Frag<DT> qa[2];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], q + (row * kHeads + 32 * blk + (lane & 31)) * RB, lane);
-  wrow[wave][lane] = w[row * kHeads + lane];
-  const float* my_w = wrow[wave];
-  const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
-
   uint32_t* my_hist = hist[wave];
   uint64_t* my_stage = stage[wave];
-  int32_t* my_q = squeue[wave];
-  for (int i = lane; i < 256; i += 64) my_hist[i] = 0u;  // threshold histogram (coarse bins until the first cut)
-  RowState rs{cand + row * (size_t)cap, 0, 0, 0, 0u, 24, 0};
-  const uint8_t* kbase = k + (size_t)b * N * RB;
-  const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
-  const float* knb = pp.knorm + (size_t)b * N;
-  const int nseed = pp.seed_count[b];
-  const int32_t* sd = pp.seeds + (size_t)b * pp.seed_stride;
-  const uint32_t* sbits = pp.seed_bits + (size_t)b * pp.bits_stride;
-  const int lk = lane & 31;
-  Tile tl;
-  tl.init(toff[wave], wave, lane);
+  int32_t* my_q = queue[wave];
+  const uint32_t* gh = pa.hist + row * 256;
+  for (int i = lane; i < 256; i += 64) my_hist[i] = gh[i];
+  RowState rs{cand + row * (size_t)cap, c.cnt, 0, c.thr, c.base, c.shift, c.added};
+  const int vis = min(max(pos[row] + 1, 0), N);
+  const int end = min(k1, vis);
+  const int W = end > k0 ? (end - k0 + 63) / 64 : 0;  // bitmask words to read
 
-  // Exact scores of up to 32 keys (lane l % 32: key keys_l, fragment f) go
-  // to the candidate buffer if their records reach the threshold.
-  auto score_and_keep = [&](const Frag<DT>& f, int key, float ks, bool live) {
-    float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
-    if constexpr (DT == kFP8) s = apply_scales(s, qscale, ks);
-    if (rs.nst > kStage - 32) {
-      rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
-      rs.nst = 0;
-    }
-    append_rec(rs, make_record(s, (uint32_t)key), live, my_stage, my_hist, topk, cap, lane);
-  };
-
-  // ---------------------------------------------------------------- 1. seeds
-  // The row's exact seed Top-K, scored beforehand by the streaming Top-K over
-  // the packed seed keys (the same score routine, so the same bits), become
-  // its first candidate records; tau is the K-th best of them.
-  {
-    const int32_t* si = pp.seed_top_idx + row * (size_t)topk;
-    const float* ss = pp.seed_top_score + row * (size_t)topk;
-    int nk = 0;
-    for (int i0 = 0; i0 < topk; i0 += 64) {
-      const int i = i0 + lane;
-      const int32_t idx = i < topk ? si[i] : -1;
-      const bool ok = valid && idx >= 0;  // rows past Q keep no records
-      const uint64_t bal = __ballot(ok);
-      if (ok)
-        rs.buf[nk + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
-            make_record(ss[i], (uint32_t)sd[idx]);
-      nk += __popcll(bal);
-    }
-    rs.cnt = nk;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
-  float tau = -INFINITY;
-  if (rs.cnt >= topk) {
-    rs.thr = min_record(rs.buf, rs.cnt, lane);
-    tau = record_score(rs.thr);
-  }
-  apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, my_stage, 0, my_hist, rs.thr, topk, cap, lane));
-  rs.added = 0;
-
-  // screen side: the 32 plan rows as one 32x32 MFMA A operand; lane l holds
-  // rows 8*(v/4) + 4*(l/32) + v%4 of the result (v = 0..15), with their
-  // coefficients in cl[v].  Rows 30 (aux) and 31 (linear) land in lanes
-  // 32..63 at v = 14, 15, whose cl is zero; they enter the bound separately.
-  Frag<DT> sa;
-  load_frag<DT>(sa, pp.rows + (row * kPlanRowsK + (lane & 31)) * RB, lane);
-  const float* co = pp.coef + row * kPlanRowsK;
-  float cl[16];
+  if (W > 0) {
+    Frag<DT> qa[2];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    cl[v] = r < kRetainedK ? co[r] : 0.0f;
-  }
-  const float m_aux = co[kAuxRowK], m_lin = co[kLinRowK];
-  const float kappa = pp.misc[row * 4 + 0], e_neg = pp.misc[row * 4 + 1];
-  const bool recover = pp.flag[row] != 0;
+    for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], q + (row * kHeads + 32 * blk + (lane & 31)) * RB, lane);
+    wrow[wave][lane] = w[row * kHeads + lane];
+    const float* my_w = wrow[wave];
+    const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
+    const uint8_t* kbase = k + (size_t)b * N * RB;
+    const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
+    const uint64_t* mrow = pa.mask + row * (size_t)pa.mask_stride;
+    const int lk = lane & 31;
 
-
-  // ---------------------------------------------------------------- 2-3. screen + refine
-  // Survivors are pushed to the row's queue my_q[qh, nq).  Refine schedule,
-  // per tile: at its start, pop up to kPend full batches of 32 queued
-  // survivors and issue the loads of their key rows (global memory; the rows
-  // were streamed moments ago, so they come from cache); score them at the
-  // tile's end, after the screen of the tile has covered the load latency.  A row whose
-  // queue still holds more than 96 keys at the tile's end refines further
-  // batches on the spot (rows with very many survivors, e.g. recovered
-  // rows), so the next tile's KT survivors always fit.
-  int qh = 0, nq = 0, screened = 0, survived = 0;
-  float thr_f = record_floor(rs.thr);
-  auto batch_keys = [&](int n) { return my_q[qh + (lk < n ? lk : 0)]; };
-  auto refine_now = [&](int n) {  // pop n <= 32 keys and rescore them synchronously
-    const int key = batch_keys(n);
-    Frag<DT> f;
-    load_frag<DT>(f, kbase + (size_t)key * RB, lane);
-    const float ks = (DT == kFP8) ? kscb[key] : 1.0f;
-    qh += n;
-    score_and_keep(f, key, ks, lane < n);
-  };
-  {
-    const int ntiles = (wg_vis + KT - 1) / KT;
-    const int words = pp.bits_stride;
-    for (int ti = 0; ti < min(ntiles, kAhead); ++ti) {
-      tl.load(ktile[ti], kbase, ti * KT, N, lane);
-      if constexpr (DT == kFP8) tl.load_words(kscale_tile[ti], kscb, ti * KT, N, lane);
-      tl.load_words(knorm_tile[ti], knb, ti * KT, N, lane);
-      tl.load_bits(sbits_tile[ti], sbits, ti * KT, words, lane);
-    }
-    wait_vmem_all();
-    __syncthreads();
-    int cur = 0;
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const int nxt = cur == kSlots - 1 ? 0 : cur + 1;
-      const int spare = cur + kAhead >= kSlots ? cur + kAhead - kSlots : cur + kAhead;  // tile ti + kAhead
-      const int ts = ti * KT;
-      if (rs.nst) {
+    // Survivor queue my_q[qh, qn): topped up from the bitmask, kGroupWords
+    // words at a time (lane j expands word g + j), whenever fewer than 64
+    // keys are queued.  The next group's words are loaded one refill ahead,
+    // so a refill never waits for memory behind the batches in flight.
+    int qh = 0, qn = 0, g = 0;
+    auto group_words = [&](int g0) { return (lane < kGroupWords && g0 + lane < W) ? mrow[g0 + lane] : 0ull; };
+    uint64_t wnext = group_words(0);
+    auto refill = [&]() {
+      while (qn - qh < 64 && g < W) {
+        if (qh > 0) {  // move the queue to the front
+          const int left = qn - qh;
+          for (int i = lane; i < left; i += 64) {
+            const int v = my_q[qh + i];
+            wave_lds_sync();
+            my_q[i] = v;
+          }
+          wave_lds_sync();
+          qn = left;
+          qh = 0;
+        }
+        const uint64_t word = wnext;
+        wnext = group_words(g + kGroupWords);
+        const uint32_t n = (uint32_t)__popcll(word);
+        const uint32_t incl = wave_prefix_incl(n, lane);
+        int at = qn + (int)(incl - n);
+        const int base_key = k0 + 64 * (g + lane);
+        for (uint64_t m = word; m; m &= m - 1) my_q[at++] = base_key + (int)__builtin_ctzll(m);
+        wave_lds_sync();
+        qn += (int)__builtin_amdgcn_readlane((int)incl, 63);
+        g += kGroupWords;
+      }
+    };
+    // exact scores of a batch (lane l % 32: key `key`, fragment f) go to the
+    // candidates if their records reach the threshold
+    auto score_and_keep = [&](const Frag<DT>& f, int key, float ks, bool live) {
+      float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
+      if constexpr (DT == kFP8) s = apply_scales(s, qscale, ks);
+      if (rs.nst > kStage - 32) {
         rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
         rs.nst = 0;
       }
-      // Keep the survivor threshold near the K-th best exact record seen so
-      // far (to within one histogram bin), at no buffer traffic.
-      if (rs.added >= kRaiseEvery) {
-        raise_threshold(rs, my_hist, topk, lane);
-        thr_f = record_floor(rs.thr);
-      }
-      if (ti + kAhead < ntiles) {
-        const int tn = (ti + kAhead) * KT;
-        tl.load(ktile[spare], kbase, tn, N, lane);
-        if constexpr (DT == kFP8) tl.load_words(kscale_tile[spare], kscb, tn, N, lane);
-        tl.load_words(knorm_tile[spare], knb, tn, N, lane);
-        tl.load_bits(sbits_tile[spare], sbits, tn, words, lane);
-      }
-      // refine batches, part 1: pop up to kPend full batches and issue the
-      // loads of their key rows
-      const int npend = min(kPend, (nq - qh) >> 5);
-      Frag<DT> rf[kPend];
-      int rkey[kPend];
-      float rks[kPend];
-#pragma unroll
-      for (int i = 0; i < kPend; ++i) {
-        rkey[i] = 0;
-        rks[i] = 1.0f;
-        if (i < npend) {
-          rkey[i] = batch_keys(32);
-          load_frag<DT>(rf[i], kbase + (size_t)rkey[i] * RB, lane);
-          if constexpr (DT == kFP8) rks[i] = kscb[rkey[i]];
-          qh += 32;
-        }
-      }
-      // screen, two 32-key blocks (64 keys, one per lane after the exchange)
-      // at a time: the 32x32 MFMA block of each (32 plan rows x 32 keys),
-      // each lane's 16 retained-row terms in two chains, then one lane swap
-      // pairs the two halves of every key's sum -- lane l ends up with key
-      // kb + l -- and two more bring the aux and linear rows' dots (rows 30,
-      // 31, held by lanes 32..63) to the same layout.
-      auto screen_pair = [&](int pr) {
-        const int kb = ts + 64 * pr;
-        Frag<DT> kf;
-        Tile::frag(kf, ktile[cur], 64 * pr + lk, lane);
-        const f32x16 dA = mma_block<DT>(sa, kf, zero16());
-        Tile::frag(kf, ktile[cur], 64 * pr + 32 + lk, lane);
-        const f32x16 dB = mma_block<DT>(sa, kf, zero16());
-        float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          a0 = __builtin_fmaf(__builtin_fabsf(dA[v]), cl[v], a0);
-          a1 = __builtin_fmaf(__builtin_fabsf(dA[v + 8]), cl[v + 8], a1);
-          b0 = __builtin_fmaf(__builtin_fabsf(dB[v]), cl[v], b0);
-          b1 = __builtin_fmaf(__builtin_fabsf(dB[v + 8]), cl[v + 8], b1);
-        }
-        float sA = a0 + a1, sB = b0 + b1;
-        swap_halves(sA, sB);
-        float xA = dA[14], xB = dB[14], yA = dA[15], yB = dB[15];
-        swap_halves(xA, xB);  // xB: row-30 (aux) dot of key kb + lane
-        swap_halves(yA, yB);  // yB: row-31 (linear) dot of key kb + lane
-        const float kn = knorm_tile[cur][64 * pr + lane];
-        float U = __builtin_fmaf(m_lin, yB, sA + sB);
-        U -= relu_bits(__builtin_fmaf(m_aux, xB, -e_neg * kn));
-        U = __builtin_fmaf(kappa, kn, U);
-        if constexpr (DT == kFP8) U = apply_scales(U, qscale, kscale_tile[cur][64 * pr + lane]);
-        const int key = kb + lane;
-        const uint32_t seedw = sbits_tile[cur][2 * pr + (lane >> 5)];
-        const bool ck = (key < vis) & !((seedw >> lk) & 1u);
-        // U >= the threshold's float floor keeps every key whose record
-        // (U, key) reaches the threshold (and at most a few equal-bound keys
-        // below it, which the refine drops)
-        const bool sv = ck & (recover | (U >= thr_f));
-        if constexpr (kBounds) {
-          if (ck) pp.st_ub[row * (size_t)N + key] = U;
-        }
-        screened += __popcll(__ballot(ck));
-        const uint64_t mask = __ballot(sv);  // bit l: key kb + l survives
-        const int before =
-            (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        my_q[sv ? nq + before : QCAP + lane] = key;  // branch-free: the others write scratch slots
-        nq += __popcll(mask);
-        survived += __popcll(mask);
-      };
-      if (ts + KT <= vis) {  // a whole visible tile: one straight run of pairs
-#pragma unroll
-        for (int pr = 0; pr < NSB / 2; ++pr) screen_pair(pr);
-      } else {
-#pragma unroll
-        for (int pr = 0; pr < NSB / 2; ++pr)
-          if (ts + 64 * pr < vis) screen_pair(pr);  // wave-uniform
-      }
-      // refine batches, part 2: score the popped keys
-#pragma unroll
-      for (int i = 0; i < kPend; ++i)
-        if (i < npend) score_and_keep(rf[i], rkey[i], rks[i], lane < 32);
-      // compact the queue to its front; refine on the spot while it is long
-      if (qh > 0) {
-        const int left = nq - qh;
-        for (int i = lane; i < left; i += 64) {
-          const int v = my_q[qh + i];
-          __builtin_amdgcn_wave_barrier();
-          my_q[i] = v;
-        }
-        nq = left;
-        qh = 0;
-      }
-      while (nq > QCAP - KT) {
-        refine_now(32);
-        const int left = nq - qh;
-        for (int i = lane; i < left; i += 64) {
-          const int v = my_q[qh + i];
-          __builtin_amdgcn_wave_barrier();
-          my_q[i] = v;
-        }
-        nq = left;
-        qh = 0;
-      }
-      thr_f = record_floor(rs.thr);
-      wait_vmem_all();
-      __syncthreads();
-      cur = nxt;
+      append_rec(rs, make_record(s, (uint32_t)key), live, my_stage, my_hist, topk, cap, lane);
+      if (rs.added >= kRaiseEvery) raise_threshold(rs, my_hist, topk, lane);
+    };
+    // Batches go through a ring of three fragments: two batches' key rows
+    // are loading while a third is scored.  A batch is issued
+    // unconditionally (an empty one reloads key 0, a valid row, never
+    // scored), so the loads form one straight sequence.
+    struct Batch {
+      Frag<DT> f;
+      int key, n;
+      float ks;
+    };
+    auto issue = [&](Batch& bt) {
+      refill();
+      bt.n = min(32, qn - qh);
+      bt.key = bt.n > 0 ? my_q[qh + (lk < bt.n ? lk : 0)] : 0;
+      load_frag<DT>(bt.f, kbase + (size_t)bt.key * RB, lane);
+      bt.ks = (DT == kFP8) ? kscb[bt.key] : 1.0f;
+      qh += bt.n;
+    };
+    Batch b0, b1, b2;
+    issue(b0);
+    issue(b1);
+    while (true) {
+      if (b0.n == 0) break;
+      issue(b2);
+      score_and_keep(b0.f, b0.key, b0.ks, lane < b0.n);
+      if (b1.n == 0) break;
+      issue(b0);
+      score_and_keep(b1.f, b1.key, b1.ks, lane < b1.n);
+      if (b2.n == 0) break;
+      issue(b1);
+      score_and_keep(b2.f, b2.key, b2.ks, lane < b2.n);
     }
-    while (nq > qh) refine_now(min(32, nq - qh));  // the last survivors
   }
 
-  // ---------------------------------------------------------------- 4. select
-  if (!valid) return;
+  if (!final_chunk) {
+    rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+    rs.nst = 0;
+    row_mem_sync();
+    uint32_t* ghw = pa.hist + row * 256;
+    for (int i = lane; i < 256; i += 64) ghw[i] = my_hist[i];
+    if (lane == 0) {
+      PruneRowCtl& cw = pa.ctl[row];
+      cw.thr = rs.thr;
+      cw.cnt = rs.cnt;
+      cw.base = rs.base;
+      cw.shift = rs.shift;
+      cw.added = rs.added;
+    }
+    return;
+  }
   emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
                out_score ? out_score + row * (size_t)topk : nullptr, lane);
   if (lane == 0) {
-    if (pp.st_tau) pp.st_tau[row] = tau;
-    if (pp.st_screened) pp.st_screened[row] = screened;
-    if (pp.st_surv) pp.st_surv[row] = survived;
-    if (pp.st_rec) pp.st_rec[row] = recover ? 1 : 0;
+    if (pa.st_tau) pa.st_tau[row] = c.tau;
+    if (pa.st_screened) pa.st_screened[row] = c.screened;
+    if (pa.st_surv) pa.st_surv[row] = c.survived;
+    if (pa.st_rec) pa.st_rec[row] = 0;
   }
 }
 
-#define DSA_PRUNED_KERNEL(DT_, B_)                                                                             \
-  template __global__ void k_topk_pruned<DT_, B_>(const uint8_t* __restrict__, const uint8_t* __restrict__,   \
-                                                  const float* __restrict__, const float* __restrict__,       \
-                                                  const float* __restrict__, const int32_t* __restrict__, int, \
-                                                  int, int, int, uint64_t* __restrict__, int32_t* __restrict__, \
-                                                  float* __restrict__, PrunePlan);
-DSA_PRUNED_KERNEL(kBF16, false)
-DSA_PRUNED_KERNEL(kBF16, true)
-DSA_PRUNED_KERNEL(kFP8, false)
-DSA_PRUNED_KERNEL(kFP8, true)
-#undef DSA_PRUNED_KERNEL
+#define DSA_SCREEN_KERNEL(DT_, B_)                                                                                \
+  template __global__ void k_screen<DT_, B_>(const float* __restrict__, const uint8_t* __restrict__,             \
+                                             const float* __restrict__, const int32_t* __restrict__, int, int, int, \
+                                             int, PruneArgs);
+DSA_SCREEN_KERNEL(kBF16, false)
+DSA_SCREEN_KERNEL(kBF16, true)
+DSA_SCREEN_KERNEL(kFP8, false)
+DSA_SCREEN_KERNEL(kFP8, true)
+#undef DSA_SCREEN_KERNEL
 
 __global__ void k_fill_nan(float* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = __builtin_nanf("");
 }
 
+// Key chunks of the screen/refine schedule: the first two of
+// max(8192, N / 16) keys (rounded up to 8192), then lengths doubling up to
+// kMaxPruneChunk.  Boundaries are multiples of 8192: whole screen tiles and
+// bitmask words.
+std::vector<std::pair<int, int>> prune_chunks(int N) {
+  std::vector<std::pair<int, int>> out;
+  int len = std::max(8192, (N / 16 + 8191) / 8192 * 8192);
+  for (int s = 0; s < N;) {
+    const int e = (int)std::min<int64_t>((int64_t)s + len, N);
+    out.emplace_back(s, e);
+    s = e;
+    if (out.size() >= 2) len = std::min(2 * len, kMaxPruneChunk);
+  }
+  return out;
+}
+
+int prune_mask_words(int N) {
+  int mx = 0;
+  for (const auto& c : prune_chunks(N)) mx = std::max(mx, c.second - c.first);
+  // the screen writes whole tiles (up to 128 keys, two words) past a
+  // chunk's last key
+  return (mx + 127) / 128 * 2;
+}
+
 hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx, float* out_score,
                               const PrunedBuffers& pb, hipStream_t st) {
+  const size_t R = (size_t)p.B * p.Q;
+  PruneArgs pa{pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag, pb.knorm, pb.seeds, pb.seed_stride,
+               pb.seed_bits, pb.bits_stride, pb.seed_top_idx, pb.seed_top_score, pb.ctl, pb.hist, pb.mask,
+               pb.mask_stride, pb.st_tau, pb.st_screened, pb.st_surv, pb.st_rec, pb.st_ub};
   if (pb.st_ub) {
-    const size_t n = (size_t)p.B * p.Q * p.N;
+    const size_t n = R * p.N;
     hipLaunchKernelGGL(k_fill_nan, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pb.st_ub, n);
   }
-  PrunePlan pp{pb.plan_rows,    pb.plan_coef,    pb.plan_misc,      pb.plan_flag,    pb.knorm,
-               pb.seeds,        pb.seed_count,   pb.seed_stride,    pb.seed_bits,    pb.bits_stride,
-               pb.seed_top_idx, pb.seed_top_score, pb.st_tau,       pb.st_screened,  pb.st_surv,
-               pb.st_rec,       pb.st_ub};
-  const int waves = p.dtype == kBF16 ? PrunedGeom<kBF16>::kWaves : PrunedGeom<kFP8>::kWaves;
-  dim3 grid((p.Q + waves - 1) / waves, p.B);
-  const int prof_slot = prof_open("k_topk_pruned", st);
-  using Kern = void (*)(const uint8_t*, const uint8_t*, const float*, const float*, const float*, const int32_t*, int,
-                        int, int, int, uint64_t*, int32_t*, float*, PrunePlan);
-  const Kern kern = p.dtype == kBF16 ? (pb.st_ub ? k_topk_pruned<kBF16, true> : k_topk_pruned<kBF16, false>)
-                                     : (pb.st_ub ? k_topk_pruned<kFP8, true> : k_topk_pruned<kFP8, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(waves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos, p.Q, p.N, topk,
-                     cap, cand, out_idx, out_score, pp);
-  prof_close(prof_slot, st);
-  return hipGetLastError();
+  const dim3 rgrid((unsigned)((R + kRefineWaves - 1) / kRefineWaves));
+  int slot = prof_open("k_prune_init", st);
+  hipLaunchKernelGGL(k_prune_init, rgrid, dim3(kRefineWaves * 64), 0, st, p.Q, R, topk, cap, cand, pa);
+  prof_close(slot, st);
+
+  using ScreenKern = void (*)(const float*, const uint8_t*, const float*, const int32_t*, int, int, int, int,
+                              PruneArgs);
+  const ScreenKern screen = p.dtype == kBF16 ? (pb.st_ub ? k_screen<kBF16, true> : k_screen<kBF16, false>)
+                                             : (pb.st_ub ? k_screen<kFP8, true> : k_screen<kFP8, false>);
+  const dim3 sgrid((unsigned)((p.Q + 2 * kScreenWaves - 1) / (2 * kScreenWaves)), p.B);
+  const auto chunks = prune_chunks(p.N);
+  for (size_t c = 0; c < chunks.size(); ++c) {
+    const int k0 = chunks[c].first, k1 = chunks[c].second;
+    const int fin = c + 1 == chunks.size() ? 1 : 0;
+    slot = prof_open("k_screen", st);
+    hipLaunchKernelGGL(screen, sgrid, dim3(kScreenWaves * 64), 0, st, p.q_scale, p.k, p.k_scale, p.pos, p.Q, p.N, k0,
+                       k1, pa);
+    prof_close(slot, st);
+    slot = prof_open("k_refine", st);
+    if (p.dtype == kBF16)
+      hipLaunchKernelGGL(k_refine<kBF16>, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
+                         p.pos, p.Q, p.N, R, k0, k1, fin, topk, cap, cand, out_idx, out_score, pa);
+    else
+      hipLaunchKernelGGL(k_refine<kFP8>, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
+                         p.pos, p.Q, p.N, R, k0, k1, fin, topk, cap, cand, out_idx, out_score, pa);
+    prof_close(slot, st);
+  }
+  // recovery: flagged rows by the unpruned streaming Top-K
+  return launch_topk_stream_rows(p, topk, cap, cand, out_idx, out_score, pb.plan_flag, "k_topk_stream_recover", st);
 }
 
 }  // namespace dsa

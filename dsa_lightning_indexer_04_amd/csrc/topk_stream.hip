@@ -95,7 +95,8 @@ template <int DT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_topk_stream(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
-    int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+    int topk, int cap, uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score,
+    const int32_t* __restrict__ row_flag) {
   using Tile = DirectTile<DT, kTileBytes, kWaves>;
   constexpr int RB = Frag<DT>::kRowBytes;
   constexpr int KT = Tile::KT;   // keys per tile
@@ -110,14 +111,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int group = gridDim.x - 1 - blockIdx.x;  // longest prefixes first
   const int b = blockIdx.y;
   const int t = group * kWaves + wave;
-  const bool valid = t < Q;
+  // with row_flag, only the flagged rows are computed (and a workgroup with
+  // none returns at once)
+  auto taken = [&](int tj) { return tj < Q && (!row_flag || row_flag[(size_t)b * Q + tj] != 0); };
+  const bool valid = taken(t);
   const size_t row = (size_t)b * Q + min(t, Q - 1);
   const int vis = valid ? min(max(pos[row] + 1, 0), N) : 0;
   int wg_vis = 0;
+  bool any = false;
   for (int j = 0; j < kWaves; ++j) {
     const int tj = group * kWaves + j;
-    if (tj < Q) wg_vis = max(wg_vis, min(max(pos[(size_t)b * Q + tj] + 1, 0), N));
+    if (taken(tj)) {
+      any = true;
+      wg_vis = max(wg_vis, min(max(pos[(size_t)b * Q + tj] + 1, 0), N));
+    }
   }
+  if (!any) return;  // workgroup-uniform, before any barrier
 
   QuerySide<DT> qs;
   load_query<DT>(qs, q + row * kHeads * RB, w + row * kHeads, lane);
@@ -209,18 +218,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
                out_score ? out_score + row * (size_t)topk : nullptr, lane);
 }
 
-hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
-                              float* out_score, hipStream_t st) {
-  const int prof_slot = prof_open("k_topk_stream", st);
+hipError_t launch_topk_stream_rows(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
+                                   float* out_score, const int32_t* row_flag, const char* prof_name, hipStream_t st) {
+  const int prof_slot = prof_open(prof_name, st);
   dim3 grid((p.Q + kWaves - 1) / kWaves, p.B);
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(k_topk_stream<kBF16>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
-                       p.Q, p.N, topk, cap, cand, out_idx, out_score);
+                       p.Q, p.N, topk, cap, cand, out_idx, out_score, row_flag);
   else
     hipLaunchKernelGGL(k_topk_stream<kFP8>, grid, dim3(kWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
-                       p.Q, p.N, topk, cap, cand, out_idx, out_score);
+                       p.Q, p.N, topk, cap, cand, out_idx, out_score, row_flag);
   prof_close(prof_slot, st);
   return hipGetLastError();
+}
+
+hipError_t launch_topk_stream(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx,
+                              float* out_score, hipStream_t st) {
+  return launch_topk_stream_rows(p, topk, cap, cand, out_idx, out_score, nullptr, "k_topk_stream", st);
 }
 
 }  // namespace dsa
