@@ -7,14 +7,18 @@ pairs: key s is visible to a row at position p iff s <= p.
 
 Prints ONE JSON line.  Default workload: the 128K chunked-prefill block (8192
 rows at positions 122880..131071, 131072 keys, top-2048, bf16) through the
-certified-pruning path (all steps: seeds, plan, screen, refine, select), with
-the unpruned path and the 1M-key fp8 block reported beside it.
+unpruned streaming Top-K (dsa_indexer_topk).  Reported beside it ("also"):
+the certified-pruning path on the same block and on the 1M-key fp8 block
+(with the unpruned 1M run, for the pruned/unpruned time ratio), the 128K
+block with noisier queries (the filter-rate sensitivity), the 32K prefill,
+decode, the projections and the sparse attention consumer.
 
-The roofline object describes the dominant kernel of the timed path: its
-duration is the mean of HIP events the library records around each launch
-on the launch stream during the timed steps; its work is the matrix-product
-FLOPs one launch executes (2*64*128 per fully scored pair, 2*128*16 per
-screened pair), against MI355X's published dense MFMA peak for the dtype.
+The roofline object describes the dominant kernel of the timed path (the one
+with the most device time): its duration is the mean of HIP events the
+library records around each launch on the launch stream during the timed
+steps; its work is the matrix-product FLOPs its launches execute (2*64*128
+per fully scored pair; the pruned path's chunk screen 2*128*32 per bounded
+pair), against MI355X's published dense MFMA peak for the dtype.
 """
 from __future__ import annotations
 
@@ -60,13 +64,17 @@ def parse():
                     help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one)")
     ap.add_argument(
         "--also",
-        default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,prefill_32k:topk,"
+        default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,"
+        "chunked_prefill_128k_noise02:pruned,prefill_32k:topk,"
         "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla,"
         "sparse_mla_decode_64x128k:sparse_mla",
         help="comma list of extra workload[:path] runs (or 'none')",
     )
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0: sized to ~15 s)")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the oracle sample (at most; see --cpu-seconds)")
+    ap.add_argument("--cpu-seconds", type=float, default=25.0, help="stop the oracle sample after this much CPU time")
+    ap.add_argument("--cpu-also", default="context_1m_fp8",
+                    help="comma list of further workloads whose oracle is timed the same way (or 'none')")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (counter calibration) and exit")
     return ap.parse_args()
@@ -396,8 +404,10 @@ def run_sparse_mla(name, steps, warmup):
     return res
 
 
-def cpu_baseline(name, rows_wanted):
-    """Time the float64 oracle (scores + sort Top-K) on a bounded row sample."""
+def cpu_baseline(name, rows_wanted, max_seconds):
+    """Time the float64 oracle (scores + sort Top-K) on a bounded row sample:
+    the last row, the first, then rows drawn by rng(0), until rows_wanted
+    rows or max_seconds of oracle time; pairs/s of the sample."""
     from dsa_lightning_indexer_04_amd import inputs
     from oracle import indexer
 
@@ -413,12 +423,10 @@ def cpu_baseline(name, rows_wanted):
     rng = np.random.default_rng(0)
     Q = wl.num_q
     threads = _blas_threads()
-    order = [Q - 1, 0] + list(rng.permutation(Q))
+    order = [Q - 1, 0] + [int(t) for t in rng.permutation(Q) if t not in (0, Q - 1)]
     done_pairs, t_total, rows = 0, 0.0, 0
     for t in order:
-        if rows_wanted and rows >= rows_wanted:
-            break
-        if not rows_wanted and t_total > 15.0:
+        if rows >= rows_wanted or t_total > max_seconds:
             break
         t0 = time.perf_counter()
         if wl.dtype == "bf16":
@@ -436,9 +444,10 @@ def cpu_baseline(name, rows_wanted):
         "unit": "pairs/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{rows} of {Q} query rows of {name} (last, first, then random by rng(0)); "
-        f"float64 numpy scores + lexsort Top-K; {done_pairs} visible pairs in {t_total:.1f}s; "
-        "pairs/s of the sample",
+        "sample": f"{rows} of {Q} query rows of {name} (last, first, then random by rng(0)), stopped at "
+        f"{rows_wanted} rows or {max_seconds:.0f} s; float64 numpy scores + lexsort Top-K; {done_pairs} visible "
+        f"pairs in {t_total:.1f} s; pairs/s of the sample (the whole block at this rate: "
+        f"{wl.visible_pairs / (done_pairs / t_total):.0f} s)",
     }
 
 
@@ -503,11 +512,14 @@ def main():
         "launch_ms": main_res["dominant_ms"],
         "flops_per_launch": main_res["dominant_flops"],
     }
-    cpu = None
+    cpu, cpu_more = None, {}
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores ...")
-        cpu = cpu_baseline(args.workload, args.cpu_rows)
-        log(f"[bench] oracle: {cpu['value']:.3e} pairs/s on {cpu['cores']} threads")
+        cpu = cpu_baseline(args.workload, args.cpu_rows, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.3e} pairs/s on {cpu['cores']} threads ({cpu['sample'][:40]}...)")
+        for name in (args.cpu_also.split(",") if args.cpu_also and args.cpu_also != "none" else []):
+            cpu_more[name] = cpu_baseline(name, args.cpu_rows, args.cpu_seconds)
+            log(f"[bench] oracle {name}: {cpu_more[name]['value']:.3e} pairs/s")
     wl = inputs.WORKLOADS[args.workload]
     line = {
         "metric": "indexer scored query-key pairs/s (+Top-K)",
@@ -536,6 +548,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baselines_more": cpu_more,
         "detail": main_res,
         "also": extra,
     }

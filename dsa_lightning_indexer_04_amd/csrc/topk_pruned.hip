@@ -445,8 +445,8 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
       append_rec(rs, make_record(s, (uint32_t)key), live, my_stage, my_hist, topk, cap, lane);
       if (rs.added >= kRaiseEvery) raise_threshold(rs, my_hist, topk, lane);
     };
-    // Batches go through a ring of three fragments: two batches' key rows
-    // are loading while a third is scored.  A batch is issued
+    // Batches go through a ring of fragments: the next batches' key rows
+    // are loading while one is scored (fp8: two in flight, bf16: one).  A batch is issued
     // unconditionally (an empty one reloads key 0, a valid row, never
     // scored), so the loads form one straight sequence.
     struct Batch {
@@ -462,19 +462,32 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
       bt.ks = (DT == kFP8) ? kscb[bt.key] : 1.0f;
       qh += bt.n;
     };
-    Batch b0, b1, b2;
-    issue(b0);
-    issue(b1);
-    while (true) {
-      if (b0.n == 0) break;
-      issue(b2);
-      score_and_keep(b0.f, b0.key, b0.ks, lane < b0.n);
-      if (b1.n == 0) break;
+    if constexpr (DT == kBF16) {  // two batches (one in flight): a third would not fit the registers
+      Batch b0, b1;
       issue(b0);
-      score_and_keep(b1.f, b1.key, b1.ks, lane < b1.n);
-      if (b2.n == 0) break;
+      while (true) {
+        if (b0.n == 0) break;
+        issue(b1);
+        score_and_keep(b0.f, b0.key, b0.ks, lane < b0.n);
+        if (b1.n == 0) break;
+        issue(b0);
+        score_and_keep(b1.f, b1.key, b1.ks, lane < b1.n);
+      }
+    } else {
+      Batch b0, b1, b2;
+      issue(b0);
       issue(b1);
-      score_and_keep(b2.f, b2.key, b2.ks, lane < b2.n);
+      while (true) {
+        if (b0.n == 0) break;
+        issue(b2);
+        score_and_keep(b0.f, b0.key, b0.ks, lane < b0.n);
+        if (b1.n == 0) break;
+        issue(b0);
+        score_and_keep(b1.f, b1.key, b1.ks, lane < b1.n);
+        if (b2.n == 0) break;
+        issue(b1);
+        score_and_keep(b2.f, b2.key, b2.ks, lane < b2.n);
+      }
     }
   }
 
@@ -520,12 +533,12 @@ __global__ void k_fill_nan(float* p, size_t n) {
 }
 
 // Key chunks of the screen/refine schedule: the first two of
-// max(8192, N / 16) keys (rounded up to 8192), then lengths doubling up to
-// kMaxPruneChunk.  Boundaries are multiples of 8192: whole screen tiles and
+// max(4096, N / 32) keys (rounded up to 4096), then lengths doubling up to
+// kMaxPruneChunk.  Boundaries are multiples of 4096: whole screen tiles and
 // bitmask words.
 std::vector<std::pair<int, int>> prune_chunks(int N) {
   std::vector<std::pair<int, int>> out;
-  int len = std::max(8192, (N / 16 + 8191) / 8192 * 8192);
+  int len = std::max(4096, (N / 32 + 4095) / 4096 * 4096);
   for (int s = 0; s < N;) {
     const int e = (int)std::min<int64_t>((int64_t)s + len, N);
     out.emplace_back(s, e);

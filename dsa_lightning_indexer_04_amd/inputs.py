@@ -65,6 +65,7 @@ class Workload:
     pos_start: int  # row t sits at absolute position pos_start + t
     pruned: bool = False
     num_seeds: int = 12288
+    query_noise: float = QUERY_NOISE  # clustered queries: per-coordinate noise scale (sigma_q)
 
     @property
     def visible_pairs(self) -> int:
@@ -83,6 +84,12 @@ WORKLOADS = {
     ),
     "context_1m_fp8": Workload(
         "context_1m_fp8", 1, 16384, 1048576, 2048, "fp8", "clustered", 1032192, pruned=True
+    ),
+    # the 128K block with noisier queries (sigma_q = 0.2 instead of 0.05): the
+    # filter-rate sensitivity of the pruned path
+    "chunked_prefill_128k_noise02": Workload(
+        "chunked_prefill_128k_noise02", 1, 8192, 131072, 2048, "bf16", "clustered", 122880, pruned=True,
+        query_noise=0.2,
     ),
 }
 
@@ -118,7 +125,7 @@ def _draw_iid(rng: np.random.Generator, B: int, Q: int, N: int):
     return q, ks, w
 
 
-def _draw_clustered(rng: np.random.Generator, B: int, Q: int, N: int):
+def _draw_clustered(rng: np.random.Generator, B: int, Q: int, N: int, query_noise: float = QUERY_NOISE):
     ks, qs, ws = [], [], []
     for _ in range(B):
         g = rng.standard_normal((NUM_CENTROIDS, HEAD_DIM))
@@ -134,7 +141,7 @@ def _draw_clustered(rng: np.random.Generator, B: int, Q: int, N: int):
         heads = np.arange(HEADS)[None, :, None]
         mix[rows, heads, order[:, None, :]] = a
         q = np.einsum("thm,md->thd", mix, cent / np.float32(CENTROID_NORM)).astype(np.float32)
-        q += np.float32(QUERY_NOISE / math.sqrt(HEAD_DIM)) * rng.standard_normal(
+        q += np.float32(query_noise / math.sqrt(HEAD_DIM)) * rng.standard_normal(
             (Q, HEADS, HEAD_DIM), dtype=np.float32
         )
         qs.append(q)
@@ -153,12 +160,14 @@ def make_inputs(
     pos_start: int | None = None,
     seed: int = 0,
     positions: np.ndarray | None = None,
+    query_noise: float = QUERY_NOISE,
 ) -> dict:
     """Draw one seeded input set as CPU torch tensors.
 
     ``pos_start`` defaults to N - Q (the query block sits at the tail of the
     sequence, which is plain causal prefill when Q == N).  ``positions``
-    overrides it with an explicit [B, Q] int array.
+    overrides it with an explicit [B, Q] int array.  ``query_noise`` is the
+    clustered generator's query noise scale sigma_q.
     """
     if dtype not in ("bf16", "fp8"):
         raise ValueError(dtype)
@@ -166,7 +175,7 @@ def make_inputs(
     if dist == "iid":
         q, ks, w = _draw_iid(rng, batch, num_q, num_k)
     elif dist == "clustered":
-        q, ks, w = _draw_clustered(rng, batch, num_q, num_k)
+        q, ks, w = _draw_clustered(rng, batch, num_q, num_k, query_noise)
     else:
         raise ValueError(dist)
     if positions is None:
@@ -195,7 +204,8 @@ def make_inputs(
 def make_workload(wl: Workload | str, seed: int = 0) -> dict:
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
-    return make_inputs(wl.batch, wl.num_q, wl.num_k, wl.dtype, wl.dist, wl.pos_start, seed)
+    return make_inputs(wl.batch, wl.num_q, wl.num_k, wl.dtype, wl.dist, wl.pos_start, seed,
+                       query_noise=wl.query_noise)
 
 
 def evenly_spaced_seeds(num_seeds: int, common_prefix_end: int) -> np.ndarray:
