@@ -41,8 +41,15 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 # sources they were taken on: reported as null once the sources change.
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
-    # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("chunked_prefill_128k", "k_topk_stream"): ("d751b8c67fe2d476", 2284446, 1380304),
+    # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB), mean per dispatch
+    ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
+    ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
+    ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
+    ("chunked_prefill_128k", "k_screen"): ("50bc6806478191c1", 76939, 21442),
+    ("chunked_prefill_128k", "k_refine"): ("50bc6806478191c1", 755489, 73728),
+    ("context_1m_fp8", "k_screen"): ("50bc6806478191c1", 451924, 209237),
+    ("context_1m_fp8", "k_refine"): ("50bc6806478191c1", 3537469, 185685),
+    ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
     ("projection_prefill_128k", "k_proj_out"): ("61f24b18bb20f769", 1073178, 553001),
     ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
 }
@@ -210,6 +217,7 @@ def run_workload(name, path, steps, warmup):
     else:
         work = {n: pairs * PAIR_FLOPS for n in per_step if n in ("k_topk_stream", "k_scores")}
     for n, v in per_step.items():
+        v["traffic_per_launch"] = measured_traffic(name, n)  # HBM bytes from stored counter readings, or None
         v["flops"] = work.get(n, 0)
         v["tflops"] = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] > 0 else 0.0
         v["frac"] = v["tflops"] / PEAK_TFLOPS[wl.dtype]
@@ -236,10 +244,12 @@ def run_workload(name, path, steps, warmup):
         sk = per_step.get("k_scores", dv)
         ms = sk["ms"] / max(sk["launches"], 1e-9)
         res["roofline"] = {"bound": "hbm", "achieved": alg / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "kernel": "k_scores", "bytes_per_launch": alg}
+                           "unit": "GB/s", "kernel": "k_scores", "bytes_per_launch": alg,
+                           "traffic": measured_traffic(name, "k_scores")}
     else:
         res["roofline"] = {"bound": "mfma", "achieved": res["achieved_tflops"], "peak": peak, "unit": "TFLOP/s",
-                           "kernel": dk, "flops_per_launch": res["dominant_flops"]}
+                           "kernel": dk, "flops_per_launch": res["dominant_flops"],
+                           "traffic": measured_traffic(name, dk)}
     res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
     log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s; "
         + ", ".join(f"{n} {v['ms']:.3f} ms" + (f" ({100 * v['frac']:.1f}%)" if v["flops"] else "")
