@@ -104,6 +104,47 @@ def index_scores(qf: np.ndarray, kf: np.ndarray, w: np.ndarray, pos: np.ndarray)
     return out
 
 
+# ---------------------------------------------------------------- fp32 error bound
+
+U32 = 2.0**-24  # unit roundoff of fp32 (round to nearest)
+
+
+def gamma(n: int) -> float:
+    """gamma_n = n u / (1 - n u): the relative error bound of n fp32 roundings
+    in a sum or product chain (standard floating-point error analysis)."""
+    return n * U32 / (1.0 - n * U32)
+
+
+def score_error_bound_row(q_row: np.ndarray, keys: np.ndarray, w_row: np.ndarray, scale=None) -> np.ndarray:
+    """Bound on |I_fp32 - I| for one query row, for any evaluation that forms
+    each head's 128-term dot product and the 64-term weighted sum of ReLUs in
+    fp32 arithmetic (any summation order), from exact products of the input
+    values (bf16 x bf16 and e4m3 x e4m3 products are exact in fp32).
+
+    q_row [H, d], keys [n, d] in the units the products are formed in (bf16
+    values, or e4m3 code values for fp8), w_row [H].  ``scale`` (fp8 only):
+    q_scale * k_scale per key ([n] or scalar), applied to the fp32 sum by two
+    more roundings (the product of the scales, then the scaling).
+
+    With x_j the exact head dots and X_j their fp32 values,
+    |X_j - x_j| <= gamma_128 sum_d |q_jd k_d|; ReLU is 1-Lipschitz, so the
+    weighted sum of the ReLUs moves by at most gamma_128 A,
+    A = sum_j |w_j| sum_d |q_jd| |k_d|; its own fp32 evaluation adds at most
+    gamma_64 (B + gamma_128 A), B = sum_j |w_j| ReLU(x_j).
+    """
+    q = np.asarray(q_row, np.float64)
+    k = np.asarray(keys, np.float64)
+    w = np.asarray(w_row, np.float64)
+    A = (np.abs(w) @ np.abs(q)) @ np.abs(k).T  # [n]
+    B = np.abs(w) @ np.maximum(q @ k.T, 0.0)  # [n]
+    code = gamma(128) * A + gamma(64) * (B + gamma(128) * A)
+    if scale is None:
+        return code
+    sc = np.asarray(scale, np.float64)
+    exact = sc * (w @ np.maximum(q @ k.T, 0.0))
+    return sc * code * (1.0 + gamma(2)) + gamma(2) * np.abs(exact)
+
+
 # ---------------------------------------------------------------- Top-K
 
 

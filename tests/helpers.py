@@ -68,17 +68,47 @@ class OracleRows:
             q = indexer.decode_e4m3fn(self.qbits[b, t]) * float(self.qs[b, t])
         return indexer.index_score_row(q, self.keys(b)[:v], self.w[b, t])
 
+    def bound(self, b: int, t: int) -> np.ndarray:
+        """fp32 evaluation error bound of row (b, t)'s visible scores
+        (oracle.indexer.score_error_bound_row; fp8 in code units, scaled)."""
+        v = self.visible(b, t)
+        if self.dtype == "bf16":
+            return indexer.score_error_bound_row(indexer.decode_bf16(self.qbits[b, t]), self.keys(b)[:v], self.w[b, t])
+        k8 = indexer.decode_e4m3fn(self.kbits[b, :v])
+        q8 = indexer.decode_e4m3fn(self.qbits[b, t])
+        scale = np.float64(np.float32(self.qs[b, t])) * self.ks[b, :v].astype(np.float64)
+        return indexer.score_error_bound_row(q8, k8, self.w[b, t], scale=scale)
+
 
 def tol(dtype: str):
     return indexer.tolerance(dtype)
 
 
 def assert_rows_ok(orc: OracleRows, idx: np.ndarray, sc: np.ndarray | None, rows, k: int):
+    """Oracle acceptance of GPU Top-K rows; with returned scores, also each
+    score within the fp32 evaluation bound of its oracle score."""
     rtol, atol = tol(orc.dtype)
     for b, t in rows:
         ref = orc.row(b, t)
         errs = indexer.check_topk_row(idx[b, t], ref, k, rtol, atol, None if sc is None else sc[b, t])
         assert not errs, f"row ({b},{t}): {errs}"
+        if sc is not None:
+            assert_within_bound(orc, b, t, idx[b, t], sc[b, t], ref)
+
+
+def assert_within_bound(orc: OracleRows, b: int, t: int, idx_row, sc_row, ref=None):
+    """GPU scores of the valid entries of a row within the fp32 error bound
+    of the oracle (plus 1e-12 relative for the oracle's own rounding)."""
+    ref = orc.row(b, t) if ref is None else ref
+    valid = np.asarray(idx_row) >= 0
+    keys = np.asarray(idx_row)[valid].astype(np.int64)
+    if keys.size == 0:
+        return
+    bnd = orc.bound(b, t)[keys]
+    err = np.abs(np.asarray(sc_row, np.float64)[valid] - ref[keys])
+    ok = err <= bnd + 1e-12 * np.abs(ref[keys])
+    assert ok.all(), f"row ({b},{t}): {int((~ok).sum())} scores outside the fp32 bound, worst err/bound " \
+        f"{float((err / np.maximum(bnd, 1e-30)).max()):.3g}"
 
 
 def lexsort_topk_of_scores(S_row: np.ndarray, vis: int, k: int) -> np.ndarray:

@@ -26,6 +26,10 @@ def _check_scores(d, S):
             got = S[b, t, :v].astype(np.float64)
             err = np.abs(got - ref)
             assert np.all(err <= atol + rtol * np.abs(ref)), (b, t, float(err.max()))
+            # and within the fp32 evaluation bound (tight enough to expose a
+            # wrong scale or index, unlike the fp8 acceptance band)
+            bnd = orc.bound(b, t)
+            assert np.all(err <= bnd + 1e-12 * np.abs(ref)), (b, t, float((err / np.maximum(bnd, 1e-30)).max()))
             worst = max(worst, float(err.max()))
     return worst
 

@@ -257,3 +257,81 @@ def test_acceptance_check_accepts_exact_and_catches_mistakes():
     assert indexer.check_topk_row(short, s, k, 2e-3, 1e-3)
     off = s[good] * (1 + 1e-2)
     assert indexer.check_topk_row(row, s, k, 2e-3, 1e-3, gpu_scores=off)
+
+
+# ---------------------------------------------------------------- fp32 error bound
+
+
+def _fp32_score_row(q, k, w, rng):
+    """One fp32 evaluation of the score (float32 products and sums in a
+    random order per head, then a random-order weighted sum): a stand-in for
+    any fp32 evaluation order."""
+    q32, k32, w32 = q.astype(np.float32), k.astype(np.float32), w.astype(np.float32)
+    n, H = k.shape[0], q.shape[0]
+    out = np.zeros(n, np.float32)
+    for s in range(n):
+        x = np.zeros(H, np.float32)
+        for j in range(H):
+            prods = q32[j] * k32[s]  # exact: products of bf16 values
+            acc = np.float32(0.0)
+            for v in prods[rng.permutation(prods.size)]:
+                acc = np.float32(acc + v)
+            x[j] = acc
+        terms = w32 * np.maximum(x, np.float32(0.0))
+        acc = np.float32(0.0)
+        for v in terms[rng.permutation(H)]:
+            acc = np.float32(acc + v)
+        out[s] = acc
+    return out
+
+
+def test_error_bound_dominates_fp32_evaluations():
+    """The bound covers real fp32 evaluations (random summation orders) of
+    random bf16 rows, and is not vacuous: it stays below 5e-4 of the row's
+    score scale, a quarter of the bf16 acceptance band."""
+    from dsa_lightning_indexer_04_amd import inputs
+
+    rng = np.random.default_rng(5)
+    d = inputs.make_inputs(1, 3, 40, "bf16", "iid", seed=5)
+    qf, kf = indexer.dequantize(inputs.to_bits(d["q"]), inputs.to_bits(d["k"]), "bf16")
+    w = d["w"].numpy().astype(np.float64)
+    for t in range(3):
+        exact = indexer.index_score_row(qf[0, t], kf[0], w[0, t])
+        bound = indexer.score_error_bound_row(qf[0, t], kf[0], w[0, t])
+        got = _fp32_score_row(qf[0, t], kf[0], w[0, t], rng).astype(np.float64)
+        assert np.all(np.abs(got - exact) <= bound)
+        assert np.all(bound < 5e-4 * np.abs(exact).max())
+
+
+def test_error_bound_catches_a_scale_mistake():
+    """A 2% mistake in a key's scale (an fp8 indexing or scaling slip) is
+    outside the bound on every key scoring at least a quarter of the row's
+    largest |score|, while the acceptance band of the fp8 comparison (3e-2
+    relative) lets it pass."""
+    from dsa_lightning_indexer_04_amd import inputs
+
+    d = inputs.make_inputs(1, 2, 64, "fp8", "clustered", seed=2)
+    qb, kb = inputs.to_bits(d["q"]), inputs.to_bits(d["k"])
+    q8, k8 = indexer.decode_e4m3fn(qb[0, 0]), indexer.decode_e4m3fn(kb[0])
+    qs, ks = float(d["q_scale"][0, 0]), d["k_scale"][0].numpy().astype(np.float64)
+    w = d["w"].numpy()[0, 0].astype(np.float64)
+    exact = ks * qs * indexer.index_score_row(q8, k8, w)
+    bound = indexer.score_error_bound_row(q8, k8, w, scale=qs * ks)
+    wrong = exact * 1.02
+    big = np.abs(exact) >= 0.25 * np.abs(exact).max()
+    assert big.sum() >= 5
+    assert np.all(np.abs(wrong - exact)[big] > bound[big])
+    rtol, atol = indexer.tolerance("fp8")
+    assert np.all(np.abs(wrong - exact) <= atol + rtol * np.abs(exact))
+
+
+def test_error_bound_closed_form_on_a_hand_example():
+    """One head, one key: x = 0.5*2 + 0.25*(-4) + 1*3 = 3, w = -2:
+    A = 2*(1 + 1 + 3) = 10, B = 2*3 = 6, bound = g128*10 + g64*(6 + g128*10)."""
+    q = np.array([[0.5, 0.25, 1.0]])
+    k = np.array([[2.0, -4.0, 3.0]])
+    w = np.array([-2.0])
+    g128, g64 = indexer.gamma(128), indexer.gamma(64)
+    want = g128 * 10 + g64 * (6 + g128 * 10)
+    assert indexer.score_error_bound_row(q, k, w)[0] == pytest.approx(want, rel=1e-12)
+    assert indexer.gamma(1) == pytest.approx(2.0**-24, rel=1e-6)
