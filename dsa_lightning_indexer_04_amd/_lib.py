@@ -57,6 +57,9 @@ class PruneStats(ctypes.Structure):
         ("survivors", ctypes.c_void_p),
         ("recovered", ctypes.c_void_p),
         ("upper_bound", ctypes.c_void_p),
+        ("plan_rows", ctypes.c_void_p),
+        ("plan_coef", ctypes.c_void_p),
+        ("plan_misc", ctypes.c_void_p),
     ]
 
 
@@ -373,12 +376,15 @@ def topk_pruned(
     return_scores: bool = True,
     stats: bool = False,
     upper_bound: bool = False,
+    plan: bool = False,
     workspace=None,
 ):
     """Exact per-row Top-K with certified pruning; same index set as topk().
 
     Returns (idx, scores or None, stats dict or None).  stats holds per-row
-    tau, screened, survivors, recovered (and the debug upper bounds if asked).
+    tau, screened, survivors, recovered (and the debug upper bounds, and with
+    plan=True each row's exported bound plan: plan_rows [B,Q,32,128] in q's
+    dtype, plan_coef [B,Q,32], plan_misc [B,Q,2] = kappa, e_neg).
     """
     lib = load()
     inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
@@ -393,7 +399,7 @@ def topk_pruned(
     sc = torch.empty((B, Q, topk), dtype=torch.float32, device=dev) if return_scores else None
     st = None
     cst = PruneStats()
-    if stats or upper_bound:
+    if stats or upper_bound or plan:
         st = {
             "tau": torch.empty((B, Q), dtype=torch.float32, device=dev),
             "screened": torch.empty((B, Q), dtype=torch.int32, device=dev),
@@ -402,7 +408,12 @@ def topk_pruned(
         }
         if upper_bound:
             st["upper_bound"] = torch.empty((B, Q, k.shape[1]), dtype=torch.float32, device=dev)
-        cst = PruneStats(*(_ptr(st.get(n)) for n in ("tau", "screened", "survivors", "recovered", "upper_bound")))
+        if plan:
+            st["plan_rows"] = torch.empty((B, Q, 32, 128), dtype=q.dtype, device=dev)
+            st["plan_coef"] = torch.empty((B, Q, 32), dtype=torch.float32, device=dev)
+            st["plan_misc"] = torch.empty((B, Q, 2), dtype=torch.float32, device=dev)
+        cst = PruneStats(*(_ptr(st.get(n)) for n in ("tau", "screened", "survivors", "recovered", "upper_bound",
+                                                      "plan_rows", "plan_coef", "plan_misc")))
     _check(
         lib.dsa_indexer_topk_pruned(
             ctypes.byref(inp),

@@ -396,11 +396,17 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
   if ((rc = check_topk_outputs(in, topk, out_idx, out_score, workspace, workspace_bytes, need))) return rc;
   if (stats) {
     const uint64_t rows = (uint64_t)in->batch * in->num_q;
-    const Range outs[] = {span(stats->tau, rows * 4), span(stats->screened, rows * 4),
-                          span(stats->survivors, rows * 4), span(stats->recovered, rows),
-                          span(stats->upper_bound, rows * in->num_k * 4)};
-    const void* ptrs[] = {stats->tau, stats->screened, stats->survivors, stats->recovered, stats->upper_bound};
-    for (int i = 0; i < 5; ++i) {
+    const Range outs[] = {span(stats->tau, rows * 4),
+                          span(stats->screened, rows * 4),
+                          span(stats->survivors, rows * 4),
+                          span(stats->recovered, rows),
+                          span(stats->upper_bound, rows * in->num_k * 4),
+                          span(stats->plan_rows, rows * 32 * 128 * elem_bytes(in->dtype)),
+                          span(stats->plan_coef, rows * 32 * 4),
+                          span(stats->plan_misc, rows * 2 * 4)};
+    const void* ptrs[] = {stats->tau,         stats->screened,  stats->survivors, stats->recovered,
+                          stats->upper_bound, stats->plan_rows, stats->plan_coef, stats->plan_misc};
+    for (int i = 0; i < 8; ++i) {
       if (!ptrs[i]) continue;
       if ((rc = check_no_alias(in, outs[i]))) return rc;
       if (overlaps(outs[i], span(workspace, need))) return fail(DSA_ERR_INVALID_ARG, "stats overlap the workspace");
@@ -441,6 +447,20 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
                                         pc.force_recover, pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag,
                                         st))))
     return rc;
+  if (stats && (stats->plan_rows || stats->plan_coef || stats->plan_misc)) {  // debug export of the plans
+    const uint64_t rows = (uint64_t)in->batch * in->num_q;
+    if (stats->plan_rows &&
+        (rc = hip_status(hipMemcpyAsync(stats->plan_rows, pb.plan_rows, rows * 32 * 128 * elem_bytes(in->dtype),
+                                        hipMemcpyDeviceToDevice, st))))
+      return rc;
+    if (stats->plan_coef &&
+        (rc = hip_status(hipMemcpyAsync(stats->plan_coef, pb.plan_coef, rows * 32 * 4, hipMemcpyDeviceToDevice, st))))
+      return rc;
+    if (stats->plan_misc &&
+        (rc = hip_status(hipMemcpy2DAsync(stats->plan_misc, 2 * 4, pb.plan_misc, 4 * 4, 2 * 4, rows,
+                                          hipMemcpyDeviceToDevice, st))))
+      return rc;
+  }
   return hip_status(
       dsa::launch_topk_pruned(p, topk, dsa::stream_capacity(topk), cand, out_idx, out_score, pb, st));
 }

@@ -160,13 +160,28 @@ typedef struct dsa_prune_opts {
  *   survivors  [B,Q] int32 keys whose bound reached the running threshold
  *   recovered  [B,Q] uint8 1 if the row was recomputed by the unpruned path
  *   upper_bound [B,Q,N] fp32 debug: the bound of every non-seed visible key
- *              (NaN elsewhere); small shapes only, costs one extra pass    */
+ *              (NaN elsewhere); small shapes only, costs one extra pass
+ *   plan_rows  [B,Q,32,128] debug: each row's bound plan, in the input dtype
+ *              (bf16 bits or e4m3 codes): rows 0..29 the retained heads'
+ *              query rows (zero past the row's retained count), row 30 the
+ *              folded negative-head row q_neg, row 31 the linear row E
+ *   plan_coef  [B,Q,32] fp32 debug: c_0..c_29 (the |d_i| coefficients), the
+ *              q_neg multiplier, the E multiplier
+ *   plan_misc  [B,Q,2] fp32 debug: kappa (the |k| coefficient, guard
+ *              included) and e_neg (the |k| coefficient of q_neg's
+ *              rounding).  With d_i = plan_rows[i] . k in code units, the
+ *              screen's bound is (for fp8 times q_scale * k_scale)
+ *                U = sum_i c_i |d_i| + c_31 d_31 - ReLU(c_30 d_30 - e_neg |k|)
+ *                    + kappa |k|                                            */
 typedef struct dsa_prune_stats {
   float* tau;
   int32_t* screened;
   int32_t* survivors;
   uint8_t* recovered;
   float* upper_bound;
+  void* plan_rows;
+  float* plan_coef;
+  float* plan_misc;
 } dsa_prune_stats;
 
 /* Exact Top-K with certified pruning (DoSA reading notes, annotation

@@ -18,8 +18,15 @@ Sources:
 * 机器之心 article on DoSA (163.com), section 03: the same two quantities
   (threshold lower bound, per-candidate upper bound) and strict exclusion.
 
-The bound here is written term by term in that order; the GPU folds the same
-terms into per-retained-head coefficients, which is algebraically equal.
+The bound here is written term by term in that order.  The GPU evaluates a
+folded form of it (``bound_from_plan``): per retained head one coefficient of
+|d_i| plus one "linear" row E, which equals the term-by-term form when the
+plan is folded from the same projection (a_i ReLU(d) + b_i ReLU(-d) =
+(a_i + b_i)/2 |d| + (a_i - b_i)/2 d), while the GPU's own plans also carry
+rounding margins (rows stored in the input dtype, a guard on |k|) and fit
+the projection differently (nonnegative coefficients).  ``bound_from_plan``
+recomputes in float64 the bound of any such plan, so that a plan the GPU
+exports can be checked against the exact scores.
 """
 from __future__ import annotations
 
@@ -130,3 +137,26 @@ def pruned_topk_row(
     pool_scores = index_score_row(q_row, keys_visible[pool], w_row)
     order = np.lexsort((pool, -pool_scores))
     return pool[order[: min(int(k), n)]], tau, survive
+
+
+def bound_from_plan(rows, coef, kappa: float, e_neg: float, keys, scale=None) -> np.ndarray:
+    """The bound of a folded plan, in float64, for every key row in ``keys``.
+
+    rows [32, d]: rows 0..29 the retained heads' query rows (zero rows are
+    unused slots), row 30 the folded negative-head row q_neg, row 31 the
+    linear row E; coef [32]: c_0..c_29, the q_neg multiplier c_30, the E
+    multiplier c_31; kappa, e_neg: the |k| coefficients of the residual (and
+    any guard) and of q_neg's rounding.  With d_i = rows[i] . k,
+
+        U = sum_{i<30} c_i |d_i| + c_31 d_31 - ReLU(c_30 d_30 - e_neg |k|) + kappa |k|,
+
+    times ``scale`` (fp8: q_scale * k_scale per key) when given.  All values
+    are in the units the plan was built in (fp8 code units for fp8 inputs).
+    """
+    R = np.asarray(rows, np.float64)
+    c = np.asarray(coef, np.float64)
+    K = np.asarray(keys, np.float64)
+    d = R @ K.T  # [32, n]
+    kn = np.linalg.norm(K, axis=1)
+    U = c[:30] @ np.abs(d[:30]) + c[31] * d[31] - np.maximum(c[30] * d[30] - float(e_neg) * kn, 0.0) + float(kappa) * kn
+    return U if scale is None else np.asarray(scale, np.float64) * U

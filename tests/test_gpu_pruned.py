@@ -134,3 +134,48 @@ def test_pruned_small_and_degenerate():
         idx, sc, _ = dsa.topk_pruned(*args, k, **kw, num_seeds=64, num_retained=nret)
         _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
     assert_rows_ok(OracleRows(d), u_idx, u_sc, [(0, t) for t in range(Q)], k)
+
+
+@pytest.mark.parametrize("dtype,dist", [("bf16", "clustered"), ("bf16", "iid"), ("fp8", "clustered")])
+def test_exported_plans_certify_the_exact_scores(dtype, dist):
+    """Every row's bound plan, exported from the GPU and re-evaluated in
+    float64 by the oracle (oracle.prune.bound_from_plan), lies above the
+    exact score of every visible key -- the certificate holds in exact
+    arithmetic, not only against the GPU's own fp32 scores -- and the GPU's
+    fp32 bounds of the screened keys agree with it to fp32 rounding."""
+    from oracle import prune
+
+    need_gpu()
+    B, Q, N, k = 1, 12, 4000, 64
+    pos = np.sort(np.random.default_rng(7).integers(N // 2, N, size=(B, Q)), axis=1)
+    pos[:, -1] = N - 1
+    d = inputs.make_inputs(B, Q, N, dtype, dist, seed=77, positions=pos)
+    dd = to_device(d)
+    args, kw = call_args(dd)
+    log(f"plan export {dtype} {dist}")
+    _, _, st = dsa.topk_pruned(*args, k, **kw, num_seeds=512, stats=True, upper_bound=True, plan=True)
+    st = {n: v.cpu() for n, v in st.items()}
+    orc = OracleRows(d)
+    rows_bits = inputs.to_bits(st["plan_rows"])
+    coef, misc, U = st["plan_coef"].numpy(), st["plan_misc"].numpy(), st["upper_bound"].numpy()
+    for t in range(Q):
+        assert not st["recovered"][0, t]
+        v = orc.visible(0, t)
+        if dtype == "bf16":
+            prow = indexer.decode_bf16(rows_bits[0, t])
+            keys, scale = orc.keys(0)[:v], None
+        else:
+            prow = indexer.decode_e4m3fn(rows_bits[0, t])
+            keys = indexer.decode_e4m3fn(orc.kbits[0, :v])
+            scale = np.float64(orc.qs[0, t]) * orc.ks[0, :v].astype(np.float64)
+        Up = prune.bound_from_plan(prow, coef[0, t], misc[0, t, 0], misc[0, t, 1], keys, scale)
+        exact = orc.row(0, t)
+        assert np.all(Up >= exact), (t, float((exact - Up).max()))
+        m = ~np.isnan(U[0, t, :v])
+        assert m.sum() > 0
+        # scale of the terms the fp32 evaluation rounds: sum |c_i| |rows_i| . |k| plus the |k| terms
+        kn = np.linalg.norm(keys, axis=1)
+        mag = np.abs(coef[0, t]) @ (np.abs(prow) @ np.abs(keys).T) + (abs(misc[0, t, 0]) + abs(misc[0, t, 1])) * kn
+        if scale is not None:
+            mag = mag * scale
+        assert np.all(np.abs(U[0, t, :v][m] - Up[m]) <= 1e-5 * mag[m] + 1e-30), t

@@ -118,3 +118,74 @@ def test_pruned_flow_equals_plain_topk(dist, nret):
     ref = indexer.topk_row(indexer.index_score_row(q, K, w), k)
     assert sorted(sel.tolist()) == sorted(ref.tolist())
     assert tau <= indexer.kth_score(indexer.index_score_row(q, K, w), k)
+
+
+def _folded_plan(q, w, R, Nf):
+    """A plan folded from the term-by-term bound's own projection: rows = the
+    retained query rows, q_neg = sum_{N'} |w_j| q_j, E = sum_i e_i q_i with
+    a_i = w_i + sum_P w_j C_ji^+, b_i = sum_P w_j C_ji^-, c_i = (a_i + b_i)/2,
+    e_i = (a_i - b_i)/2, kappa = rho = sum_P w_j |r_j|, e_neg = 0."""
+    H = q.shape[0]
+    omitted = np.setdiff1d(np.arange(H), R)
+    P = omitted[w[omitted] > 0]
+    C, resid = prune.project_positive_heads(q, R, P)
+    a = w[R] + w[P] @ np.maximum(C, 0.0)
+    b = w[P] @ np.maximum(-C, 0.0)
+    rows = np.zeros((32, q.shape[1]))
+    rows[: len(R)] = q[R]
+    rows[30] = np.abs(w[Nf]) @ q[Nf]
+    rows[31] = ((a - b) / 2) @ q[R]
+    coef = np.zeros(32)
+    coef[: len(R)] = (a + b) / 2
+    coef[30] = coef[31] = 1.0
+    rho = w[P] @ np.linalg.norm(resid, axis=1)
+    return rows, coef, rho
+
+
+@pytest.mark.parametrize("dist", ["iid", "clustered"])
+@pytest.mark.parametrize("nret", [1, 12, 30])
+def test_plan_form_equals_the_term_by_term_bound(dist, nret):
+    """A plan folded from the same projection evaluates to the term-by-term
+    bound (the GPU's folded form is that bound, not a different one), and
+    dominates the exact scores; dropping the b_i half of the fold (a planted
+    mistake) changes it."""
+    q, K, w = _row(40 + nret, dist)
+    pos = np.nonzero(w > 0)[0]
+    R = pos[: min(nret, pos.size)]
+    Nf = np.nonzero(w < 0)[0]
+    rows, coef, rho = _folded_plan(q, w, R, Nf)
+    Up = prune.bound_from_plan(rows, coef, rho, 0.0, K)
+    Ut = prune.upper_bound(q, w, K, R, Nf)
+    scale = np.abs(w) @ np.linalg.norm(q, axis=1) * np.linalg.norm(K, axis=1)
+    assert np.allclose(Up, Ut, rtol=0, atol=1e-10 * scale.max())
+    assert np.all(Up >= indexer.index_score_row(q, K, w) - 1e-10 * scale)
+    # planted mistake: c_i = a_i / 2 (the ReLU(-d) half dropped)
+    H = q.shape[0]
+    omitted = np.setdiff1d(np.arange(H), R)
+    P = omitted[w[omitted] > 0]
+    C, _ = prune.project_positive_heads(q, R, P)
+    if P.size and np.any(C < 0):
+        bad = coef.copy()
+        bad[: len(R)] = (w[R] + w[P] @ np.maximum(C, 0.0)) / 2
+        assert not np.allclose(prune.bound_from_plan(rows, bad, rho, 0.0, K), Ut, rtol=0, atol=1e-10 * scale.max())
+
+
+def test_plan_margins_keep_the_bound_valid():
+    """Rounding the folded rows to bf16 and putting the rounding error on
+    |k| (|E - E_bf16| into kappa, |q_neg - q_neg_bf16| into e_neg) keeps the
+    plan's bound above every exact score."""
+    q, K, w = _row(77, "clustered")
+    R = np.nonzero(w > 0)[0][:20]
+    Nf = np.nonzero(w < 0)[0]
+    rows, coef, rho = _folded_plan(q, w, R, Nf)
+    r16 = indexer.decode_bf16(inputs.to_bits(torch_bf16(rows)))
+    e_lin = np.linalg.norm(rows[31] - r16[31]) * abs(coef[31])
+    e_neg = np.linalg.norm(rows[30] - r16[30])
+    Up = prune.bound_from_plan(r16, coef, rho + e_lin, e_neg, K)
+    assert np.all(Up >= indexer.index_score_row(q, K, w) - 1e-9)
+
+
+def torch_bf16(x):
+    import torch
+
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
