@@ -517,9 +517,11 @@ int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_ou
                            static_cast<const uint16_t*>(in->w_ik),
                            static_cast<const uint16_t*>(in->w_iw)};
   std::string err;
-  if (dsa::run_projection(p, mode, static_cast<uint8_t*>(q_out), q_scale, static_cast<uint8_t*>(k_out), k_scale,
-                          w_out, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream), &err))
-    return fail(DSA_ERR_HIP, err);
+  const int prc = dsa::run_projection(p, mode, static_cast<uint8_t*>(q_out), q_scale, static_cast<uint8_t*>(k_out),
+                                      k_scale, w_out, static_cast<uint8_t*>(workspace),
+                                      static_cast<hipStream_t>(stream), &err);
+  if (prc == 2) return fail(DSA_ERR_UNSUPPORTED, err);
+  if (prc) return fail(DSA_ERR_HIP, err);
   return DSA_OK;
 }
 

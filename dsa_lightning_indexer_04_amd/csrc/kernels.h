@@ -125,7 +125,9 @@ constexpr size_t kProjBlasScratch = size_t(32) << 20;
 int proj_block_tokens(int T, int requested);
 size_t proj_workspace_bytes(int T, int hidden, int block_tokens);
 // The GEMMs and the output pass; out 0 = fp8 + scales, 1 = bf16, 2 = fp32.
-// Returns 0, or 1 with *err set.
+// Returns 0; 1 with *err set on a HIP or rocBLAS failure; 2 with *err set
+// if the call would have to create the thread's rocBLAS handle while `st`
+// is capturing a graph.
 int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale, uint8_t* k_out, float* k_scale,
                    float* w_out, uint8_t* ws, hipStream_t st, std::string* err);
 

@@ -139,8 +139,10 @@ __global__ __launch_bounds__(kOutThreads) void k_proj_out(const float* __restric
 const char* blas_name(rocblas_status s) { return rocblas_status_to_string(s); }
 
 // One handle per thread and device (rocBLAS handles are not thread-safe).
-// They live until the process ends.
-rocblas_handle blas_handle(std::string* err) {
+// They live until the process ends.  Creating one allocates device memory,
+// which a stream under graph capture cannot take: a first call on a
+// capturing stream is refused (*unsupported set) instead.
+rocblas_handle blas_handle(hipStream_t st, std::string* err, bool* unsupported) {
   thread_local std::unordered_map<int, rocblas_handle> handles;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -149,6 +151,13 @@ rocblas_handle blas_handle(std::string* err) {
   }
   auto it = handles.find(dev);
   if (it != handles.end()) return it->second;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    *err = "the first dsa_indexer_project call on a thread and device creates a rocBLAS handle, which allocates: "
+           "make one call outside graph capture first";
+    *unsupported = true;
+    return nullptr;
+  }
   rocblas_handle h = nullptr;
   rocblas_status s = rocblas_create_handle(&h);
   if (s != rocblas_status_success) {
@@ -185,8 +194,9 @@ int run_projection(const ProjProblem& p, int out, uint8_t* q_out, float* q_scale
   uint16_t* wcat = reinterpret_cast<uint16_t*>(ws + up((size_t)blk * kQCols * 4) + up((size_t)p.T * kKWCols * 4));
   uint8_t* scratch = reinterpret_cast<uint8_t*>(wcat) + up((size_t)kKWCols * p.hidden * 2);
 
-  rocblas_handle h = blas_handle(err);
-  if (!h) return 1;
+  bool unsupported = false;
+  rocblas_handle h = blas_handle(st, err, &unsupported);
+  if (!h) return unsupported ? 2 : 1;
   rocblas_status s = rocblas_set_stream(h, st);
   if (s == rocblas_status_success) s = rocblas_set_workspace(h, scratch, kProjBlasScratch);
   if (s != rocblas_status_success) {

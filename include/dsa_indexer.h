@@ -258,7 +258,10 @@ enum { DSA_F32 = 2 }; /* projection outputs only: the raw fp32 projections */
  * the GEMM scratch.  The three products run as two rocBLAS GEMMs per token
  * block (X is read once for W_IK and W_IW together) on `stream`; the first
  * call on a thread and device creates that thread's rocBLAS handle, whose
- * state rocBLAS allocates then; after that the call allocates nothing.
+ * state rocBLAS allocates then; after that the call allocates nothing.  A
+ * first call on a stream that is capturing a HIP graph returns
+ * DSA_ERR_UNSUPPORTED (it would allocate): make one call outside capture
+ * first, after which captured calls are fine.
  * Results are bit-reproducible for a given shape: rocBLAS atomics are off.
  * Errors as for the other entry points; a rocBLAS failure is DSA_ERR_HIP.   */
 int dsa_indexer_project(const dsa_proj_inputs* in, int32_t out_dtype, void* q_out, float* q_scale, void* k_out,

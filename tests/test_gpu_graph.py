@@ -3,7 +3,8 @@ only (no allocation, memset or host synchronisation inside the library), so a
 captured call replays to the eager result.  Each graph is replayed several
 times with eager work and synchronisation between replays, and every replay
 is compared bit for bit with the eager call.  (The projection entry point
-runs rocBLAS and is not captured here.)"""
+runs rocBLAS and is not replayed here; its first call on a thread refuses
+a capturing stream, which the last test checks.)"""
 import math
 
 import numpy as np
@@ -83,3 +84,43 @@ def test_sparse_mla_graph_split_path():
     log("[graph] sparse mla")
     eager = dsa.sparse_mla(q, kv, idx, 1.0 / math.sqrt(576), workspace=ws)
     _replays_match(lambda: dsa.sparse_mla(q, kv, idx, 1.0 / math.sqrt(576), workspace=ws), eager)
+
+
+def test_projection_refuses_to_create_its_handle_under_capture():
+    """The projection's first call on a thread creates a rocBLAS handle, which
+    allocates: on a capturing stream that first call returns
+    DSA_ERR_UNSUPPORTED (the capture stays clean), and a later call outside
+    capture works.  Run on a fresh thread, whose handle does not exist yet."""
+    import threading
+
+    need_gpu()
+    d = {n: v.cuda() for n, v in inputs.make_projection_inputs(16, 256, 128, seed=1).items()}
+    args = (d["c_q"], d["x"], d["w_iq"], d["w_ik"], d["w_iw"])
+    ws = torch.empty(_lib.project_workspace_bytes(_lib.make_proj_struct(*args)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    seen = {}
+
+    def body():
+        try:
+            s = torch.cuda.Stream()
+            g = torch.cuda.CUDAGraph()
+            try:
+                with torch.cuda.graph(g, stream=s):
+                    dsa.project(*args, out="f32", workspace=ws)
+            except _lib.IndexerError as e:
+                seen["code"] = e.code
+            except Exception as e:  # the capture context may re-raise on exit
+                seen.setdefault("other", repr(e))
+            torch.cuda.synchronize()
+            out = dsa.project(*args, out="f32", workspace=ws)  # outside capture: creates the handle
+            torch.cuda.synchronize()
+            seen["after"] = bool(torch.isfinite(out["q"]).all().item())
+        except Exception as e:
+            seen["thread_error"] = repr(e)
+
+    th = threading.Thread(target=body)
+    th.start()
+    th.join(timeout=120)
+    log(f"[graph] projection under capture: {seen}")
+    assert seen.get("code") == 2, seen  # DSA_ERR_UNSUPPORTED
+    assert seen.get("after") is True
