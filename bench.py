@@ -67,11 +67,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunked_prefill_128k")
-    ap.add_argument("--path", choices=["auto", "topk", "pruned"], default="topk",
-                    help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one)")
+    ap.add_argument("--path", choices=["auto", "topk", "pruned", "pruned_tau"], default="topk",
+                    help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one; "
+                    "pruned_tau: the pruned path with every row's threshold starting at tau)")
     ap.add_argument(
         "--also",
-        default="chunked_prefill_128k:pruned,context_1m_fp8:topk,context_1m_fp8:pruned,"
+        default="chunked_prefill_128k:pruned,chunked_prefill_128k:pruned_tau,context_1m_fp8:topk,"
+        "context_1m_fp8:pruned,context_1m_fp8:pruned_tau,"
         "chunked_prefill_128k_noise02:pruned,prefill_32k:topk,"
         "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla,"
         "sparse_mla_decode_64x128k:sparse_mla",
@@ -158,24 +160,28 @@ def run_workload(name, path, steps, warmup):
     qs = None if d["q_scale"] is None else d["q_scale"].to(dev)
     ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
     del d
-    use_pruned = path == "pruned" or (path == "auto" and wl.pruned)
+    use_pruned = path in ("pruned", "pruned_tau") or (path == "auto" and wl.pruned)
+    start = "tau" if path == "pruned_tau" else "raised"
     inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
     stats = None
     if use_pruned:
-        opts = _lib.PruneOpts(0, 0, None, None)
+        opts = _lib.PruneOpts(0, 0, None, None, _lib.PRUNE_STARTS[start])
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                          device=dev)
 
         def call():
-            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False, workspace=ws)
+            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start, return_scores=False,
+                                   workspace=ws)
 
-        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, return_scores=False,
-                                   workspace=ws, stats=True)
+        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start,
+                                   return_scores=False, workspace=ws, stats=True)
         scr = int(st["screened"].sum().item())
         sur = int(st["survivors"].sum().item())
         seeds = min(12288, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced seeds, visible to every row
         stats = {"screened_pairs": scr, "survivor_pairs": sur, "seed_pairs": seeds,
-                 "filter_rate": 1.0 - sur / max(1, scr), "recovered_rows": int(st["recovered"].sum().item())}
+                 "filter_rate": 1.0 - sur / max(1, scr), "start": start,
+                 "recovered_rows": int((st["recovered"] != 0).sum().item()),
+                 "start_misses": int((st["recovered"] == 2).sum().item())}
     else:
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK, inp, wl.topk), dtype=torch.uint8, device=dev)
 
@@ -196,7 +202,7 @@ def run_workload(name, path, steps, warmup):
     pairs = wl.visible_pairs
     res = {
         "workload": name,
-        "path": "pruned" if use_pruned else "unpruned",
+        "path": ("pruned_tau" if start == "tau" else "pruned") if use_pruned else "unpruned",
         "dtype": wl.dtype,
         "visible_pairs": pairs,
         "ms_per_step": wall * 1e3 / steps,
@@ -506,9 +512,10 @@ def main():
         runs = [r for r in [main_res, *extra.values()]
                 if r["workload"] == wname and r["path"] not in ("project", "sparse_mla")]
         t = {r["path"]: r["ms_per_step"] for r in runs}
-        if "pruned" in t and "unpruned" in t:
+        if "unpruned" in t:
             for r in runs:
-                r["pruned_over_unpruned_time"] = t["pruned"] / t["unpruned"]
+                if r["path"] in ("pruned", "pruned_tau"):
+                    r["pruned_over_unpruned_time"] = t[r["path"]] / t["unpruned"]
     peak = PEAK_TFLOPS[main_res["dtype"]]
     roofline = {
         "bound": "mfma",

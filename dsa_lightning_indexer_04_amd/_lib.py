@@ -47,7 +47,13 @@ class PruneOpts(ctypes.Structure):
         ("num_retained", ctypes.c_int32),
         ("seed_idx", ctypes.c_void_p),
         ("force_recover", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+# Pruning flags (dsa_prune_opts.flags) and the starts they select.
+DSA_PRUNE_START_AT_TAU = 1 << 0
+PRUNE_STARTS = {"raised": 0, "tau": DSA_PRUNE_START_AT_TAU}
 
 
 class PruneStats(ctypes.Structure):
@@ -373,6 +379,7 @@ def topk_pruned(
     num_retained: int = 0,
     seed_idx=None,
     force_recover=None,
+    start: str = "raised",
     return_scores: bool = True,
     stats: bool = False,
     upper_bound: bool = False,
@@ -381,16 +388,22 @@ def topk_pruned(
 ):
     """Exact per-row Top-K with certified pruning; same index set as topk().
 
+    start: "raised" (default) starts each row's running threshold at a seed
+    record above tau, verified at the end (a row short of K records at its
+    start is recomputed unpruned); "tau" starts at tau, the K-th seed score.
     Returns (idx, scores or None, stats dict or None).  stats holds per-row
-    tau, screened, survivors, recovered (and the debug upper bounds, and with
-    plan=True each row's exported bound plan: plan_rows [B,Q,32,128] in q's
-    dtype, plan_coef [B,Q,32], plan_misc [B,Q,2] = kappa, e_neg).
+    tau, screened, survivors, recovered (1: plan/seeds/forced, 2: raised
+    start missed), the debug upper bounds, and with plan=True each row's
+    exported bound plan: plan_rows [B,Q,32,128] in q's dtype, plan_coef
+    [B,Q,32], plan_misc [B,Q,2] = kappa, e_neg.
     """
+    if start not in PRUNE_STARTS:
+        raise ValueError(f"start must be one of {sorted(PRUNE_STARTS)}, not {start!r}")
     lib = load()
     inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
     check_prune_args(seed_idx, force_recover, q.shape[0], q.shape[1], num_seeds)
     _check_device((("seed_idx", seed_idx), ("force_recover", force_recover)), q.device)
-    opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover))
+    opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover), PRUNE_STARTS[start])
     nbytes = workspace_bytes(DSA_OP_TOPK_PRUNED, inp, topk, opts)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
     B, Q = q.shape[:2]

@@ -170,9 +170,13 @@ struct PruneConfig {
   int num_retained;
   const int32_t* seed_idx;
   const uint8_t* force_recover;
+  bool raised_start;
 };
 
 int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
+  const uint32_t flags = o ? o->flags : 0u;
+  if (flags & ~(uint32_t)DSA_PRUNE_START_AT_TAU) return fail(DSA_ERR_INVALID_ARG, "unknown pruning flags");
+  pc->raised_start = !(flags & DSA_PRUNE_START_AT_TAU);
   pc->num_seeds = (o && o->num_seeds) ? o->num_seeds : 12288;
   pc->num_retained = (o && o->num_retained) ? o->num_retained : 30;
   pc->seed_idx = o ? o->seed_idx : nullptr;
@@ -415,6 +419,7 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
   dsa::PrunedBuffers pb{};
   uint64_t* cand = nullptr;
   pruned_layout(in, topk, pc, static_cast<uint8_t*>(workspace), &pb, &cand);
+  pb.raised_start = pc.raised_start ? 1 : 0;
   if (stats) {
     pb.st_tau = stats->tau;
     pb.st_screened = stats->screened;

@@ -57,7 +57,8 @@ struct PruneRowCtl {
   int32_t screened;   // statistics: bounded keys
   int32_t survived;   // statistics: keys whose bound reached the threshold
   float tau;          // threshold from the seeds
-  int32_t pad[3];
+  int32_t raised;     // 1: the row started above tau (needs K records at its start)
+  int32_t pad[2];
 };
 
 // Longest key chunk of the screen/refine schedule.
@@ -92,6 +93,7 @@ struct PrunedBuffers {
   int32_t* st_surv;
   uint8_t* st_rec;
   float* st_ub;
+  int raised_start;       // 1: rows start above tau (verified at the end; misses recover)
 };
 
 hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, int32_t* seeds, int32_t* seed_count,

@@ -11,7 +11,7 @@
 //     homogeneous,
 //       w_j ReLU(q_j.k) <= w_j sum_i [C_ji^+ ReLU(d_i) + C_ji^- ReLU(-d_i)]
 //                          + w_j |r_j| |k|;
-//   * negative-weight heads (none is retained): the selected subset N'
+//   * negative-weight heads (none is retained): all of them, N' = N,
 //     folded by |w| into one row q_neg; sum |w_j| ReLU(q_j.k) >= ReLU(q_neg . k).
 // Summing:  I <= sum_{i in R} [a_i ReLU(d_i) + b_i ReLU(-d_i)] + rho |k|
 //                - ReLU(q_neg . k),
@@ -191,9 +191,11 @@ __global__ __launch_bounds__(256) void k_seed_positions(const int32_t* __restric
 
 // ---------------------------------------------------------------- planner
 
-constexpr int kRetained = 30;   // retained heads: plan rows 0..29
+constexpr int kRetained = 30;   // retained heads: plan rows 0..29 (fp8: 0..27)
 constexpr int kAuxRow = 30;     // folded negative-head row
 constexpr int kLinRow = 31;     // linear row E
+constexpr int kLinLoRow = 28;   // fp8: low part of E, a |d| row
+constexpr int kAuxLoRow = 29;   // fp8: low part of q_neg, a |d| row
 constexpr int kPlanRows = 32;
 constexpr int kSweeps = 20;     // coordinate-descent sweeps of the projection
 constexpr int kSamples = 128;   // sample keys for the activation statistics
@@ -320,11 +322,11 @@ __global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
   const int nseed = seed_count[b];
   const int32_t* sb = seeds + (size_t)b * seed_stride;
   const int nsamp = min(kSamples, nseed > 0 ? nseed : vis);
-  float pa[2][16], pn[2][16];
+  float pa[2][16];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) pa[blk][v] = pn[blk][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) pa[blk][v] = 0.0f;
   for (int s0 = 0; s0 < nsamp; s0 += 32) {
     const int si = s0 + (lane & 31);
     const bool okc = si < nsamp;
@@ -335,30 +337,17 @@ __global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
     for (int blk = 0; blk < 2; ++blk) {
       const f32x16 x = mma_block<DT>(qa[blk], f, zero16());
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        pa[blk][v] += okc ? relu_bits(x[v]) : 0.0f;
-        pn[blk][v] += (okc && x[v] > 0.0f) ? 1.0f : 0.0f;
-      }
+      for (int v = 0; v < 16; ++v) pa[blk][v] += okc ? relu_bits(x[v]) : 0.0f;
     }
   }
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = pa[blk][v];
+  wave_sync();
   float act = 0.0f;
-  int npos = 0;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        red[32 * blk + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][lane & 31] = pass ? pn[blk][v] : pa[blk][v];
-    wave_sync();
-    float sum = 0.0f;
-    for (int c = 0; c < 32; ++c) sum += red[lane][c];
-    if (pass)
-      npos = (int)sum;
-    else
-      act = sum;
-    wave_sync();
-  }
+  for (int c = 0; c < 32; ++c) act += red[lane][c];
+  wave_sync();
 
   // 3. retained set: the (at most nret) positive-weight heads with the
   //    largest w_j * activation
@@ -370,6 +359,7 @@ __global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
   }
   const int npos_heads = __popcll(__ballot(wj > 0.0f));
   nret = min(nret, npos_heads);
+  if constexpr (DT == kFP8) nret = min(nret, kLinLoRow);  // rows 28, 29 hold the low parts
   const bool retained = wj > 0.0f && rank < nret;
   if (retained) ridx[rank] = lane;
   wave_sync();
@@ -489,12 +479,12 @@ __global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
   }
   rho *= 1.0f + 1e-5f;  // nonnegative terms: sum low by at most gamma_34
 
-  // 8. folded negative row: negative heads active on >= half the samples
-  //    (all negative heads if none is)
-  const bool negom = !retained && wj < 0.0f;
-  const bool act_half = negom && 2 * npos >= nsamp && nsamp > 0;
-  const bool use_half = __ballot(act_half) != 0;
-  const bool in_N = use_half ? act_half : negom;
+  // 8. folded negative row: every negative-weight head (none is retained).
+  //    Any subset gives a valid penalty: leaving a head out raises the fold
+  //    on keys where that head is inactive and lowers it where it is
+  //    active.  On keys that score near the K-th score the full fold
+  //    excludes the most (almost as many as exact per-head penalties would).
+  const bool in_N = !retained && wj < 0.0f;
 
   // 9. E = sum_a c_a q_a and q_neg = sum_N' |w_j| q_j in fp32 (lanes =
   //    dims) with their component error bounds gamma_n * (sum of |terms|)
@@ -519,52 +509,77 @@ __global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
     mN0 = __builtin_fmaf(aw, fabsf(qj0), mN0);
     mN1 = __builtin_fmaf(aw, fabsf(qj1), mN1);
   }
-  // row multipliers: 1 for bf16; for fp8 a power of two that brings the
-  // row's largest magnitude within the e4m3 range
-  double mult[2] = {1.0, 1.0};
-  if constexpr (DT == kFP8) {
-    float am[2] = {fmaxf(fabsf(E0), fabsf(E1)), fmaxf(fabsf(N0), fabsf(N1))};
+  // Stored rows.  bf16: E and q_neg rounded to bf16.  fp8 (3 mantissa
+  // bits): each is split into a high part x_h = e4m3(x / m_h) m_h (the
+  // linear / aux row) and a low part x_l = e4m3((x - x_h) / m_l) m_l (plan
+  // row 28 for E, 29 for q_neg), m_h, m_l powers of two that bring the
+  // part's largest magnitude within the e4m3 range.  The low parts enter
+  // the bound as |d| rows with coefficient m_l:
+  //   E.k <= x_h.k + |x_l.k| + |E - x_h - x_l| |k|, and
+  //   ReLU(q_neg.k) >= ReLU(x_h.k - e_neg |k|) - |x_l.k|
+  // (ReLU is monotone and 1-Lipschitz), so both stay upper bounds while the
+  // |k| coefficients shrink to the rounding error of the two-part sum.
+  // |x - stored| <= |x_fp32 - stored| + gamma_30 |mE| (q_neg: gamma_64),
+  // differences and norms in fp64.
+  auto pow2_step = [](float am) {  // smallest power of two m with am / m <= 448
+    return am > 0.0f ? ldexp(1.0, (int)ceil(log2((double)am / 448.0))) : 1.0;
+  };
+  auto wave_max_f = [](float x) {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-#pragma unroll
-      for (int dd = 32; dd >= 1; dd >>= 1) am[v] = fmaxf(am[v], __shfl_xor(am[v], dd, 64));
-      mult[v] = am[v] > 0.0f ? ldexp(1.0, (int)ceil(log2((double)am[v] / 448.0))) : 1.0;
-    }
-  }
-  // store the rounded rows; |E - E_stored| <= |E_fp32 - E_stored| + gamma_30 |mE|
-  // (likewise q_neg with gamma_64), differences and norms in fp64
+    for (int dd = 32; dd >= 1; dd >>= 1) x = fmaxf(x, __shfl_xor(x, dd, 64));
+    return x;
+  };
   uint8_t* prow = plan_rows + row * kPlanRows * RB;
-  double err2[2] = {0.0, 0.0}, nrm2[2] = {0.0, 0.0}, mag2[2] = {0.0, 0.0};
+  double err2[2] = {0.0, 0.0}, nrm2[2] = {0.0, 0.0}, mag2[2] = {0.0, 0.0}, lo2[2] = {0.0, 0.0};
+  double mult[2] = {1.0, 1.0}, mult_lo[2] = {1.0, 1.0};
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
+    const float xs[2] = {v == 0 ? E0 : N0, v == 0 ? E1 : N1};
+    const float gs[2] = {v == 0 ? mE0 : mN0, v == 0 ? mE1 : mN1};
+    if constexpr (DT == kFP8) mult[v] = pow2_step(wave_max_f(fmaxf(fabsf(xs[0]), fabsf(xs[1]))));
     uint8_t* dst = prow + (size_t)(v == 0 ? kLinRow : kAuxRow) * RB;
-    const float x0 = v == 0 ? E0 : N0, x1 = v == 0 ? E1 : N1;
-    const float g0 = v == 0 ? mE0 : mN0, g1 = v == 0 ? mE1 : mN1;
+    double stored[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int d = h ? d1 : d0;
-      const double x = h ? x1 : x0;
       uint32_t code;
-      const double rv = round_to_dtype<DT>(x / mult[v], &code) * mult[v];
+      stored[h] = round_to_dtype<DT>((double)xs[h] / mult[v], &code) * mult[v];
       if constexpr (DT == kBF16)
-        reinterpret_cast<uint16_t*>(dst)[d] = (uint16_t)code;
+        reinterpret_cast<uint16_t*>(dst)[h ? d1 : d0] = (uint16_t)code;
       else
-        dst[d] = (uint8_t)code;
-      err2[v] = fma(x - rv, x - rv, err2[v]);
-      nrm2[v] = fma(rv, rv, nrm2[v]);
-      const double g = h ? g1 : g0;
-      mag2[v] = fma(g, g, mag2[v]);
+        dst[h ? d1 : d0] = (uint8_t)code;
+      nrm2[v] = fma(stored[h], stored[h], nrm2[v]);
+    }
+    if constexpr (DT == kFP8) {
+      const double r[2] = {(double)xs[0] - stored[0], (double)xs[1] - stored[1]};  // exact
+      mult_lo[v] = pow2_step(wave_max_f(fmaxf((float)fabs(r[0]), (float)fabs(r[1]))));
+      uint8_t* dlo = prow + (size_t)(v == 0 ? kLinLoRow : kAuxLoRow) * RB;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t code;
+        const double lo = round_to_dtype<DT>(r[h] / mult_lo[v], &code) * mult_lo[v];
+        dlo[h ? d1 : d0] = (uint8_t)code;
+        stored[h] += lo;
+        lo2[v] = fma(lo, lo, lo2[v]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const double e = (double)xs[h] - stored[h];
+      err2[v] = fma(e, e, err2[v]);
+      mag2[v] = fma((double)gs[h], (double)gs[h], mag2[v]);
     }
     err2[v] = wave_sum_d(err2[v]);
     nrm2[v] = wave_sum_d(nrm2[v]);
     mag2[v] = wave_sum_d(mag2[v]);
+    lo2[v] = wave_sum_d(lo2[v]);
   }
   const double e_lin = (sqrt(err2[0]) + (double)gamma_f(32) * sqrt(mag2[0]) * (1.0 + 1e-6)) * (1.0 + 1e-12);
   const double e_neg = (sqrt(err2[1]) + (double)gamma_f(66) * sqrt(mag2[1]) * (1.0 + 1e-6)) * (1.0 + 1e-12);
-  const double n_lin = sqrt(nrm2[0]), n_neg = sqrt(nrm2[1]);
+  // norms of the high rows and (fp8) of the low rows, for the guard
+  const double n_lin = sqrt(nrm2[0]), n_neg = sqrt(nrm2[1]), n_lo = sqrt(lo2[0]) + sqrt(lo2[1]);
 
-  // retained rows: the query's own codes
-  for (int a = 0; a < kRetained; ++a) {
+  // retained rows: the query's own codes (fp8: rows 28, 29 hold the low parts)
+  for (int a = 0; a < (DT == kFP8 ? kLinLoRow : kRetained); ++a) {
     uint8_t* dst = prow + (size_t)a * RB;
     const uint8_t* src = qrow + (size_t)(a < nret ? ridx[a] : 0) * RB;
     for (int x = lane; x < RB / 4; x += 64)
@@ -582,17 +597,22 @@ __global__ __launch_bounds__(kPlanWaves * 64) void k_plan(
   const double u = 5.9604644775390625e-08;
   auto gam = [u](double n) { return n * u / (1.0 - n * u); };
   const double W1 = wave_sum_d(fabs((double)wj) * (double)qnorm);
-  double Wb = n_lin + n_neg;
+  double Wb = n_lin + n_neg + n_lo;
   for (int a = 0; a < nret; ++a) Wb += (double)cch[a] * (double)__shfl(qnorm, ridx[a], 64);
   const double guard =
       2.0 * ((gam(128) + 2.0 * gam(64) + gam(4)) * W1 + (gam(128) + gam(24)) * Wb + gam(24) * (e_neg + rho + e_lin));
   const double kappa = ((double)rho + e_lin + guard) * (1.0 + 1e-9);
 
-  bool finite = isfinite(kappa) && isfinite(e_neg) && isfinite(mult[0]) && isfinite(mult[1]);
+  bool finite = isfinite(kappa) && isfinite(e_neg) && isfinite(mult[0]) && isfinite(mult[1]) &&
+                isfinite(mult_lo[0]) && isfinite(mult_lo[1]);
   for (int a = 0; a < kRetained; ++a) finite = finite && isfinite(cch[a]);
   if (lane == 0) {
     float* co = plan_coef + row * kPlanRows;
     for (int a = 0; a < kRetained; ++a) co[a] = cch[a];
+    if constexpr (DT == kFP8) {
+      co[kLinLoRow] = (float)mult_lo[0];
+      co[kAuxLoRow] = (float)mult_lo[1];
+    }
     co[kAuxRow] = (float)mult[1];
     co[kLinRow] = (float)mult[0];
     float* mi = plan_misc + row * 4;

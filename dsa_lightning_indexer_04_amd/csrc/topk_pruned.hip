@@ -61,12 +61,14 @@ struct PruneArgs {
   const uint8_t* rows;       // [R][32][128] dtype: bound rows
   const float* coef;         // [R][32]: c_0..c_29, aux multiplier, linear multiplier
   const float* misc;         // [R][4]: kappa, e_neg
-  const int32_t* flag;       // [R]: 1 = recover (no pruning)
+  int32_t* flag;             // [R]: 1 = recover (no pruning); the final refine sets it on a raised-start miss
   const float* knorm;        // [B][N]: |k|, rounded up
   const int32_t* seeds;      // [B][seed_stride] ascending
   int seed_stride;
   const uint32_t* seed_bits; // [B][bits_stride]
   int bits_stride;
+  const int32_t* seed_pos;       // [R]: the row's visible seeds - 1
+  int raised_start;
   const int32_t* seed_top_idx;   // [R][topk]: the row's exact seed Top-K (seed numbers, -1 padded)
   const float* seed_top_score;   // [R][topk]: their scores
   PruneRowCtl* ctl;          // [R]
@@ -82,10 +84,26 @@ struct PruneArgs {
 
 // ---------------------------------------------------------------- 1. seeds
 
+// Seed rank of a row's raised start: with S seeds spread evenly over the
+// row's V visible keys, the number of seeds at or above the K-th score is
+// about mu = K S / V (a binomial count when the scores do not depend on the
+// position), so the m-th best seed, m = ceil(mu + 5 sqrt(mu)) + 1, is a
+// score that at least K keys reach unless the count falls five standard
+// deviations short.  m >= K means no raise.
+__device__ __forceinline__ int raised_start_rank(int topk, int seeds, int vis) {
+  if (seeds <= 0 || vis <= 0) return topk;
+  const float mu = (float)topk * (float)seeds / (float)vis;
+  if (mu >= (float)topk) return topk;
+  return (int)ceilf(mu + 5.0f * sqrtf(mu)) + 1;
+}
+
 // One wave per row: the row's seed Top-K records into its candidate buffer,
-// tau = the K-th of them, the threshold histogram fitted to them; the row's
-// state goes to its control block.
-__global__ __launch_bounds__(kRefineWaves * 64) void k_prune_init(int Q, size_t R, int topk, int cap,
+// tau = the K-th of them.  The running threshold starts at tau, or (raised
+// start) at the record of seed rank raised_start_rank, and the buffer keeps
+// the seed records that reach it; the threshold histogram is fitted to them
+// and the row's state goes to its control block.
+__global__ __launch_bounds__(kRefineWaves * 64) void k_prune_init(const int32_t* __restrict__ pos, int Q, int N,
+                                                                  size_t R, int topk, int cap,
                                                                   uint64_t* __restrict__ cand, PruneArgs pa) {
   __shared__ __align__(16) uint32_t hist[kRefineWaves][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -112,15 +130,22 @@ __global__ __launch_bounds__(kRefineWaves * 64) void k_prune_init(int Q, size_t 
   rs.cnt = nk;
   row_mem_sync();
   float tau = -INFINITY;
+  int raised = 0;
   if (rs.cnt >= topk) {
     rs.thr = min_record(rs.buf, rs.cnt, lane);
     tau = record_score(rs.thr);
+    const int vis = min(max(pos[row] + 1, 0), N);
+    const int m = pa.raised_start && !pa.flag[row] ? raised_start_rank(topk, pa.seed_pos[row] + 1, vis) : topk;
+    if (m < topk) {  // the m best records: exactly those at or above the selection's prefix
+      rs.thr = select_records_d8(rs.buf, rs.cnt, (uint32_t)m, my_hist, true, 0, lane).prefix;
+      raised = 1;
+    }
   }
   apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, nullptr, 0, my_hist, rs.thr, topk, cap, lane));
   row_mem_sync();
   uint32_t* gh = pa.hist + row * 256;
   for (int i = lane; i < 256; i += 64) gh[i] = my_hist[i];
-  if (lane == 0) pa.ctl[row] = PruneRowCtl{rs.thr, rs.cnt, rs.base, rs.shift, 0, 0, 0, tau, {0, 0, 0}};
+  if (lane == 0) pa.ctl[row] = PruneRowCtl{rs.thr, rs.cnt, rs.base, rs.shift, 0, 0, 0, tau, raised, {0, 0}};
 }
 
 // ---------------------------------------------------------------- 2. screen
@@ -507,6 +532,20 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
     }
     return;
   }
+  // Every kept record reaches the row's start and every key whose record
+  // does was kept, so with fewer than K of them (possible only after a
+  // raised start) the K-th best record lies below the start: the streaming
+  // Top-K recomputes the row.
+  if (rs.cnt + rs.nst < topk && c.raised) {
+    if (lane == 0) {
+      pa.flag[row] = 1;
+      if (pa.st_tau) pa.st_tau[row] = c.tau;
+      if (pa.st_screened) pa.st_screened[row] = c.screened;
+      if (pa.st_surv) pa.st_surv[row] = c.survived;
+      if (pa.st_rec) pa.st_rec[row] = 2;
+    }
+    return;
+  }
   emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
                out_score ? out_score + row * (size_t)topk : nullptr, lane);
   if (lane == 0) {
@@ -559,16 +598,18 @@ int prune_mask_words(int N) {
 hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* cand, int32_t* out_idx, float* out_score,
                               const PrunedBuffers& pb, hipStream_t st) {
   const size_t R = (size_t)p.B * p.Q;
-  PruneArgs pa{pb.plan_rows, pb.plan_coef, pb.plan_misc, pb.plan_flag, pb.knorm, pb.seeds, pb.seed_stride,
-               pb.seed_bits, pb.bits_stride, pb.seed_top_idx, pb.seed_top_score, pb.ctl, pb.hist, pb.mask,
-               pb.mask_stride, pb.st_tau, pb.st_screened, pb.st_surv, pb.st_rec, pb.st_ub};
+  PruneArgs pa{pb.plan_rows,   pb.plan_coef,    pb.plan_misc,    pb.plan_flag,   pb.knorm,
+               pb.seeds,       pb.seed_stride,  pb.seed_bits,    pb.bits_stride, pb.seed_pos,
+               pb.raised_start, pb.seed_top_idx, pb.seed_top_score, pb.ctl,        pb.hist,
+               pb.mask,        pb.mask_stride,  pb.st_tau,       pb.st_screened, pb.st_surv,
+               pb.st_rec,      pb.st_ub};
   if (pb.st_ub) {
     const size_t n = R * p.N;
     hipLaunchKernelGGL(k_fill_nan, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, pb.st_ub, n);
   }
   const dim3 rgrid((unsigned)((R + kRefineWaves - 1) / kRefineWaves));
   int slot = prof_open("k_prune_init", st);
-  hipLaunchKernelGGL(k_prune_init, rgrid, dim3(kRefineWaves * 64), 0, st, p.Q, R, topk, cap, cand, pa);
+  hipLaunchKernelGGL(k_prune_init, rgrid, dim3(kRefineWaves * 64), 0, st, p.pos, p.Q, p.N, R, topk, cap, cand, pa);
   prof_close(slot, st);
 
   using ScreenKern = void (*)(const float*, const uint8_t*, const float*, const int32_t*, int, int, int, int,

@@ -138,19 +138,41 @@ int dsa_indexer_topk_noalloc(const dsa_indexer_inputs* in, int32_t topk, int32_t
  *                 LBKERZAW, step 1)
  *   num_retained  positive-weight heads whose dot products the bound uses
  *                 directly (0 -> 30, range 1..30, else DSA_ERR_UNSUPPORTED;
- *                 fewer if the row has fewer positive heads); the bound also
- *                 uses one folded negative-head row and one linear row that
- *                 carries the projected positive heads (32 rows in all)
+ *                 fewer if the row has fewer positive heads, and at most 28
+ *                 for fp8 inputs); the bound also uses one folded
+ *                 negative-head row (every negative-weight head, folded by
+ *                 |w|) and one linear row that carries the projected
+ *                 positive heads (32 rows in all).  For fp8 inputs these two
+ *                 rows are stored as high and low e4m3 parts: the low parts
+ *                 take plan rows 28 and 29
  *   seed_idx      [B,num_seeds] int32 device array of ascending, distinct
  *                 key indices, or NULL for evenly spaced seeds
  *                 floor(i*(p0+1)/S) over the common prefix 0..p0
  *   force_recover [B,Q] uint8 device mask, or NULL: rows marked non-zero
- *                 take the recovery (unpruned) path; for tests             */
+ *                 take the recovery (unpruned) path; for tests
+ *   flags         0, or DSA_PRUNE_* bits below; other bits are
+ *                 DSA_ERR_INVALID_ARG
+ *
+ * Starting threshold.  The pages start the running threshold at tau, the
+ * K-th best seed score.  By default a row starts higher, at its m-th best
+ * seed record with m = ceil(mu + 5 sqrt(mu)) + 1 and mu = K * (its visible
+ * seeds) / (its visible keys): with evenly spread seeds about mu seeds lie
+ * at or above the K-th score, so the m-th one is an estimate of a score
+ * that at least K keys reach.  Only rows with m < K start raised.  A key
+ * below the start is excluded with the same certified bound test, so
+ * every key whose exact score reaches the start is found.  If at least K
+ * do, the Top-K is exact as before; if fewer do, the row is recomputed by
+ * the unpruned path (statistics: recovered = 2).  The results are the same
+ * index set either way.  DSA_PRUNE_START_AT_TAU starts every row at tau. */
+enum {
+  DSA_PRUNE_START_AT_TAU = 1u << 0
+};
 typedef struct dsa_prune_opts {
   int32_t num_seeds;
   int32_t num_retained;
   const int32_t* seed_idx;
   const uint8_t* force_recover;
+  uint32_t flags;
 } dsa_prune_opts;
 
 /* Optional per-row statistics of the pruned path (device pointers, each may
@@ -158,13 +180,17 @@ typedef struct dsa_prune_opts {
  *   tau        [B,Q] fp32  threshold from the seeds (K-th seed score)
  *   screened   [B,Q] int32 non-seed visible keys that were bounded
  *   survivors  [B,Q] int32 keys whose bound reached the running threshold
- *   recovered  [B,Q] uint8 1 if the row was recomputed by the unpruned path
+ *   recovered  [B,Q] uint8 0, or the reason the row was recomputed by the
+ *              unpruned path: 1 its plan or seeds (or force_recover), 2
+ *              fewer than K exact scores reached its raised start
  *   upper_bound [B,Q,N] fp32 debug: the bound of every non-seed visible key
  *              (NaN elsewhere); small shapes only, costs one extra pass
  *   plan_rows  [B,Q,32,128] debug: each row's bound plan, in the input dtype
  *              (bf16 bits or e4m3 codes): rows 0..29 the retained heads'
- *              query rows (zero past the row's retained count), row 30 the
- *              folded negative-head row q_neg, row 31 the linear row E
+ *              query rows (zero past the row's retained count; fp8: rows
+ *              28 and 29 the low parts of E and q_neg), row 30 the folded
+ *              negative-head row q_neg, row 31 the linear row E (fp8: their
+ *              high parts)
  *   plan_coef  [B,Q,32] fp32 debug: c_0..c_29 (the |d_i| coefficients), the
  *              q_neg multiplier, the E multiplier
  *   plan_misc  [B,Q,2] fp32 debug: kappa (the |k| coefficient, guard

@@ -142,11 +142,13 @@ def pruned_topk_row(
 def bound_from_plan(rows, coef, kappa: float, e_neg: float, keys, scale=None) -> np.ndarray:
     """The bound of a folded plan, in float64, for every key row in ``keys``.
 
-    rows [32, d]: rows 0..29 the retained heads' query rows (zero rows are
-    unused slots), row 30 the folded negative-head row q_neg, row 31 the
-    linear row E; coef [32]: c_0..c_29, the q_neg multiplier c_30, the E
-    multiplier c_31; kappa, e_neg: the |k| coefficients of the residual (and
-    any guard) and of q_neg's rounding.  With d_i = rows[i] . k,
+    rows [32, d]: rows 0..29 the |d| rows (the retained heads' query rows,
+    zero rows for unused slots, and any other row whose |dot| the plan
+    adds, such as the low part of a row split in two), row 30 the folded
+    negative-head row q_neg, row 31 the linear row E; coef [32]:
+    c_0..c_29, the q_neg multiplier c_30, the E multiplier c_31; kappa,
+    e_neg: the |k| coefficients of the residual (and any guard) and of
+    q_neg's rounding.  With d_i = rows[i] . k,
 
         U = sum_{i<30} c_i |d_i| + c_31 d_31 - ReLU(c_30 d_30 - e_neg |k|) + kappa |k|,
 

@@ -78,6 +78,12 @@ int main() {
       po.num_retained = 31;
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, nullptr, ws, pneed, nullptr), DSA_ERR_UNSUPPORTED);
       po.num_retained = 0;
+      po.flags = DSA_PRUNE_START_AT_TAU;
+      EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_OK);
+      po.flags = 2;
+      EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_ERR_INVALID_ARG);
+      EXPECT(dsa_indexer_workspace_bytes(DSA_OP_TOPK_PRUNED, &in, 2048, &po) == 0 ? 0 : 1, 0);
+      po.flags = 0;
       st.tau = static_cast<float*>(ws);  // stats inside the workspace
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_ERR_INVALID_ARG);
     }

@@ -220,6 +220,25 @@ def test_bad_flags_are_rejected(lib, flags):
     assert lib.dsa_indexer_last_error()
 
 
+@pytest.mark.parametrize("flags,ok", [(0, True), (1, True), (2, False), (1 << 31, False)])
+def test_prune_flags(lib, flags, ok):
+    """dsa_prune_opts.flags: only DSA_PRUNE_START_AT_TAU is known; the start
+    does not change the workspace."""
+    import torch
+
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _inputs(_lib)
+    base = lib.dsa_indexer_workspace_bytes(2, ctypes.byref(inp), 16, ctypes.byref(_lib.PruneOpts(0, 0, None, None, 0)))
+    got = lib.dsa_indexer_workspace_bytes(2, ctypes.byref(inp), 16, ctypes.byref(_lib.PruneOpts(0, 0, None, None, flags)))
+    assert base > 0
+    assert got == (base if ok else 0)
+    if not ok:
+        assert b"flags" in lib.dsa_indexer_last_error()
+    with pytest.raises(ValueError, match="start"):
+        _lib.topk_pruned(*[torch.zeros(1)] * 4, 16, start="high")
+
+
 def test_route_flags_set_the_workspace(lib):
     """The key-split route stores [B*Q, N] fp32 score rows plus a 2048-bin
     histogram per row; the streaming route (4*topk + 640) 8-byte records per

@@ -4,7 +4,9 @@ Pins: the pruned index set is bit-identical to the unpruned GPU set (and its
 scores equal); every screened bound dominates the GPU's own score of that pair
 and the float64 oracle score; the seed threshold tau equals the K-th best GPU
 score among the row's seeds and never exceeds the row's true K-th score;
-forced recovery and invalid seeds still give the same result.
+forced recovery and invalid seeds still give the same result; a raised
+start that misses (fewer than K exact scores reach it) recovers the row and
+still gives the same result.
 """
 import numpy as np
 import pytest
@@ -44,22 +46,27 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("start", ["raised", "tau"])
 @pytest.mark.parametrize("B,Q,N,k,dtype,dist,ns", CASES)
-def test_pruned_bit_identical_and_bounds(B, Q, N, k, dtype, dist, ns):
+def test_pruned_bit_identical_and_bounds(B, Q, N, k, dtype, dist, ns, start):
     need_gpu()
     rng = np.random.default_rng(N)
     pos = np.sort(rng.integers(N // 2, N, size=(B, Q)), axis=1)
     pos[:, -1] = N - 1
     d = inputs.make_inputs(B, Q, N, dtype, dist, seed=N + Q, positions=pos)
     dd = to_device(d)
-    log(f"pruned B={B} Q={Q} N={N} k={k} {dtype} {dist} seeds={ns}")
+    log(f"pruned B={B} Q={Q} N={N} k={k} {dtype} {dist} seeds={ns} start={start}")
     args, kw = call_args(dd)
-    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, stats=True, upper_bound=True)
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start=start, stats=True, upper_bound=True)
     idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     st = {n: v.cpu().numpy() for n, v in st.items()}
     u_idx, u_sc = _unpruned(dd, k)
     _same_sets(idx, sc, u_idx, u_sc)
-    assert not st["recovered"].any()
+    # a tau start never recovers; a raised start only on a miss (code 2)
+    assert not (st["recovered"] == 1).any()
+    if start == "tau":
+        assert not st["recovered"].any()
+    log(f"  raised-start misses: {int((st['recovered'] == 2).sum())}")
     # bounds dominate the GPU's own scores (bitwise float compare) and the oracle
     S = dsa.scores(*args, **kw).cpu().numpy()
     U = st["upper_bound"]
@@ -118,6 +125,38 @@ def test_forced_recovery_and_invalid_seeds(dtype):
     idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=300, seed_idx=torch.from_numpy(good).cuda(), stats=True)
     _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
     assert not st["recovered"].cpu().numpy().any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_raised_start_miss_recovers(dtype):
+    """Nonnegative head weights and seed keys doubled (bf16 values, or fp8
+    key scales, times 2): every score is a sum of ReLUs, so doubling a key
+    doubles its score and the seeds hold the best scores of every row.  The
+    raised start (seed rank m = 106 < K = 256 here) is then reached by m
+    keys only (checked in float64 when the case was chosen), every row must
+    be recomputed unpruned (recovered = 2) and the result is still the
+    exact Top-K; with a tau start the same inputs need no recovery."""
+    need_gpu()
+    B, Q, N, k, ns = 1, 12, 4000, 256, 1000
+    d = inputs.make_inputs(B, Q, N, dtype, "iid", seed=21)
+    d["w"] = d["w"].abs()
+    seeds = inputs.evenly_spaced_seeds(ns, int(d["pos"].min()))
+    if dtype == "bf16":
+        d["k"][:, seeds] = d["k"][:, seeds] * 2
+    else:
+        d["k_scale"][:, seeds] = d["k_scale"][:, seeds] * 2
+    dd = to_device(d)
+    args, kw = call_args(dd)
+    log(f"raised-start miss {dtype}")
+    u_idx, u_sc = _unpruned(dd, k)
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, stats=True)
+    _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
+    rec = st["recovered"].cpu().numpy()
+    assert (rec == 2).all(), rec
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start="tau", stats=True)
+    _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
+    assert not st["recovered"].cpu().numpy().any()
+    assert_rows_ok(OracleRows(d), u_idx, u_sc, [(0, t) for t in range(Q)], k)
 
 
 def test_pruned_small_and_degenerate():
