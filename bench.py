@@ -45,10 +45,10 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
     ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
     ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
-    ("chunked_prefill_128k", "k_screen"): ("50bc6806478191c1", 76939, 21442),
-    ("chunked_prefill_128k", "k_refine"): ("50bc6806478191c1", 755489, 73728),
-    ("context_1m_fp8", "k_screen"): ("50bc6806478191c1", 451924, 209237),
-    ("context_1m_fp8", "k_refine"): ("50bc6806478191c1", 3537469, 185685),
+    ("chunked_prefill_128k", "k_screen"): ("a2fc3193ec8d8500", 76922, 21441),
+    ("chunked_prefill_128k", "k_refine"): ("a2fc3193ec8d8500", 340127, 45914),
+    ("context_1m_fp8", "k_screen"): ("a2fc3193ec8d8500", 451756, 209404),
+    ("context_1m_fp8", "k_refine"): ("a2fc3193ec8d8500", 884820, 78086),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
     ("projection_prefill_128k", "k_proj_out"): ("61f24b18bb20f769", 1073178, 553001),
     ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
