@@ -223,7 +223,9 @@ def run_workload(name, path, steps, warmup):
     else:
         work = {n: pairs * PAIR_FLOPS for n in per_step if n in ("k_topk_stream", "k_scores")}
     for n, v in per_step.items():
-        v["traffic_per_launch"] = measured_traffic(name, n)  # HBM bytes from stored counter readings, or None
+        # HBM bytes from stored counter readings, or None (in the pruned path the
+        # streaming kernel scores the packed seeds: no reading is stored for that)
+        v["traffic_per_launch"] = None if (use_pruned and n == "k_topk_stream") else measured_traffic(name, n)
         v["flops"] = work.get(n, 0)
         v["tflops"] = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] > 0 else 0.0
         v["frac"] = v["tflops"] / PEAK_TFLOPS[wl.dtype]
