@@ -45,10 +45,10 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
     ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
     ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
-    ("chunked_prefill_128k", "k_screen"): ("a2fc3193ec8d8500", 76922, 21441),
-    ("chunked_prefill_128k", "k_refine"): ("a2fc3193ec8d8500", 340127, 45914),
-    ("context_1m_fp8", "k_screen"): ("a2fc3193ec8d8500", 451756, 209404),
-    ("context_1m_fp8", "k_refine"): ("a2fc3193ec8d8500", 884820, 78086),
+    ("chunked_prefill_128k", "k_screen"): ("f3d7bc1e406ea83d", 77014, 21444),
+    ("chunked_prefill_128k", "k_refine"): ("f3d7bc1e406ea83d", 351708, 45864),
+    ("context_1m_fp8", "k_screen"): ("f3d7bc1e406ea83d", 451306, 209436),
+    ("context_1m_fp8", "k_refine"): ("f3d7bc1e406ea83d", 896547, 78040),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
     ("projection_prefill_128k", "k_proj_out"): ("61f24b18bb20f769", 1073178, 553001),
     ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
@@ -67,13 +67,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunked_prefill_128k")
-    ap.add_argument("--path", choices=["auto", "topk", "pruned", "pruned_tau"], default="topk",
+    ap.add_argument("--path", choices=["auto", "topk", "pruned", "pruned_tau", "pruned_compact"], default="topk",
                     help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one; "
-                    "pruned_tau: the pruned path with every row's threshold starting at tau)")
+                    "pruned_tau: the pruned path with every row's threshold starting at tau; pruned_compact: "
+                    "the pruned path with 32-bit candidate records)")
     ap.add_argument(
         "--also",
-        default="chunked_prefill_128k:pruned,chunked_prefill_128k:pruned_tau,context_1m_fp8:topk,"
-        "context_1m_fp8:pruned,context_1m_fp8:pruned_tau,"
+        default="chunked_prefill_128k:pruned,chunked_prefill_128k:pruned_tau,chunked_prefill_128k:pruned_compact,"
+        "context_1m_fp8:topk,context_1m_fp8:pruned,context_1m_fp8:pruned_tau,context_1m_fp8:pruned_compact,"
         "chunked_prefill_128k_noise02:pruned,prefill_32k:topk,"
         "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla,"
         "sparse_mla_decode_64x128k:sparse_mla",
@@ -160,26 +161,27 @@ def run_workload(name, path, steps, warmup):
     qs = None if d["q_scale"] is None else d["q_scale"].to(dev)
     ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
     del d
-    use_pruned = path in ("pruned", "pruned_tau") or (path == "auto" and wl.pruned)
+    use_pruned = path in ("pruned", "pruned_tau", "pruned_compact") or (path == "auto" and wl.pruned)
     start = "tau" if path == "pruned_tau" else "raised"
+    records = "compact" if path == "pruned_compact" else "exact"
     inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
     stats = None
     if use_pruned:
-        opts = _lib.PruneOpts(0, 0, None, None, _lib.PRUNE_STARTS[start])
+        opts = _lib.PruneOpts(0, 0, None, None, _lib.PRUNE_STARTS[start] | _lib.PRUNE_RECORDS[records])
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                          device=dev)
 
         def call():
-            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start, return_scores=False,
-                                   workspace=ws)
+            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start, records=records,
+                                   return_scores=False, workspace=ws)
 
-        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start,
+        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start, records=records,
                                    return_scores=False, workspace=ws, stats=True)
         scr = int(st["screened"].sum().item())
         sur = int(st["survivors"].sum().item())
         seeds = min(12288, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced seeds, visible to every row
         stats = {"screened_pairs": scr, "survivor_pairs": sur, "seed_pairs": seeds,
-                 "filter_rate": 1.0 - sur / max(1, scr), "start": start,
+                 "filter_rate": 1.0 - sur / max(1, scr), "start": start, "records": records,
                  "recovered_rows": int((st["recovered"] != 0).sum().item()),
                  "start_misses": int((st["recovered"] == 2).sum().item())}
     else:
@@ -202,7 +204,7 @@ def run_workload(name, path, steps, warmup):
     pairs = wl.visible_pairs
     res = {
         "workload": name,
-        "path": ("pruned_tau" if start == "tau" else "pruned") if use_pruned else "unpruned",
+        "path": (path if path.startswith("pruned") else "pruned") if use_pruned else "unpruned",
         "dtype": wl.dtype,
         "visible_pairs": pairs,
         "ms_per_step": wall * 1e3 / steps,
@@ -516,7 +518,7 @@ def main():
         t = {r["path"]: r["ms_per_step"] for r in runs}
         if "unpruned" in t:
             for r in runs:
-                if r["path"] in ("pruned", "pruned_tau"):
+                if r["path"].startswith("pruned"):
                     r["pruned_over_unpruned_time"] = t[r["path"]] / t["unpruned"]
     peak = PEAK_TFLOPS[main_res["dtype"]]
     roofline = {

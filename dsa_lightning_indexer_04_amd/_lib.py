@@ -51,9 +51,12 @@ class PruneOpts(ctypes.Structure):
     ]
 
 
-# Pruning flags (dsa_prune_opts.flags) and the starts they select.
+# Pruning flags (dsa_prune_opts.flags): the row's starting threshold and the
+# candidate record format they select.
 DSA_PRUNE_START_AT_TAU = 1 << 0
+DSA_PRUNE_COMPACT_RECORDS = 1 << 1
 PRUNE_STARTS = {"raised": 0, "tau": DSA_PRUNE_START_AT_TAU}
+PRUNE_RECORDS = {"exact": 0, "compact": DSA_PRUNE_COMPACT_RECORDS}
 
 
 class PruneStats(ctypes.Structure):
@@ -380,6 +383,7 @@ def topk_pruned(
     seed_idx=None,
     force_recover=None,
     start: str = "raised",
+    records: str = "exact",
     return_scores: bool = True,
     stats: bool = False,
     upper_bound: bool = False,
@@ -391,19 +395,26 @@ def topk_pruned(
     start: "raised" (default) starts each row's running threshold at a seed
     record above tau, verified at the end (a row short of K records at its
     start is recomputed unpruned); "tau" starts at tau, the K-th seed score.
+    records: "exact" (default) keeps 64-bit candidate records; "compact"
+    keeps 32-bit records (row-relative score code + key index) and resolves
+    the Top-K boundary by rescoring.
     Returns (idx, scores or None, stats dict or None).  stats holds per-row
     tau, screened, survivors, recovered (1: plan/seeds/forced, 2: raised
-    start missed), the debug upper bounds, and with plan=True each row's
+    start missed, 3: compact records did not fit), the debug upper bounds,
+    and with plan=True each row's
     exported bound plan: plan_rows [B,Q,32,128] in q's dtype, plan_coef
     [B,Q,32], plan_misc [B,Q,2] = kappa, e_neg.
     """
     if start not in PRUNE_STARTS:
         raise ValueError(f"start must be one of {sorted(PRUNE_STARTS)}, not {start!r}")
+    if records not in PRUNE_RECORDS:
+        raise ValueError(f"records must be one of {sorted(PRUNE_RECORDS)}, not {records!r}")
     lib = load()
     inp = make_inputs_struct(q, k, w, positions, q_scale, k_scale)
     check_prune_args(seed_idx, force_recover, q.shape[0], q.shape[1], num_seeds)
     _check_device((("seed_idx", seed_idx), ("force_recover", force_recover)), q.device)
-    opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover), PRUNE_STARTS[start])
+    opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover),
+                     PRUNE_STARTS[start] | PRUNE_RECORDS[records])
     nbytes = workspace_bytes(DSA_OP_TOPK_PRUNED, inp, topk, opts)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
     B, Q = q.shape[:2]

@@ -171,12 +171,15 @@ struct PruneConfig {
   const int32_t* seed_idx;
   const uint8_t* force_recover;
   bool raised_start;
+  bool compact;
 };
 
 int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
   const uint32_t flags = o ? o->flags : 0u;
-  if (flags & ~(uint32_t)DSA_PRUNE_START_AT_TAU) return fail(DSA_ERR_INVALID_ARG, "unknown pruning flags");
+  if (flags & ~(uint32_t)(DSA_PRUNE_START_AT_TAU | DSA_PRUNE_COMPACT_RECORDS))
+    return fail(DSA_ERR_INVALID_ARG, "unknown pruning flags");
   pc->raised_start = !(flags & DSA_PRUNE_START_AT_TAU);
+  pc->compact = (flags & DSA_PRUNE_COMPACT_RECORDS) != 0;
   pc->num_seeds = (o && o->num_seeds) ? o->num_seeds : 12288;
   pc->num_retained = (o && o->num_retained) ? o->num_retained : 30;
   pc->seed_idx = o ? o->seed_idx : nullptr;
@@ -186,6 +189,14 @@ int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
   if (pc->num_retained < 1 || pc->num_retained > 30)
     return fail(DSA_ERR_UNSUPPORTED, "num_retained must be in 1..30");
   if (pc->seed_idx && !aligned16(pc->seed_idx)) return fail(DSA_ERR_INVALID_ARG, "seed_idx must be 16-byte aligned");
+  return DSA_OK;
+}
+
+// Compact records keep the key index in the low bits of 32: at most 24 of
+// them, so that the score code keeps at least 8.
+int check_prune_fit(const dsa_indexer_inputs* in, const PruneConfig& pc) {
+  if (pc.compact && in->num_k > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "compact records need num_k <= 2^24");
   return DSA_OK;
 }
 
@@ -381,7 +392,7 @@ size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t
   if (op == DSA_OP_TOPK) return topk_workspace(in, topk);
   if (op == DSA_OP_TOPK_PRUNED) {
     PruneConfig pc;
-    if (prune_config(opts, &pc)) return 0;
+    if (prune_config(opts, &pc) || check_prune_fit(in, pc)) return 0;
     return pruned_layout(in, topk, pc, nullptr, nullptr);
   }
   fail(DSA_ERR_INVALID_ARG, "unknown op");
@@ -396,6 +407,7 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
   if ((rc = check_topk(topk))) return rc;
   PruneConfig pc;
   if ((rc = prune_config(opts, &pc))) return rc;
+  if ((rc = check_prune_fit(in, pc))) return rc;
   const size_t need = pruned_layout(in, topk, pc, nullptr, nullptr);
   if ((rc = check_topk_outputs(in, topk, out_idx, out_score, workspace, workspace_bytes, need))) return rc;
   if (stats) {
@@ -420,6 +432,7 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
   uint64_t* cand = nullptr;
   pruned_layout(in, topk, pc, static_cast<uint8_t*>(workspace), &pb, &cand);
   pb.raised_start = pc.raised_start ? 1 : 0;
+  pb.compact = pc.compact ? 1 : 0;
   if (stats) {
     pb.st_tau = stats->tau;
     pb.st_screened = stats->screened;

@@ -58,7 +58,10 @@ struct PruneRowCtl {
   int32_t survived;   // statistics: keys whose bound reached the threshold
   float tau;          // threshold from the seeds
   int32_t raised;     // 1: the row started above tau (needs K records at its start)
-  int32_t pad[2];
+  uint32_t cbase;     // compact records: monotone code of the row's start
+  int32_t cshift;     // compact records: score code = (monotone code - cbase) >> cshift
+  int32_t reason;     // 0, or why the streaming Top-K recomputes the row (statistics)
+  int32_t pad[3];
 };
 
 // Longest key chunk of the screen/refine schedule.
@@ -94,6 +97,7 @@ struct PrunedBuffers {
   uint8_t* st_rec;
   float* st_ub;
   int raised_start;       // 1: rows start above tau (verified at the end; misses recover)
+  int compact;            // 1: 32-bit candidate records (score code + key), boundary resolved by rescoring
 };
 
 hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, int32_t* seeds, int32_t* seed_count,

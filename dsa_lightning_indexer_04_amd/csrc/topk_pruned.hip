@@ -52,10 +52,10 @@ constexpr int kScreenWaves = 4;      // screen: waves per workgroup, two rows ea
 constexpr int kScreenTile = 16384;   // screen: key bytes of an LDS tile
 constexpr int kScreenSlots = 3;      // screen: tile slots (two tiles loaded ahead)
 constexpr int kRefineWaves = 4;      // refine: rows per workgroup, one per wave
-constexpr int kGroupWords = 32;      // refine: bitmask words expanded at a time
+constexpr int kGroupWords = 64;      // refine: bitmask words expanded at a time (one per lane)
 constexpr int kQueue = 64 * kGroupWords + 64;  // refine: survivor queue per row
 
-static_assert(sizeof(PruneRowCtl) == 48, "row control block layout");
+static_assert(sizeof(PruneRowCtl) == 64, "row control block layout");
 
 struct PruneArgs {
   const uint8_t* rows;       // [R][32][128] dtype: bound rows
@@ -69,6 +69,7 @@ struct PruneArgs {
   int bits_stride;
   const int32_t* seed_pos;       // [R]: the row's visible seeds - 1
   int raised_start;
+  int compact;                   // 32-bit candidate records
   const int32_t* seed_top_idx;   // [R][topk]: the row's exact seed Top-K (seed numbers, -1 padded)
   const float* seed_top_score;   // [R][topk]: their scores
   PruneRowCtl* ctl;          // [R]
@@ -83,6 +84,225 @@ struct PruneArgs {
 };
 
 // ---------------------------------------------------------------- 1. seeds
+
+// ---------------------------------------------------------------- compact records
+
+// Key index bits of a compact record for N keys.
+__device__ __forceinline__ int key_bits(int N) { return N <= 2 ? 1 : 32 - __builtin_clz((uint32_t)(N - 1)); }
+
+// A row's compact 32-bit record (DoSA reading notes, annotation TMIF4XYF:
+// a compact monotone score code plus the exact key index): the low kb bits
+// hold 2^kb - 1 - key, the high 32 - kb bits the code
+//   c(m) = min(2^(32-kb) - 1, (m - cbase) >> cshift)
+// of the score's monotone code m, for m >= cbase (the row's start; records
+// below the start are never kept).  c is monotone in the score: records of
+// different codes are ordered by score, records of one code are not.
+struct Code32 {
+  uint32_t cbase;
+  int cshift, kb;
+  __device__ __forceinline__ uint32_t cmax() const { return 0xFFFFFFFFu >> kb; }
+  __device__ __forceinline__ uint32_t kmask() const { return (1u << kb) - 1u; }
+  __device__ __forceinline__ uint32_t code(uint32_t m) const {
+    return m <= cbase ? 0u : min(cmax(), (m - cbase) >> cshift);
+  }
+  __device__ __forceinline__ uint32_t make(uint64_t rec) const {
+    return (code((uint32_t)(rec >> 32)) << kb) | (kmask() - record_key(rec));
+  }
+  __device__ __forceinline__ uint32_t key(uint32_t r) const { return kmask() - (r & kmask()); }
+  // The 64-bit threshold record of code c >= 1: every record whose code is
+  // at least c is at least this (the lower edge of code c).
+  __device__ __forceinline__ uint64_t edge(uint32_t c) const {
+    const uint64_t m = (uint64_t)cbase + ((uint64_t)c << cshift);
+    return (m > 0xFFFFFFFFull ? 0xFFFFFFFFull : m) << 32;
+  }
+};
+
+// Candidate state of one row with compact records (wave-uniform).  thr is
+// the 64-bit threshold record (the start, or the lower edge of code cthr):
+// a record is kept iff it reaches thr, so every kept record reaches the
+// start.  The threshold histogram counts kept codes, bin
+// min(255, (c - hbase) >> hshift), hbase <= cthr.  dead: a cut could not
+// make room (one code holds too many records); the row is recomputed.
+struct RowState32 {
+  uint32_t* buf;
+  int cnt, nst;
+  uint64_t thr;
+  uint32_t cthr, hbase;
+  int hshift, added;
+  bool dead;
+};
+
+// In place, in order: keep the records whose code is at least cmin.
+static __device__ __noinline__ int compact32(uint32_t* buf, int cnt, uint32_t cmin, int kb, int lane) {
+  int base = 0;
+  for (int i0 = 0; i0 < cnt; i0 += 512) {
+    uint32_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      r[j] = i < cnt ? buf[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      const bool keep = i < cnt && (r[j] >> kb) >= cmin;
+      const uint64_t bal = __ballot(keep);
+      if (keep) buf[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = r[j];
+      base += __popcll(bal);
+    }
+  }
+  return base;
+}
+
+// Radix selection over the codes of cnt records (1 <= need <= cnt): digits
+// of at most 8 code bits from the top.  Returns a code-aligned threshold
+// cmin with `above` records in higher digit groups and `at` in cmin's group
+// (above < need <= above + at).  It stops once the boundary group is taken
+// whole (above + at == need), or, given a goal, once above + at <= goal;
+// otherwise every code bit is fixed and cmin's group is the single code
+// cmin.
+struct CodeCut {
+  uint32_t cmin, above, at;
+};
+static __device__ __noinline__ CodeCut select_code32(const uint32_t* buf, int cnt, uint32_t need, int kb,
+                                                      uint32_t* hist, uint32_t goal, int lane) {
+  const int cb = 32 - kb;
+  uint32_t prefix = 0, remaining = need, above = 0, at = (uint32_t)cnt;
+  int done = 0;
+  while (done < cb) {
+    const int width = min(8, cb - done);
+    const int lo = kb + cb - done - width;  // lowest record bit of this digit
+    const int hi = lo + width;              // record bits from here up hold the fixed prefix
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+    wave_lds_sync();
+    for (int i0 = 0; i0 < cnt; i0 += 512) {
+      uint32_t r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + 64 * j + lane;
+        r[j] = i < cnt ? buf[i] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + 64 * j + lane;
+        const uint32_t top = hi >= 32 ? 0u : r[j] >> hi;
+        if (i < cnt && top == prefix) atomicAdd(&hist[(r[j] >> lo) & dmask], 1u);
+      }
+    }
+    wave_lds_sync();
+    uint32_t bin, ab, count;
+    find_boundary(hist, 256, remaining, lane, bin, ab, count);
+    prefix = (prefix << width) | bin;
+    above += ab;
+    remaining -= ab;
+    at = count;
+    done += width;
+    if (count == remaining) break;
+    if (goal && above + count <= goal) break;
+  }
+  return {prefix << (cb - done), above, at};
+}
+
+// Flush the stage; keep the records of codes >= cthr; if more than `goal`
+// remain, cut to the codes of the best topk (whole codes: the threshold
+// becomes the boundary code's lower edge); mark the row dead when the cut
+// leaves no room for two more stages; refit the histogram.  (Arguments and
+// result by value: a reference to the caller's row state would put that
+// state in scratch memory for the whole refine loop.)
+struct Rebuilt32 {
+  int cnt;
+  uint64_t thr;
+  uint32_t cthr, hbase;
+  int hshift;
+  bool dead;
+};
+static __device__ __noinline__ Rebuilt32 rebuild32(uint32_t* buf, int cnt, const uint32_t* stage, int nst,
+                                                   uint32_t* hist, Code32 code, uint64_t thr, uint32_t cthr,
+                                                   int topk, int goal, int cap, int lane) {
+  for (int i = lane; i < nst; i += 64) buf[cnt + i] = stage[i];
+  cnt += nst;
+  row_mem_sync();
+  cnt = compact32(buf, cnt, cthr, code.kb, lane);
+  if (cnt > goal) {
+    row_mem_sync();
+    const CodeCut cut = select_code32(buf, cnt, (uint32_t)topk, code.kb, hist, (uint32_t)goal, lane);
+    if (cut.cmin > cthr) {
+      row_mem_sync();
+      cnt = compact32(buf, cnt, cut.cmin, code.kb, lane);
+      cthr = cut.cmin;
+      thr = code.edge(cut.cmin);
+    }
+  }
+  row_mem_sync();
+  uint32_t mx = cthr;
+  for (int i = lane; i < cnt; i += 64) mx = max(mx, buf[i] >> code.kb);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  const uint32_t span = mx - cthr;
+  const int hshift = span ? max(0, 24 - (int)__builtin_clz(span)) : 0;
+  for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+  wave_lds_sync();
+  for (int i = lane; i < cnt; i += 64) atomicAdd(&hist[thr_bin(buf[i] >> code.kb, cthr, hshift)], 1u);
+  wave_lds_sync();
+  return {cnt, thr, cthr, cthr, hshift, cnt > cap - 4 * kStage};
+}
+
+// raise_threshold on the code histogram: the threshold rises to the lower
+// edge of the highest code that at least topk kept records reach.
+__device__ __forceinline__ void raise32(RowState32& rc, const uint32_t* hist, const Code32& code, int topk, int lane) {
+  const u32x4 h = reinterpret_cast<const u32x4*>(hist)[63 - lane];  // h.w: bin 255 - 4 lane
+  const uint32_t local = h.x + h.y + h.z + h.w;
+  const uint32_t above = wave_prefix_incl(local, lane) - local;
+  const uint64_t bal = __ballot(above < (uint32_t)topk && (uint32_t)topk <= above + local);
+  rc.added = 0;
+  if (!bal) return;
+  const int src = __builtin_ctzll(bal);
+  uint32_t b = 4u * (63 - lane);
+  if (above + h.w >= (uint32_t)topk)
+    b += 3;
+  else if (above + h.w + h.z >= (uint32_t)topk)
+    b += 2;
+  else if (above + h.w + h.z + h.y >= (uint32_t)topk)
+    b += 1;
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+  const uint32_t c = rc.hbase + (b << rc.hshift);
+  if (c > rc.cthr) {
+    rc.cthr = c;
+    rc.thr = code.edge(c);
+  }
+}
+
+// append_rec with compact records: the 64-bit record decides (it must
+// reach thr), the compact one is stored.
+__device__ __forceinline__ void append32(RowState32& rc, uint64_t rec, bool live, uint32_t* stage, uint32_t* hist,
+                                         const Code32& code, int topk, int cap, int lane) {
+  bool keep = live && !rc.dead && rec >= rc.thr;
+  uint64_t bal = __ballot(keep);
+  if (bal) {
+    if (rc.cnt + rc.nst + __popcll(bal) > cap) {
+      const Rebuilt32 rb = rebuild32(rc.buf, rc.cnt, stage, rc.nst, hist, code, rc.thr, rc.cthr, topk,
+                                     cut_goal(topk, cap), cap, lane);
+      rc.cnt = rb.cnt;
+      rc.nst = 0;
+      rc.thr = rb.thr;
+      rc.cthr = rb.cthr;
+      rc.hbase = rb.hbase;
+      rc.hshift = rb.hshift;
+      rc.added = kRaiseEvery;
+      rc.dead = rc.dead || rb.dead;
+      keep = live && !rc.dead && rec >= rc.thr;
+      bal = __ballot(keep);
+    }
+    if (keep) {
+      const uint32_t r = code.make(rec);
+      stage[rc.nst + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = r;
+      atomicAdd(&hist[thr_bin(r >> code.kb, rc.hbase, rc.hshift)], 1u);
+    }
+    rc.nst += __popcll(bal);
+    rc.added += __popcll(bal);
+  }
+}
 
 // Seed rank of a row's raised start: with S seeds spread evenly over the
 // row's V visible keys, the number of seeds at or above the K-th score is
@@ -101,7 +321,11 @@ __device__ __forceinline__ int raised_start_rank(int topk, int seeds, int vis) {
 // tau = the K-th of them.  The running threshold starts at tau, or (raised
 // start) at the record of seed rank raised_start_rank, and the buffer keeps
 // the seed records that reach it; the threshold histogram is fitted to them
-// and the row's state goes to its control block.
+// and the row's state goes to its control block.  Compact records: the row's
+// code is fitted (cbase = the start's code; cshift so that twice the span
+// from the start to the best seed fits the code bits) and the kept seed
+// records are rewritten as compact records into the second half of the
+// row's buffer (the first half is the scratch of the final rescoring).
 __global__ __launch_bounds__(kRefineWaves * 64) void k_prune_init(const int32_t* __restrict__ pos, int Q, int N,
                                                                   size_t R, int topk, int cap,
                                                                   uint64_t* __restrict__ cand, PruneArgs pa) {
@@ -143,9 +367,40 @@ __global__ __launch_bounds__(kRefineWaves * 64) void k_prune_init(const int32_t*
   }
   apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, nullptr, 0, my_hist, rs.thr, topk, cap, lane));
   row_mem_sync();
+  uint32_t cbase = 0;
+  int cshift = 0;
+  if (pa.compact) {
+    cbase = (uint32_t)(rs.thr >> 32);
+    uint32_t top = cbase;
+    for (int i = lane; i < rs.cnt; i += 64) top = max(top, (uint32_t)(rs.buf[i] >> 32));
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, d, 64));
+    const int kb = key_bits(N);
+    const uint64_t span2 = 2ull * (uint64_t)(top - cbase);
+    cshift = span2 ? max(0, (64 - (int)__builtin_clzll(span2)) - (32 - kb)) : 0;
+    const Code32 code{cbase, cshift, kb};
+    uint32_t* b32 = reinterpret_cast<uint32_t*>(rs.buf) + cap;
+    uint32_t mx = 0;
+    for (int i = lane; i < rs.cnt; i += 64) {
+      const uint32_t r = code.make(rs.buf[i]);
+      b32[i] = r;
+      mx = max(mx, r >> kb);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+    // the code histogram from code 0 (the start)
+    rs.base = 0u;
+    rs.shift = mx ? max(0, 24 - (int)__builtin_clz(mx)) : 0;
+    for (int i = lane; i < 256; i += 64) my_hist[i] = 0u;
+    wave_lds_sync();
+    for (int i = lane; i < rs.cnt; i += 64) atomicAdd(&my_hist[thr_bin(b32[i] >> kb, 0u, rs.shift)], 1u);
+    wave_lds_sync();
+    row_mem_sync();
+  }
   uint32_t* gh = pa.hist + row * 256;
   for (int i = lane; i < 256; i += 64) gh[i] = my_hist[i];
-  if (lane == 0) pa.ctl[row] = PruneRowCtl{rs.thr, rs.cnt, rs.base, rs.shift, 0, 0, 0, tau, raised, {0, 0}};
+  if (lane == 0)
+    pa.ctl[row] = PruneRowCtl{rs.thr, rs.cnt, rs.base, rs.shift, 0, 0, 0, tau, raised, cbase, cshift, 0, {0, 0, 0}};
 }
 
 // ---------------------------------------------------------------- 2. screen
@@ -376,8 +631,10 @@ __device__ __forceinline__ void append_rec(RowState& rs, uint64_t rec, bool live
 // current batch is scored; records that reach the threshold become
 // candidates, and every 32 kept records raise the threshold.  `final`: after
 // the last chunk, select the row's exact Top-K and write the statistics;
-// otherwise save the row's state for the next chunk.
-template <int DT>
+// otherwise save the row's state for the next chunk.  kCompact: candidates
+// are compact records, and the final select resolves the boundary code by
+// rescoring its keys.
+template <int DT, bool kCompact>
 __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_refine(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const int32_t* __restrict__ pos, int Q, int N,
@@ -398,9 +655,9 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
   if (recover) {  // the streaming Top-K recomputes the row afterwards
     if (final_chunk && lane == 0) {
       if (pa.st_tau) pa.st_tau[row] = c.tau;
-      if (pa.st_screened) pa.st_screened[row] = 0;
-      if (pa.st_surv) pa.st_surv[row] = 0;
-      if (pa.st_rec) pa.st_rec[row] = 1;
+      if (pa.st_screened) pa.st_screened[row] = c.reason ? c.screened : 0;
+      if (pa.st_surv) pa.st_surv[row] = c.reason ? c.survived : 0;
+      if (pa.st_rec) pa.st_rec[row] = (uint8_t)(c.reason ? c.reason : 1);
     }
     return;
   }
@@ -410,21 +667,28 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
   const uint32_t* gh = pa.hist + row * 256;
   for (int i = lane; i < 256; i += 64) my_hist[i] = gh[i];
   RowState rs{cand + row * (size_t)cap, c.cnt, 0, c.thr, c.base, c.shift, c.added};
+  const Code32 code{c.cbase, c.cshift, key_bits(N)};
+  RowState32 rc{reinterpret_cast<uint32_t*>(cand + row * (size_t)cap) + cap,
+                c.cnt, 0, c.thr, code.code((uint32_t)(c.thr >> 32)), c.base, c.shift, c.added, false};
+  uint32_t* my_stage32 = reinterpret_cast<uint32_t*>(my_stage);  // compact records: 2 kStage of them
   const int vis = min(max(pos[row] + 1, 0), N);
   const int end = min(k1, vis);
   const int W = end > k0 ? (end - k0 + 63) / 64 : 0;  // bitmask words to read
 
-  if (W > 0) {
-    Frag<DT> qa[2];
+  Frag<DT> qa[2];
+  const float* my_w = wrow[wave];
+  const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
+  const uint8_t* kbase = k + (size_t)b * N * RB;
+  const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
+  const int lk = lane & 31;
+  if (W > 0) {  // the query block and weights
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], q + (row * kHeads + 32 * blk + (lane & 31)) * RB, lane);
     wrow[wave][lane] = w[row * kHeads + lane];
-    const float* my_w = wrow[wave];
-    const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
-    const uint8_t* kbase = k + (size_t)b * N * RB;
-    const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
+  }
+
+  if (W > 0) {
     const uint64_t* mrow = pa.mask + row * (size_t)pa.mask_stride;
-    const int lk = lane & 31;
 
     // Survivor queue my_q[qh, qn): topped up from the bitmask, kGroupWords
     // words at a time (lane j expands word g + j), whenever fewer than 64
@@ -463,12 +727,22 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
     auto score_and_keep = [&](const Frag<DT>& f, int key, float ks, bool live) {
       float s = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
       if constexpr (DT == kFP8) s = apply_scales(s, qscale, ks);
-      if (rs.nst > kStage - 32) {
-        rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
-        rs.nst = 0;
+      if constexpr (kCompact) {
+        if (rc.nst > 2 * kStage - 32) {
+          for (int i = lane; i < rc.nst; i += 64) rc.buf[rc.cnt + i] = my_stage32[i];
+          rc.cnt += rc.nst;
+          rc.nst = 0;
+        }
+        append32(rc, make_record(s, (uint32_t)key), live, my_stage32, my_hist, code, topk, cap, lane);
+        if (rc.added >= kRaiseEvery) raise32(rc, my_hist, code, topk, lane);
+      } else {
+        if (rs.nst > kStage - 32) {
+          rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+          rs.nst = 0;
+        }
+        append_rec(rs, make_record(s, (uint32_t)key), live, my_stage, my_hist, topk, cap, lane);
+        if (rs.added >= kRaiseEvery) raise_threshold(rs, my_hist, topk, lane);
       }
-      append_rec(rs, make_record(s, (uint32_t)key), live, my_stage, my_hist, topk, cap, lane);
-      if (rs.added >= kRaiseEvery) raise_threshold(rs, my_hist, topk, lane);
     };
     // Batches go through a ring of fragments: the next batches' key rows
     // are loading while one is scored (fp8: two in flight, bf16: one).  A batch is issued
@@ -516,44 +790,215 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
     }
   }
 
-  if (!final_chunk) {
-    rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
-    rs.nst = 0;
-    row_mem_sync();
+  if (!final_chunk || kCompact) {  // compact records: the select runs in k_emit_compact
     uint32_t* ghw = pa.hist + row * 256;
-    for (int i = lane; i < 256; i += 64) ghw[i] = my_hist[i];
-    if (lane == 0) {
-      PruneRowCtl& cw = pa.ctl[row];
-      cw.thr = rs.thr;
-      cw.cnt = rs.cnt;
-      cw.base = rs.base;
-      cw.shift = rs.shift;
-      cw.added = rs.added;
+    if constexpr (kCompact) {
+      for (int i = lane; i < rc.nst; i += 64) rc.buf[rc.cnt + i] = my_stage32[i];
+      rc.cnt += rc.nst;
+      rc.nst = 0;
+      row_mem_sync();
+      for (int i = lane; i < 256; i += 64) ghw[i] = my_hist[i];
+      if (lane == 0) {
+        PruneRowCtl& cw = pa.ctl[row];
+        cw.thr = rc.thr;
+        cw.cnt = rc.cnt;
+        cw.base = rc.hbase;
+        cw.shift = rc.hshift;
+        cw.added = rc.added;
+        if (rc.dead) {  // later launches skip the row; the streaming Top-K recomputes it
+          cw.reason = 3;
+          pa.flag[row] = 1;
+        }
+      }
+    } else {
+      rs.cnt = flush_stage(rs.buf, rs.cnt, my_stage, rs.nst, lane);
+      rs.nst = 0;
+      row_mem_sync();
+      for (int i = lane; i < 256; i += 64) ghw[i] = my_hist[i];
+      if (lane == 0) {
+        PruneRowCtl& cw = pa.ctl[row];
+        cw.thr = rs.thr;
+        cw.cnt = rs.cnt;
+        cw.base = rs.base;
+        cw.shift = rs.shift;
+        cw.added = rs.added;
+      }
     }
     return;
   }
-  // Every kept record reaches the row's start and every key whose record
-  // does was kept, so with fewer than K of them (possible only after a
-  // raised start) the K-th best record lies below the start: the streaming
-  // Top-K recomputes the row.
-  if (rs.cnt + rs.nst < topk && c.raised) {
+  auto recover_row = [&](int reason) {  // the streaming Top-K recomputes the row
     if (lane == 0) {
       pa.flag[row] = 1;
       if (pa.st_tau) pa.st_tau[row] = c.tau;
       if (pa.st_screened) pa.st_screened[row] = c.screened;
       if (pa.st_surv) pa.st_surv[row] = c.survived;
-      if (pa.st_rec) pa.st_rec[row] = 2;
+      if (pa.st_rec) pa.st_rec[row] = (uint8_t)reason;
     }
+  };
+  auto row_stats = [&]() {
+    if (lane == 0) {
+      if (pa.st_tau) pa.st_tau[row] = c.tau;
+      if (pa.st_screened) pa.st_screened[row] = c.screened;
+      if (pa.st_surv) pa.st_surv[row] = c.survived;
+      if (pa.st_rec) pa.st_rec[row] = 0;
+    }
+  };
+  int32_t* oi = out_idx + row * (size_t)topk;
+  float* os = out_score ? out_score + row * (size_t)topk : nullptr;
+  // Every kept record reaches the row's start and every key whose record
+  // does was kept, so with fewer than K of them (possible only after a
+  // raised start) the K-th best record lies below the start: the streaming
+  // Top-K recomputes the row.
+  if (rs.cnt + rs.nst < topk && c.raised) {
+    recover_row(2);
     return;
   }
-  emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, out_idx + row * (size_t)topk,
-               out_score ? out_score + row * (size_t)topk : nullptr, lane);
-  if (lane == 0) {
-    if (pa.st_tau) pa.st_tau[row] = c.tau;
-    if (pa.st_screened) pa.st_screened[row] = c.screened;
-    if (pa.st_surv) pa.st_surv[row] = c.survived;
-    if (pa.st_rec) pa.st_rec[row] = 0;
+  emit_topk_d8(rs.buf, rs.cnt, my_stage, rs.nst, my_hist, topk, oi, os, lane);
+  row_stats();
+}
+
+// Final select of the rows with compact records, after the last chunk's
+// refine (one wave per row): radix select over the codes finds the Top-K's
+// boundary code; the records above it are in.  If only part of the boundary
+// code's records are needed, or the scores are requested, the keys in
+// question are rescored with all heads by the shared routine into exact
+// 64-bit records (in the first half of the row's buffer) and those are
+// selected exactly (DoSA reading notes, annotation TMIF4XYF: records above
+// the boundary code are kept, the boundary is resolved by the original
+// scores).  Rows that cannot be resolved in the buffer, and missed raised
+// starts, are flagged for the streaming Top-K.
+template <int DT>
+__global__ __launch_bounds__(kRefineWaves * 64) void k_emit_compact(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
+    const float* __restrict__ qsc, const float* __restrict__ ksc, int Q, int N, size_t R, int topk, int cap,
+    uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_score, PruneArgs pa) {
+  constexpr int RB = Frag<DT>::kRowBytes;
+  __shared__ __align__(16) uint32_t hist[kRefineWaves][256];
+  __shared__ int32_t queue[kRefineWaves][kQueue];
+  __shared__ __align__(16) float wrow[kRefineWaves][kHeads];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * kRefineWaves + wave;
+  if (row >= R) return;  // whole wave; the waves share nothing
+  const int b = (int)(row / (size_t)Q);
+  const PruneRowCtl c = pa.ctl[row];
+  auto stats = [&](int reason, bool counts) {
+    if (lane == 0) {
+      if (pa.st_tau) pa.st_tau[row] = c.tau;
+      if (pa.st_screened) pa.st_screened[row] = counts ? c.screened : 0;
+      if (pa.st_surv) pa.st_surv[row] = counts ? c.survived : 0;
+      if (pa.st_rec) pa.st_rec[row] = (uint8_t)reason;
+    }
+  };
+  if (pa.flag[row]) {  // flagged before (plan, seeds, forced, or a buffer the refine could not cut)
+    stats(c.reason ? c.reason : 1, c.reason != 0);
+    return;
   }
+  auto recover_row = [&](int reason) {
+    if (lane == 0) pa.flag[row] = 1;
+    stats(reason, true);
+  };
+  const Code32 code{c.cbase, c.cshift, key_bits(N)};
+  const uint32_t* buf = reinterpret_cast<const uint32_t*>(cand + row * (size_t)cap) + cap;
+  const int cnt = c.cnt;
+  if (cnt < topk && c.raised) {  // fewer than K records reach the raised start: it was missed
+    recover_row(2);
+    return;
+  }
+  uint32_t* my_hist = hist[wave];
+  int32_t* my_q = queue[wave];
+  int32_t* oi = out_idx + row * (size_t)topk;
+  float* os = out_score ? out_score + row * (size_t)topk : nullptr;
+  const int need = min(topk, cnt);
+  const bool all = os != nullptr;
+  CodeCut sel{0u, 0u, 0u};
+  int nres = 0;
+  if (need > 0) {
+    sel = select_code32(buf, cnt, (uint32_t)need, code.kb, my_hist, 0u, lane);
+    nres = all ? (int)(sel.above + sel.at) : (sel.above + sel.at == (uint32_t)need ? 0 : (int)sel.at);
+    if (nres > cap / 2) {
+      recover_row(3);
+      return;
+    }
+  }
+  int base = 0;
+  auto emit_codes = [&](bool above_only) {  // the records of code >= cmin (> cmin)
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+      const int i = i0 + lane;
+      const uint32_t r = i < cnt ? buf[i] : 0u;
+      const uint32_t rc = r >> code.kb;
+      const bool keep = i < cnt && (above_only ? rc > sel.cmin : rc >= sel.cmin);
+      const uint64_t bal = __ballot(keep);
+      if (keep)
+        oi[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+            (int32_t)code.key(r);
+      base += __popcll(bal);
+    }
+  };
+  if (nres == 0) {
+    emit_codes(false);  // exactly need of them
+  } else {
+    Frag<DT> qa[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) load_frag<DT>(qa[blk], q + (row * kHeads + 32 * blk + (lane & 31)) * RB, lane);
+    wrow[wave][lane] = w[row * kHeads + lane];
+    const float* my_w = wrow[wave];
+    const float qscale = (DT == kFP8) ? qsc[row] : 1.0f;
+    const uint8_t* kbase = k + (size_t)b * N * RB;
+    const float* kscb = (DT == kFP8) ? ksc + (size_t)b * N : nullptr;
+    const int lk = lane & 31;
+    uint64_t* scratch = cand + row * (size_t)cap;
+    int nscr = 0, qn = 0;
+    auto score_queue = [&]() {  // exact records of the queued keys, 32 at a time
+      for (int i0 = 0; i0 < qn; i0 += 32) {
+        const int n = min(32, qn - i0);
+        const int key = my_q[i0 + (lk < n ? lk : 0)];
+        Frag<DT> f;
+        load_frag<DT>(f, kbase + (size_t)key * RB, lane);
+        const float ks = (DT == kFP8) ? kscb[key] : 1.0f;
+        float sc = combine_swap(query_partial_w<DT>(qa, f, my_w, lane));
+        if constexpr (DT == kFP8) sc = apply_scales(sc, qscale, ks);
+        if (lane < n) scratch[nscr + lane] = make_record(sc, (uint32_t)key);
+        nscr += n;
+      }
+      qn = 0;
+      wave_lds_sync();
+    };
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+      const int i = i0 + lane;
+      const uint32_t r = i < cnt ? buf[i] : 0u;
+      const uint32_t rc = r >> code.kb;
+      const bool take = i < cnt && (all ? rc >= sel.cmin : rc == sel.cmin);
+      const uint64_t bal = __ballot(take);
+      if (take)
+        my_q[qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+            (int32_t)code.key(r);
+      qn += __popcll(bal);
+      wave_lds_sync();
+      if (qn > kQueue - 64) score_queue();
+    }
+    if (qn > 0) score_queue();
+    row_mem_sync();
+    const SelectResult s2 =
+        select_records_d8(scratch, nscr, (uint32_t)(all ? need : need - (int)sel.above), my_hist, true, 0, lane);
+    if (!all) emit_codes(true);  // the records above the boundary code
+    for (int i0 = 0; i0 < nscr; i0 += 64) {
+      const int i = i0 + lane;
+      const uint64_t r = i < nscr ? scratch[i] : 0ull;
+      const bool keep = i < nscr && (r & s2.mask) >= s2.prefix;
+      const uint64_t bal = __ballot(keep);
+      const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep) {
+        oi[at] = (int32_t)record_key(r);
+        if (os) os[at] = record_score(r);
+      }
+      base += __popcll(bal);
+    }
+  }
+  for (int j = need + lane; j < topk; j += 64) {
+    oi[j] = -1;
+    if (os) os[j] = -INFINITY;
+  }
+  stats(0, true);
 }
 
 #define DSA_SCREEN_KERNEL(DT_, B_)                                                                                \
@@ -600,7 +1045,7 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
   const size_t R = (size_t)p.B * p.Q;
   PruneArgs pa{pb.plan_rows,   pb.plan_coef,    pb.plan_misc,    pb.plan_flag,   pb.knorm,
                pb.seeds,       pb.seed_stride,  pb.seed_bits,    pb.bits_stride, pb.seed_pos,
-               pb.raised_start, pb.seed_top_idx, pb.seed_top_score, pb.ctl,        pb.hist,
+               pb.raised_start, pb.compact,     pb.seed_top_idx, pb.seed_top_score, pb.ctl, pb.hist,
                pb.mask,        pb.mask_stride,  pb.st_tau,       pb.st_screened, pb.st_surv,
                pb.st_rec,      pb.st_ub};
   if (pb.st_ub) {
@@ -616,6 +1061,11 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
                               PruneArgs);
   const ScreenKern screen = p.dtype == kBF16 ? (pb.st_ub ? k_screen<kBF16, true> : k_screen<kBF16, false>)
                                              : (pb.st_ub ? k_screen<kFP8, true> : k_screen<kFP8, false>);
+  using RefineKern = void (*)(const uint8_t*, const uint8_t*, const float*, const float*, const float*,
+                              const int32_t*, int, int, size_t, int, int, int, int, int, uint64_t*, int32_t*, float*,
+                              PruneArgs);
+  const RefineKern refine = p.dtype == kBF16 ? (pb.compact ? k_refine<kBF16, true> : k_refine<kBF16, false>)
+                                             : (pb.compact ? k_refine<kFP8, true> : k_refine<kFP8, false>);
   const dim3 sgrid((unsigned)((p.Q + 2 * kScreenWaves - 1) / (2 * kScreenWaves)), p.B);
   const auto chunks = prune_chunks(p.N);
   for (size_t c = 0; c < chunks.size(); ++c) {
@@ -626,12 +1076,18 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
                        k1, pa);
     prof_close(slot, st);
     slot = prof_open("k_refine", st);
+    hipLaunchKernelGGL(refine, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale, p.pos,
+                       p.Q, p.N, R, k0, k1, pb.compact ? 0 : fin, topk, cap, cand, out_idx, out_score, pa);
+    prof_close(slot, st);
+  }
+  if (pb.compact) {
+    slot = prof_open("k_emit_compact", st);
     if (p.dtype == kBF16)
-      hipLaunchKernelGGL(k_refine<kBF16>, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
-                         p.pos, p.Q, p.N, R, k0, k1, fin, topk, cap, cand, out_idx, out_score, pa);
+      hipLaunchKernelGGL(k_emit_compact<kBF16>, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale,
+                         p.k_scale, p.Q, p.N, R, topk, cap, cand, out_idx, out_score, pa);
     else
-      hipLaunchKernelGGL(k_refine<kFP8>, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale, p.k_scale,
-                         p.pos, p.Q, p.N, R, k0, k1, fin, topk, cap, cand, out_idx, out_score, pa);
+      hipLaunchKernelGGL(k_emit_compact<kFP8>, rgrid, dim3(kRefineWaves * 64), 0, st, p.q, p.k, p.w, p.q_scale,
+                         p.k_scale, p.Q, p.N, R, topk, cap, cand, out_idx, out_score, pa);
     prof_close(slot, st);
   }
   // recovery: flagged rows by the unpruned streaming Top-K

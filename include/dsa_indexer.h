@@ -163,9 +163,24 @@ int dsa_indexer_topk_noalloc(const dsa_indexer_inputs* in, int32_t topk, int32_t
  * every key whose exact score reaches the start is found.  If at least K
  * do, the Top-K is exact as before; if fewer do, the row is recomputed by
  * the unpruned path (statistics: recovered = 2).  The results are the same
- * index set either way.  DSA_PRUNE_START_AT_TAU starts every row at tau. */
+ * index set either way.  DSA_PRUNE_START_AT_TAU starts every row at tau.
+ *
+ * Candidate records.  By default a kept candidate is a 64-bit record (the
+ * score's monotone 32-bit code, then the inverted key index), which orders
+ * candidates exactly.  DSA_PRUNE_COMPACT_RECORDS keeps 32-bit records
+ * instead (DoSA reading notes, annotation TMIF4XYF; 机器之心 DoSA article,
+ * section 04): the low kb bits hold the key index (kb = bits of N - 1) and
+ * the high 32 - kb bits a score code relative to the row, c = min(2^(32-kb)
+ * - 1, (code(s) - code(start)) >> shift), with the shift fitted at the start
+ * so that twice the row's best seed score still fits.  Records of different
+ * codes are ordered by score; the Top-K boundary code is resolved by
+ * rescoring its keys with all heads (all selected keys when out_score is
+ * requested).  A row whose boundary or buffer cannot be resolved in the
+ * workspace is recomputed by the unpruned path (recovered = 3).  Needs
+ * N <= 2^24 (else DSA_ERR_UNSUPPORTED).  Same index set and scores. */
 enum {
-  DSA_PRUNE_START_AT_TAU = 1u << 0
+  DSA_PRUNE_START_AT_TAU = 1u << 0,
+  DSA_PRUNE_COMPACT_RECORDS = 1u << 1
 };
 typedef struct dsa_prune_opts {
   int32_t num_seeds;
@@ -182,7 +197,8 @@ typedef struct dsa_prune_opts {
  *   survivors  [B,Q] int32 keys whose bound reached the running threshold
  *   recovered  [B,Q] uint8 0, or the reason the row was recomputed by the
  *              unpruned path: 1 its plan or seeds (or force_recover), 2
- *              fewer than K exact scores reached its raised start
+ *              fewer than K exact scores reached its raised start, 3 its
+ *              compact records did not fit the workspace
  *   upper_bound [B,Q,N] fp32 debug: the bound of every non-seed visible key
  *              (NaN elsewhere); small shapes only, costs one extra pass
  *   plan_rows  [B,Q,32,128] debug: each row's bound plan, in the input dtype

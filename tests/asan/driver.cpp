@@ -80,7 +80,9 @@ int main() {
       po.num_retained = 0;
       po.flags = DSA_PRUNE_START_AT_TAU;
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_OK);
-      po.flags = 2;
+      po.flags = DSA_PRUNE_START_AT_TAU | DSA_PRUNE_COMPACT_RECORDS;
+      EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_OK);
+      po.flags = 4;
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_ERR_INVALID_ARG);
       EXPECT(dsa_indexer_workspace_bytes(DSA_OP_TOPK_PRUNED, &in, 2048, &po) == 0 ? 0 : 1, 0);
       po.flags = 0;

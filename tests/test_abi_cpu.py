@@ -220,10 +220,10 @@ def test_bad_flags_are_rejected(lib, flags):
     assert lib.dsa_indexer_last_error()
 
 
-@pytest.mark.parametrize("flags,ok", [(0, True), (1, True), (2, False), (1 << 31, False)])
+@pytest.mark.parametrize("flags,ok", [(0, True), (1, True), (2, True), (3, True), (4, False), (1 << 31, False)])
 def test_prune_flags(lib, flags, ok):
-    """dsa_prune_opts.flags: only DSA_PRUNE_START_AT_TAU is known; the start
-    does not change the workspace."""
+    """dsa_prune_opts.flags: DSA_PRUNE_START_AT_TAU and
+    DSA_PRUNE_COMPACT_RECORDS are known; neither changes the workspace."""
     import torch
 
     from dsa_lightning_indexer_04_amd import _lib
@@ -237,6 +237,21 @@ def test_prune_flags(lib, flags, ok):
         assert b"flags" in lib.dsa_indexer_last_error()
     with pytest.raises(ValueError, match="start"):
         _lib.topk_pruned(*[torch.zeros(1)] * 4, 16, start="high")
+    with pytest.raises(ValueError, match="records"):
+        _lib.topk_pruned(*[torch.zeros(1)] * 4, 16, records="short")
+
+
+def test_compact_records_need_at_most_2_24_keys(lib):
+    """Compact records keep the key index in the low bits of 32 (at most 24
+    of them)."""
+    from dsa_lightning_indexer_04_amd import _lib
+
+    opts = _lib.PruneOpts(0, 0, None, None, _lib.DSA_PRUNE_COMPACT_RECORDS)
+    assert lib.dsa_indexer_workspace_bytes(2, ctypes.byref(_inputs(_lib, num_q=4, num_k=1 << 24)), 16,
+                                           ctypes.byref(opts)) > 0
+    assert lib.dsa_indexer_workspace_bytes(2, ctypes.byref(_inputs(_lib, num_q=4, num_k=(1 << 24) + 1)), 16,
+                                           ctypes.byref(opts)) == 0
+    assert b"2^24" in lib.dsa_indexer_last_error()
 
 
 def test_route_flags_set_the_workspace(lib):

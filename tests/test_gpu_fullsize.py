@@ -43,12 +43,13 @@ def _unpruned(wl, args, kw, scores=False):
     return (idx, sc) if scores else idx
 
 
-def _pruned(wl, args, kw):
+def _pruned(wl, args, kw, records="exact"):
     inp = _lib.make_inputs_struct(*args, kw["q_scale"], kw["k_scale"])
-    opts = _lib.PruneOpts(0, 0, None, None)
+    opts = _lib.PruneOpts(0, 0, None, None, _lib.PRUNE_RECORDS[records])
     ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                      device="cuda")
-    idx, _, st = dsa.topk_pruned(*args, wl.topk, **kw, return_scores=False, workspace=ws, stats=True)
+    idx, _, st = dsa.topk_pruned(*args, wl.topk, **kw, records=records, return_scores=False, workspace=ws,
+                                 stats=True)
     torch.cuda.synchronize()
     return idx, st
 
@@ -109,11 +110,16 @@ def test_fullsize_pruned_equals_unpruned(name):
     wl, d, args, kw = _device_inputs(name)
     log(f"{name}: unpruned and pruned Top-K at full size")
     u_idx, u_sc = _unpruned(wl, args, kw, scores=True)
-    p_idx, st = _pruned(wl, args, kw)
-    assert torch.equal(torch.sort(u_idx, dim=-1).values, torch.sort(p_idx, dim=-1).values)
-    assert not bool(st["recovered"].any().item())
-    screened, surv = int(st["screened"].sum().item()), int(st["survivors"].sum().item())
-    log(f"  {name}: identical sets on all {wl.batch * wl.num_q} rows; survivors {surv} of {screened} screened")
+    u_sorted = torch.sort(u_idx, dim=-1).values
+    # both candidate record formats (64-bit exact; 32-bit compact with the
+    # boundary resolved by rescoring)
+    for records in ("compact", "exact"):
+        p_idx, st = _pruned(wl, args, kw, records)
+        assert torch.equal(u_sorted, torch.sort(p_idx, dim=-1).values), records
+        assert not bool(st["recovered"].any().item()), records
+        screened, surv = int(st["screened"].sum().item()), int(st["survivors"].sum().item())
+        log(f"  {name} ({records} records): identical sets on all {wl.batch * wl.num_q} rows; "
+            f"survivors {surv} of {screened} screened")
     # the unpruned rows against the oracle (the pruned sets equal them)
     _check(name, u_idx, u_sc, d, wl, 64)
     # tau <= the row's K-th best score.  The sampled rows' scores come from

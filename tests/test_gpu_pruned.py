@@ -46,24 +46,32 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("start", ["raised", "tau"])
+@pytest.mark.parametrize("start,records", [("raised", "exact"), ("tau", "exact"), ("raised", "compact"),
+                                           ("tau", "compact")])
 @pytest.mark.parametrize("B,Q,N,k,dtype,dist,ns", CASES)
-def test_pruned_bit_identical_and_bounds(B, Q, N, k, dtype, dist, ns, start):
+def test_pruned_bit_identical_and_bounds(B, Q, N, k, dtype, dist, ns, start, records):
     need_gpu()
     rng = np.random.default_rng(N)
     pos = np.sort(rng.integers(N // 2, N, size=(B, Q)), axis=1)
     pos[:, -1] = N - 1
     d = inputs.make_inputs(B, Q, N, dtype, dist, seed=N + Q, positions=pos)
     dd = to_device(d)
-    log(f"pruned B={B} Q={Q} N={N} k={k} {dtype} {dist} seeds={ns} start={start}")
+    log(f"pruned B={B} Q={Q} N={N} k={k} {dtype} {dist} seeds={ns} start={start} records={records}")
     args, kw = call_args(dd)
-    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start=start, stats=True, upper_bound=True)
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start=start, records=records, stats=True,
+                                  upper_bound=True)
     idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     st = {n: v.cpu().numpy() for n, v in st.items()}
     u_idx, u_sc = _unpruned(dd, k)
     _same_sets(idx, sc, u_idx, u_sc)
-    # a tau start never recovers; a raised start only on a miss (code 2)
+    # without scores (compact records: only the boundary code is rescored)
+    idx2, _, _ = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start=start, records=records, return_scores=False)
+    idx2 = idx2.cpu().numpy()
+    assert np.array_equal(np.sort(idx2, axis=-1), np.sort(u_idx, axis=-1))
+    # a tau start never misses; a raised start only on a miss (code 2); the
+    # compact records fit these rows (code 3 would recompute them)
     assert not (st["recovered"] == 1).any()
+    assert not (st["recovered"] == 3).any()
     if start == "tau":
         assert not st["recovered"].any()
     log(f"  raised-start misses: {int((st['recovered'] == 2).sum())}")
@@ -153,10 +161,49 @@ def test_raised_start_miss_recovers(dtype):
     _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
     rec = st["recovered"].cpu().numpy()
     assert (rec == 2).all(), rec
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, records="compact", stats=True)
+    _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
+    assert (st["recovered"].cpu().numpy() == 2).all()
     idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start="tau", stats=True)
     _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
     assert not st["recovered"].cpu().numpy().any()
     assert_rows_ok(OracleRows(d), u_idx, u_sc, [(0, t) for t in range(Q)], k)
+
+
+@pytest.mark.parametrize("start,records", [("raised", "exact"), ("tau", "exact"), ("raised", "compact"),
+                                           ("tau", "compact")])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_ties_and_zero_weights(dtype, start, records):
+    """Rows with all-zero weights score every key 0, so their Top-K is keys
+    0..k-1 by the tie rule, and every key at or below the start's key is a
+    candidate.  With a tau start that is about 2480 keys (the 128th of 1024
+    seeds over 20000 keys).  Exact records are cut as usual.  Compact records
+    put them all in one score code, which no cut can split, so the buffer
+    (4k + 640 = 1152 records) cannot make room and the row is recomputed
+    unpruned (recovered = 3).  With the raised start (seed rank 21, about
+    390 keys) the boundary code is rescored instead.  Every combination
+    gives the unpruned sets, with and without scores."""
+    need_gpu()
+    B, Q, N, k = 1, 12, 20000, 128
+    d = inputs.make_inputs(B, Q, N, dtype, "clustered", seed=5)
+    d["w"][0, ::3] = 0.0
+    dd = to_device(d)
+    args, kw = call_args(dd)
+    log(f"ties {dtype} {start} {records}")
+    u_idx, u_sc = _unpruned(dd, k)
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=1024, start=start, records=records, stats=True)
+    _same_sets(idx.cpu().numpy(), sc.cpu().numpy(), u_idx, u_sc)
+    idx2, _, st2 = dsa.topk_pruned(*args, k, **kw, num_seeds=1024, start=start, records=records,
+                                   return_scores=False, stats=True)
+    assert np.array_equal(np.sort(idx2.cpu().numpy(), axis=-1), np.sort(u_idx, axis=-1))
+    zero_rows = np.arange(Q) % 3 == 0
+    assert np.array_equal(np.sort(u_idx[0, zero_rows], axis=-1), np.tile(np.arange(k), (zero_rows.sum(), 1)))
+    for s_ in (st, st2):
+        rec = s_["recovered"].cpu().numpy()[0]
+        assert not rec[~zero_rows].any(), rec
+        want = 3 if (records == "compact" and start == "tau") else 0
+        assert (rec[zero_rows] == want).all(), rec
+    log(f"  recovered: {st['recovered'].cpu().numpy()[0].tolist()}")
 
 
 def test_pruned_small_and_degenerate():
