@@ -45,8 +45,8 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
     ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
     ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
-    ("chunked_prefill_128k", "k_screen"): ("f3d7bc1e406ea83d", 77014, 21444),
-    ("chunked_prefill_128k", "k_refine"): ("f3d7bc1e406ea83d", 351708, 45864),
+    ("chunked_prefill_128k", "k_screen"): ("f3d7bc1e406ea83d", 77017, 21445),
+    ("chunked_prefill_128k", "k_refine"): ("f3d7bc1e406ea83d", 426806, 51930),
     ("context_1m_fp8", "k_screen"): ("f3d7bc1e406ea83d", 451306, 209436),
     ("context_1m_fp8", "k_refine"): ("f3d7bc1e406ea83d", 896547, 78040),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
@@ -167,21 +167,21 @@ def run_workload(name, path, steps, warmup):
     inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
     stats = None
     if use_pruned:
-        opts = _lib.PruneOpts(0, 0, None, None, _lib.PRUNE_STARTS[start] | _lib.PRUNE_RECORDS[records])
+        opts = _lib.PruneOpts(wl.num_seeds, 0, None, None, _lib.PRUNE_STARTS[start] | _lib.PRUNE_RECORDS[records])
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                          device=dev)
 
         def call():
-            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start, records=records,
-                                   return_scores=False, workspace=ws)
+            return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, num_seeds=wl.num_seeds, start=start,
+                                   records=records, return_scores=False, workspace=ws)
 
-        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, start=start, records=records,
-                                   return_scores=False, workspace=ws, stats=True)
+        _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, num_seeds=wl.num_seeds,
+                                   start=start, records=records, return_scores=False, workspace=ws, stats=True)
         scr = int(st["screened"].sum().item())
         sur = int(st["survivors"].sum().item())
-        seeds = min(12288, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced seeds, visible to every row
+        seeds = min(wl.num_seeds, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced seeds, visible to every row
         stats = {"screened_pairs": scr, "survivor_pairs": sur, "seed_pairs": seeds,
-                 "filter_rate": 1.0 - sur / max(1, scr), "start": start, "records": records,
+                 "filter_rate": 1.0 - sur / max(1, scr), "start": start, "records": records, "seeds": wl.num_seeds,
                  "recovered_rows": int((st["recovered"] != 0).sum().item()),
                  "start_misses": int((st["recovered"] == 2).sum().item())}
     else:

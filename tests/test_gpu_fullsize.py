@@ -45,11 +45,11 @@ def _unpruned(wl, args, kw, scores=False):
 
 def _pruned(wl, args, kw, records="exact"):
     inp = _lib.make_inputs_struct(*args, kw["q_scale"], kw["k_scale"])
-    opts = _lib.PruneOpts(0, 0, None, None, _lib.PRUNE_RECORDS[records])
+    opts = _lib.PruneOpts(wl.num_seeds, 0, None, None, _lib.PRUNE_RECORDS[records])
     ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                      device="cuda")
-    idx, _, st = dsa.topk_pruned(*args, wl.topk, **kw, records=records, return_scores=False, workspace=ws,
-                                 stats=True)
+    idx, _, st = dsa.topk_pruned(*args, wl.topk, **kw, num_seeds=wl.num_seeds, records=records,
+                                 return_scores=False, workspace=ws, stats=True)
     torch.cuda.synchronize()
     return idx, st
 
