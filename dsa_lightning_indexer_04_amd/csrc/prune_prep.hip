@@ -197,7 +197,7 @@ constexpr int kLinRow = 31;     // linear row E
 constexpr int kLinLoRow = 28;   // fp8: low part of E, a |d| row
 constexpr int kAuxLoRow = 29;   // fp8: low part of q_neg, a |d| row
 constexpr int kPlanRows = 32;
-constexpr int kSweeps = 20;     // coordinate-descent sweeps of the projection
+constexpr int kSweeps = 10;     // coordinate-descent sweeps of the projection
 constexpr int kSamples = 128;   // sample keys for the activation statistics
 constexpr int kPlanWaves = 4;   // query rows per planner workgroup (one per wave)
 
