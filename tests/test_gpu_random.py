@@ -7,7 +7,8 @@ case:
   * both Top-K routes (split and streaming) return, on every row, the exact
     lexicographic Top-K of the GPU's own scores, then -1 padding;
   * the first rows pass the float64 oracle's acceptance check;
-  * the pruned path returns the same index sets as the unpruned path.
+  * the pruned path returns the same index sets as the unpruned path, with
+    either start, either record format and a drawn seed count.
 """
 import numpy as np
 import pytest
@@ -48,5 +49,13 @@ def test_random_shapes(case):
             assert np.all(idx[b, t, n:] == -1), (path, b, t)
         assert_rows_ok(OracleRows(d), idx, sc, rows[:4], k)
         sets[path] = np.sort(idx, -1)
-    pidx, _, _ = dsa.topk_pruned(*args, k, **kw)
-    assert np.array_equal(np.sort(pidx.cpu().numpy(), -1), sets["stream"])
+    # the pruned path in every start / record combination, with and without
+    # scores (seed count drawn too, fewer or more than k)
+    ns = int(rng.choice([0, 64, 1024, 4096]))
+    for start in ("raised", "tau"):
+        for records in ("exact", "compact"):
+            if records == "compact" and N > (1 << 24):
+                continue
+            pidx, psc, _ = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start=start, records=records,
+                                           return_scores=records == "compact")
+            assert np.array_equal(np.sort(pidx.cpu().numpy(), -1), sets["stream"]), (start, records)
