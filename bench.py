@@ -18,7 +18,10 @@ with the most device time): its duration is the mean of HIP events the
 library records around each launch on the launch stream during the timed
 steps; its work is the matrix-product FLOPs its launches execute (2*64*128
 per fully scored pair; the pruned path's chunk screen 2*128*32 per bounded
-pair), against MI355X's published dense MFMA peak for the dtype.
+pair), against MI355X's published dense MFMA peak for the dtype.  Beside
+it, the rate the same score step sustains on this part with no memory
+traffic (the library's probe on synthetic full-entropy operands): under a
+full MFMA load the clock drops below the one the nominal peak assumes.
 """
 from __future__ import annotations
 
@@ -87,6 +90,8 @@ def parse():
                     help="comma list of further workloads whose oracle is timed the same way (or 'none')")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (counter calibration) and exit")
+    ap.add_argument("--sustained-only", action="store_true",
+                    help="only measure the score step's sustained MFMA rates (bf16, fp8), print them and exit")
     return ap.parse_args()
 
 
@@ -144,6 +149,37 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": mib << 20, "copy_bytes_written": mib << 20, "launches": 3}), flush=True)
+
+
+def sustained_rates(dtype, launches=5, warmup=2):
+    """The score step's sustained MFMA rate on this part (TFLOP/s): the
+    library's probe (dsa_indexer_mfma_ceiling) runs the streaming kernel's
+    32-key block step on synthetic full-entropy operands in registers and LDS,
+    without memory traffic or candidate bookkeeping, long enough (about 10 ms
+    a launch) for the clock to settle.  mode 0: MFMAs and fragment reloads
+    only; mode 1: with the ReLU-weighted head sum and the combine."""
+    import torch
+    from dsa_lightning_indexer_04_amd import _lib
+
+    iters = 16000 if dtype == "bf16" else 32000
+    wg = _lib.mfma_ceiling(dtype, 1, iters)
+    out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    flops = wg * 4 * iters * 2 * 64 * 32 * 128
+    res = {"unit": "TFLOP/s", "workgroups": wg, "flops_per_launch": flops}
+    for mode, key in ((0, "mfma_only"), (1, "score_step")):
+        for _ in range(warmup):
+            _lib.mfma_ceiling(dtype, mode, iters, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            _lib.mfma_ceiling(dtype, mode, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        res[key] = flops / (ms * 1e-3) / 1e12
+        res[key + "_ms"] = ms
+    return res
 
 
 def run_workload(name, path, steps, warmup):
@@ -488,6 +524,13 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.sustained_only:
+        res = {dt: sustained_rates(dt) for dt in ("bf16", "fp8")}
+        for dt, r in res.items():
+            r["mfma_only_frac"] = r["mfma_only"] / PEAK_TFLOPS[dt]
+            r["score_step_frac"] = r["score_step"] / PEAK_TFLOPS[dt]
+        print(json.dumps({"sustained_mfma": res}), flush=True)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; rows shard across GPUs with no "
                           "collective (see the design notes), so no multi-GPU figure is produced",
@@ -533,6 +576,18 @@ def main():
         "launch_ms": main_res["dominant_ms"],
         "flops_per_launch": main_res["dominant_flops"],
     }
+    sustained = {dt: sustained_rates(dt) for dt in ("bf16", "fp8")}
+    st = sustained[main_res["dtype"]]
+    roofline["sustained"] = {k: st[k] for k in ("mfma_only", "score_step", "unit")}
+    roofline["frac_of_sustained_score_step"] = main_res["achieved_tflops"] / st["score_step"]
+    for r in extra.values():  # other lines whose dominant kernel is the streaming Top-K
+        if r.get("dominant_kernel") == "k_topk_stream" and r.get("dtype") in sustained:
+            r["roofline"]["frac_of_sustained_score_step"] = (r["achieved_tflops"] /
+                                                            sustained[r["dtype"]]["score_step"])
+    for dt, r in sustained.items():
+        log(f"[bench] sustained {dt}: MFMA only {r['mfma_only']:.0f} TFLOP/s "
+            f"({100 * r['mfma_only'] / PEAK_TFLOPS[dt]:.1f}% of nominal), score step {r['score_step']:.0f} TFLOP/s "
+            f"({100 * r['score_step'] / PEAK_TFLOPS[dt]:.1f}% of nominal)")
     cpu, cpu_more = None, {}
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores ...")
@@ -570,6 +625,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baselines_more": cpu_more,
+        "sustained_mfma": sustained,
         "detail": main_res,
         "also": extra,
     }

@@ -122,6 +122,7 @@ EXPORTED = [
     "dsa_indexer_last_error",
     "dsa_indexer_profile_begin",
     "dsa_indexer_profile_end",
+    "dsa_indexer_mfma_ceiling",
 ]
 
 _lib = None
@@ -176,6 +177,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(I32),
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_int]
     lib.dsa_indexer_profile_end.restype = ctypes.c_int
+    lib.dsa_indexer_mfma_ceiling.argtypes = [I32, I32, I32, P, SZ, P, ctypes.POINTER(I32)]
+    lib.dsa_indexer_mfma_ceiling.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -582,3 +585,21 @@ def profile_end(max_kernels: int = 16) -> dict:
     if n < 0:
         raise IndexerError(4, "profile window: HIP error")
     return {names[i].decode(): (int(counts[i]), float(means[i])) for i in range(min(n, max_kernels))}
+
+
+def mfma_ceiling(dtype: str, mode: int, iters: int, out=None) -> int:
+    """The score step on synthetic operands (dsa_indexer_mfma_ceiling) on the
+    current stream; returns the launch's workgroup count.  With out=None only
+    the count is returned, nothing is launched."""
+    if dtype not in ("bf16", "fp8"):
+        raise ValueError(f"dtype must be bf16 or fp8, got {dtype!r}")
+    lib = load()
+    wg = ctypes.c_int32(0)
+    if out is not None:
+        _check_device([("out", out)])
+        if out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor")
+    rc = lib.dsa_indexer_mfma_ceiling(DSA_BF16 if dtype == "bf16" else DSA_FP8_E4M3, mode, iters, _ptr(out),
+                                      0 if out is None else out.numel(), _stream(), ctypes.byref(wg))
+    _check(rc)
+    return int(wg.value)

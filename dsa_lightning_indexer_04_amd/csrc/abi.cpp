@@ -11,6 +11,7 @@
 #include <string>
 
 #include "../../include/dsa_indexer.h"
+#include "../../include/dsa_indexer_profile.h"
 #include "kernels.h"
 
 namespace {
@@ -612,5 +613,20 @@ const char* dsa_indexer_error_string(int code) {
 }
 
 const char* dsa_indexer_last_error(void) { return g_last_error.c_str(); }
+
+int dsa_indexer_mfma_ceiling(int32_t dtype, int32_t mode, int32_t iters, float* out, size_t out_len, void* stream,
+                             int32_t* workgroups) {
+  if (!workgroups) return fail(DSA_ERR_INVALID_ARG, "workgroups must not be NULL");
+  if (dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "unknown dtype");
+  if (mode != 0 && mode != 1) return fail(DSA_ERR_INVALID_ARG, "mode must be 0 or 1");
+  if (iters < 2 || (iters & 1)) return fail(DSA_ERR_INVALID_ARG, "iters must be even and >= 2");
+  const int wg = dsa::mfma_ceiling_workgroups();
+  if (wg < 1) return fail(DSA_ERR_HIP, "device query failed");
+  *workgroups = wg;
+  if (!out) return DSA_OK;
+  if (out_len < (size_t)wg * 256) return fail(DSA_ERR_INVALID_ARG, "out holds fewer than workgroups * 256 floats");
+  return hip_status(dsa::launch_mfma_ceiling(dtype, mode, iters, wg, out,
+                                             static_cast<hipStream_t>(stream)));
+}
 
 }  // extern "C"

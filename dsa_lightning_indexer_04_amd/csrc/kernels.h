@@ -158,6 +158,16 @@ int mla_splits(int rows, int requested);
 hipError_t launch_sparse_mla(const MlaProblem& p, float sm_scale, uint16_t* out, float* lse, float* row_max,
                              int32_t* retry, int nsplit, float* part_o, float* part_ml, hipStream_t st);
 
+// ---------------------------------------------------------------- sustained-rate probe
+
+// Workgroups of the probe launch: two per compute unit of the current device
+// (-1 on a HIP error).
+int mfma_ceiling_workgroups();
+// The score step on synthetic operands held in registers and LDS; mode 0:
+// MFMAs and key-fragment reloads only, mode 1: with the head sum and the
+// combine.  `out`: workgroups * 256 floats (per-lane sinks).
+hipError_t launch_mfma_ceiling(int dtype, int mode, int iters, int workgroups, float* out, hipStream_t st);
+
 // ---------------------------------------------------------------- fixed scratch
 
 // Bytes of the per-device scratch array behind dsa_indexer_topk_noalloc.

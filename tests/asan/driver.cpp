@@ -9,6 +9,7 @@
 #include <initializer_list>
 
 #include "dsa_indexer.h"
+#include "dsa_indexer_profile.h"
 
 extern int g_launches;
 static int g_checks = 0, g_bad = 0;
@@ -131,6 +132,14 @@ int main() {
   }
   mi.num_splits = 9;
   EXPECT(dsa_sparse_mla_workspace_bytes(&mi) == 0 ? 0 : 1, 0);
+  // sustained-rate probe: the count alone, a launch, a short buffer
+  int32_t wg = 0;
+  EXPECT(dsa_indexer_mfma_ceiling(DSA_BF16, 1, 64, nullptr, 0, nullptr, &wg), DSA_OK);
+  EXPECT(wg > 0 ? 0 : 1, 0);
+  EXPECT(dsa_indexer_mfma_ceiling(DSA_FP8_E4M3, 0, 64, static_cast<float*>(P(20 << 10)), (size_t)wg * 256, nullptr, &wg),
+         DSA_OK);
+  EXPECT(dsa_indexer_mfma_ceiling(DSA_BF16, 0, 64, static_cast<float*>(P(20 << 10)), (size_t)wg * 256 - 1, nullptr, &wg),
+         DSA_ERR_INVALID_ARG);
   std::printf("%d checks, %d failed, %d stubbed launches\n", g_checks, g_bad, g_launches);
   return g_bad ? 1 : 0;
 }

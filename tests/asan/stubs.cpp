@@ -70,6 +70,11 @@ hipError_t launch_sparse_mla(const MlaProblem&, float, uint16_t*, float*, float*
   ++g_launches;
   return hipSuccess;
 }
+int mfma_ceiling_workgroups() { return 512; }
+hipError_t launch_mfma_ceiling(int, int, int, int, float*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 int noalloc_scratch(void** ptr, std::string*) {
   static char fake[256] __attribute__((aligned(256)));
   *ptr = fake;  // never dereferenced: the launchers above are stand-ins

@@ -420,3 +420,19 @@ def test_noalloc_rejects_calls_beyond_the_fixed_scratch(lib):
     # argument errors come first, as for dsa_indexer_topk
     assert lib.dsa_indexer_topk_noalloc(ctypes.byref(_inputs(_lib, heads=32)), 16, None, None, None) == 2
     assert lib.dsa_indexer_topk_noalloc(ctypes.byref(_inputs(_lib)), 0, None, None, None) == 1
+
+
+@pytest.mark.parametrize("dtype,mode,iters,wg_null", [
+    (2, 0, 16, False),   # unknown dtype
+    (0, 2, 16, False),   # unknown mode
+    (0, 1, 15, False),   # odd iteration count
+    (1, 0, 0, False),    # no iterations
+    (0, 0, 16, True),    # nowhere to report the workgroup count
+])
+def test_mfma_ceiling_arguments(lib, dtype, mode, iters, wg_null):
+    """The sustained-rate probe checks its arguments before any device query."""
+    wg = ctypes.c_int32(-7)
+    rc = lib.dsa_indexer_mfma_ceiling(dtype, mode, iters, None, 0, None, None if wg_null else ctypes.byref(wg))
+    assert rc == 1
+    assert wg.value == -7
+    assert lib.dsa_indexer_last_error()
