@@ -228,7 +228,7 @@ size_t pruned_layout(const dsa_indexer_inputs* in, int32_t topk, const PruneConf
   uint8_t* spos = take(R * 4);
   uint8_t* stidx = take(R * (uint64_t)topk * 4);
   uint8_t* stsc = take(R * (uint64_t)topk * 4);
-  const uint64_t mwords = (uint64_t)dsa::prune_mask_words(in->num_k);
+  const uint64_t mwords = (uint64_t)dsa::prune_mask_words(in->num_k, 128 * (int)elem_bytes(in->dtype));
   uint8_t* ctl = take(R * sizeof(dsa::PruneRowCtl));
   uint8_t* hist = take(R * 256 * 4);
   uint8_t* mask = take(R * mwords * 8);

@@ -64,10 +64,13 @@ struct PruneRowCtl {
   int32_t pad[3];
 };
 
-// Longest key chunk of the screen/refine schedule.
-constexpr int kMaxPruneChunk = 131072;
-// Bitmask words per row: the longest chunk of the schedule for N keys / 64.
-int prune_mask_words(int N);
+// Key bytes of the longest chunk of the screen/refine schedule: a chunk's
+// key rows then fit one XCD's 4 MiB L2, so the row groups that screen it
+// after the first ones read it from there (16384 bf16 or 32768 fp8 keys).
+constexpr int kPruneChunkBytes = 4 << 20;
+// Bitmask words per row: the longest chunk of the schedule for N keys of
+// row_bytes each (256 bf16, 128 fp8), / 64.
+int prune_mask_words(int N, int row_bytes);
 
 // Device buffers of the pruned Top-K (workspace carve-up and optional stats).
 struct PrunedBuffers {

@@ -1017,24 +1017,25 @@ __global__ void k_fill_nan(float* p, size_t n) {
 }
 
 // Key chunks of the screen/refine schedule: the first two of
-// max(4096, N / 32) keys (rounded up to 4096), then lengths doubling up to
-// kMaxPruneChunk.  Boundaries are multiples of 4096: whole screen tiles and
-// bitmask words.
-std::vector<std::pair<int, int>> prune_chunks(int N) {
+// max(4096, N / 32) keys (rounded up to 4096), then lengths doubling, none
+// longer than kPruneChunkBytes of key rows.  Boundaries are multiples of
+// 4096: whole screen tiles and bitmask words.
+std::vector<std::pair<int, int>> prune_chunks(int N, int row_bytes) {
+  const int max_len = kPruneChunkBytes / row_bytes;
   std::vector<std::pair<int, int>> out;
-  int len = std::max(4096, (N / 32 + 4095) / 4096 * 4096);
+  int len = std::min(max_len, std::max(4096, (N / 32 + 4095) / 4096 * 4096));
   for (int s = 0; s < N;) {
     const int e = (int)std::min<int64_t>((int64_t)s + len, N);
     out.emplace_back(s, e);
     s = e;
-    if (out.size() >= 2) len = std::min(2 * len, kMaxPruneChunk);
+    if (out.size() >= 2) len = std::min(2 * len, max_len);
   }
   return out;
 }
 
-int prune_mask_words(int N) {
+int prune_mask_words(int N, int row_bytes) {
   int mx = 0;
-  for (const auto& c : prune_chunks(N)) mx = std::max(mx, c.second - c.first);
+  for (const auto& c : prune_chunks(N, row_bytes)) mx = std::max(mx, c.second - c.first);
   // the screen writes whole tiles (up to 128 keys, two words) past a
   // chunk's last key
   return (mx + 127) / 128 * 2;
@@ -1067,7 +1068,7 @@ hipError_t launch_topk_pruned(const Problem& p, int topk, int cap, uint64_t* can
   const RefineKern refine = p.dtype == kBF16 ? (pb.compact ? k_refine<kBF16, true> : k_refine<kBF16, false>)
                                              : (pb.compact ? k_refine<kFP8, true> : k_refine<kFP8, false>);
   const dim3 sgrid((unsigned)((p.Q + 2 * kScreenWaves - 1) / (2 * kScreenWaves)), p.B);
-  const auto chunks = prune_chunks(p.N);
+  const auto chunks = prune_chunks(p.N, p.dtype == kBF16 ? 256 : 128);
   for (size_t c = 0; c < chunks.size(); ++c) {
     const int k0 = chunks[c].first, k1 = chunks[c].second;
     const int fin = c + 1 == chunks.size() ? 1 : 0;

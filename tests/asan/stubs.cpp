@@ -49,7 +49,7 @@ hipError_t launch_topk_pruned(const Problem&, int, int, uint64_t*, int32_t*, flo
   ++g_launches;
   return hipSuccess;
 }
-int prune_mask_words(int N) { return (std::min(N, kMaxPruneChunk) + 127) / 128 * 2; }
+int prune_mask_words(int N, int row_bytes) { return (std::min(N, kPruneChunkBytes / row_bytes) + 127) / 128 * 2; }
 int proj_block_tokens(int T, int requested) { return std::min(T, requested > 0 ? requested : 65536); }
 size_t proj_workspace_bytes(int T, int hidden, int block_tokens) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
