@@ -48,10 +48,10 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
     ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
     ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
-    ("chunked_prefill_128k", "k_screen"): ("f3d7bc1e406ea83d", 77017, 21445),
-    ("chunked_prefill_128k", "k_refine"): ("f3d7bc1e406ea83d", 426806, 51930),
-    ("context_1m_fp8", "k_screen"): ("f3d7bc1e406ea83d", 451306, 209436),
-    ("context_1m_fp8", "k_refine"): ("f3d7bc1e406ea83d", 896547, 78040),
+    ("chunked_prefill_128k", "k_screen"): ("dce06e78e21f85b8", 59868, 12966),
+    ("chunked_prefill_128k", "k_refine"): ("dce06e78e21f85b8", 166099, 34512),
+    ("context_1m_fp8", "k_screen"): ("dce06e78e21f85b8", 133928, 65545),
+    ("context_1m_fp8", "k_refine"): ("dce06e78e21f85b8", 204732, 35775),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
     ("projection_prefill_128k", "k_proj_out"): ("61f24b18bb20f769", 1073178, 553001),
     ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
