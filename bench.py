@@ -70,14 +70,18 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunked_prefill_128k")
-    ap.add_argument("--path", choices=["auto", "topk", "pruned", "pruned_tau", "pruned_compact"], default="topk",
+    ap.add_argument("--path", choices=["auto", "topk", "pruned", "pruned_tau", "pruned_compact", "pruned_anchor"],
+                    default="topk",
                     help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one; "
                     "pruned_tau: the pruned path with every row's threshold starting at tau; pruned_compact: "
-                    "the pruned path with 32-bit candidate records)")
+                    "the pruned path with 32-bit candidate records; pruned_anchor: the pruned path with seeds from "
+                    "anchor queries, starting at tau)")
     ap.add_argument(
         "--also",
         default="chunked_prefill_128k:pruned,chunked_prefill_128k:pruned_tau,chunked_prefill_128k:pruned_compact,"
+        "chunked_prefill_128k:pruned_anchor,"
         "context_1m_fp8:topk,context_1m_fp8:pruned,context_1m_fp8:pruned_tau,context_1m_fp8:pruned_compact,"
+        "context_1m_fp8:pruned_anchor,"
         "chunked_prefill_128k_noise02:pruned,prefill_32k:topk,"
         "decode_64x128k:topk,projection_prefill_128k:project,sparse_mla_128k:sparse_mla,"
         "sparse_mla_decode_64x128k:sparse_mla",
@@ -197,27 +201,40 @@ def run_workload(name, path, steps, warmup):
     qs = None if d["q_scale"] is None else d["q_scale"].to(dev)
     ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
     del d
-    use_pruned = path in ("pruned", "pruned_tau", "pruned_compact") or (path == "auto" and wl.pruned)
-    start = "tau" if path == "pruned_tau" else "raised"
+    use_pruned = path in ("pruned", "pruned_tau", "pruned_compact", "pruned_anchor") or (path == "auto" and wl.pruned)
+    start = "tau" if path in ("pruned_tau", "pruned_anchor") else "raised"
     records = "compact" if path == "pruned_compact" else "exact"
+    seeds_from = "anchor" if path == "pruned_anchor" else "even"
     inp = _lib.make_inputs_struct(q, k, w, pos, qs, ks)
     stats = None
     if use_pruned:
-        opts = _lib.PruneOpts(wl.num_seeds, 0, None, None, _lib.PRUNE_STARTS[start] | _lib.PRUNE_RECORDS[records])
+        opts = _lib.PruneOpts(wl.num_seeds, 0, None, None,
+                              _lib.PRUNE_STARTS[start] | _lib.PRUNE_RECORDS[records] | _lib.PRUNE_SEEDS[seeds_from])
         ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                          device=dev)
 
         def call():
             return dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, num_seeds=wl.num_seeds, start=start,
-                                   records=records, return_scores=False, workspace=ws)
+                                   records=records, seeds=seeds_from, return_scores=False, workspace=ws)
 
         _, _, st = dsa.topk_pruned(q, k, w, pos, wl.topk, q_scale=qs, k_scale=ks, num_seeds=wl.num_seeds,
-                                   start=start, records=records, return_scores=False, workspace=ws, stats=True)
+                                   start=start, records=records, seeds=seeds_from, return_scores=False, workspace=ws,
+                                   stats=True)
         scr = int(st["screened"].sum().item())
         sur = int(st["survivors"].sum().item())
-        seeds = min(wl.num_seeds, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced seeds, visible to every row
-        stats = {"screened_pairs": scr, "survivor_pairs": sur, "seed_pairs": seeds,
+        anchor_pairs = 0
+        if seeds_from == "anchor":
+            # every visible pair is a seed pair or screened (no row recovers
+            # here); the anchor rows' own Top-K scores all their visible keys
+            seeds = wl.visible_pairs - scr
+            A = min(wl.num_q, max(1, wl.num_seeds // wl.topk))
+            anchor_pairs = wl.batch * sum(min(wl.num_k, wl.pos_start + ((2 * i + 1) * wl.num_q) // (2 * A) + 1)
+                                          for i in range(A))
+        else:
+            seeds = min(wl.num_seeds, wl.pos_start + 1) * wl.num_q * wl.batch  # evenly spaced, visible to every row
+        stats = {"screened_pairs": scr, "survivor_pairs": sur, "seed_pairs": seeds, "anchor_pairs": anchor_pairs,
                  "filter_rate": 1.0 - sur / max(1, scr), "start": start, "records": records, "seeds": wl.num_seeds,
+                 "seed_source": seeds_from,
                  "recovered_rows": int((st["recovered"] != 0).sum().item()),
                  "start_misses": int((st["recovered"] == 2).sum().item())}
     else:
@@ -255,6 +272,7 @@ def run_workload(name, path, steps, warmup):
         # bounds the other visible keys (32 plan rows each); the refine
         # rescores the survivors with all 64 heads
         work = {"k_topk_stream": stats["seed_pairs"] * PAIR_FLOPS,
+                "k_topk_stream_anchors": stats["anchor_pairs"] * PAIR_FLOPS,
                 "k_screen": stats["screened_pairs"] * SCREEN_FLOPS,
                 "k_refine": stats["survivor_pairs"] * PAIR_FLOPS}
         res["prune"] = stats

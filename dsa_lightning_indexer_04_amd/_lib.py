@@ -55,8 +55,10 @@ class PruneOpts(ctypes.Structure):
 # candidate record format they select.
 DSA_PRUNE_START_AT_TAU = 1 << 0
 DSA_PRUNE_COMPACT_RECORDS = 1 << 1
+DSA_PRUNE_ANCHOR_SEEDS = 1 << 2
 PRUNE_STARTS = {"raised": 0, "tau": DSA_PRUNE_START_AT_TAU}
 PRUNE_RECORDS = {"exact": 0, "compact": DSA_PRUNE_COMPACT_RECORDS}
+PRUNE_SEEDS = {"even": 0, "anchor": DSA_PRUNE_ANCHOR_SEEDS}
 
 
 class PruneStats(ctypes.Structure):
@@ -385,8 +387,9 @@ def topk_pruned(
     num_retained: int = 0,
     seed_idx=None,
     force_recover=None,
-    start: str = "raised",
+    start: str | None = None,
     records: str = "exact",
+    seeds: str = "even",
     return_scores: bool = True,
     stats: bool = False,
     upper_bound: bool = False,
@@ -395,9 +398,14 @@ def topk_pruned(
 ):
     """Exact per-row Top-K with certified pruning; same index set as topk().
 
-    start: "raised" (default) starts each row's running threshold at a seed
-    record above tau, verified at the end (a row short of K records at its
-    start is recomputed unpruned); "tau" starts at tau, the K-th seed score.
+    start: "raised" (the default with even seeds) starts each row's running
+    threshold at a seed record above tau, verified at the end (a row short of
+    K records at its start is recomputed unpruned); "tau" (the default, and
+    the only start, with anchor seeds) starts at tau, the K-th seed score.
+    seeds: "even" (default) spaces num_seeds seeds evenly over the keys every
+    row sees, or takes seed_idx; "anchor" takes the distinct keys of the
+    exact Top-K of num_seeds // topk anchor rows per sequence (num_seeds >=
+    topk, no seed_idx).
     records: "exact" (default) keeps 64-bit candidate records; "compact"
     keeps 32-bit records (row-relative score code + key index) and resolves
     the Top-K boundary by rescoring.
@@ -408,8 +416,19 @@ def topk_pruned(
     exported bound plan: plan_rows [B,Q,32,128] in q's dtype, plan_coef
     [B,Q,32], plan_misc [B,Q,2] = kappa, e_neg.
     """
+    if seeds not in PRUNE_SEEDS:
+        raise ValueError(f"seeds must be one of {sorted(PRUNE_SEEDS)}, not {seeds!r}")
+    if start is None:
+        start = "tau" if seeds == "anchor" else "raised"
     if start not in PRUNE_STARTS:
         raise ValueError(f"start must be one of {sorted(PRUNE_STARTS)}, not {start!r}")
+    if seeds == "anchor":
+        if start != "tau":
+            raise ValueError("anchor seeds start every row at tau (start='tau')")
+        if seed_idx is not None:
+            raise ValueError("anchor seeds take no seed_idx")
+        if (num_seeds or 12288) < topk:
+            raise ValueError(f"anchor seeds need num_seeds >= topk ({num_seeds} < {topk})")
     if records not in PRUNE_RECORDS:
         raise ValueError(f"records must be one of {sorted(PRUNE_RECORDS)}, not {records!r}")
     lib = load()
@@ -417,7 +436,7 @@ def topk_pruned(
     check_prune_args(seed_idx, force_recover, q.shape[0], q.shape[1], num_seeds)
     _check_device((("seed_idx", seed_idx), ("force_recover", force_recover)), q.device)
     opts = PruneOpts(num_seeds, num_retained, _ptr(seed_idx), _ptr(force_recover),
-                     PRUNE_STARTS[start] | PRUNE_RECORDS[records])
+                     PRUNE_STARTS[start] | PRUNE_RECORDS[records] | PRUNE_SEEDS[seeds])
     nbytes = workspace_bytes(DSA_OP_TOPK_PRUNED, inp, topk, opts)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
     B, Q = q.shape[:2]

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -173,13 +174,16 @@ struct PruneConfig {
   const uint8_t* force_recover;
   bool raised_start;
   bool compact;
+  bool anchor;
 };
 
 int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
   const uint32_t flags = o ? o->flags : 0u;
-  if (flags & ~(uint32_t)(DSA_PRUNE_START_AT_TAU | DSA_PRUNE_COMPACT_RECORDS))
+  if (flags & ~(uint32_t)(DSA_PRUNE_START_AT_TAU | DSA_PRUNE_COMPACT_RECORDS | DSA_PRUNE_ANCHOR_SEEDS))
     return fail(DSA_ERR_INVALID_ARG, "unknown pruning flags");
-  pc->raised_start = !(flags & DSA_PRUNE_START_AT_TAU);
+  pc->anchor = (flags & DSA_PRUNE_ANCHOR_SEEDS) != 0;
+  // anchor seeds are no even sample of the keys: every row starts at tau
+  pc->raised_start = !(flags & DSA_PRUNE_START_AT_TAU) && !pc->anchor;
   pc->compact = (flags & DSA_PRUNE_COMPACT_RECORDS) != 0;
   pc->num_seeds = (o && o->num_seeds) ? o->num_seeds : 12288;
   pc->num_retained = (o && o->num_retained) ? o->num_retained : 30;
@@ -190,15 +194,22 @@ int prune_config(const dsa_prune_opts* o, PruneConfig* pc) {
   if (pc->num_retained < 1 || pc->num_retained > 30)
     return fail(DSA_ERR_UNSUPPORTED, "num_retained must be in 1..30");
   if (pc->seed_idx && !aligned16(pc->seed_idx)) return fail(DSA_ERR_INVALID_ARG, "seed_idx must be 16-byte aligned");
+  if (pc->anchor && pc->seed_idx) return fail(DSA_ERR_INVALID_ARG, "anchor seeds and seed_idx exclude each other");
   return DSA_OK;
 }
 
 // Compact records keep the key index in the low bits of 32: at most 24 of
 // them, so that the score code keeps at least 8.
-int check_prune_fit(const dsa_indexer_inputs* in, const PruneConfig& pc) {
+int check_prune_fit(const dsa_indexer_inputs* in, const PruneConfig& pc, int32_t topk) {
   if (pc.compact && in->num_k > (1 << 24))
     return fail(DSA_ERR_UNSUPPORTED, "compact records need num_k <= 2^24");
+  if (pc.anchor && pc.num_seeds < topk) return fail(DSA_ERR_INVALID_ARG, "anchor seeds need num_seeds >= topk");
   return DSA_OK;
+}
+
+// Anchor rows per sequence: num_seeds / topk, at least 1, at most Q.
+int anchor_count(const dsa_indexer_inputs* in, const PruneConfig& pc, int32_t topk) {
+  return std::min(in->num_q, std::max(1, pc.num_seeds / topk));
 }
 
 // Workspace carve-up of the pruned path; returns the total bytes.  With a
@@ -393,7 +404,7 @@ size_t dsa_indexer_workspace_bytes(int op, const dsa_indexer_inputs* in, int32_t
   if (op == DSA_OP_TOPK) return topk_workspace(in, topk);
   if (op == DSA_OP_TOPK_PRUNED) {
     PruneConfig pc;
-    if (prune_config(opts, &pc) || check_prune_fit(in, pc)) return 0;
+    if (prune_config(opts, &pc) || check_prune_fit(in, pc, topk)) return 0;
     return pruned_layout(in, topk, pc, nullptr, nullptr);
   }
   fail(DSA_ERR_INVALID_ARG, "unknown op");
@@ -408,7 +419,7 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
   if ((rc = check_topk(topk))) return rc;
   PruneConfig pc;
   if ((rc = prune_config(opts, &pc))) return rc;
-  if ((rc = check_prune_fit(in, pc))) return rc;
+  if ((rc = check_prune_fit(in, pc, topk))) return rc;
   const size_t need = pruned_layout(in, topk, pc, nullptr, nullptr);
   if ((rc = check_topk_outputs(in, topk, out_idx, out_score, workspace, workspace_bytes, need))) return rc;
   if (stats) {
@@ -443,9 +454,23 @@ int dsa_indexer_topk_pruned(const dsa_indexer_inputs* in, int32_t topk, const ds
   }
   const dsa::Problem p = problem_of(in);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_status(dsa::launch_seed_prep(p, pc.num_seeds, pc.seed_idx, pb.seeds, pb.seed_count, pb.seed_bits,
-                                             pb.batch_flag, st))))
+  if (pc.anchor) {
+    // seeds from anchor queries: the anchor rows' exact Top-K by the
+    // unpruned streaming path (into their rows of the seed Top-K buffer; the
+    // planner's row flags serve as the row mask until the planner writes
+    // them), then the distinct keys of those sets
+    const int A = anchor_count(in, pc, topk);
+    if ((rc = hip_status(dsa::launch_anchor_rows(p, A, pb.plan_flag, st)))) return rc;
+    if ((rc = hip_status(dsa::launch_topk_stream_rows(p, topk, dsa::stream_capacity(topk), cand, pb.seed_top_idx,
+                                                      pb.seed_top_score, pb.plan_flag, "k_topk_stream_anchors", st))))
+      return rc;
+    if ((rc = hip_status(dsa::launch_anchor_seeds(p, A, topk, pb.seed_top_idx, pb.seed_stride, pb.seeds,
+                                                  pb.seed_count, pb.seed_bits, pb.batch_flag, st))))
+      return rc;
+  } else if ((rc = hip_status(dsa::launch_seed_prep(p, pc.num_seeds, pc.seed_idx, pb.seeds, pb.seed_count,
+                                                    pb.seed_bits, pb.batch_flag, st)))) {
     return rc;
+  }
   if ((rc = hip_status(dsa::launch_key_norms(p, pb.knorm, st)))) return rc;
   // the seeds' exact Top-K per row: the streaming Top-K over the packed seed
   // keys (the same score routine, so the same scores)

@@ -106,6 +106,12 @@ struct PrunedBuffers {
 hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, int32_t* seeds, int32_t* seed_count,
                             uint32_t* bits, int32_t* batch_flag, hipStream_t st);
 hipError_t launch_key_norms(const Problem& p, float* knorm, hipStream_t st);
+// Anchor seeds: flag[b*Q + t] = 1 on the A anchor rows of every sequence,
+// else 0; then, from the anchor rows' Top-K (top_idx, [B*Q][topk]), each
+// sequence's seeds (the distinct keys, ascending, at most S), count, bitmap.
+hipError_t launch_anchor_rows(const Problem& p, int A, int32_t* flag, hipStream_t st);
+hipError_t launch_anchor_seeds(const Problem& p, int A, int topk, const int32_t* top_idx, int S, int32_t* seeds,
+                               int32_t* seed_count, uint32_t* bits, int32_t* batch_flag, hipStream_t st);
 // Packs the seed keys (and fp8 scales) of every sequence and counts each
 // row's visible seeds, so the streaming Top-K can score the seeds.
 hipError_t launch_seed_pack(const Problem& p, const int32_t* seeds, const int32_t* seed_count, int seed_stride,

@@ -106,6 +106,70 @@ __global__ __launch_bounds__(256) void k_seed_prep(const int32_t* __restrict__ p
   }
 }
 
+// Anchor seeds (seeds from a few anchor queries): the A anchor rows of a
+// sequence are t_i = floor((2i + 1) Q / (2A)), i < A (distinct for A <= Q).
+__device__ __forceinline__ int anchor_row(int i, int Q, int A) { return (int)(((int64_t)(2 * i + 1) * Q) / (2 * A)); }
+
+// flag[b * Q + t] = 1 if row t is an anchor row of its sequence, else 0.
+// t_i lies within one of t * A / Q, so three candidates decide it.
+__global__ __launch_bounds__(256) void k_anchor_rows(int Q, int A, size_t R, int32_t* __restrict__ flag) {
+  const size_t row = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= R) return;
+  const int t = (int)(row % (size_t)Q);
+  const int c = (int)(((int64_t)t * A) / Q);
+  int is = 0;
+  for (int i = max(0, c - 1); i <= min(A - 1, c + 1); ++i) is |= anchor_row(i, Q, A) == t;
+  flag[row] = is;
+}
+
+// One workgroup per sequence: the distinct keys of the anchor rows' Top-K
+// sets (top_idx rows, -1 padded) as the sequence's seeds, ascending, and
+// their bitmap.  The bitmap is set first; then each thread takes a run of
+// words, the runs' key counts are prefix-summed over the workgroup, and each
+// thread writes its run's keys in order.  At most A * topk <= S keys.
+__global__ __launch_bounds__(256) void k_anchor_seeds(int Q, int N, int A, int topk, const int32_t* __restrict__ top_idx,
+                                                      int S, int32_t* __restrict__ seeds,
+                                                      int32_t* __restrict__ seed_count, uint32_t* __restrict__ bits,
+                                                      int words, int32_t* __restrict__ batch_flag) {
+  __shared__ int scan[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  uint32_t* bb = bits + (size_t)b * words;
+  for (int i = tid; i < words; i += 256) bb[i] = 0u;
+  __syncthreads();
+  for (int a = 0; a < A; ++a) {
+    const int32_t* ti = top_idx + ((size_t)b * Q + anchor_row(a, Q, A)) * (size_t)topk;
+    for (int j = tid; j < topk; j += 256) {
+      const int key = ti[j];
+      if (key >= 0 && key < N) atomicOr(&bb[key >> 5], 1u << (key & 31));
+    }
+  }
+  __syncthreads();
+  const int per = (words + 255) / 256;
+  const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bb[w]);
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive prefix sum over the workgroup
+    const int v = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int o = scan[tid] - cnt;
+  int32_t* sb = seeds + (size_t)b * S;
+  for (int w = w0; w < w1; ++w) {
+    for (uint32_t x = bb[w]; x; x &= x - 1u) {
+      if (o < S) sb[o] = w * 32 + __builtin_ctz(x);
+      ++o;
+    }
+  }
+  if (tid == 255) {
+    seed_count[b] = min(scan[255], S);
+    batch_flag[b] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- key norms
 
 // |k_s| (code units for fp8): each lane squares the values of one 16-byte
@@ -632,6 +696,22 @@ hipError_t launch_seed_prep(const Problem& p, int S, const int32_t* user_seeds, 
   const int prof_slot = prof_open("k_seed_prep", st);
   const int words = (p.N + 31) / 32;
   hipLaunchKernelGGL(k_seed_prep, dim3(p.B), dim3(256), 0, st, p.pos, p.Q, p.N, S, user_seeds, seeds, seed_count,
+                     bits, words, batch_flag);
+  prof_close(prof_slot, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_anchor_rows(const Problem& p, int A, int32_t* flag, hipStream_t st) {
+  const size_t rows = (size_t)p.B * p.Q;
+  hipLaunchKernelGGL(k_anchor_rows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p.Q, A, rows, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_anchor_seeds(const Problem& p, int A, int topk, const int32_t* top_idx, int S, int32_t* seeds,
+                               int32_t* seed_count, uint32_t* bits, int32_t* batch_flag, hipStream_t st) {
+  const int prof_slot = prof_open("k_anchor_seeds", st);
+  const int words = (p.N + 31) / 32;
+  hipLaunchKernelGGL(k_anchor_seeds, dim3(p.B), dim3(256), 0, st, p.Q, p.N, A, topk, top_idx, S, seeds, seed_count,
                      bits, words, batch_flag);
   prof_close(prof_slot, st);
   return hipGetLastError();

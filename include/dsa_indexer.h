@@ -177,10 +177,22 @@ int dsa_indexer_topk_noalloc(const dsa_indexer_inputs* in, int32_t topk, int32_t
  * rescoring its keys with all heads (all selected keys when out_score is
  * requested).  A row whose boundary or buffer cannot be resolved in the
  * workspace is recomputed by the unpruned path (recovered = 3).  Needs
- * N <= 2^24 (else DSA_ERR_UNSUPPORTED).  Same index set and scores. */
+ * N <= 2^24 (else DSA_ERR_UNSUPPORTED).  Same index set and scores.
+ *
+ * Anchor seeds.  DSA_PRUNE_ANCHOR_SEEDS takes the seeds from a few anchor
+ * queries instead of spacing them evenly (机器之心 DoSA article, section 03,
+ * seed sources): A = num_seeds / K anchor rows per sequence (at least 1, at
+ * most Q), the rows floor((2i + 1) Q / (2A)), i < A, have their exact Top-K
+ * computed first by the unpruned path, and the sequence's seeds are the
+ * distinct keys of those Top-K sets, ascending (at most A * K <= num_seeds).
+ * Such seeds are not an even sample, so every row starts at tau (the flag
+ * implies DSA_PRUNE_START_AT_TAU); a row that sees fewer than K seeds starts
+ * with no threshold.  Needs num_seeds >= K and seed_idx == NULL (else
+ * DSA_ERR_INVALID_ARG).  Same index set and scores. */
 enum {
   DSA_PRUNE_START_AT_TAU = 1u << 0,
-  DSA_PRUNE_COMPACT_RECORDS = 1u << 1
+  DSA_PRUNE_COMPACT_RECORDS = 1u << 1,
+  DSA_PRUNE_ANCHOR_SEEDS = 1u << 2
 };
 typedef struct dsa_prune_opts {
   int32_t num_seeds;

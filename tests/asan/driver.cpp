@@ -83,7 +83,12 @@ int main() {
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_OK);
       po.flags = DSA_PRUNE_START_AT_TAU | DSA_PRUNE_COMPACT_RECORDS;
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_OK);
-      po.flags = 4;
+      po.flags = DSA_PRUNE_ANCHOR_SEEDS;  // 12288 seeds: 6 anchor rows of top-2048
+      EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_OK);
+      po.num_seeds = 1024;  // fewer seeds than topk
+      EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_ERR_INVALID_ARG);
+      po.num_seeds = 0;
+      po.flags = 8;
       EXPECT(dsa_indexer_topk_pruned(&in, 2048, &po, oi, os, &st, ws, pneed, nullptr), DSA_ERR_INVALID_ARG);
       EXPECT(dsa_indexer_workspace_bytes(DSA_OP_TOPK_PRUNED, &in, 2048, &po) == 0 ? 0 : 1, 0);
       po.flags = 0;

@@ -34,6 +34,12 @@ hipError_t launch_seed_prep(const Problem&, int, const int32_t*, int32_t*, int32
   return hipSuccess;
 }
 hipError_t launch_key_norms(const Problem&, float*, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_anchor_rows(const Problem&, int, int32_t*, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_anchor_seeds(const Problem&, int, int, const int32_t*, int, int32_t*, int32_t*, uint32_t*, int32_t*,
+                               hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_seed_pack(const Problem&, const int32_t*, const int32_t*, int, uint8_t*, float*, int32_t*,
                             hipStream_t) {
   ++g_launches;

@@ -220,10 +220,11 @@ def test_bad_flags_are_rejected(lib, flags):
     assert lib.dsa_indexer_last_error()
 
 
-@pytest.mark.parametrize("flags,ok", [(0, True), (1, True), (2, True), (3, True), (4, False), (1 << 31, False)])
+@pytest.mark.parametrize("flags,ok", [(0, True), (1, True), (2, True), (3, True), (4, True), (7, True), (8, False),
+                                      (1 << 31, False)])
 def test_prune_flags(lib, flags, ok):
-    """dsa_prune_opts.flags: DSA_PRUNE_START_AT_TAU and
-    DSA_PRUNE_COMPACT_RECORDS are known; neither changes the workspace."""
+    """dsa_prune_opts.flags: DSA_PRUNE_START_AT_TAU, DSA_PRUNE_COMPACT_RECORDS
+    and DSA_PRUNE_ANCHOR_SEEDS are known; none changes the workspace."""
     import torch
 
     from dsa_lightning_indexer_04_amd import _lib
@@ -436,3 +437,29 @@ def test_mfma_ceiling_arguments(lib, dtype, mode, iters, wg_null):
     assert rc == 1
     assert wg.value == -7
     assert lib.dsa_indexer_last_error()
+
+
+def test_anchor_seed_arguments(lib):
+    """Anchor seeds need num_seeds >= topk and exclude seed_idx, in the C ABI
+    and in the wrapper (which also refuses a raised start with them)."""
+    import torch
+
+    from dsa_lightning_indexer_04_amd import _lib
+
+    inp = _inputs(_lib)
+    A = _lib.DSA_PRUNE_ANCHOR_SEEDS
+    assert lib.dsa_indexer_workspace_bytes(2, ctypes.byref(inp), 16, ctypes.byref(_lib.PruneOpts(16, 0, None, None, A))) > 0
+    assert lib.dsa_indexer_workspace_bytes(2, ctypes.byref(inp), 16, ctypes.byref(_lib.PruneOpts(15, 0, None, None, A))) == 0
+    assert b"num_seeds" in lib.dsa_indexer_last_error()
+    fake = ctypes.c_void_p(FAKE * 4)
+    assert lib.dsa_indexer_workspace_bytes(2, ctypes.byref(inp), 16, ctypes.byref(_lib.PruneOpts(16, 0, fake, None, A))) == 0
+    assert b"seed_idx" in lib.dsa_indexer_last_error()
+    z = [torch.zeros(1)] * 4
+    with pytest.raises(ValueError, match="seeds must be"):
+        _lib.topk_pruned(*z, 16, seeds="history")
+    with pytest.raises(ValueError, match="tau"):
+        _lib.topk_pruned(*z, 16, seeds="anchor", start="raised")
+    with pytest.raises(ValueError, match="seed_idx"):
+        _lib.topk_pruned(*z, 16, seeds="anchor", seed_idx=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="num_seeds"):
+        _lib.topk_pruned(*z, 2048, seeds="anchor", num_seeds=1024)

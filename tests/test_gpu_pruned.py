@@ -6,7 +6,8 @@ and the float64 oracle score; the seed threshold tau equals the K-th best GPU
 score among the row's seeds and never exceeds the row's true K-th score;
 forced recovery and invalid seeds still give the same result; a raised
 start that misses (fewer than K exact scores reach it) recovers the row and
-still gives the same result.
+still gives the same result; with seeds from anchor queries tau is the K-th
+best GPU score among the anchors' Top-K keys the row sees.
 """
 import numpy as np
 import pytest
@@ -107,6 +108,55 @@ def test_pruned_bit_identical_and_bounds(B, Q, N, k, dtype, dist, ns, start, rec
     log(f"  screened {st['screened'].sum()}, survivors {st['survivors'].sum()} "
         f"({100 * (1 - st['survivors'].sum() / max(1, st['screened'].sum())):.1f}% pruned)")
     assert_rows_ok(orc, idx, sc, [(b, t) for b in range(B) for t in range(Q)], k)
+
+
+ANCHOR_CASES = [
+    # B, Q, N, k, dtype, dist, seeds, positions from (fraction of N)
+    (1, 16, 3000, 64, "bf16", "clustered", 256, 0.5),
+    (2, 12, 2500, 100, "fp8", "clustered", 400, 0.5),
+    (1, 24, 6000, 128, "bf16", "iid", 1024, 0.5),
+    (1, 32, 2000, 64, "bf16", "clustered", 192, 0.0),  # early rows see fewer than k seeds
+    (1, 8, 12000, 4096, "bf16", "clustered", 8192, 0.5),  # the largest supported k, 2 anchors
+]
+
+
+@pytest.mark.parametrize("records", ["exact", "compact"])
+@pytest.mark.parametrize("B,Q,N,k,dtype,dist,ns,lo", ANCHOR_CASES)
+def test_anchor_seeds(B, Q, N, k, dtype, dist, ns, lo, records):
+    """Seeds from anchor queries: the pruned set and scores equal the
+    unpruned ones, and each row's tau is the K-th best GPU score among the
+    visible keys of the union of its sequence's anchor rows' Top-K sets
+    (anchor rows floor((2i + 1) Q / (2A)), A = num_seeds // k)."""
+    need_gpu()
+    rng = np.random.default_rng(N + 7)
+    pos = np.sort(rng.integers(int(lo * N), N, size=(B, Q)), axis=1)
+    pos[:, -1] = N - 1
+    d = inputs.make_inputs(B, Q, N, dtype, dist, seed=N + 2 * Q, positions=pos)
+    dd = to_device(d)
+    log(f"anchor seeds B={B} Q={Q} N={N} k={k} {dtype} {dist} seeds={ns} records={records}")
+    args, kw = call_args(dd)
+    idx, sc, st = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, seeds="anchor", records=records, stats=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    st = {n: v.cpu().numpy() for n, v in st.items()}
+    u_idx, u_sc = _unpruned(dd, k)
+    _same_sets(idx, sc, u_idx, u_sc)
+    assert not st["recovered"].any()
+    S = dsa.scores(*args, **kw).cpu().numpy()
+    A = min(Q, max(1, ns // k))
+    anchors = [((2 * i + 1) * Q) // (2 * A) for i in range(A)]
+    assert len(set(anchors)) == A
+    for b in range(B):
+        union = np.unique(np.concatenate([u_idx[b, t][u_idx[b, t] >= 0] for t in anchors]))
+        assert union.size <= ns
+        for t in range(Q):
+            seeds = union[union <= pos[b, t]]
+            if seeds.size >= k:
+                want = np.sort(S[b, t, seeds])[::-1][k - 1]
+                assert st["tau"][b, t] == want, (b, t)
+            else:
+                assert np.isneginf(st["tau"][b, t]), (b, t)
+    log(f"  survivors {st['survivors'].sum()} of {st['screened'].sum()} screened")
+    assert_rows_ok(OracleRows(d), idx, sc, [(b, t) for b in range(B) for t in range(Q)], k)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
