@@ -43,12 +43,12 @@ def _unpruned(wl, args, kw, scores=False):
     return (idx, sc) if scores else idx
 
 
-def _pruned(wl, args, kw, records="exact"):
+def _pruned(wl, args, kw, records="exact", seeds="even"):
     inp = _lib.make_inputs_struct(*args, kw["q_scale"], kw["k_scale"])
-    opts = _lib.PruneOpts(wl.num_seeds, 0, None, None, _lib.PRUNE_RECORDS[records])
+    opts = _lib.PruneOpts(wl.num_seeds, 0, None, None, _lib.PRUNE_RECORDS[records] | _lib.PRUNE_SEEDS[seeds])
     ws = torch.empty(_lib.workspace_bytes(_lib.DSA_OP_TOPK_PRUNED, inp, wl.topk, opts), dtype=torch.uint8,
                      device="cuda")
-    idx, _, st = dsa.topk_pruned(*args, wl.topk, **kw, num_seeds=wl.num_seeds, records=records,
+    idx, _, st = dsa.topk_pruned(*args, wl.topk, **kw, num_seeds=wl.num_seeds, records=records, seeds=seeds,
                                  return_scores=False, workspace=ws, stats=True)
     torch.cuda.synchronize()
     return idx, st
@@ -120,6 +120,11 @@ def test_fullsize_pruned_equals_unpruned(name):
         screened, surv = int(st["screened"].sum().item()), int(st["survivors"].sum().item())
         log(f"  {name} ({records} records): identical sets on all {wl.batch * wl.num_q} rows; "
             f"survivors {surv} of {screened} screened")
+    # seeds from anchor queries (num_seeds / k anchor rows)
+    a_idx, a_st = _pruned(wl, args, kw, "exact", "anchor")
+    assert torch.equal(u_sorted, torch.sort(a_idx, dim=-1).values), "anchor"
+    assert not bool(a_st["recovered"].any().item()), "anchor"
+    log(f"  {name} (anchor seeds): identical sets; survivors {int(a_st['survivors'].sum().item())}")
     # the unpruned rows against the oracle (the pruned sets equal them)
     _check(name, u_idx, u_sc, d, wl, 64)
     # tau <= the row's K-th best score.  The sampled rows' scores come from

@@ -8,7 +8,8 @@ case:
     lexicographic Top-K of the GPU's own scores, then -1 padding;
   * the first rows pass the float64 oracle's acceptance check;
   * the pruned path returns the same index sets as the unpruned path, with
-    either start, either record format and a drawn seed count.
+    either start, either record format and a drawn seed count, and with
+    seeds from 1 to 3 anchor rows.
 """
 import numpy as np
 import pytest
@@ -59,3 +60,7 @@ def test_random_shapes(case):
             pidx, psc, _ = dsa.topk_pruned(*args, k, **kw, num_seeds=ns, start=start, records=records,
                                            return_scores=records == "compact")
             assert np.array_equal(np.sort(pidx.cpu().numpy(), -1), sets["stream"]), (start, records)
+    # seeds from anchor queries (num_seeds a drawn multiple of k: 1 to 3 anchor rows)
+    na = int(rng.integers(1, 4)) * k
+    pidx, _, _ = dsa.topk_pruned(*args, k, **kw, num_seeds=na, seeds="anchor", return_scores=False)
+    assert np.array_equal(np.sort(pidx.cpu().numpy(), -1), sets["stream"]), "anchor"
