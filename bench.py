@@ -282,6 +282,9 @@ def run_workload(name, path, steps, warmup):
         # HBM bytes from stored counter readings, or None (in the pruned path the
         # streaming kernel scores the packed seeds: no reading is stored for that)
         v["traffic_per_launch"] = None if (use_pruned and n == "k_topk_stream") else measured_traffic(name, n)
+        # HBM rate of the kernel's counted traffic over its device time
+        v["hbm_gbs"] = (v["traffic_per_launch"] * v["launches"] / (v["ms"] * 1e-3) / 1e9
+                        if v["traffic_per_launch"] and v["ms"] > 0 else None)
         v["flops"] = work.get(n, 0)
         v["tflops"] = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] > 0 else 0.0
         v["frac"] = v["tflops"] / PEAK_TFLOPS[wl.dtype]
@@ -296,6 +299,9 @@ def run_workload(name, path, steps, warmup):
     res["dominant_flops"] = dv["flops"] / max(dv["launches"], 1e-9)  # per launch
     res["achieved_tflops"] = dv["tflops"]
     res["effective_tflops"] = pairs * PAIR_FLOPS / (res["ms_per_step"] * 1e-3) / 1e12
+    # every visible pair counted at 16,384 FLOP over the whole call's time (for a
+    # pruned call this exceeds the work it executes)
+    res["effective_frac"] = res["effective_tflops"] / PEAK_TFLOPS[wl.dtype]
     peak = PEAK_TFLOPS[wl.dtype]
     if wl.num_q == 1:
         # one query row per sequence (decode): every key row is read once and
@@ -318,7 +324,8 @@ def run_workload(name, path, steps, warmup):
     log(f"[bench] {name} {res['path']}: {res['ms_per_step']:.3f} ms/step, {res['pairs_per_s']:.3e} pairs/s; "
         + ", ".join(f"{n} {v['ms']:.3f} ms" + (f" ({100 * v['frac']:.1f}%)" if v["flops"] else "")
                     for n, v in sorted(per_step.items(), key=lambda kv: -kv[1]["ms"]))
-        + (f"; filter rate {100 * stats['filter_rate']:.1f}%" if stats else ""))
+        + (f"; filter rate {100 * stats['filter_rate']:.1f}%; effective {100 * res['effective_frac']:.1f}% of "
+           f"{wl.dtype} MFMA" if stats else ""))
     del q, k, w, pos, qs, ks, ws
     torch.cuda.empty_cache()
     return res
