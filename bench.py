@@ -48,8 +48,8 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
     ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
     ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
-    ("chunked_prefill_128k", "k_screen"): ("dce06e78e21f85b8", 59868, 12966),
-    ("chunked_prefill_128k", "k_refine"): ("dce06e78e21f85b8", 166099, 34512),
+    ("chunked_prefill_128k", "k_screen"): ("dce06e78e21f85b8", 59864, 12966),
+    ("chunked_prefill_128k", "k_refine"): ("dce06e78e21f85b8", 177568, 37519),
     ("context_1m_fp8", "k_screen"): ("dce06e78e21f85b8", 133928, 65545),
     ("context_1m_fp8", "k_refine"): ("dce06e78e21f85b8", 204732, 35775),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
@@ -87,6 +87,8 @@ def parse():
         "sparse_mla_decode_64x128k:sparse_mla",
         help="comma list of extra workload[:path] runs (or 'none')",
     )
+    ap.add_argument("--num-seeds", type=int, default=0,
+                    help="seeds per sequence of the pruned paths (0: the workload's own count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the oracle sample (at most; see --cpu-seconds)")
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="stop the oracle sample after this much CPU time")
@@ -186,13 +188,17 @@ def sustained_rates(dtype, launches=5, warmup=2):
     return res
 
 
-def run_workload(name, path, steps, warmup):
+def run_workload(name, path, steps, warmup, num_seeds=0):
+    import dataclasses
+
     import torch
 
     import dsa_lightning_indexer_04_amd as dsa
     from dsa_lightning_indexer_04_amd import _lib, inputs
 
     wl = inputs.WORKLOADS[name]
+    if num_seeds:  # a seed count other than the workload's (pruned paths)
+        wl = dataclasses.replace(wl, num_seeds=num_seeds)
     t0 = time.time()
     d = inputs.make_workload(wl)
     log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
@@ -566,7 +572,7 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     from dsa_lightning_indexer_04_amd import inputs
 
-    main_res = run_workload(args.workload, args.path, args.steps, args.warmup)
+    main_res = run_workload(args.workload, args.path, args.steps, args.warmup, args.num_seeds)
     extra = {}
     if args.also and args.also != "none":
         for item in args.also.split(","):
@@ -579,7 +585,8 @@ def main():
             if name in MLA_WORKLOADS:
                 extra[item] = run_sparse_mla(name, max(3, args.steps // 2), max(1, args.warmup // 2))
                 continue
-            extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2))
+            extra[item] = run_workload(name, pth or args.path, max(3, args.steps // 2), max(1, args.warmup // 2),
+                                       args.num_seeds)
     for wname in {args.workload} | {k.partition(":")[0] for k in extra}:
         runs = [r for r in [main_res, *extra.values()]
                 if r["workload"] == wname and r["path"] not in ("project", "sparse_mla")]
