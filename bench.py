@@ -57,6 +57,7 @@ MEASURED_KIB = {
     ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
 }
 PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
+PAGES_SEEDS = 12288  # the pages' seed count (the library's default)
 SCREEN_FLOPS = 2 * 128 * 32  # 32-row bound (30 retained heads, aux row, linear row) of one pair
 
 
@@ -73,9 +74,9 @@ def parse():
     ap.add_argument("--path", choices=["auto", "topk", "pruned", "pruned_tau", "pruned_compact", "pruned_anchor"],
                     default="topk",
                     help="exact Top-K route of the main line (auto: pruned where the workload is a pruning one; "
-                    "pruned_tau: the pruned path with every row's threshold starting at tau; pruned_compact: "
-                    "the pruned path with 32-bit candidate records; pruned_anchor: the pruned path with seeds from "
-                    "anchor queries, starting at tau)")
+                    "pruned_tau: the pruned path with every row's threshold starting at tau (12288 seeds); "
+                    "pruned_compact: the pruned path with 32-bit candidate records; pruned_anchor: the pruned path "
+                    "with seeds from anchor queries (12288 seeds: 6 anchor rows), starting at tau)")
     ap.add_argument(
         "--also",
         default="chunked_prefill_128k:pruned,chunked_prefill_128k:pruned_tau,chunked_prefill_128k:pruned_compact,"
@@ -199,6 +200,11 @@ def run_workload(name, path, steps, warmup, num_seeds=0):
     wl = inputs.WORKLOADS[name]
     if num_seeds:  # a seed count other than the workload's (pruned paths)
         wl = dataclasses.replace(wl, num_seeds=num_seeds)
+    elif path in ("pruned_tau", "pruned_anchor"):
+        # the pages' start (tau) and the anchor seeds take the pages' seed
+        # count: tau is the K-th best seed score, so it needs seeds well
+        # beyond K, which the raised start does not
+        wl = dataclasses.replace(wl, num_seeds=PAGES_SEEDS)
     t0 = time.time()
     d = inputs.make_workload(wl)
     log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
