@@ -7,6 +7,10 @@
  * for those events and reports, per kernel name, the number of launches and
  * their mean duration.  Outside a window the library records no events.
  *
+ * The events come from a pool that opening a window tops up to 1024 pairs
+ * (on the current device; the pool is rebuilt when the device changes), so
+ * a window of up to 1024 launches creates no events while it is open.
+ *
  * Not thread-safe: open, run and close a window from one host thread.
  */
 #ifndef DSA_INDEXER_PROFILE_H_
