@@ -164,7 +164,10 @@ def sustained_rates(dtype, launches=5, warmup=2):
     32-key block step on synthetic full-entropy operands in registers and LDS,
     without memory traffic or candidate bookkeeping, long enough (about 10 ms
     a launch) for the clock to settle.  mode 0: MFMAs and fragment reloads
-    only; mode 1: with the ReLU-weighted head sum and the combine."""
+    only; mode 1: with the ReLU-weighted head sum and the combine; mode 2
+    (bf16): the head sum as (w/2)(x + |x|), one abs-FMA per head and key plus
+    the linear term on 8 more 16x16x32 MFMAs per 32 keys (rate over the same
+    64-head FLOPs)."""
     import torch
     from dsa_lightning_indexer_04_amd import _lib
 
@@ -173,7 +176,8 @@ def sustained_rates(dtype, launches=5, warmup=2):
     out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
     flops = wg * 4 * iters * 2 * 64 * 32 * 128
     res = {"unit": "TFLOP/s", "workgroups": wg, "flops_per_launch": flops}
-    for mode, key in ((0, "mfma_only"), (1, "score_step")):
+    modes = ((0, "mfma_only"), (1, "score_step")) + (((2, "score_step_abs_form"),) if dtype == "bf16" else ())
+    for mode, key in modes:
         for _ in range(warmup):
             _lib.mfma_ceiling(dtype, mode, iters, out)
         torch.cuda.synchronize()
@@ -564,8 +568,9 @@ def main():
     if args.sustained_only:
         res = {dt: sustained_rates(dt) for dt in ("bf16", "fp8")}
         for dt, r in res.items():
-            r["mfma_only_frac"] = r["mfma_only"] / PEAK_TFLOPS[dt]
-            r["score_step_frac"] = r["score_step"] / PEAK_TFLOPS[dt]
+            for key in ("mfma_only", "score_step", "score_step_abs_form"):
+                if key in r:
+                    r[key + "_frac"] = r[key] / PEAK_TFLOPS[dt]
         print(json.dumps({"sustained_mfma": res}), flush=True)
         return
     if args.gpus != 1:
@@ -625,7 +630,9 @@ def main():
     for dt, r in sustained.items():
         log(f"[bench] sustained {dt}: MFMA only {r['mfma_only']:.0f} TFLOP/s "
             f"({100 * r['mfma_only'] / PEAK_TFLOPS[dt]:.1f}% of nominal), score step {r['score_step']:.0f} TFLOP/s "
-            f"({100 * r['score_step'] / PEAK_TFLOPS[dt]:.1f}% of nominal)")
+            f"({100 * r['score_step'] / PEAK_TFLOPS[dt]:.1f}% of nominal)"
+            + (f", |x| form {r['score_step_abs_form']:.0f} TFLOP/s "
+               f"({100 * r['score_step_abs_form'] / PEAK_TFLOPS[dt]:.1f}%)" if "score_step_abs_form" in r else ""))
     cpu, cpu_more = None, {}
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores ...")

@@ -643,7 +643,8 @@ int dsa_indexer_mfma_ceiling(int32_t dtype, int32_t mode, int32_t iters, float* 
                              int32_t* workgroups) {
   if (!workgroups) return fail(DSA_ERR_INVALID_ARG, "workgroups must not be NULL");
   if (dtype != DSA_BF16 && dtype != DSA_FP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "unknown dtype");
-  if (mode != 0 && mode != 1) return fail(DSA_ERR_INVALID_ARG, "mode must be 0 or 1");
+  if (mode < 0 || mode > 2) return fail(DSA_ERR_INVALID_ARG, "mode must be 0, 1 or 2");
+  if (mode == 2 && dtype != DSA_BF16) return fail(DSA_ERR_INVALID_ARG, "mode 2 is bf16 only");
   if (iters < 2 || (iters & 1)) return fail(DSA_ERR_INVALID_ARG, "iters must be even and >= 2");
   const int wg = dsa::mfma_ceiling_workgroups();
   if (wg < 1) return fail(DSA_ERR_HIP, "device query failed");

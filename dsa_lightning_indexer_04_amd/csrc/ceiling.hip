@@ -14,7 +14,13 @@
 //   mode 0: the MFMAs and key-fragment reloads alone (accumulators chained);
 //   mode 1: mode 0 plus the ReLU-weighted head sum and the cross-half
 //           combine of every block, i.e. the streaming kernel's block step
-//           without candidate appends, tile loads or barriers.
+//           without candidate appends, tile loads or barriers;
+//   mode 2 (bf16): the step in the form w ReLU(x) = (w/2)(x + |x|): one FMA
+//           with an absolute-value source per head and key, plus the linear
+//           term u . k (u = sum_j (w_j/2) q_j as high and low bf16 rows) on
+//           a 16-row block, 8 more 16x16x32 MFMAs per 32 keys, its key
+//           fragments read from the same tile and its sums moved to the
+//           score's lanes by two LDS permutes.
 // Work per launch: workgroups x 4 waves x iters blocks x 2*64*32*128 FLOP.
 #include "kernels.h"
 #include "stream_common.h"
@@ -96,6 +102,14 @@ __global__ __launch_bounds__(kCeilWaves * 64) __attribute__((amdgpu_waves_per_eu
   f32x16 acc[2][2];
   acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = zero16();
   float tot = 0.0f;
+  // mode 2: the linear row's A operand (rows 0, 1 of a 16-row block; lane l
+  // holds row l % 16, dims 8 (l / 16) .. + 8 of each 32-dim k-step)
+  bf16x8 ua[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 v = (lane & 15) < 2 ? synth16<kBF16>(wseed + 0x777u + (uint32_t)(ks * 64 + lane)) : u32x4{0u, 0u, 0u, 0u};
+    ua[ks] = __builtin_bit_cast(bf16x8, v);
+  }
   for (int it = 0; it + 1 < iters; it += 2) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -107,6 +121,51 @@ __global__ __launch_bounds__(kCeilWaves * 64) __attribute__((amdgpu_waves_per_eu
           acc[sub][1] = mma_step<DT>(qs.a[1], f, i, acc[sub][1]);
           Tile::frag_step(f, tile, nkey, i, lane);
         }
+      } else if constexpr (MODE == 2) {
+        // the |x| form: 16 MFMAs interleaved with one abs-FMA per head and
+        // key of the previous block, then the linear row of this block
+        const f32x16& p0 = acc[sub ^ 1][0];
+        const f32x16& p1 = acc[sub ^ 1][1];
+        acc[sub][0] = zero16();
+        acc[sub][1] = zero16();
+        float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 2 * Frag<DT>::kSteps; ++m) {
+          if ((m & 1) == 0) {
+            acc[sub][0] = mma_step<DT>(qs.a[0], f, m >> 1, acc[sub][0]);
+          } else {
+            acc[sub][1] = mma_step<DT>(qs.a[1], f, m >> 1, acc[sub][1]);
+            Tile::frag_step(f, tile, nkey, m >> 1, lane);
+          }
+#pragma unroll
+          for (int u = 2 * m; u < 2 * m + 2; ++u) {
+            const int e = u >> 2, g = u & 3;
+            const float x = e < 4 ? p0[4 * g + e] : p1[4 * g + e - 4];
+            const float wv = e < 4 ? qs.wl[0][4 * g + e] : qs.wl[1][4 * g + e - 4];
+            c[g] = __builtin_fmaf(__builtin_fabsf(x), wv, c[g]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (m & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        // the linear row: keys 16 h + l % 16 of this block, dims 32 ks + 8 (l / 16)
+        const int kb = 32 * (sub & 1);
+        f32x4 lin[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          lin[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 kf = tile[(kb + 16 * h + (lane & 15)) * (CPR + 1) + 4 * ks + (lane >> 4)];
+            lin[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[ks], __builtin_bit_cast(bf16x8, kf), lin[h], 0, 0, 0);
+          }
+        }
+        // rows 0 and 1 (lanes 0..15, v = 0, 1) to the lanes of key l % 32
+        const float l0 = lin[0][0] + lin[0][1], l1 = lin[1][0] + lin[1][1];
+        const int src = lane & 15;
+        const float a0 = __shfl(l0, src, 64), a1 = __shfl(l1, src, 64);
+        const float lk_term = (lane & 16) ? a1 : a0;
+        tot += combine_single((c[0] + c[1]) + (c[2] + c[3])) + lk_term;
       } else {
         tot += combine_single(pipelined_partial<DT>(qs, f, acc[sub ^ 1][0], acc[sub ^ 1][1], acc[sub][0],
                                                     acc[sub][1],
@@ -134,8 +193,10 @@ hipError_t launch_mfma_ceiling(int dtype, int mode, int iters, int workgroups, f
   if (dtype == kBF16) {
     if (mode == 0)
       hipLaunchKernelGGL((k_mfma_ceiling<kBF16, 0>), grid, block, 0, st, out, iters);
-    else
+    else if (mode == 1)
       hipLaunchKernelGGL((k_mfma_ceiling<kBF16, 1>), grid, block, 0, st, out, iters);
+    else
+      hipLaunchKernelGGL((k_mfma_ceiling<kBF16, 2>), grid, block, 0, st, out, iters);
   } else {
     if (mode == 0)
       hipLaunchKernelGGL((k_mfma_ceiling<kFP8, 0>), grid, block, 0, st, out, iters);

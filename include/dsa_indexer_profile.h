@@ -42,7 +42,10 @@ int dsa_indexer_profile_end(const char** names, int32_t* launches, double* mean_
  * dtype: DSA_BF16 or DSA_FP8_E4M3 of dsa_indexer.h (full-entropy codes).  mode 0: the MFMAs and
  * key-fragment LDS reads alone; mode 1: also the ReLU-weighted head sum and
  * the cross-half combine of every 32-key block, as the streaming Top-K issues
- * them.  The launch has *workgroups (two per compute unit of the current
+ * them; mode 2 (bf16 only): the head sum in the form (w/2)(x + |x|), one FMA
+ * with an absolute-value source per head and key, plus the linear term on a
+ * 16-row MFMA block (8 more 16x16x32 MFMAs per 32 keys; its FLOPs are not
+ * counted below).  The launch has *workgroups (two per compute unit of the current
  * device) workgroups of four waves; each wave scores `iters` (even, >= 2)
  * blocks of 32 keys against 64 heads x 128 dims, so a launch does
  * (*workgroups) * 4 * iters * 2 * 64 * 32 * 128 MFMA FLOP.  The caller times
@@ -51,8 +54,8 @@ int dsa_indexer_profile_end(const char** names, int32_t* launches, double* mean_
  * out: device buffer of out_len floats, at least (*workgroups) * 256 (per-lane
  * sinks that keep the work live; contents unspecified), or NULL to report
  * *workgroups only, launching nothing.  workgroups must not be NULL.
- * Returns 0 or a DSA_ERR_* code of dsa_indexer.h: DSA_ERR_INVALID_ARG (dtype, mode or iters out of range, out_len
- * too small, workgroups NULL); DSA_ERR_HIP (device query or launch failed). */
+ * Returns 0 or a DSA_ERR_* code of dsa_indexer.h: DSA_ERR_INVALID_ARG (dtype, mode or iters out of range, mode 2
+ * with fp8, out_len too small, workgroups NULL); DSA_ERR_HIP (device query or launch failed). */
 int dsa_indexer_mfma_ceiling(int32_t dtype, int32_t mode, int32_t iters, float* out, size_t out_len, void* stream,
                              int32_t* workgroups);
 

@@ -425,7 +425,8 @@ def test_noalloc_rejects_calls_beyond_the_fixed_scratch(lib):
 
 @pytest.mark.parametrize("dtype,mode,iters,wg_null", [
     (2, 0, 16, False),   # unknown dtype
-    (0, 2, 16, False),   # unknown mode
+    (0, 3, 16, False),   # unknown mode
+    (1, 2, 16, False),   # the |x| form is bf16 only
     (0, 1, 15, False),   # odd iteration count
     (1, 0, 0, False),    # no iterations
     (0, 0, 16, True),    # nowhere to report the workgroup count
