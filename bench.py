@@ -53,8 +53,8 @@ MEASURED_KIB = {
     ("context_1m_fp8", "k_screen"): ("dce06e78e21f85b8", 133928, 65545),
     ("context_1m_fp8", "k_refine"): ("dce06e78e21f85b8", 204732, 35775),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
-    ("projection_prefill_128k", "k_proj_out"): ("61f24b18bb20f769", 1073178, 553001),
-    ("sparse_mla_128k", "k_sparse_mla"): ("ac0750a9ce4545fc", 6478318, 1127364),
+    ("projection_prefill_128k", "k_proj_out"): ("c339d5bbec5abf88", 1073178, 553000),
+    ("sparse_mla_128k", "k_sparse_mla"): ("2d225659671baf9a", 6519512, 1126288),
 }
 PAIR_FLOPS = 2 * 64 * 128  # full 64-head score of one pair
 PAGES_SEEDS = 12288  # the pages' seed count (the library's default)
