@@ -45,9 +45,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB), mean per dispatch
-    ("chunked_prefill_128k", "k_topk_stream"): ("22429f79feba56de", 2243960, 1313016),
-    ("context_1m_fp8", "k_topk_stream"): ("22429f79feba56de", 10365071, 3438020),
-    ("prefill_32k", "k_topk_stream"): ("22429f79feba56de", 4780953, 2843980),
+    ("chunked_prefill_128k", "k_topk_stream"): ("00b64abedb47a724", 2357158, 1326540),
+    ("context_1m_fp8", "k_topk_stream"): ("00b64abedb47a724", 10711910, 3489157),
+    ("prefill_32k", "k_topk_stream"): ("00b64abedb47a724", 5129468, 2897950),
     ("chunked_prefill_128k", "k_screen"): ("dce06e78e21f85b8", 59864, 12966),
     ("chunked_prefill_128k", "k_refine"): ("dce06e78e21f85b8", 177568, 37519),
     ("context_1m_fp8", "k_screen"): ("dce06e78e21f85b8", 133928, 65545),

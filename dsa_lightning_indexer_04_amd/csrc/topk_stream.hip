@@ -5,7 +5,7 @@
 // "Full-prefix index scoring"); this kernel does that without ever storing
 // the score matrix.  Each row keeps a running threshold and a candidate
 // buffer of records in global memory; a key is appended only if its record
-// is not below the threshold.  Every 32 kept records the threshold rises to
+// is not below the threshold.  Every 256 kept records the threshold rises to
 // within one bin of the K-th best record seen, read off a per-row histogram
 // of the kept score codes; when the buffer fills it is compacted to the
 // records above the threshold and, if still too full, cut by radix select.
@@ -37,6 +37,11 @@ namespace dsa {
 constexpr int kWaves = 4;           // query rows per workgroup, one per wave (two workgroups per CU)
 constexpr int kTileBytes = 16384;   // key bytes of one LDS tile: 64 bf16 or 128 fp8 keys
 constexpr int kSlots = 3;           // LDS key-tile slots
+// Kept records between threshold raises.  A raise is a wave-wide prefix sum
+// over the histogram; early in a row, when most keys are kept, raising every
+// 256 records instead of every 32 lets the threshold lag a little but costs
+// far fewer raises (the prefill blocks ran 1-3% faster).
+constexpr int kStreamRaiseEvery = 256;
 
 template <int DT>
 struct BlockAcc {
@@ -69,7 +74,7 @@ __device__ __forceinline__ void append_pair(RowState& rs, float thr_f, float s, 
 // Tile-boundary bookkeeping of a row: count the staged records in the
 // threshold histogram (here, where no key-tile load is in flight, rather than
 // at each append) and flush them to the buffer; every
-// kRaiseEvery kept records raise the threshold from the histogram (to within
+// kStreamRaiseEvery kept records raise the threshold from the histogram (to within
 // one bin of the K-th best record seen, no buffer traffic); if `room` more
 // records could overflow the buffer, rebuild: keep the records >= thr, cut
 // them by radix select when too many remain, and rebuild the histogram with
@@ -81,13 +86,14 @@ __device__ __forceinline__ void tile_bookkeeping(RowState& rs, float& thr_f, uin
     rs.cnt = flush_stage(rs.buf, rs.cnt, stage, rs.nst, lane);
     rs.nst = 0;
   }
-  if (rs.added >= kRaiseEvery) {
+  if (rs.added >= kStreamRaiseEvery) {
     raise_threshold(rs, hist, topk, lane);
     thr_f = record_floor(rs.thr);
   }
   if (rs.cnt > cap - room) {
     apply_rebuild(rs, rebuild_candidates(rs.buf, rs.cnt, stage, 0, hist, rs.thr, topk, cut_goal(topk, cap), lane));
     thr_f = record_floor(rs.thr);
+    rs.added = kStreamRaiseEvery;  // raise from the refitted bins at the next tile
   }
 }
 
