@@ -48,10 +48,10 @@ MEASURED_KIB = {
     ("chunked_prefill_128k", "k_topk_stream"): ("00b64abedb47a724", 2357158, 1326540),
     ("context_1m_fp8", "k_topk_stream"): ("00b64abedb47a724", 10711910, 3489157),
     ("prefill_32k", "k_topk_stream"): ("00b64abedb47a724", 5129468, 2897950),
-    ("chunked_prefill_128k", "k_screen"): ("9a5bf5dd396267f1", 59861, 12967),
-    ("chunked_prefill_128k", "k_refine"): ("9a5bf5dd396267f1", 177527, 37517),
-    ("context_1m_fp8", "k_screen"): ("9a5bf5dd396267f1", 134086, 65545),
-    ("context_1m_fp8", "k_refine"): ("9a5bf5dd396267f1", 205144, 35770),
+    ("chunked_prefill_128k", "k_screen"): ("3877989fe06155ea", 59857, 12966),
+    ("chunked_prefill_128k", "k_refine"): ("3877989fe06155ea", 177539, 37512),
+    ("context_1m_fp8", "k_screen"): ("3877989fe06155ea", 134041, 65545),
+    ("context_1m_fp8", "k_refine"): ("3877989fe06155ea", 205164, 35769),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
     ("projection_prefill_128k", "k_proj_out"): ("c339d5bbec5abf88", 1073178, 553000),
     ("sparse_mla_128k", "k_sparse_mla"): ("2d225659671baf9a", 6519512, 1126288),
