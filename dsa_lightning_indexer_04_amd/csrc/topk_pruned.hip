@@ -722,8 +722,6 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
         g += kGroupWords;
       }
     };
-    // exact scores of a batch (lane l % 32: key `key`, fragment f) go to the
-    // candidates if their records reach the threshold
     // fp8 has the registers to hold the row's head weights for the whole
     // scan; bf16 would spill, so it reads them from LDS at the start of each
     // batch, ahead of its MFMAs.  Either way the weight reads stay off the
@@ -734,6 +732,8 @@ __global__ __launch_bounds__(kRefineWaves * 64) __attribute__((amdgpu_waves_per_
       wave_lds_sync();
       load_wl(wl, my_w, lane);
     }
+    // exact scores of a batch (lane l % 32: key `key`, fragment f) go to the
+    // candidates if their records reach the threshold
     auto score_and_keep = [&](const Frag<DT>& f, int key, float ks, bool live) {
       float s;
       if constexpr (DT == kFP8) {
