@@ -59,22 +59,26 @@ static __device__ __noinline__ void emit_topk_d8(uint64_t* buf, int cnt, const u
   SelectResult sel = {0, 0, 0};
   if (need > 0) sel = select_records_d8(buf, cnt, (uint32_t)need, hist, true, 0, lane);
   int base = 0;
-  for (int i0 = 0; i0 < cnt; i0 += 64) {
-    const int i = i0 + lane;
-    uint64_t r = 0;
-    bool keep = false;
-    if (i < cnt) {
-      r = buf[i];
-      keep = (r & sel.mask) >= sel.prefix;
+  for (int i0 = 0; i0 < cnt; i0 += 512) {  // eight records per lane in flight
+    uint64_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      r[j] = i < cnt ? buf[i] : 0;
     }
-    const uint64_t bal = __ballot(keep);
-    const uint32_t before =
-        __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (keep) {
-      oi[base + before] = (int32_t)record_key(r);
-      if (os) os[base + before] = record_score(r);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      const bool keep = i < cnt && (r[j] & sel.mask) >= sel.prefix;
+      const uint64_t bal = __ballot(keep);
+      const uint32_t before =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep) {
+        oi[base + before] = (int32_t)record_key(r[j]);
+        if (os) os[base + before] = record_score(r[j]);
+      }
+      base += __popcll(bal);
     }
-    base += __popcll(bal);
   }
   for (int j = need + lane; j < topk; j += 64) {
     oi[j] = -1;
