@@ -47,13 +47,14 @@ class OracleRows:
         self.ks = None if d["k_scale"] is None else d["k_scale"].numpy()
         self.N = self.kbits.shape[1]
         self._kf = {}
+        self._k8 = {}
 
     def keys(self, b: int) -> np.ndarray:
         if b not in self._kf:
             if self.dtype == "bf16":
                 self._kf[b] = indexer.decode_bf16(self.kbits[b])
             else:
-                self._kf[b] = indexer.decode_e4m3fn(self.kbits[b]) * self.ks[b].astype(np.float64)[:, None]
+                self._kf[b] = self.codes(b) * self.ks[b].astype(np.float64)[:, None]
         return self._kf[b]
 
     def visible(self, b: int, t: int) -> int:
@@ -68,16 +69,24 @@ class OracleRows:
             q = indexer.decode_e4m3fn(self.qbits[b, t]) * float(self.qs[b, t])
         return indexer.index_score_row(q, self.keys(b)[:v], self.w[b, t])
 
-    def bound(self, b: int, t: int) -> np.ndarray:
+    def codes(self, b: int) -> np.ndarray:
+        """e4m3 code values of sequence b's keys (fp8 inputs), decoded once."""
+        if b not in self._k8:
+            self._k8[b] = indexer.decode_e4m3fn(self.kbits[b])
+        return self._k8[b]
+
+    def bound(self, b: int, t: int, keys=None) -> np.ndarray:
         """fp32 evaluation error bound of row (b, t)'s visible scores
-        (oracle.indexer.score_error_bound_row; fp8 in code units, scaled)."""
+        (oracle.indexer.score_error_bound_row; fp8 in code units, scaled),
+        or of the visible keys ``keys`` only (the bound is per key)."""
         v = self.visible(b, t)
+        sel = np.arange(v) if keys is None else np.asarray(keys, np.int64)
+        assert sel.size == 0 or (sel.min() >= 0 and sel.max() < v)
         if self.dtype == "bf16":
-            return indexer.score_error_bound_row(indexer.decode_bf16(self.qbits[b, t]), self.keys(b)[:v], self.w[b, t])
-        k8 = indexer.decode_e4m3fn(self.kbits[b, :v])
+            return indexer.score_error_bound_row(indexer.decode_bf16(self.qbits[b, t]), self.keys(b)[sel], self.w[b, t])
         q8 = indexer.decode_e4m3fn(self.qbits[b, t])
-        scale = np.float64(np.float32(self.qs[b, t])) * self.ks[b, :v].astype(np.float64)
-        return indexer.score_error_bound_row(q8, k8, self.w[b, t], scale=scale)
+        scale = np.float64(np.float32(self.qs[b, t])) * self.ks[b, sel].astype(np.float64)
+        return indexer.score_error_bound_row(q8, self.codes(b)[sel], self.w[b, t], scale=scale)
 
 
 def tol(dtype: str):
@@ -104,7 +113,7 @@ def assert_within_bound(orc: OracleRows, b: int, t: int, idx_row, sc_row, ref=No
     keys = np.asarray(idx_row)[valid].astype(np.int64)
     if keys.size == 0:
         return
-    bnd = orc.bound(b, t)[keys]
+    bnd = orc.bound(b, t, keys)
     err = np.abs(np.asarray(sc_row, np.float64)[valid] - ref[keys])
     ok = err <= bnd + 1e-12 * np.abs(ref[keys])
     assert ok.all(), f"row ({b},{t}): {int((~ok).sum())} scores outside the fp32 bound, worst err/bound " \
