@@ -45,13 +45,13 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 FETCH_SCALE, WRITE_SCALE = 2.000, 1.000
 MEASURED_KIB = {
     # (workload, kernel): (source digest, FETCH_SIZE KiB, WRITE_SIZE KiB), mean per dispatch
-    ("chunked_prefill_128k", "k_topk_stream"): ("00b64abedb47a724", 2357158, 1326540),
-    ("context_1m_fp8", "k_topk_stream"): ("00b64abedb47a724", 10711910, 3489157),
-    ("prefill_32k", "k_topk_stream"): ("00b64abedb47a724", 5129468, 2897950),
-    ("chunked_prefill_128k", "k_screen"): ("3877989fe06155ea", 59857, 12966),
-    ("chunked_prefill_128k", "k_refine"): ("3877989fe06155ea", 177539, 37512),
-    ("context_1m_fp8", "k_screen"): ("3877989fe06155ea", 134041, 65545),
-    ("context_1m_fp8", "k_refine"): ("3877989fe06155ea", 205164, 35769),
+    ("chunked_prefill_128k", "k_topk_stream"): ("ed5c0288e30347f3", 2356716, 1326594),
+    ("context_1m_fp8", "k_topk_stream"): ("ed5c0288e30347f3", 10755417, 3490426),
+    ("prefill_32k", "k_topk_stream"): ("ed5c0288e30347f3", 5149960, 2898887),
+    ("chunked_prefill_128k", "k_screen"): ("d2a4107fa2b71100", 59863, 12966),
+    ("chunked_prefill_128k", "k_refine"): ("d2a4107fa2b71100", 178890, 37518),
+    ("context_1m_fp8", "k_screen"): ("d2a4107fa2b71100", 133744, 65544),
+    ("context_1m_fp8", "k_refine"): ("d2a4107fa2b71100", 206915, 35770),
     ("decode_64x128k", "k_scores"): ("08c4ecbd515913c3", 1067502, 33264),
     ("projection_prefill_128k", "k_proj_out"): ("c339d5bbec5abf88", 1073178, 553000),
     ("sparse_mla_128k", "k_sparse_mla"): ("2d225659671baf9a", 6519512, 1126288),
