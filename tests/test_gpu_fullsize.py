@@ -9,6 +9,9 @@ output).  Then:
     returned scores lie within the fp32 evaluation bound of the oracle's;
   * the number of selected indices equals the closed form: the sum over rows
     of min(k, visible), i.e. N_sel of the FLOPs notes for a full prefill;
+  * on 6 sampled rows of every workload, the returned set is exactly the
+    Top-K (score descending, then index ascending) of the GPU's own scores
+    of that row, from the score entry point (the same score routine);
   * for the 128K and 1M blocks, the pruned path returns the same index set as
     the unpruned path on every row, recovers no row, and its tau never
     exceeds the row's K-th score (on the sampled rows).
@@ -19,7 +22,7 @@ import torch
 
 import dsa_lightning_indexer_04_amd as dsa
 from dsa_lightning_indexer_04_amd import _lib, inputs
-from helpers import OracleRows, assert_rows_ok, log, need_gpu
+from helpers import OracleRows, assert_rows_ok, lexsort_topk_of_scores, log, need_gpu
 from oracle import counts
 
 pytestmark = pytest.mark.gpu
@@ -87,6 +90,31 @@ def _check(name, idx, sc, d, wl, n_rows, n_short=0):
     assert_rows_ok(OracleRows(d), idx.cpu().numpy(), None if sc is None else sc.cpu().numpy(), rows, wl.topk)
 
 
+def _row_scores(args, kw, b, t):
+    """The GPU's scores of row (b, t) from the score entry point on one-row
+    slices of the inputs (clone(): fresh, aligned copies; a slice keeps its
+    offset)."""
+    q, k, w, pos = args
+    sub = (q[b:b + 1, t:t + 1].clone(), k[b:b + 1], w[b:b + 1, t:t + 1].clone(), pos[b:b + 1, t:t + 1].clone())
+    skw = dict(q_scale=None if kw["q_scale"] is None else kw["q_scale"][b:b + 1, t:t + 1].clone(),
+               k_scale=None if kw["k_scale"] is None else kw["k_scale"][b:b + 1])
+    return dsa.scores(*sub, **skw)[0, 0]
+
+
+def _check_exact(name, wl, args, kw, idx, n_rows=6):
+    """Sampled rows: the returned set equals the exact Top-K of the GPU's own
+    scores of the row (a total order, so the set is unique)."""
+    pos = args[3]
+    for b, t in _sample_rows(wl, n_rows):
+        vis = max(0, min(int(pos[b, t].item()) + 1, wl.num_k))
+        S = _row_scores(args, kw, b, t).cpu().numpy()
+        want = lexsort_topk_of_scores(S, vis, wl.topk)
+        got = np.sort(idx[b, t].cpu().numpy())
+        got = got[got >= 0]
+        assert np.array_equal(got, want), (name, b, t)
+    log(f"  {name}: {n_rows} rows exactly the Top-K of the GPU's own scores")
+
+
 def test_fullsize_prefill_32k():
     need_gpu()
     wl, d, args, kw = _device_inputs("prefill_32k")
@@ -94,6 +122,7 @@ def test_fullsize_prefill_32k():
     log("prefill_32k: unpruned Top-K at full size")
     idx, sc = _unpruned(wl, args, kw, scores=True)
     _check("prefill_32k", idx, sc, d, wl, 64, n_short=16)
+    _check_exact("prefill_32k", wl, args, kw, idx)
 
 
 def test_fullsize_decode_64x128k():
@@ -102,6 +131,7 @@ def test_fullsize_decode_64x128k():
     log("decode_64x128k: Top-K at full size")
     idx, sc = _unpruned(wl, args, kw, scores=True)
     _check("decode_64x128k", idx, sc, d, wl, 64)
+    _check_exact("decode_64x128k", wl, args, kw, idx)
 
 
 @pytest.mark.parametrize("name", ["chunked_prefill_128k", "context_1m_fp8"])
@@ -127,17 +157,11 @@ def test_fullsize_pruned_equals_unpruned(name):
     log(f"  {name} (anchor seeds): identical sets; survivors {int(a_st['survivors'].sum().item())}")
     # the unpruned rows against the oracle (the pruned sets equal them)
     _check(name, u_idx, u_sc, d, wl, 64)
-    # tau <= the row's K-th best score.  The sampled rows' scores come from
-    # the score entry point on one-row slices of the inputs (the same score
-    # routine as the Top-K paths, so bit-identical); the K-th best is the
-    # lowest score in the returned exact set.
-    q, k, w, pos = args
+    # the returned set is exactly the Top-K of the GPU's own row scores, and
+    # tau <= the row's K-th best score (the lowest score in that set)
+    _check_exact(name, wl, args, kw, u_idx)
     tau = st["tau"].cpu().numpy()
     for b, t in _sample_rows(wl, 6):
-        # clone(): fresh, aligned one-row copies (a slice keeps its offset)
-        sub = (q[b:b + 1, t:t + 1].clone(), k[b:b + 1], w[b:b + 1, t:t + 1].clone(), pos[b:b + 1, t:t + 1].clone())
-        skw = dict(q_scale=None if kw["q_scale"] is None else kw["q_scale"][b:b + 1, t:t + 1].clone(),
-                   k_scale=None if kw["k_scale"] is None else kw["k_scale"][b:b + 1])
-        S = dsa.scores(*sub, **skw)[0, 0]
+        S = _row_scores(args, kw, b, t)
         kth = S[p_idx[b, t].long()].min().item()
         assert tau[b, t] <= kth, (b, t, tau[b, t], kth)
